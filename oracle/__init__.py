@@ -1,0 +1,228 @@
+"""fp64 CPU oracle for block-sparse attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package.  The GPU library never imports, links or calls
+it, and this package never imports the GPU library.
+
+The arithmetic lives in ``bsa_oracle.c`` (plain C, fp64, OpenMP over
+independent outputs); this module only marshals numpy arrays.  The shared
+library is compiled with gcc on first use (or by ``build()``).
+
+Every function follows the definitions stated in ``bsa_oracle.c``:
+  pool_mean               mean of each block's rows
+  scores_meanpool_proj    S_ij = (W^T qbar_i) . (W^T kbar_j)
+  scores_exact_avgpool    S_ij = block-average of softmax(scale * Q K^T)
+  select_rows / select    text rows dense, text columns forced, top-k per
+                          column group with lower-index tie-break
+  arrow                   closed-form arrow / full / skip layout
+  forward                 dense softmax restricted to the kept blocks
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+import threading
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bsa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+HEAD_FULL, HEAD_ARROW, HEAD_SKIP = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, -O2, OpenMP).  Returns the .so path."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        D = ctypes.c_double
+        lib.oracle_pool_mean.argtypes = [P, I, I, I, I, I, P]
+        lib.oracle_pool_mean.restype = ctypes.c_int
+        lib.oracle_scores_meanpool_proj.argtypes = [P, P, I, I, I, I, I, P, I, P]
+        lib.oracle_scores_meanpool_proj.restype = ctypes.c_int
+        lib.oracle_scores_exact_avgpool.argtypes = [P, P, I, I, I, I, I, D, P, I, P]
+        lib.oracle_scores_exact_avgpool.restype = ctypes.c_int
+        lib.oracle_select_rows.argtypes = [P, P, I, I, I, P, I, P, P, I]
+        lib.oracle_select_rows.restype = ctypes.c_int64
+        lib.oracle_arrow.argtypes = [I, I, I, I, P, P, P, P, I]
+        lib.oracle_arrow.restype = ctypes.c_int64
+        lib.oracle_forward.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, D, P, I, P, P]
+        lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, "bf16 tensors are passed as uint16 bit patterns"
+    return a
+
+
+def _check(rc: int, what: str):
+    if rc < 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def n_blocks(N: int, block: int) -> int:
+    return -(-N // block)
+
+
+def threads() -> int:
+    return int(_load().oracle_threads())
+
+
+def pool_mean(x: np.ndarray, block: int) -> np.ndarray:
+    """[B,H,N,D] bf16 bits -> fp64 [B,H,nB,D] block means."""
+    x = _u16(x)
+    B, H, N, D = x.shape
+    out = np.empty((B, H, n_blocks(N, block), D), dtype=np.float64)
+    _check(_load().oracle_pool_mean(_ptr(x), B, H, N, D, block, _ptr(out)), "pool_mean")
+    return out
+
+
+def scores_meanpool_proj(q: np.ndarray, k: np.ndarray, block: int, w: np.ndarray) -> np.ndarray:
+    """fp64 S [B,H,nB,nB] from mean-pooled, projected blocks."""
+    q, k = _u16(q), _u16(k)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    B, H, N, D = q.shape
+    assert k.shape == q.shape and w.shape[0] == D
+    nB = n_blocks(N, block)
+    S = np.empty((B, H, nB, nB), dtype=np.float64)
+    _check(_load().oracle_scores_meanpool_proj(_ptr(q), _ptr(k), B, H, N, D, block,
+                                               _ptr(w), w.shape[1], _ptr(S)), "scores_meanpool_proj")
+    return S
+
+
+def scores_exact_avgpool(q: np.ndarray, k: np.ndarray, block: int, scale: Optional[float] = None,
+                         rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """fp64 block-averaged softmax attention.  With rows=None returns
+    [B,H,nB,nB]; otherwise [len(rows), nB] for the listed flat rows
+    (b*H + h)*nB + i."""
+    q, k = _u16(q), _u16(k)
+    B, H, N, D = q.shape
+    nB = n_blocks(N, block)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lib = _load()
+    if rows is None:
+        S = np.empty((B, H, nB, nB), dtype=np.float64)
+        _check(lib.oracle_scores_exact_avgpool(_ptr(q), _ptr(k), B, H, N, D, block, scale,
+                                               None, 0, _ptr(S)), "scores_exact_avgpool")
+        return S
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    S = np.empty((len(r), nB), dtype=np.float64)
+    _check(lib.oracle_scores_exact_avgpool(_ptr(q), _ptr(k), B, H, N, D, block, scale,
+                                           _ptr(r), len(r), _ptr(S)), "scores_exact_avgpool")
+    return S
+
+
+def _groups_arr(groups) -> np.ndarray:
+    g = np.ascontiguousarray(np.array(groups, dtype=np.int32).reshape(-1, 3))
+    return g
+
+
+def select_rows(S_rows: np.ndarray, qblock: Sequence[int], text_blocks: int,
+                groups) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k selection for a list of rows.  S_rows [n, nB] (any float dtype,
+    widened to fp64 exactly), qblock[n] = each row's query-block index."""
+    S_rows = np.ascontiguousarray(S_rows, dtype=np.float64)
+    n, nB = S_rows.shape
+    qb = np.ascontiguousarray(qblock, dtype=np.int32)
+    g = _groups_arr(groups)
+    cap = n * nB
+    row_ptr = np.zeros(n + 1, dtype=np.int32)
+    col_idx = np.zeros(max(cap, 1), dtype=np.int32)
+    nnz = _load().oracle_select_rows(_ptr(S_rows), _ptr(qb), n, nB, text_blocks, _ptr(g),
+                                     len(g), _ptr(row_ptr), _ptr(col_idx), cap)
+    _check(nnz, "select_rows")
+    return row_ptr, col_idx[:nnz].copy()
+
+
+def select(S: np.ndarray, text_blocks: int, groups) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k selection over a full [B,H,nB,nB] score tensor -> CSR over (b,h,i)."""
+    B, H, nB, nB2 = S.shape
+    assert nB == nB2
+    qb = np.tile(np.arange(nB, dtype=np.int32), B * H)
+    return select_rows(S.reshape(B * H * nB, nB), qb, text_blocks, groups)
+
+
+def arrow(B: int, H: int, nB: int, text_blocks: int, modes: np.ndarray,
+          windows: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Arrow / full / skip layout as CSR over (b,h,i)."""
+    modes = np.ascontiguousarray(modes, dtype=np.int8)
+    windows = np.ascontiguousarray(windows, dtype=np.int32)
+    lib = _load()
+    row_ptr = np.zeros(B * H * nB + 1, dtype=np.int32)
+    nnz = lib.oracle_arrow(B, H, nB, text_blocks, _ptr(modes), _ptr(windows), _ptr(row_ptr),
+                           None, 0)
+    _check(nnz, "arrow")
+    col_idx = np.zeros(max(nnz, 1), dtype=np.int32)
+    nnz2 = lib.oracle_arrow(B, H, nB, text_blocks, _ptr(modes), _ptr(windows), _ptr(row_ptr),
+                            _ptr(col_idx), nnz)
+    _check(nnz2, "arrow")
+    return row_ptr, col_idx[:nnz].copy()
+
+
+def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, block: int,
+            row_ptr: np.ndarray, col_idx: np.ndarray, modes: Optional[np.ndarray] = None,
+            o_cache: Optional[np.ndarray] = None, lse_cache: Optional[np.ndarray] = None,
+            scale: Optional[float] = None,
+            rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense softmax over the kept blocks.  rows=None -> O [B,H,N,D], LSE
+    [B,H,N]; otherwise O [n, D], LSE [n] for flat token rows (b*H + h)*N + t."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, H, N, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if col_idx.size == 0:
+        col_idx = np.zeros(1, dtype=np.int32)
+    assert row_ptr.shape[0] == B * H * n_blocks(N, block) + 1
+    modes_a = None if modes is None else np.ascontiguousarray(modes, dtype=np.int8)
+    oc = None if o_cache is None else _u16(o_cache)
+    lc = None if lse_cache is None else np.ascontiguousarray(lse_cache, dtype=np.float32)
+    lib = _load()
+    if rows is None:
+        O = np.empty((B, H, N, D), dtype=np.float64)
+        L = np.empty((B, H, N), dtype=np.float64)
+        rc = lib.oracle_forward(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, block, _ptr(row_ptr),
+                                _ptr(col_idx), _ptr(modes_a), _ptr(oc), _ptr(lc), scale,
+                                None, 0, _ptr(O), _ptr(L))
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        O = np.empty((len(r), D), dtype=np.float64)
+        L = np.empty((len(r),), dtype=np.float64)
+        rc = lib.oracle_forward(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, block, _ptr(row_ptr),
+                                _ptr(col_idx), _ptr(modes_a), _ptr(oc), _ptr(lc), scale,
+                                _ptr(r), len(r), _ptr(O), _ptr(L))
+    _check(rc, "forward")
+    return O, L

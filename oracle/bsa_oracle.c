@@ -1,0 +1,421 @@
+/*
+ * CPU oracle for block-sparse attention -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously correct fp64 definitions of every step of the
+ * block-sparse attention path.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the product path
+ * never does.  It shares no code, header, table or helper with the GPU
+ * library.
+ *
+ * Inputs are the same bfloat16 tensors the GPU consumes (uint16 bit
+ * patterns, widened exactly), laid out contiguously as [B][H][N][D].
+ * Every reduction runs in a fixed sequential order per output element, and
+ * OpenMP only distributes independent outputs, so results do not depend on
+ * the thread count.
+ *
+ * Sources (page title, section):
+ *  - "Block Sparse Attention in multimodal DiT" write-up (lmnt.cn), 2.2:
+ *    each block is mean-pooled to one vector, a small linear layer projects
+ *    it, query-block / key-block similarity is scored and the top-k key
+ *    blocks per query block are kept.  2.3: rows and columns that involve
+ *    text stay dense.  3.1: the kept blocks are computed FlashAttention-style
+ *    (exactly the dense softmax restricted to the kept set).
+ *  - DiTFastAttnV2 notes, "Head-wise Arrow Attention" / "Head-wise Caching" /
+ *    "Fused Kernel": vision-vision region keeps a diagonal local window,
+ *    every region touching text stays dense; per head one of full, arrow(w)
+ *    or skip (reuse the cached output).
+ *  - SparseD notes, "Isolated selection": A' = avgpool(A, block) of the
+ *    post-softmax attention map, top-rho% blocks chosen separately over the
+ *    prefill and the generation columns and unioned.
+ *
+ * Readings where the pages leave a step open (documented with the tests):
+ *  - a partial last block (N not a multiple of the block size) pools over
+ *    the tokens it holds; avgpool divides by the actual counts;
+ *  - a block that holds any text token is a text block;
+ *  - the arrow window is measured in whole blocks, |i - j| <= w;
+ *  - top-k ties keep the lower column index;
+ *  - a row with no kept key gives O = 0 and LSE = -inf.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+#define OR_ECAPACITY (-3)
+#define OR_ENOMEM (-4)
+
+#define HEAD_FULL 0
+#define HEAD_ARROW 1
+#define HEAD_SKIP 2
+
+static double widen_bf16(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int64_t nblocks(int64_t N, int64_t beta) { return (N + beta - 1) / beta; }
+
+static int64_t block_len(int64_t N, int64_t beta, int64_t i)
+{
+    int64_t lo = i * beta, hi = lo + beta;
+    if (hi > N) hi = N;
+    return hi - lo;
+}
+
+/* ------------------------------------------------------------------------
+ * Mean pooling: pooled[b][h][i][:] = (1/n_i) * sum_{t in block i} x[b][h][t][:]
+ * ---------------------------------------------------------------------- */
+int oracle_pool_mean(const uint16_t *x, int64_t B, int64_t H, int64_t N, int64_t D,
+                     int64_t beta, double *pooled)
+{
+    if (!x || !pooled || B <= 0 || H <= 0 || N <= 0 || D <= 0 || beta <= 0) return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta);
+    const int64_t total = B * H * nB;
+#pragma omp parallel for schedule(static)
+    for (int64_t item = 0; item < total; ++item) {
+        const int64_t bh = item / nB, i = item % nB;
+        const int64_t n_i = block_len(N, beta, i);
+        double *out = pooled + item * D;
+        for (int64_t d = 0; d < D; ++d) {
+            double s = 0.0;
+            for (int64_t t = i * beta; t < i * beta + n_i; ++t)
+                s += widen_bf16(x[(bh * N + t) * D + d]);
+            out[d] = s / (double)n_i;
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Content-driven block score (block-sparse DiT write-up, 2.2):
+ *   p_i  = W^T qbar_i,  p'_j = W^T kbar_j,  S_ij = p_i . p'_j
+ * W is [D][r] row-major, one matrix for queries and keys and all heads.
+ * ---------------------------------------------------------------------- */
+int oracle_scores_meanpool_proj(const uint16_t *q, const uint16_t *k,
+                                int64_t B, int64_t H, int64_t N, int64_t D, int64_t beta,
+                                const float *w, int64_t r, double *S)
+{
+    if (!q || !k || !w || !S || r <= 0) return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta);
+    double *qbar = malloc(sizeof(double) * B * H * nB * D);
+    double *kbar = malloc(sizeof(double) * B * H * nB * D);
+    double *pq = malloc(sizeof(double) * B * H * nB * r);
+    double *pk = malloc(sizeof(double) * B * H * nB * r);
+    int rc = OR_OK;
+    if (!qbar || !kbar || !pq || !pk) { rc = OR_ENOMEM; goto done; }
+    if ((rc = oracle_pool_mean(q, B, H, N, D, beta, qbar)) != OR_OK) goto done;
+    if ((rc = oracle_pool_mean(k, B, H, N, D, beta, kbar)) != OR_OK) goto done;
+
+    const int64_t total = B * H * nB;
+#pragma omp parallel for schedule(static)
+    for (int64_t item = 0; item < total; ++item) {
+        for (int64_t m = 0; m < r; ++m) {
+            double a = 0.0, c = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                a += (double)w[d * r + m] * qbar[item * D + d];
+                c += (double)w[d * r + m] * kbar[item * D + d];
+            }
+            pq[item * r + m] = a;
+            pk[item * r + m] = c;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t item = 0; item < total; ++item) {
+        const int64_t bh = item / nB;
+        for (int64_t j = 0; j < nB; ++j) {
+            double s = 0.0;
+            for (int64_t m = 0; m < r; ++m)
+                s += pq[item * r + m] * pk[(bh * nB + j) * r + m];
+            S[item * nB + j] = s;
+        }
+    }
+done:
+    free(qbar); free(kbar); free(pq); free(pk);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Exact block score (SparseD notes, isolated selection):
+ *   A_ts = softmax_s(scale * Q_t . K_s) over all N keys of the head;
+ *   S_ij = (1 / (n_i n_j)) * sum_{t in block i} sum_{s in block j} A_ts.
+ * Computed one query row at a time (the notes compute A' chunk by chunk
+ * over Q).  `rows` lists flat query-block rows (b*H + h)*nB + i; NULL means
+ * all of them in order.  Output S_rows is [n_rows][nB].
+ * ---------------------------------------------------------------------- */
+int oracle_scores_exact_avgpool(const uint16_t *q, const uint16_t *k,
+                                int64_t B, int64_t H, int64_t N, int64_t D, int64_t beta,
+                                double scale, const int64_t *rows, int64_t n_rows,
+                                double *S_rows)
+{
+    if (!q || !k || !S_rows || B <= 0 || H <= 0 || N <= 0 || D <= 0 || beta <= 0)
+        return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta);
+    if (!rows) n_rows = B * H * nB;
+    for (int64_t x = 0; x < n_rows; ++x) {
+        int64_t row = rows ? rows[x] : x;
+        if (row < 0 || row >= B * H * nB) return OR_EINVAL;
+    }
+    /* one partial row of block sums per query token, reduced afterwards in
+       token order so that the result does not depend on the thread count */
+    const int64_t tok = n_rows * beta;
+    double *part = calloc((size_t)(tok * nB), sizeof(double));
+    if (!part) return OR_ENOMEM;
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *z = malloc(sizeof(double) * N);
+        double *qt = malloc(sizeof(double) * D);
+        if (!z || !qt) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t u = 0; u < tok; ++u) {
+                const int64_t x = u / beta, tt = u % beta;
+                const int64_t row = rows ? rows[x] : x;
+                const int64_t bh = row / nB, i = row % nB;
+                const int64_t t = i * beta + tt;
+                if (t >= N) continue;
+                for (int64_t d = 0; d < D; ++d) qt[d] = widen_bf16(q[(bh * N + t) * D + d]);
+                double m = -INFINITY;
+                for (int64_t s = 0; s < N; ++s) {
+                    const uint16_t *ks = k + (bh * N + s) * D;
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d) acc += qt[d] * widen_bf16(ks[d]);
+                    z[s] = scale * acc;
+                    if (z[s] > m) m = z[s];
+                }
+                double l = 0.0;
+                for (int64_t s = 0; s < N; ++s) l += exp(z[s] - m);
+                double *p = part + u * nB;
+                for (int64_t s = 0; s < N; ++s) p[s / beta] += exp(z[s] - m) / l;
+            }
+        }
+        free(z);
+        free(qt);
+    }
+    if (rc == OR_OK) {
+        for (int64_t x = 0; x < n_rows; ++x) {
+            const int64_t row = rows ? rows[x] : x;
+            const int64_t i = row % nB;
+            const int64_t n_i = block_len(N, beta, i);
+            for (int64_t j = 0; j < nB; ++j) {
+                double s = 0.0;
+                for (int64_t tt = 0; tt < n_i; ++tt) s += part[(x * beta + tt) * nB + j];
+                S_rows[x * nB + j] = s / ((double)n_i * (double)block_len(N, beta, j));
+            }
+        }
+    }
+    free(part);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Top-k block selection (write-up 2.2 and 2.3; SparseD isolated selection).
+ * For each listed row (its query-block index qblock[x] and its nB scores):
+ *   - a text query block (qblock < text_blocks) keeps every column;
+ *   - otherwise keep F = {j < text_blocks} united with, for each group g
+ *     (column range [c_g, e_g), budget k_g), the first k_g columns of that
+ *     range ordered by descending score, lower column first on equal scores.
+ * Output: CSR over the listed rows, columns ascending.  Returns nnz >= 0 or
+ * a negative error.
+ * ---------------------------------------------------------------------- */
+typedef struct { double s; int32_t j; } scored_col;
+
+static int cmp_scored(const void *a, const void *b)
+{
+    const scored_col *x = a, *y = b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j < y->j) ? -1 : (x->j > y->j);
+}
+
+int64_t oracle_select_rows(const double *S_rows, const int32_t *qblock, int64_t n_rows,
+                           int64_t nB, int64_t text_blocks, const int32_t *groups, int64_t n_groups,
+                           int32_t *row_ptr, int32_t *col_idx, int64_t capacity)
+{
+    if (!S_rows || !qblock || !row_ptr || nB <= 0 || text_blocks < 0 || n_groups < 0)
+        return OR_EINVAL;
+    for (int64_t g = 0; g < n_groups; ++g) {
+        int32_t c0 = groups[3 * g], c1 = groups[3 * g + 1], kk = groups[3 * g + 2];
+        if (c0 < 0 || c1 > nB || c0 >= c1 || kk < 0 || kk > c1 - c0) return OR_EINVAL;
+    }
+    unsigned char *keep = malloc((size_t)nB);
+    scored_col *buf = malloc(sizeof(scored_col) * (size_t)nB);
+    if (!keep || !buf) { free(keep); free(buf); return OR_ENOMEM; }
+    int64_t nnz = 0;
+    row_ptr[0] = 0;
+    for (int64_t x = 0; x < n_rows; ++x) {
+        const double *s = S_rows + x * nB;
+        memset(keep, 0, (size_t)nB);
+        if (qblock[x] < text_blocks) {
+            memset(keep, 1, (size_t)nB);
+        } else {
+            for (int64_t j = 0; j < nB && j < text_blocks; ++j) keep[j] = 1;
+            for (int64_t g = 0; g < n_groups; ++g) {
+                int32_t c0 = groups[3 * g], c1 = groups[3 * g + 1], kk = groups[3 * g + 2];
+                int64_t n = 0;
+                for (int32_t j = c0; j < c1; ++j) { buf[n].s = s[j]; buf[n].j = j; ++n; }
+                qsort(buf, (size_t)n, sizeof(scored_col), cmp_scored);
+                for (int64_t a = 0; a < kk; ++a) keep[buf[a].j] = 1;
+            }
+        }
+        for (int64_t j = 0; j < nB; ++j) {
+            if (!keep[j]) continue;
+            if (col_idx) {
+                if (nnz >= capacity) { free(keep); free(buf); return OR_ECAPACITY; }
+                col_idx[nnz] = (int32_t)j;
+            }
+            ++nnz;
+        }
+        row_ptr[x + 1] = (int32_t)nnz;
+    }
+    free(keep);
+    free(buf);
+    return nnz;
+}
+
+/* ------------------------------------------------------------------------
+ * Arrow layout (DiTFastAttnV2 notes, head-wise arrow attention):
+ *   ARROW head: keep(i, j) = i < T_b or j < T_b or |i - j| <= w_h
+ *   FULL head : keep every (i, j)
+ *   SKIP head : no rows are computed (every row is empty)
+ * Rows are ordered (b, h, i); columns ascending.  Returns nnz or an error.
+ * ---------------------------------------------------------------------- */
+int64_t oracle_arrow(int64_t B, int64_t H, int64_t nB, int64_t text_blocks,
+                     const int8_t *modes, const int32_t *windows,
+                     int32_t *row_ptr, int32_t *col_idx, int64_t capacity)
+{
+    if (B <= 0 || H <= 0 || nB <= 0 || text_blocks < 0 || !modes || !windows || !row_ptr)
+        return OR_EINVAL;
+    int64_t nnz = 0;
+    row_ptr[0] = 0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+            if (modes[h] != HEAD_FULL && modes[h] != HEAD_ARROW && modes[h] != HEAD_SKIP)
+                return OR_EINVAL;
+            if (modes[h] == HEAD_ARROW && windows[h] < 0) return OR_EINVAL;
+            for (int64_t i = 0; i < nB; ++i) {
+                for (int64_t j = 0; j < nB; ++j) {
+                    int kp;
+                    if (modes[h] == HEAD_SKIP) kp = 0;
+                    else if (modes[h] == HEAD_FULL) kp = 1;
+                    else kp = (i < text_blocks) || (j < text_blocks) ||
+                              (llabs(i - j) <= (int64_t)windows[h]);
+                    if (!kp) continue;
+                    if (col_idx) {
+                        if (nnz >= capacity) return OR_ECAPACITY;
+                        col_idx[nnz] = (int32_t)j;
+                    }
+                    ++nnz;
+                }
+                row_ptr[(b * H + h) * nB + i + 1] = (int32_t)nnz;
+            }
+        }
+    return nnz;
+}
+
+/* ------------------------------------------------------------------------
+ * Block-sparse attention forward, by definition:
+ *   z_s = scale * Q_t . K_s   if key block floor(s/beta) is kept for query
+ *                             block floor(t/beta) of this head, else -inf
+ *   m = max_s z_s,  l = sum_s e^{z_s - m},
+ *   O_t = sum_s e^{z_s - m} V_s / l,   LSE_t = m + ln l.
+ * SKIP heads (modes != NULL and modes[h] == SKIP) return the cached row
+ * unchanged (O from o_cache, LSE from lse_cache, NaN when lse_cache is NULL).
+ * `rows` lists flat token rows (b*H + h)*N + t; NULL means every row.
+ * Outputs O [n_rows][D], LSE [n_rows].
+ * ---------------------------------------------------------------------- */
+int oracle_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   int64_t B, int64_t H, int64_t N, int64_t D, int64_t beta,
+                   const int32_t *row_ptr, const int32_t *col_idx,
+                   const int8_t *modes, const uint16_t *o_cache, const float *lse_cache,
+                   double scale, const int64_t *rows, int64_t n_rows,
+                   double *O, double *LSE)
+{
+    if (!q || !k || !v || !row_ptr || !O || !LSE || B <= 0 || H <= 0 || N <= 0 || D <= 0 ||
+        beta <= 0)
+        return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta);
+    if (row_ptr[0] != 0) return OR_EINVAL;
+    for (int64_t r = 0; r < B * H * nB; ++r) {
+        if (row_ptr[r + 1] < row_ptr[r]) return OR_EINVAL;
+        for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e)
+            if (!col_idx || col_idx[e] < 0 || col_idx[e] >= nB) return OR_EINVAL;
+    }
+    if (!rows) n_rows = B * H * N;
+    for (int64_t x = 0; x < n_rows; ++x) {
+        int64_t row = rows ? rows[x] : x;
+        if (row < 0 || row >= B * H * N) return OR_EINVAL;
+        int64_t h = (row / N) % H;
+        if (modes && modes[h] == HEAD_SKIP && !o_cache) return OR_EINVAL;
+    }
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *z = malloc(sizeof(double) * N);
+        unsigned char *kept = malloc((size_t)nB);
+        if (!z || !kept) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t x = 0; x < n_rows; ++x) {
+                const int64_t row = rows ? rows[x] : x;
+                const int64_t bh = row / N, t = row % N, h = bh % H;
+                double *o = O + x * D;
+                if (modes && modes[h] == HEAD_SKIP) {
+                    for (int64_t d = 0; d < D; ++d) o[d] = widen_bf16(o_cache[row * D + d]);
+                    LSE[x] = lse_cache ? (double)lse_cache[row] : NAN;
+                    continue;
+                }
+                const int64_t r = bh * nB + t / beta;
+                memset(kept, 0, (size_t)nB);
+                for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) kept[col_idx[e]] = 1;
+                double m = -INFINITY;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (!kept[s / beta]) { z[s] = -INFINITY; continue; }
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        acc += widen_bf16(q[row * D + d]) * widen_bf16(k[(bh * N + s) * D + d]);
+                    z[s] = scale * acc;
+                    if (z[s] > m) m = z[s];
+                }
+                if (m == -INFINITY) {
+                    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                    LSE[x] = -INFINITY;
+                    continue;
+                }
+                double l = 0.0;
+                for (int64_t s = 0; s < N; ++s)
+                    if (z[s] != -INFINITY) l += exp(z[s] - m);
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (z[s] == -INFINITY) continue;
+                    const double p = exp(z[s] - m);
+                    for (int64_t d = 0; d < D; ++d) o[d] += p * widen_bf16(v[(bh * N + s) * D + d]);
+                }
+                for (int64_t d = 0; d < D; ++d) o[d] /= l;
+                LSE[x] = m + log(l);
+            }
+        }
+        free(z);
+        free(kept);
+    }
+    return rc;
+}
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
