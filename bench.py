@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path for the workload over one batch of
+synthetic input already resident in HBM: the arrow block layout
+(bsa_build_arrow_layout) followed by the block-sparse forward (bsa_forward)
+for the 2K MMDiT shape (B=1, H=24, N=16896 = 512 text + 128x128 image
+tokens, D=128, block 128, arrow window 8 on every head).  Content-driven
+workloads (--workload C1/C3/C5) run pool_scores + select_topk + forward.
+
+Prints ONE JSON line.  `value` is the actual (kept-block) TFLOP/s of the
+step; the dense-equivalent rate, the fraction of the bf16 MFMA peak, the
+forward kernel's roofline entry (timed with HIP events on the launch stream)
+and the CPU oracle's rate on a bounded sample are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "block-sparse attn fwd TFLOP/s (actual + dense-equiv) and % bf16 MFMA peak"
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    p = os.path.join(ROOT, "block_sparse_attention_18_amd", "csrc", "forward.hip")
+    h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per forward launch from committed rocprofv3 counter runs, if they
+    were taken on the current forward kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"forward_{workload.lower()}_traffic.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("forward_src_sha") != _src_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C4")
+    ap.add_argument("--window", type=int, default=None, help="override the arrow window")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only: the block-sparse path shards by (batch, head) "
+              f"with no exchange, so a multi-GPU figure is not measured here (asked for "
+              f"{args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_18_amd as bsa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bsa.load()
+
+    wl = synth.WORKLOADS[args.workload]
+    if args.window is not None:
+        wl = wl.replace(arrow_window=args.window)
+    x = synth.make_inputs(wl)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
+    nB = wl.n_blocks
+    q, k, v = d(x["q"]), d(x["k"]), d(x["v"])
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if wl.layout == "arrow":
+        modes, wins = x["head_modes"], x["head_windows"]
+        cap = bsa.arrow_capacity(B, H, N, block, wl.text_len, modes, wins)
+        row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        o_cache = d(x["o_cache"]) if "o_cache" in x else None
+        lse_cache = torch.from_numpy(x["lse_cache"]).to(dev) if "lse_cache" in x else None
+        kept_pairs = cap
+        computed_heads = B * int((modes != bsa.HEAD_SKIP).sum())
+
+        def layout():
+            bsa.build_arrow_layout(B, H, N, block, wl.text_len, modes, wins, device=dev,
+                                   row_ptr=row_ptr, col_idx=col_idx)
+        fwd_kw = dict(head_modes=modes, o_cache=o_cache, lse_cache=lse_cache)
+    else:
+        w = torch.from_numpy(x["w"]).to(dev) if "w" in x else None
+        scores = torch.empty((B, H, nB, nB), dtype=torch.float32, device=dev)
+        ws_s = torch.empty(max(bsa.pool_scores_workspace_size(B, H, N, D, block, wl.score_mode,
+                                                              wl.r if w is not None else 0), 16),
+                           dtype=torch.uint8, device=dev)
+        cap = bsa.select_capacity(B, H, nB, wl.text_blocks, wl.groups)
+        row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        ws_sel = torch.empty(max(int(bsa.load().bsa_select_workspace_size(B, H, nB)), 16),
+                             dtype=torch.uint8, device=dev)
+
+        def layout():
+            bsa.pool_scores(q, k, block, wl.score_mode, w=w, out=scores, workspace=ws_s)
+            bsa.select_topk(scores, wl.text_blocks, wl.groups, row_ptr=row_ptr, col_idx=col_idx,
+                            workspace=ws_sel)
+        fwd_kw = {}
+        computed_heads = B * H
+
+    def forward():
+        bsa.forward(q, k, v, block, row_ptr, col_idx, out=out, lse=lse, **fwd_kw)
+
+    # warmup (also fixes kept_pairs for content-driven selection)
+    for _ in range(max(args.warmup, 1)):
+        layout()
+        forward()
+    torch.cuda.synchronize()
+    if wl.layout != "arrow":
+        kept_pairs = int(row_ptr[-1].item())
+
+    flop_pair = 4.0 * block * block * D
+    actual_flop = flop_pair * kept_pairs
+    dense_flop = 4.0 * N * N * D * B * H
+
+    # timed region: K steps, per-forward events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s in range(args.steps):
+        layout()
+        ev[s][0].record(stream)
+        forward()
+        ev[s][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    fwd_ms = [a.elapsed_time(b) for a, b in ev]
+    fwd_avg = float(np.mean(fwd_ms))
+
+    value = actual_flop / (ms_step * 1e-3) / 1e12
+    achieved = actual_flop / (fwd_avg * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.description}",
+            "B": B, "H": H, "N": N, "D": D, "block": block,
+            "layout": (f"arrow w={wl.arrow_window}" if wl.layout == "arrow"
+                       else f"select groups={list(wl.groups)} text_blocks={wl.text_blocks}"),
+            "kept_pairs": kept_pairs,
+            "kept_fraction": round(kept_pairs / (B * H * nB * nB), 4),
+            "parallelism": "single GPU",
+        },
+        "dense_equiv_tflops": round(dense_flop / (ms_step * 1e-3) / 1e12, 2),
+        "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "forward_ms": round(fwd_avg, 4),
+        "forward_dense_equiv_tflops": round(dense_flop / (fwd_avg * 1e-3) / 1e12, 2),
+        "step_wall_ms": round(wall * 1e3 / args.steps, 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "bsa::fwd_kernel",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic(wl.name),
+            "algorithmic_flop_per_launch": actual_flop,
+        },
+        "cpu_baseline": None,
+    }
+
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, x, row_ptr, col_idx, args.cpu_seconds,
+                                           fwd_kw.get("head_modes"))
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(wl, x, row_ptr, col_idx, seconds, modes):
+    """The fp64 CPU oracle's forward on a bounded sample of the workload's rows."""
+    import oracle
+    rp = row_ptr.cpu().numpy()
+    ci = col_idx.cpu().numpy()[:rp[-1]]
+    B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
+    nB = wl.n_blocks
+    rng = np.random.default_rng(0)
+    comp = [h for h in range(H) if modes is None or modes[h] != 2]
+
+    def rows_of(n):
+        b = rng.integers(0, B, n)
+        h = np.array(comp)[rng.integers(0, len(comp), n)]
+        t = rng.integers(0, N, n)
+        return ((b * H + h) * N + t).astype(np.int64)
+
+    def flop(rows):
+        bh = rows // N
+        r = bh * nB + (rows % N) // block
+        kept = (rp[r + 1] - rp[r]).astype(np.float64)
+        return float((4.0 * block * D * kept).sum())
+
+    probe = rows_of(64)
+    t = time.perf_counter()
+    oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=probe)
+    dt = max(time.perf_counter() - t, 1e-3)
+    n = int(min(max(64 * seconds / dt, 64), 200000))
+    rows = rows_of(n)
+    t = time.perf_counter()
+    oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=rows)
+    dt = time.perf_counter() - t
+    return {"value": round(flop(rows) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{n} random query rows of the {wl.name} forward (fp64, kept blocks only), "
+                      f"{dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

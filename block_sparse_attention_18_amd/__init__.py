@@ -1,0 +1,269 @@
+"""Block-sparse attention forward for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in ``include/bsa.h``.  Every
+step of the path runs in the HIP kernels of ``libbsa.so``; this module only
+marshals torch tensors (device memory, current stream) into the C calls and
+allocates outputs and workspaces when the caller does not pass them.  If the
+library is not built, every call raises: there is no fallback.
+
+The four calls mirror the C ABI:
+
+  pool_scores          block score matrix (mean-pool + projection, or the
+                       block average of exact softmax attention)
+  select_topk          CSR block list: text rows / columns dense, top-k per
+                       column group
+  build_arrow_layout   CSR block list of the arrow / full / skip layout
+  forward              online-softmax attention over the CSR block list,
+                       returning O (bf16) and LSE (fp32, natural log)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsa.so")
+
+HEAD_FULL, HEAD_ARROW, HEAD_SKIP = 0, 1, 2
+SCORE_MEANPOOL_PROJ, SCORE_EXACT_AVGPOOL = 0, 1
+
+STATUS = {0: "BSA_OK", 1: "BSA_ERR_INVALID_ARG", 2: "BSA_ERR_UNSUPPORTED",
+          3: "BSA_ERR_CAPACITY", 4: "BSA_ERR_WORKSPACE", 5: "BSA_ERR_HIP"}
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class BsaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_n", ctypes.c_int64)]
+
+
+class BsaGroup(ctypes.Structure):
+    _fields_ = [("col_begin", ctypes.c_int32), ("col_end", ctypes.c_int32),
+                ("k", ctypes.c_int32)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libbsa.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is not built; run `python -m block_sparse_attention_18_amd.build`")
+        lib = ctypes.CDLL(p)
+        V, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        F = ctypes.c_float
+        TP = ctypes.POINTER(BsaTensor)
+        GP = ctypes.POINTER(BsaGroup)
+        sig = {
+            "bsa_pool_scores_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32, I32]),
+            "bsa_pool_scores": (I32, [TP, TP, I32, I32, V, I32, F, V, V, SZ, V]),
+            "bsa_select_capacity": (I64, [I64, I64, I32, I32, GP, I32]),
+            "bsa_select_workspace_size": (SZ, [I64, I64, I32]),
+            "bsa_select_topk": (I32, [V, I64, I64, I32, I32, GP, I32, V, V, I64, V, SZ, V]),
+            "bsa_arrow_capacity": (I64, [I64, I64, I64, I32, I64, V, V]),
+            "bsa_build_arrow_layout": (I32, [I64, I64, I64, I32, I64, V, V, V, V, I64, V]),
+            "bsa_forward": (I32, [TP, TP, TP, I32, V, V, V, TP, V, F, TP, V, V]),
+            "bsa_status_string": (ctypes.c_char_p, [I32]),
+            "bsa_last_error": (ctypes.c_char_p, []),
+            "bsa_version": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().bsa_last_error().decode(errors="replace")
+        raise BsaError(status, msg)
+
+
+def _desc(t: Optional[torch.Tensor], name: str) -> Optional[BsaTensor]:
+    if t is None:
+        return None
+    if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name}: expected a bfloat16 [B, H, N, D] tensor with D contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    B, H, N, D = t.shape
+    sb, sh, sn, _ = t.stride()
+    return BsaTensor(t.data_ptr(), B, H, N, D, sb, sh, sn)
+
+
+def _ref(d: Optional[BsaTensor]):
+    return None if d is None else ctypes.byref(d)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _groups(groups) -> Tuple[ctypes.Array, int]:
+    gl = [tuple(int(v) for v in g) for g in groups]
+    arr = (BsaGroup * max(len(gl), 1))(*[BsaGroup(*g) for g in gl])
+    return arr, len(gl)
+
+
+def n_blocks(N: int, block: int) -> int:
+    return -(-N // block)
+
+
+# ---------------------------------------------------------------------------
+def pool_scores_workspace_size(B, H, N, D, block, mode=SCORE_MEANPOOL_PROJ, r=32) -> int:
+    return int(load().bsa_pool_scores_workspace_size(B, H, N, D, block, mode, r))
+
+
+def pool_scores(q: torch.Tensor, k: torch.Tensor, block: int, mode: int = SCORE_MEANPOOL_PROJ,
+                w: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block scores S [B, H, nB, nB] (fp32).  MEANPOOL_PROJ needs w [D, r]
+    (fp32, contiguous); EXACT_AVGPOOL uses `scale` (default 1/sqrt(D))."""
+    lib = load()
+    B, H, N, D = q.shape
+    nB = n_blocks(N, block)
+    r = 0
+    if mode == SCORE_MEANPOOL_PROJ:
+        if w is None or w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 2:
+            raise ValueError("w must be a contiguous fp32 [D, r] device tensor")
+        r = int(w.shape[1])
+    if out is None:
+        out = torch.empty((B, H, nB, nB), dtype=torch.float32, device=q.device)
+    ws_need = pool_scores_workspace_size(B, H, N, D, block, mode, r)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk = _desc(q, "q"), _desc(k, "k")
+    _check(lib.bsa_pool_scores(ctypes.byref(dq), ctypes.byref(dk), block, mode, _ptr(w), r,
+                               float(scale or 0.0), _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return out
+
+
+def select_capacity(B, H, nB, text_blocks, groups) -> int:
+    arr, ng = _groups(groups)
+    return int(load().bsa_select_capacity(B, H, nB, text_blocks, arr, ng))
+
+
+def select_topk(scores: torch.Tensor, text_blocks: int, groups: Sequence[Tuple[int, int, int]],
+                row_ptr: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """CSR block list from fp32 scores [B, H, nB, nB].  col_idx is sized to the
+    capacity bound; the entries in use are col_idx[:row_ptr[-1]]."""
+    lib = load()
+    if scores.dtype != torch.float32 or not scores.is_contiguous() or scores.dim() != 4:
+        raise ValueError("scores must be a contiguous fp32 [B, H, nB, nB] device tensor")
+    B, H, nB, _ = scores.shape
+    arr, ng = _groups(groups)
+    cap = int(lib.bsa_select_capacity(B, H, nB, text_blocks, arr, ng))
+    dev = scores.device
+    if row_ptr is None:
+        row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        ws = int(lib.bsa_select_workspace_size(B, H, nB))
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+    _check(lib.bsa_select_topk(_ptr(scores), B, H, nB, text_blocks, arr, ng, _ptr(row_ptr),
+                               _ptr(col_idx), col_idx.numel(), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(dev)))
+    return row_ptr, col_idx
+
+
+def _host_i8(x, H) -> ctypes.Array:
+    vals = [int(v) for v in x]
+    if len(vals) != H:
+        raise ValueError("head array length must equal H")
+    return (ctypes.c_int8 * H)(*vals)
+
+
+def _host_i32(x, H) -> ctypes.Array:
+    vals = [int(v) for v in x]
+    if len(vals) != H:
+        raise ValueError("head array length must equal H")
+    return (ctypes.c_int32 * H)(*vals)
+
+
+def arrow_capacity(B, H, N, block, text_len, head_modes, head_windows) -> int:
+    m, w = _host_i8(head_modes, H), _host_i32(head_windows, H)
+    return int(load().bsa_arrow_capacity(B, H, N, block, text_len, m, w))
+
+
+def build_arrow_layout(B: int, H: int, N: int, block: int, text_len: int, head_modes,
+                       head_windows, device=None,
+                       row_ptr: Optional[torch.Tensor] = None,
+                       col_idx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """CSR block list of the arrow layout (exactly sized)."""
+    lib = load()
+    dev = torch.device(device) if device is not None else torch.device("cuda")
+    m, w = _host_i8(head_modes, H), _host_i32(head_windows, H)
+    cap = int(lib.bsa_arrow_capacity(B, H, N, block, text_len, m, w))
+    if cap < 0:
+        _check(lib.bsa_build_arrow_layout(B, H, N, block, text_len, m, w, None, None, 0, None))
+    nB = n_blocks(N, block)
+    if row_ptr is None:
+        row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    _check(lib.bsa_build_arrow_layout(B, H, N, block, text_len, m, w, _ptr(row_ptr), _ptr(col_idx),
+                                      col_idx.numel(), _stream(dev)))
+    return row_ptr, col_idx[:cap] if cap > 0 else col_idx[:0]
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
+            row_ptr: torch.Tensor, col_idx: torch.Tensor, head_modes=None,
+            o_cache: Optional[torch.Tensor] = None, lse_cache: Optional[torch.Tensor] = None,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None,
+            return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Block-sparse attention forward.  Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N])."""
+    lib = load()
+    B, H, N, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    if lse_cache is not None and (lse_cache.dtype != torch.float32 or not lse_cache.is_contiguous()):
+        raise ValueError("lse_cache must be a contiguous fp32 [B, H, N] tensor")
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    modes = None if head_modes is None else _host_i8(head_modes, H)
+    dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
+    dc = _desc(o_cache, "o_cache")
+    _check(lib.bsa_forward(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), block,
+                           _ptr(row_ptr), _ptr(col_idx), modes, _ref(dc), _ptr(lse_cache),
+                           float(scale or 0.0), ctypes.byref(do), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
+def version() -> str:
+    return load().bsa_version().decode()

@@ -1,0 +1,411 @@
+// C ABI of the block-sparse attention library: argument validation and
+// kernel launches.  Every check runs before anything is enqueued, so a call
+// that fails did no work.  No device memory is allocated or freed here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "bsa.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsa_status fail(bsa_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bsa_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(BSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates one [B][H][N][D] bfloat16 tensor descriptor.
+bsa_status check_tensor(const bsa_tensor *t, const char *name)
+{
+    if (!t) return fail(BSA_ERR_INVALID_ARG, "%s: null descriptor", name);
+    if (!t->data) return fail(BSA_ERR_INVALID_ARG, "%s: null data pointer", name);
+    if (t->B <= 0 || t->H <= 0 || t->N <= 0 || t->D <= 0)
+        return fail(BSA_ERR_INVALID_ARG, "%s: shape must be positive (B=%lld H=%lld N=%lld D=%lld)",
+                    name, (long long)t->B, (long long)t->H, (long long)t->N, (long long)t->D);
+    if (t->D != 64 && t->D != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "%s: head dim %lld not supported (64 or 128)", name,
+                    (long long)t->D);
+    if (t->N > (1ll << 30) || t->B * t->H > (1ll << 30))
+        return fail(BSA_ERR_UNSUPPORTED, "%s: N or B*H too large", name);
+    if (!aligned16(t->data)) return fail(BSA_ERR_INVALID_ARG, "%s: data not 16-byte aligned", name);
+    if (t->stride_b % 8 || t->stride_h % 8 || t->stride_n % 8 || t->stride_b < 0 ||
+        t->stride_h < 0 || t->stride_n < t->D)
+        return fail(BSA_ERR_INVALID_ARG,
+                    "%s: strides must be non-negative multiples of 8 with stride_n >= D", name);
+    return BSA_OK;
+}
+
+bool same_shape(const bsa_tensor *a, const bsa_tensor *b)
+{
+    return a->B == b->B && a->H == b->H && a->N == b->N && a->D == b->D;
+}
+
+bsa::Tensor4 t4(const bsa_tensor *t)
+{
+    return bsa::Tensor4{static_cast<const uint16_t *>(t->data), t->stride_b, t->stride_h,
+                        t->stride_n};
+}
+
+bool block_ok(int32_t block) { return block == 64 || block == 128; }
+
+size_t exact_slot_bytes(int64_t nB, int32_t block) { return (size_t)nB * block * sizeof(float); }
+
+int64_t select_row_bound(int64_t nB, int64_t tb, const bsa_group *g, int32_t ng)
+{
+    int64_t k = tb;
+    for (int32_t x = 0; x < ng; ++x) k += g[x].k;
+    return k < nB ? k : nB;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bsa_status_string(bsa_status s)
+{
+    switch (s) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_ERR_INVALID_ARG: return "BSA_ERR_INVALID_ARG";
+    case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+    case BSA_ERR_CAPACITY: return "BSA_ERR_CAPACITY";
+    case BSA_ERR_WORKSPACE: return "BSA_ERR_WORKSPACE";
+    case BSA_ERR_HIP: return "BSA_ERR_HIP";
+    default: return "BSA_ERR_UNKNOWN";
+    }
+}
+
+const char *bsa_last_error(void) { return g_err; }
+
+const char *bsa_version(void) { return "bsa 0.1.0 gfx950"; }
+
+// ---------------------------------------------------------------------------
+size_t bsa_pool_scores_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int32_t block,
+                                      int32_t mode, int32_t r)
+{
+    (void)D;
+    if (B <= 0 || H <= 0 || N <= 0 || !block_ok(block)) return 0;
+    const int64_t nB = ceil_div(N, block);
+    if (mode == BSA_SCORE_MEANPOOL_PROJ) {
+        if (r <= 0) return 0;
+        return (size_t)(2 * B * H * nB * (int64_t)r) * sizeof(float);
+    }
+    if (mode == BSA_SCORE_EXACT_AVGPOOL) {
+        int64_t slots = B * H * nB;
+        if (slots > bsa::kExactSlots) slots = bsa::kExactSlots;
+        return (size_t)slots * exact_slot_bytes(nB, block);
+    }
+    return 0;
+}
+
+bsa_status bsa_pool_scores(const bsa_tensor *q, const bsa_tensor *k, int32_t block, int32_t mode,
+                           const float *w, int32_t r, float scale, float *scores, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSA_OK) return st;
+    if (!same_shape(q, k)) return fail(BSA_ERR_INVALID_ARG, "q and k shapes differ");
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    if (!scores) return fail(BSA_ERR_INVALID_ARG, "scores is null");
+    if (mode != BSA_SCORE_MEANPOOL_PROJ && mode != BSA_SCORE_EXACT_AVGPOOL)
+        return fail(BSA_ERR_UNSUPPORTED, "unknown scoring mode %d", mode);
+    if (std::isnan(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
+    const int64_t nB = ceil_div(q->N, block);
+    const size_t need = bsa_pool_scores_workspace_size(q->B, q->H, q->N, q->D, block, mode, r);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+
+    if (mode == BSA_SCORE_MEANPOOL_PROJ) {
+        if (!w) return fail(BSA_ERR_INVALID_ARG, "projection w is null");
+        if (r < 1 || r > 64) return fail(BSA_ERR_INVALID_ARG, "projection width r=%d outside 1..64", r);
+        if (!workspace || workspace_bytes < need)
+            return fail(BSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+        bsa::PoolParams pp{};
+        pp.x[0] = t4(q);
+        pp.x[1] = t4(k);
+        pp.w = w;
+        pp.proj = static_cast<float *>(workspace);
+        pp.B = (int32_t)q->B; pp.H = (int32_t)q->H; pp.N = (int32_t)q->N;
+        pp.nB = (int32_t)nB; pp.r = r;
+        if ((e = bsa::launch_pool_proj(pp, block, (int)q->D, s)) != hipSuccess)
+            return hip_fail(e, "pool launch");
+        bsa::ScoreParams sp{};
+        sp.proj = pp.proj;
+        sp.S = scores;
+        sp.BH = (int32_t)(q->B * q->H);
+        sp.nB = (int32_t)nB;
+        sp.r = r;
+        if ((e = bsa::launch_scores(sp, s)) != hipSuccess) return hip_fail(e, "score launch");
+        return BSA_OK;
+    }
+
+    // EXACT_AVGPOOL
+    const size_t slot = exact_slot_bytes(nB, block);
+    if (!workspace || workspace_bytes < slot)
+        return fail(BSA_ERR_WORKSPACE, "workspace needs at least %zu bytes (%zu for full speed)", slot,
+                    need);
+    int64_t slots = (int64_t)(workspace_bytes / slot);
+    const int64_t items = q->B * q->H * nB;
+    if (slots > items) slots = items;
+    if (slots > bsa::kExactSlots) slots = bsa::kExactSlots;
+    bsa::ExactParams ep{};
+    ep.q = t4(q);
+    ep.k = t4(k);
+    ep.S = scores;
+    ep.scratch = static_cast<float *>(workspace);
+    ep.B = (int32_t)q->B; ep.H = (int32_t)q->H; ep.N = (int32_t)q->N; ep.nB = (int32_t)nB;
+    const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
+    ep.scale_log2 = sc * 1.4426950408889634f;
+    if ((e = bsa::launch_exact_scores(ep, block, (int)q->D, (int)slots, s)) != hipSuccess)
+        return hip_fail(e, "exact score launch");
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+int64_t bsa_select_capacity(int64_t B, int64_t H, int32_t n_blocks, int32_t text_blocks,
+                            const bsa_group *groups, int32_t n_groups)
+{
+    if (B <= 0 || H <= 0 || n_blocks <= 0 || text_blocks < 0 || text_blocks > n_blocks ||
+        n_groups < 0 || (n_groups > 0 && !groups))
+        return -1;
+    const int64_t per_row = select_row_bound(n_blocks, text_blocks, groups, n_groups);
+    return B * H * ((int64_t)text_blocks * n_blocks + (int64_t)(n_blocks - text_blocks) * per_row);
+}
+
+size_t bsa_select_workspace_size(int64_t B, int64_t H, int32_t n_blocks)
+{
+    if (B <= 0 || H <= 0 || n_blocks <= 0) return 0;
+    return (size_t)(B * H * n_blocks) * (size_t)ceil_div(n_blocks, 32) * sizeof(uint32_t);
+}
+
+bsa_status bsa_select_topk(const float *scores, int64_t B, int64_t H, int32_t n_blocks,
+                           int32_t text_blocks, const bsa_group *groups, int32_t n_groups,
+                           int32_t *row_ptr, int32_t *col_idx, int64_t capacity, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    if (!scores || !row_ptr || !col_idx) return fail(BSA_ERR_INVALID_ARG, "null pointer argument");
+    if (B <= 0 || H <= 0 || n_blocks <= 0)
+        return fail(BSA_ERR_INVALID_ARG, "B, H and n_blocks must be positive");
+    if (n_blocks > bsa::kMaxSelectBlocks)
+        return fail(BSA_ERR_UNSUPPORTED, "n_blocks %d above %d", n_blocks, bsa::kMaxSelectBlocks);
+    if (text_blocks < 0 || text_blocks > n_blocks)
+        return fail(BSA_ERR_INVALID_ARG, "text_blocks %d outside [0, %d]", text_blocks, n_blocks);
+    if (n_groups < 0 || n_groups > 8) return fail(BSA_ERR_UNSUPPORTED, "at most 8 groups");
+    if (n_groups > 0 && !groups) return fail(BSA_ERR_INVALID_ARG, "groups is null");
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const bsa_group &x = groups[g];
+        if (x.col_begin < 0 || x.col_end > n_blocks || x.col_begin >= x.col_end || x.k < 0 ||
+            x.k > x.col_end - x.col_begin)
+            return fail(BSA_ERR_INVALID_ARG, "group %d = [%d, %d) k=%d invalid for %d blocks", g,
+                        x.col_begin, x.col_end, x.k, n_blocks);
+    }
+    const int64_t rows = B * H * n_blocks;
+    if (rows >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many rows");
+    const int64_t need = bsa_select_capacity(B, H, n_blocks, text_blocks, groups, n_groups);
+    if (need >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "nnz bound exceeds int32");
+    if (capacity < need)
+        return fail(BSA_ERR_CAPACITY, "capacity %lld below bound %lld", (long long)capacity,
+                    (long long)need);
+    const size_t ws = bsa_select_workspace_size(B, H, n_blocks);
+    if (!workspace || workspace_bytes < ws)
+        return fail(BSA_ERR_WORKSPACE, "workspace needs %zu bytes", ws);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bsa::SelectParams sp{};
+    sp.S = scores;
+    sp.row_ptr = row_ptr;
+    sp.bits = static_cast<uint32_t *>(workspace);
+    sp.rows = rows;
+    sp.nB = n_blocks;
+    sp.words = (int32_t)ceil_div(n_blocks, 32);
+    sp.text_blocks = text_blocks;
+    sp.n_groups = n_groups;
+    for (int32_t g = 0; g < n_groups; ++g) {
+        sp.g_begin[g] = groups[g].col_begin;
+        sp.g_end[g] = groups[g].col_end;
+        sp.g_k[g] = groups[g].k;
+    }
+    hipError_t e;
+    if ((e = bsa::launch_select(sp, s)) != hipSuccess) return hip_fail(e, "select launch");
+    if ((e = bsa::launch_scan(row_ptr, rows, s)) != hipSuccess) return hip_fail(e, "scan launch");
+    bsa::ExpandParams xp{};
+    xp.bits = sp.bits;
+    xp.row_ptr = row_ptr;
+    xp.col_idx = col_idx;
+    xp.rows = rows;
+    xp.capacity = capacity;
+    xp.words = sp.words;
+    if ((e = bsa::launch_expand(xp, s)) != hipSuccess) return hip_fail(e, "expand launch");
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+static bsa_status arrow_check(int64_t B, int64_t H, int64_t N, int32_t block, int64_t text_len,
+                              const int8_t *modes, const int32_t *windows)
+{
+    if (B <= 0 || H <= 0 || N <= 0) return fail(BSA_ERR_INVALID_ARG, "B, H, N must be positive");
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    if (text_len < 0 || text_len > N) return fail(BSA_ERR_INVALID_ARG, "text_len outside [0, N]");
+    if (!modes || !windows) return fail(BSA_ERR_INVALID_ARG, "head_modes / head_windows null");
+    if (H > bsa::kMaxArrowHeads) return fail(BSA_ERR_UNSUPPORTED, "H above %d", bsa::kMaxArrowHeads);
+    if (ceil_div(N, block) > 65536) return fail(BSA_ERR_UNSUPPORTED, "more than 65536 blocks");
+    for (int64_t h = 0; h < H; ++h) {
+        if (modes[h] != BSA_HEAD_FULL && modes[h] != BSA_HEAD_ARROW && modes[h] != BSA_HEAD_SKIP)
+            return fail(BSA_ERR_INVALID_ARG, "head %lld: unknown mode %d", (long long)h, modes[h]);
+        if (modes[h] == BSA_HEAD_ARROW && windows[h] < 0)
+            return fail(BSA_ERR_INVALID_ARG, "head %lld: negative window", (long long)h);
+    }
+    return BSA_OK;
+}
+
+int64_t bsa_arrow_capacity(int64_t B, int64_t H, int64_t N, int32_t block, int64_t text_len,
+                           const int8_t *head_modes, const int32_t *head_windows)
+{
+    if (arrow_check(B, H, N, block, text_len, head_modes, head_windows) != BSA_OK) return -1;
+    const int64_t nB = ceil_div(N, block), tb = ceil_div(text_len, block);
+    int64_t per_batch = 0;
+    for (int64_t h = 0; h < H; ++h) {
+        for (int64_t i = 0; i < nB; ++i) {
+            const int m = head_modes[h];
+            if (m == BSA_HEAD_SKIP) continue;
+            if (m == BSA_HEAD_FULL || i < tb) { per_batch += nB; continue; }
+            const int64_t w = head_windows[h];
+            const int64_t lo = std::max(tb, i - w), hi = std::min(nB - 1, i + w);
+            per_batch += tb + (hi >= lo ? hi - lo + 1 : 0);
+        }
+    }
+    return B * per_batch;
+}
+
+bsa_status bsa_build_arrow_layout(int64_t B, int64_t H, int64_t N, int32_t block, int64_t text_len,
+                                  const int8_t *head_modes, const int32_t *head_windows,
+                                  int32_t *row_ptr, int32_t *col_idx, int64_t capacity, void *stream)
+{
+    bsa_status st = arrow_check(B, H, N, block, text_len, head_modes, head_windows);
+    if (st != BSA_OK) return st;
+    if (!row_ptr || !col_idx) return fail(BSA_ERR_INVALID_ARG, "row_ptr / col_idx null");
+    const int64_t need = bsa_arrow_capacity(B, H, N, block, text_len, head_modes, head_windows);
+    if (need >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "nnz %lld exceeds int32", (long long)need);
+    if (capacity < need)
+        return fail(BSA_ERR_CAPACITY, "capacity %lld below %lld", (long long)capacity, (long long)need);
+    bsa::ArrowParams ap{};
+    ap.row_ptr = row_ptr;
+    ap.col_idx = col_idx;
+    ap.capacity = capacity;
+    ap.per_batch = need / B;
+    ap.B = (int32_t)B;
+    ap.H = (int32_t)H;
+    ap.nB = (int32_t)ceil_div(N, block);
+    ap.text_blocks = (int32_t)ceil_div(text_len, block);
+    for (int64_t h = 0; h < H; ++h) {
+        ap.mode[h] = head_modes[h];
+        ap.window[h] = head_modes[h] == BSA_HEAD_ARROW ? head_windows[h] : 0;
+    }
+    hipError_t e = bsa::launch_arrow(ap, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "arrow launch");
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,
+                       const int32_t *row_ptr, const int32_t *col_idx, const int8_t *head_modes,
+                       const bsa_tensor *o_cache, const float *lse_cache, float scale,
+                       const bsa_tensor *o, float *lse, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSA_OK) return st;
+    if ((st = check_tensor(v, "v")) != BSA_OK) return st;
+    if ((st = check_tensor(o, "o")) != BSA_OK) return st;
+    if (!same_shape(q, k) || !same_shape(q, v) || !same_shape(q, o))
+        return fail(BSA_ERR_INVALID_ARG, "q, k, v and o shapes differ");
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    if (!row_ptr || !col_idx) return fail(BSA_ERR_INVALID_ARG, "row_ptr / col_idx null");
+    if (std::isnan(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
+    const int64_t H = q->H;
+    if (H > bsa::kMaxSkipHeads) return fail(BSA_ERR_UNSUPPORTED, "H above %d", bsa::kMaxSkipHeads);
+    const int64_t nB = ceil_div(q->N, block);
+    if (q->B * H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many query blocks");
+
+    bsa::FwdParams fp{};
+    bool any_skip = false;
+    if (head_modes) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int8_t m = head_modes[h];
+            if (m != BSA_HEAD_FULL && m != BSA_HEAD_ARROW && m != BSA_HEAD_SKIP)
+                return fail(BSA_ERR_INVALID_ARG, "head %lld: unknown mode %d", (long long)h, m);
+            if (m == BSA_HEAD_SKIP) {
+                fp.skip_bits[h >> 5] |= 1u << (h & 31);
+                any_skip = true;
+            }
+        }
+    }
+    if (any_skip) {
+        if ((st = check_tensor(o_cache, "o_cache")) != BSA_OK) return st;
+        if (!same_shape(q, o_cache)) return fail(BSA_ERR_INVALID_ARG, "o_cache shape differs");
+    }
+
+    fp.q = t4(q);
+    fp.k = t4(k);
+    fp.v = t4(v);
+    fp.o = static_cast<uint16_t *>(o->data);
+    fp.o_sb = o->stride_b;
+    fp.o_sh = o->stride_h;
+    fp.o_sn = o->stride_n;
+    fp.lse = lse;
+    fp.row_ptr = row_ptr;
+    fp.col_idx = col_idx;
+    fp.B = (int32_t)q->B;
+    fp.H = (int32_t)H;
+    fp.N = (int32_t)q->N;
+    fp.nB = (int32_t)nB;
+    const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
+    fp.scale_log2 = sc * 1.4426950408889634f;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if ((e = bsa::launch_forward(fp, block, (int)q->D, s)) != hipSuccess)
+        return hip_fail(e, "forward launch");
+    if (any_skip) {
+        bsa::SkipCopyParams cp{};
+        cp.src = t4(o_cache);
+        cp.dst = static_cast<uint16_t *>(o->data);
+        cp.d_sb = o->stride_b;
+        cp.d_sh = o->stride_h;
+        cp.d_sn = o->stride_n;
+        cp.lse_src = lse_cache;
+        cp.lse_dst = lse;
+        cp.B = (int32_t)q->B;
+        cp.H = (int32_t)H;
+        cp.N = (int32_t)q->N;
+        cp.D = (int32_t)q->D;
+        cp.copy_o = !(o_cache->data == o->data && o_cache->stride_b == o->stride_b &&
+                      o_cache->stride_h == o->stride_h && o_cache->stride_n == o->stride_n);
+        std::memcpy(cp.skip_bits, fp.skip_bits, sizeof cp.skip_bits);
+        if (cp.copy_o || (lse_cache && lse && lse_cache != lse))
+            if ((e = bsa::launch_skip_copy(cp, s)) != hipSuccess) return hip_fail(e, "skip copy launch");
+    }
+    return BSA_OK;
+}
+
+}  // extern "C"

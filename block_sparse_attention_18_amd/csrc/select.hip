@@ -1,0 +1,220 @@
+// Top-k block selection on gfx950 (multimodal-DiT write-up, sections 2.2 and
+// 2.3; SparseD notes, isolated selection).
+//
+// Three small kernels:
+//  1. select: one wavefront per query-block row.  Text rows keep every
+//     column; other rows keep the text columns plus, per column group, the
+//     k best columns.  Each group is ranked by a bitonic sort inside the
+//     wavefront: up to 1024 64-bit keys, 16 per lane in registers, exchanged
+//     across lanes with shuffles for strides below 64 and within a lane
+//     above.  A key is (order-preserving bits of the score) << 32 | ~column,
+//     so a descending sort ranks larger scores first and, on equal scores,
+//     the lower column first; -0.0 is folded onto +0.0 before encoding.  The
+//     kept set is a per-row bitmask; its population count is the row length.
+//  2. scan: one workgroup turns the row lengths into row_ptr in place.
+//  3. expand: one wavefront per row writes the set bits as ascending
+//     column indices at row_ptr[row].
+#include "common.h"
+#include "internal.h"
+
+namespace bsa {
+
+__device__ __forceinline__ uint64_t score_key(float s, int col)
+{
+    if (s == 0.f) s = 0.f;   // -0.0 ranks equal to +0.0
+    uint32_t u = __float_as_uint(s);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(col));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+{
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Sort E*64 keys descending; element x = e*64 + lane lives in k[e] of that lane.
+template <int E>
+__device__ __forceinline__ void wave_bitonic_desc(uint64_t (&k)[E])
+{
+    const int lane = threadIdx.x & 63;
+    constexpr int P = E * 64;
+#pragma unroll
+    for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= 64) {
+                const int es = stride / 64;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int pe = e ^ es;
+                    if (pe > e) {
+                        const int x = e * 64 + lane;          // the lower index of the pair
+                        const bool desc = (x & size) == 0;
+                        const uint64_t a = k[e], bb = k[pe];
+                        const bool sw = desc ? (a < bb) : (a > bb);
+                        k[e] = sw ? bb : a;
+                        k[pe] = sw ? a : bb;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int x = e * 64 + lane;
+                    const uint64_t other = shfl_xor_u64(k[e], stride);
+                    const bool lower = (lane & stride) == 0;
+                    const bool desc = (x & size) == 0;
+                    const uint64_t mx = k[e] > other ? k[e] : other;
+                    const uint64_t mn = k[e] > other ? other : k[e];
+                    k[e] = (lower == desc) ? mx : mn;
+                }
+            }
+        }
+    }
+}
+
+template <int E>
+__device__ void select_group(const float *srow, int c0, int c1, int kk, uint32_t *wbits)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int col = c0 + e * 64 + lane;
+        key[e] = col < c1 ? score_key(srow[col], col) : 0ull;   // padding ranks last
+    }
+    wave_bitonic_desc<E>(key);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int x = e * 64 + lane;
+        if (x < kk) {
+            const int col = (int)(~static_cast<uint32_t>(key[e]));
+            atomicOr(&wbits[col >> 5], 1u << (col & 31));
+        }
+    }
+}
+
+__global__ __launch_bounds__(64) void select_kernel(const SelectParams p)
+{
+    __shared__ uint32_t wbits[kMaxSelectBlocks / 32];
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int i = (int)(row % p.nB);
+    const float *srow = p.S + row * p.nB;
+
+    for (int w = lane; w < p.words; w += 64) {
+        uint32_t v = 0u;
+        const int lim = (i < p.text_blocks) ? p.nB : p.text_blocks;   // dense row / text columns
+        const int lo = w * 32;
+        if (lim >= lo + 32) v = 0xFFFFFFFFu;
+        else if (lim > lo) v = (1u << (lim - lo)) - 1u;
+        wbits[w] = v;
+    }
+    __syncthreads();
+    if (i >= p.text_blocks) {
+        for (int g = 0; g < p.n_groups; ++g) {
+            const int c0 = p.g_begin[g], c1 = p.g_end[g], kk = p.g_k[g];
+            const int width = c1 - c0;
+            if (kk <= 0) continue;
+            if (width <= 64) select_group<1>(srow, c0, c1, kk, wbits);
+            else if (width <= 128) select_group<2>(srow, c0, c1, kk, wbits);
+            else if (width <= 256) select_group<4>(srow, c0, c1, kk, wbits);
+            else if (width <= 512) select_group<8>(srow, c0, c1, kk, wbits);
+            else select_group<16>(srow, c0, c1, kk, wbits);
+            __syncthreads();
+        }
+    }
+    int cnt = 0;
+    for (int w = lane; w < p.words; w += 64) {
+        const uint32_t v = wbits[w];
+        p.bits[row * p.words + w] = v;
+        cnt += __popc(v);
+    }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) cnt += __shfl_xor(cnt, d, 64);
+    if (lane == 0) {
+        p.row_ptr[row + 1] = cnt;
+        if (row == 0) p.row_ptr[0] = 0;
+    }
+}
+
+hipError_t launch_select(const SelectParams &p, hipStream_t s)
+{
+    if (p.rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(select_kernel, dim3((unsigned)p.rows), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+// In-place inclusive scan of row_ptr[1 .. rows] by one workgroup.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t *rp, int64_t rows)
+{
+    constexpr int PER = 4;
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int carry = 0;
+    for (int64_t base = 0; base < rows; base += 1024 * PER) {
+        int v[PER];
+        int tsum = 0;
+#pragma unroll
+        for (int a = 0; a < PER; ++a) {
+            const int64_t idx = base + (int64_t)tid * PER + a;
+            v[a] = idx < rows ? rp[1 + idx] : 0;
+            tsum += v[a];
+        }
+        const int incl = wave_incl_scan(tsum);
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        int wpre = 0, total = 0;
+        for (int x = 0; x < 16; ++x) {
+            if (x < wv) wpre += wsum[x];
+            total += wsum[x];
+        }
+        int run = carry + wpre + incl - tsum;
+#pragma unroll
+        for (int a = 0; a < PER; ++a) {
+            const int64_t idx = base + (int64_t)tid * PER + a;
+            run += v[a];
+            if (idx < rows) rp[1 + idx] = run;
+        }
+        carry += total;
+        __syncthreads();
+    }
+    if (tid == 0) rp[0] = 0;
+}
+
+hipError_t launch_scan(int32_t *row_ptr, int64_t rows, hipStream_t s)
+{
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, row_ptr, rows);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(64) void expand_kernel(const ExpandParams p)
+{
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    int64_t start = p.row_ptr[row];
+    for (int w0 = 0; w0 < p.words; w0 += 64) {
+        const int w = w0 + lane;
+        uint32_t v = w < p.words ? p.bits[row * p.words + w] : 0u;
+        const int cnt = __popc(v);
+        const int incl = wave_incl_scan(cnt);
+        int64_t pos = start + incl - cnt;
+        while (v) {
+            const int bit = __ffs(v) - 1;
+            v &= v - 1u;
+            if (pos < p.capacity) p.col_idx[pos] = w * 32 + bit;
+            ++pos;
+        }
+        start += __shfl(incl, 63, 64);
+    }
+}
+
+hipError_t launch_expand(const ExpandParams &p, hipStream_t s)
+{
+    if (p.rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(expand_kernel, dim3((unsigned)p.rows), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace bsa

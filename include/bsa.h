@@ -1,0 +1,201 @@
+/*
+ * bsa.h -- block-sparse attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * A small C ABI over hand-written HIP kernels.  Four calls make up the path:
+ *
+ *   bsa_pool_scores         block scores for content-driven selection
+ *   bsa_select_topk         per query block, keep the top-k key blocks
+ *   bsa_build_arrow_layout  arrow / full / skip block layout per head
+ *   bsa_forward             online-softmax attention over the kept blocks
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory.  Every tensor, score matrix, block list and workspace pointer is
+ * DEVICE memory allocated and owned by the caller.  Arrays documented as
+ * "host" (head modes, windows, groups) are read during the call only.  The
+ * library allocates and frees nothing and keeps no mutable global state, so
+ * calls are reentrant; calls that share output buffers must be ordered by
+ * the caller.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Every
+ * call only enqueues work on it and never synchronises.  Device-side faults
+ * surface at the caller's next synchronisation.
+ *
+ * Errors.  All arguments are validated before anything is enqueued, so a
+ * call that returns an error did no work.  bsa_status_string() names a code;
+ * bsa_last_error() returns a thread-local message describing the most
+ * recent failure on the calling thread.
+ *
+ * Tensors.  Q, K, V, O and the output cache are bfloat16 [B][H][N][D] with
+ * D contiguous and arbitrary element strides for B, H and N (each a
+ * multiple of 8, data 16-byte aligned).  Supported: D in {64, 128}, block
+ * size in {64, 128}, any N >= 1 (a last partial block is allowed).
+ *
+ * Block lists (CSR).  Row r = (b*H + h)*nB + i lists the key blocks kept for
+ * query block i of head (b, h), nB = ceil(N / block): row_ptr int32
+ * [B*H*nB + 1] (row_ptr[0] = 0, non-decreasing) and col_idx int32 [nnz],
+ * strictly ascending within a row.  A block list can be reused by any
+ * number of bsa_forward calls.
+ *
+ * Sources (page title and section the operations are defined in):
+ *  [W]  "Block-sparse attention in multimodal DiT" write-up (lmnt.cn):
+ *       2.2 content-driven block selection, 2.3 cross-modal handling,
+ *       3.1 FlashAttention-style kernel over block indices, 3.2 block size.
+ *  [D]  DiTFastAttnV2 notes (ICCV 2025): head-wise arrow attention,
+ *       head-wise caching, fused kernel with full / skip / arrow(w) modes.
+ *  [S]  SparseD notes (ICLR 2026): isolated selection on avgpool of the
+ *       attention map, computed once and reused.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bsa_status;
+enum {
+    BSA_OK = 0,
+    BSA_ERR_INVALID_ARG = 1,  /* null pointer, bad shape, stride or range   */
+    BSA_ERR_UNSUPPORTED = 2,  /* D, block size or a limit not supported    */
+    BSA_ERR_CAPACITY = 3,     /* col_idx capacity below the required bound */
+    BSA_ERR_WORKSPACE = 4,    /* workspace missing or too small            */
+    BSA_ERR_HIP = 5           /* a HIP runtime call failed                 */
+};
+
+/* Per-head modes [D]: FULL keeps every block pair, ARROW keeps the arrow
+ * pattern with window w, SKIP computes nothing and returns the cached
+ * output of the head. */
+enum { BSA_HEAD_FULL = 0, BSA_HEAD_ARROW = 1, BSA_HEAD_SKIP = 2 };
+
+/* Block scoring modes. */
+enum { BSA_SCORE_MEANPOOL_PROJ = 0, BSA_SCORE_EXACT_AVGPOOL = 1 };
+
+/* A bfloat16 tensor [B][H][N][D] in device memory, D contiguous. */
+typedef struct bsa_tensor {
+    void *data;
+    int64_t B, H, N, D;
+    int64_t stride_b, stride_h, stride_n; /* in elements */
+} bsa_tensor;
+
+/* One top-k budget: keep the k best columns of [col_begin, col_end). */
+typedef struct bsa_group {
+    int32_t col_begin, col_end, k;
+} bsa_group;
+
+/* ------------------------------------------------------------------------
+ * bsa_pool_scores -- block score matrix S [B][H][nB][nB] (fp32, row-major,
+ * device), S[b][h][i][j] scoring query block i against key block j.
+ *
+ * BSA_SCORE_MEANPOOL_PROJ  ([W] 2.2): every block of Q and of K is mean-
+ *   pooled over the tokens it holds, projected by one small linear map
+ *   w [D][r] (fp32, row-major, device; shared by queries, keys and heads,
+ *   no bias) and scored by a dot product:
+ *       S_ij = (W^T qbar_i) . (W^T kbar_j).
+ *   `scale` is ignored.
+ * BSA_SCORE_EXACT_AVGPOOL  ([S] isolated selection): the average over the
+ *   block pair of the post-softmax attention map over all N keys,
+ *       A = softmax_row(scale * Q K^T),  S_ij = mean_{t in i, s in j} A_ts,
+ *   computed per query block without materialising A.  `w` and `r` are
+ *   ignored; scale <= 0 selects 1/sqrt(D).
+ *
+ * workspace: device memory of at least bsa_pool_scores_workspace_size()
+ * bytes (scratch; contents on return are unspecified).
+ * Errors: INVALID_ARG (null pointers, q/k shapes differ, r outside 1..64,
+ * misaligned data or strides), UNSUPPORTED (D or block), WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t bsa_pool_scores_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
+                                      int32_t block, int32_t mode, int32_t r);
+bsa_status bsa_pool_scores(const bsa_tensor *q, const bsa_tensor *k, int32_t block,
+                           int32_t mode, const float *w, int32_t r, float scale,
+                           float *scores, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_select_topk -- CSR block list from a score matrix ([W] 2.2, 2.3;
+ * [S] isolated selection).  For row (b, h, i):
+ *   - a text query block (i < text_blocks) keeps every key block;
+ *   - otherwise it keeps the text key blocks {j < text_blocks} united with,
+ *     for every group g, the k_g columns of [col_begin, col_end) with the
+ *     largest scores; equal scores keep the lower column (-0.0 equals +0.0).
+ * Columns are written ascending.  Scores must be finite.
+ *
+ * scores  : fp32 [B][H][nB][nB] device.   groups: host [n_groups].
+ * row_ptr : int32 [B*H*nB + 1] device (written).
+ * col_idx : int32 [capacity] device (written); capacity must be at least
+ *           bsa_select_capacity(); the actual nnz is row_ptr[B*H*nB].
+ * workspace: at least bsa_select_workspace_size() bytes.
+ * Errors: INVALID_ARG (null pointers, group range outside [0, nB), k larger
+ * than its range, text_blocks outside [0, nB]), UNSUPPORTED (nB > 1024),
+ * CAPACITY, WORKSPACE.
+ * ---------------------------------------------------------------------- */
+int64_t bsa_select_capacity(int64_t B, int64_t H, int32_t n_blocks, int32_t text_blocks,
+                            const bsa_group *groups, int32_t n_groups);
+size_t bsa_select_workspace_size(int64_t B, int64_t H, int32_t n_blocks);
+bsa_status bsa_select_topk(const float *scores, int64_t B, int64_t H, int32_t n_blocks,
+                           int32_t text_blocks, const bsa_group *groups, int32_t n_groups,
+                           int32_t *row_ptr, int32_t *col_idx, int64_t capacity,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_build_arrow_layout -- CSR block list of the arrow layout ([D] head-
+ * wise arrow attention).  Text occupies tokens [0, text_len); every block
+ * holding a text token is a text block, T_b = ceil(text_len / block).
+ *   ARROW head (window w >= 0, in blocks):
+ *       keep(i, j) = i < T_b  or  j < T_b  or  |i - j| <= w
+ *   FULL head : every (i, j);   SKIP head: every row empty.
+ * head_modes int8 [H] and head_windows int32 [H] are host arrays shared by
+ * every batch entry.  capacity must be at least bsa_arrow_capacity().
+ * Errors: INVALID_ARG (unknown mode, negative window, text_len outside
+ * [0, N]), UNSUPPORTED (H > 1024 or nB > 65536), CAPACITY.
+ * ---------------------------------------------------------------------- */
+int64_t bsa_arrow_capacity(int64_t B, int64_t H, int64_t N, int32_t block, int64_t text_len,
+                           const int8_t *head_modes, const int32_t *head_windows);
+bsa_status bsa_build_arrow_layout(int64_t B, int64_t H, int64_t N, int32_t block,
+                                  int64_t text_len, const int8_t *head_modes,
+                                  const int32_t *head_windows, int32_t *row_ptr,
+                                  int32_t *col_idx, int64_t capacity, void *stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_forward -- block-sparse attention forward ([W] 3.1, [D] fused
+ * kernel, [S] sparse attention with a precomputed mask).  For every token
+ * t of a computed head, with i = t / block:
+ *     z_s = scale * Q_t . K_s  for keys s in the blocks of row (b, h, i),
+ *     O_t = sum_s softmax(z)_s V_s   (bfloat16, fp32 accumulation),
+ *     LSE_t = ln sum_s exp(z_s)      (fp32, natural log).
+ * Blocks are visited in CSR order with an online softmax; key blocks are
+ * all-in or all-out (no masking inside a block except past N).  A row with
+ * no kept block gives O = 0 and LSE = -inf.  Column indices outside
+ * [0, nB) are ignored; columns of one row must be distinct.
+ *
+ * head_modes: host int8 [H] or NULL (every head computed).  A SKIP head is
+ * not computed: O[b][h] is copied from o_cache[b][h] bit-exactly (nothing is
+ * copied when o_cache aliases o with the same strides) and LSE from
+ * lse_cache (device fp32 [B][H][N]) when lse_cache is not NULL, else left
+ * untouched ([D] head-wise caching).  o_cache is required iff some head is
+ * SKIP.
+ * scale <= 0 selects 1/sqrt(D).  lse: device fp32 [B][H][N] or NULL.
+ * Errors: INVALID_ARG (null pointers, shape mismatch, misalignment, SKIP
+ * without o_cache), UNSUPPORTED (D or block size).
+ * ---------------------------------------------------------------------- */
+bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                       int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                       const int8_t *head_modes, const bsa_tensor *o_cache,
+                       const float *lse_cache, float scale, const bsa_tensor *o, float *lse,
+                       void *stream);
+
+/* Name of a status code (static string). */
+const char *bsa_status_string(bsa_status status);
+/* Message describing the most recent failure on the calling thread. */
+const char *bsa_last_error(void);
+/* Library version string. */
+const char *bsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

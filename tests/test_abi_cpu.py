@@ -1,0 +1,179 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/bsa.h declares, and rejects bad arguments before enqueuing anything.
+
+Device pointers passed here are fake (never dereferenced): every call below
+must fail in host-side validation, which runs before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_18_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bsa.LIB_PATH),
+                                reason="libbsa.so not built (run __graft_entry__.build())")
+
+FAKE = 0x7F0000000000      # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_symbols_are_exported():
+    lib = ctypes.CDLL(bsa.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in ["bsa_pool_scores", "bsa_select_topk", "bsa_build_arrow_layout", "bsa_forward"]:
+        assert n in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in bsa.h but not exported"
+
+
+def test_status_strings_and_version():
+    lib = bsa.load()
+    for code, name in bsa.STATUS.items():
+        assert lib.bsa_status_string(code).decode() == name
+    assert lib.bsa_status_string(99).decode() == "BSA_ERR_UNKNOWN"
+    assert "gfx950" in bsa.version()
+
+
+def _t(B=1, H=2, N=256, D=64, data=FAKE, sb=None, sh=None, sn=None):
+    sn = D if sn is None else sn
+    sh = N * sn if sh is None else sh
+    sb = H * sh if sb is None else sb
+    return bsa.BsaTensor(data, B, H, N, D, sb, sh, sn)
+
+
+def _fwd(q=None, k=None, v=None, o=None, block=64, rp=FAKE, ci=FAKE, modes=None, oc=None,
+         scale=0.0):
+    lib = bsa.load()
+    q = q or _t()
+    k = k or _t()
+    v = v or _t()
+    o = o or _t()
+    ref = lambda d: None if d is None else ctypes.byref(d)
+    return lib.bsa_forward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), block,
+                           ctypes.c_void_p(rp) if rp else None, ctypes.c_void_p(ci) if ci else None,
+                           modes, ref(oc), None, scale, ctypes.byref(o), None, None)
+
+
+def _err():
+    return bsa.load().bsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=_t(data=0)), 1, "null data"),
+    (dict(q=_t(D=96)), 2, "head dim"),
+    (dict(k=_t(N=128)), 1, "shapes differ"),
+    (dict(q=_t(data=FAKE + 8)), 1, "aligned"),
+    (dict(v=_t(sn=60)), 1, "strides"),
+    (dict(o=_t(sh=-64)), 1, "strides"),
+    (dict(block=32), 2, "block size"),
+    (dict(rp=0), 1, "row_ptr"),
+    (dict(scale=float("nan")), 1, "NaN"),
+])
+def test_forward_validation(kw, code, msg):
+    assert _fwd(**kw) == code
+    assert msg in _err()
+
+
+def test_forward_skip_requires_cache_and_known_modes():
+    modes = (ctypes.c_int8 * 2)(bsa.HEAD_FULL, bsa.HEAD_SKIP)
+    assert _fwd(modes=modes) == 1 and "o_cache" in _err()
+    assert _fwd(modes=modes, oc=_t(N=128)) == 1 and "o_cache" in _err()
+    bad = (ctypes.c_int8 * 2)(0, 7)
+    assert _fwd(modes=bad) == 1 and "unknown mode" in _err()
+
+
+def test_pool_scores_validation():
+    lib = bsa.load()
+    q, k = _t(), _t()
+    call = lambda mode=0, w=FAKE, r=32, ws=FAKE, wsb=1 << 20, block=64, scores=FAKE: lib.bsa_pool_scores(
+        ctypes.byref(q), ctypes.byref(k), block, mode, ctypes.c_void_p(w) if w else None, r, 0.0,
+        ctypes.c_void_p(scores) if scores else None, ctypes.c_void_p(ws) if ws else None, wsb, None)
+    assert call(mode=5) == 2
+    assert call(w=0) == 1 and "projection" in _err()
+    assert call(r=0) == 1 and call(r=65) == 1
+    assert call(wsb=16) == 4 and "workspace" in _err()
+    assert call(ws=0) == 4
+    assert call(block=96) == 2
+    assert call(scores=0) == 1
+    # exact mode needs at least one scratch slot: nB * block floats
+    assert call(mode=1, wsb=4 * 64 * 4 - 4) == 4
+    need = lib.bsa_pool_scores_workspace_size(1, 2, 256, 64, 64, 0, 32)
+    assert need == 2 * 1 * 2 * 4 * 32 * 4
+    need_exact = lib.bsa_pool_scores_workspace_size(1, 2, 256, 64, 64, 1, 0)
+    assert need_exact == (1 * 2 * 4) * 4 * 64 * 4
+
+
+def test_select_validation_and_capacity():
+    lib = bsa.load()
+    G = bsa.BsaGroup
+    g = (G * 2)(G(0, 480, 144), G(480, 512, 10))
+    cap = lib.bsa_select_capacity(1, 32, 512, 0, g, 2)
+    assert cap == 32 * 512 * 154
+    g1 = (G * 1)(G(0, 8, 4))
+    # text rows dense, other rows at most text + k
+    assert lib.bsa_select_capacity(1, 2, 8, 1, g1, 1) == 2 * (8 + 7 * 5)
+    assert lib.bsa_select_workspace_size(1, 2, 40) == 2 * 40 * 2 * 4
+    call = lambda nb=8, tb=1, grp=g1, ng=1, cap=10 ** 6, ws=FAKE, wsb=1 << 20: lib.bsa_select_topk(
+        ctypes.c_void_p(FAKE), 1, 2, nb, tb, grp, ng, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+        cap, ctypes.c_void_p(ws) if ws else None, wsb, None)
+    assert call(nb=2000) == 2
+    assert call(tb=9) == 1
+    assert call(grp=(G * 1)(G(0, 9, 4))) == 1 and "group" in _err()
+    assert call(grp=(G * 1)(G(2, 6, 5))) == 1
+    assert call(grp=(G * 1)(G(5, 5, 0))) == 1
+    assert call(cap=2 * (8 + 7 * 5) - 1) == 3 and "capacity" in _err()
+    assert call(wsb=8) == 4
+    assert call(ng=9) == 2
+
+
+def _arrow_count(nB, tb, w):
+    n = nB - tb
+    if w >= n - 1:
+        return nB * nB
+    return tb * nB + n * tb + n * (2 * w + 1) - w * (w + 1)
+
+
+def test_arrow_validation_and_capacity():
+    lib = bsa.load()
+    H = 3
+    modes = (ctypes.c_int8 * H)(bsa.HEAD_ARROW, bsa.HEAD_FULL, bsa.HEAD_SKIP)
+    wins = (ctypes.c_int32 * H)(8, 0, 0)
+    cap = lib.bsa_arrow_capacity(2, H, 16896, 128, 512, modes, wins)
+    assert cap == 2 * (_arrow_count(132, 4, 8) + 132 * 132)
+    # ragged text: 300 text tokens with block 128 -> 3 text blocks
+    cap2 = lib.bsa_arrow_capacity(1, 1, 4396, 128, 300, (ctypes.c_int8 * 1)(1), (ctypes.c_int32 * 1)(2))
+    assert cap2 == _arrow_count(35, 3, 2)
+    call = lambda B=1, N=1024, block=128, tl=0, m=modes, w=wins, cap=10 ** 7, rp=FAKE: \
+        lib.bsa_build_arrow_layout(B, H, N, block, tl, m, w, ctypes.c_void_p(rp) if rp else None,
+                                   ctypes.c_void_p(FAKE), cap, None)
+    assert call(block=32) == 2
+    assert call(tl=2000) == 1
+    assert call(m=(ctypes.c_int8 * H)(1, 4, 0)) == 1
+    assert call(w=(ctypes.c_int32 * H)(-1, 0, 0)) == 1
+    assert call(cap=5) == 3
+    assert call(rp=0) == 1
+    assert call(B=0) == 1
+    many = (ctypes.c_int8 * 300)(*([0] * 300))
+    wm = (ctypes.c_int32 * 300)(*([0] * 300))
+    assert lib.bsa_build_arrow_layout(1, 300, 1024, 128, 0, many, wm, ctypes.c_void_p(FAKE),
+                                      ctypes.c_void_p(FAKE), 10 ** 7, None) == 2
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsa._desc(q, "q")
+    with pytest.raises(ValueError):
+        bsa._desc(torch.zeros(1, 1, 64, 64), "q")

@@ -1,0 +1,352 @@
+"""GPU parity: every step of the HIP path against the fp64 CPU oracle.
+
+Small cases span several tiles, ragged tails, empty and full rows, strided
+and aliased tensors; the five workloads run at full size with the oracle
+evaluated on sampled rows (or whole small parts).  Oracle inputs never come
+from the GPU: block lists fed to both sides are built by the oracle or by
+the seeded generator."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import block_sparse_attention_18_amd as bsa
+from helpers import (bf16_bits, bf16_to_f64, check_csr_valid, check_forward, check_selection,
+                     csr_rows, dev, sample_rows, to_dev_bf16)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
+
+
+def _run_forward(q, k, v, block, rp, ci, **kw):
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    O, L = bsa.forward(qd, kd, vd, block, _i32(rp), _i32(ci), **kw)
+    torch.cuda.synchronize()
+    return O, L
+
+
+# ---------------------------------------------------------------------------
+# forward, small shapes
+# ---------------------------------------------------------------------------
+FWD_CASES = [
+    (2, 3, 4 * 64 + 17, 64, 64, 101),
+    (1, 2, 5 * 128 + 3, 128, 128, 102),
+    (2, 2, 3 * 128, 64, 128, 103),
+    (1, 3, 6 * 64, 128, 64, 104),
+    (1, 1, 40, 128, 128, 105),          # a single partial block
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,block,seed", FWD_CASES)
+def test_forward_random_block_lists(B, H, N, D, block, seed):
+    _log(f"forward B={B} H={H} N={N} D={D} block={block}")
+    q, k, v = synth.random_qkv(B, H, N, D, seed=seed)
+    nB = -(-N // block)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=seed + 1, density=0.5, empty_rows=1, full_rows=2)
+    O, L = _run_forward(q, k, v, block, rp, ci)
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci)
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "random")
+    # rows of an empty block row are exactly zero with LSE = -inf
+    empty = [x for x in range(B * H * nB) if rp[x] == rp[x + 1]]
+    for x in empty:
+        bh, i = divmod(x, nB)
+        b, h = divmod(bh, H)
+        t0, t1 = i * block, min(N, (i + 1) * block)
+        assert torch.all(O[b, h, t0:t1] == 0)
+        assert torch.all(torch.isneginf(L[b, h, t0:t1]))
+
+
+def test_forward_scale_and_large_logits():
+    B, H, N, D, block = 1, 2, 3 * 128, 128, 128
+    q, k, v = synth.random_qkv(B, H, N, D, seed=110, scale=3.0)
+    nB = N // block
+    rp, ci = synth.random_block_lists(B, H, nB, seed=111, density=0.6)
+    O, L = _run_forward(q, k, v, block, rp, ci, scale=0.2)
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci, scale=0.2)
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "scale 0.2")
+
+
+def test_forward_strided_skip_and_alias():
+    B, H, N, D, block = 2, 4, 3 * 64 + 5, 64, 64
+    q, k, v = synth.random_qkv(B, H, N, D, seed=120)
+    nB = -(-N // block)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=121, density=0.5)
+    modes = np.array([bsa.HEAD_FULL, bsa.HEAD_SKIP, bsa.HEAD_ARROW, bsa.HEAD_SKIP], np.int8)
+    cache = synth.f32_to_bf16(np.random.default_rng(5).standard_normal((B, H, N, D)).astype(np.float32))
+    lse_c = np.random.default_rng(6).standard_normal((B, H, N)).astype(np.float32)
+
+    # [B, N, H, D] storage viewed as [B, H, N, D]: non-contiguous strides
+    def strided(a):
+        t = to_dev_bf16(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+        return t.permute(0, 2, 1, 3)
+    qd, kd, vd = strided(q), strided(k), strided(v)
+    out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev()).permute(0, 2, 1, 3)
+    oc = to_dev_bf16(cache)
+    lc = torch.from_numpy(lse_c).to(dev())
+    O, L = bsa.forward(qd, kd, vd, block, _i32(rp), _i32(ci), head_modes=modes, o_cache=oc,
+                       lse_cache=lc, out=out)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci, modes=modes, o_cache=cache, lse_cache=lse_c)
+    comp = modes != bsa.HEAD_SKIP
+    check_forward(bf16_to_f64(O)[:, comp], L.cpu().numpy()[:, comp].astype(np.float64),
+                  Oo[:, comp], Lo[:, comp], "strided")
+    # skip heads: bit-exact copies of the caches
+    Ob = bf16_bits(O)
+    np.testing.assert_array_equal(Ob[:, ~comp], cache[:, ~comp])
+    np.testing.assert_array_equal(L.cpu().numpy()[:, ~comp], lse_c[:, ~comp])
+
+    # in place: o_cache aliases the output -> skip heads keep their contents
+    o2 = to_dev_bf16(cache)
+    O2, _ = bsa.forward(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), block, _i32(rp), _i32(ci),
+                        head_modes=modes, o_cache=o2, out=o2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(O2)[:, ~comp], cache[:, ~comp])
+    np.testing.assert_array_equal(bf16_bits(O2)[:, comp], Ob[:, comp])
+
+
+def test_forward_is_deterministic():
+    B, H, N, D, block = 1, 4, 8 * 128, 128, 128
+    q, k, v = synth.random_qkv(B, H, N, D, seed=130)
+    rp, ci = synth.random_block_lists(B, H, N // block, seed=131, density=0.5)
+    O1, L1 = _run_forward(q, k, v, block, rp, ci)
+    O2, L2 = _run_forward(q, k, v, block, rp, ci)
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+    assert torch.equal(L1, L2)
+
+
+# ---------------------------------------------------------------------------
+# arrow layout
+# ---------------------------------------------------------------------------
+ARROW_CASES = [
+    (1, 3, 4608, 128, 512, [1, 0, 2], [1, 0, 0]),
+    (2, 4, 4396, 128, 300, [1, 1, 0, 2], [0, 5, 0, 0]),      # ragged text and tail
+    (1, 2, 16896, 128, 512, [1, 1], [8, 200]),
+    (1, 2, 1000, 64, 0, [1, 1], [2, 0]),                      # no text at all
+    (1, 1, 640, 64, 640, [1], [1]),                           # text only
+]
+
+
+@pytest.mark.parametrize("B,H,N,block,text_len,modes,wins", ARROW_CASES)
+def test_arrow_layout_matches_oracle(B, H, N, block, text_len, modes, wins):
+    nB = -(-N // block)
+    tb = -(-text_len // block)
+    rp, ci = bsa.build_arrow_layout(B, H, N, block, text_len, modes, wins, device=dev())
+    torch.cuda.synchronize()
+    rpo, cio = oracle.arrow(B, H, nB, tb, np.array(modes, np.int8), np.array(wins, np.int32))
+    np.testing.assert_array_equal(rp.cpu().numpy(), rpo)
+    np.testing.assert_array_equal(ci.cpu().numpy(), cio)
+
+
+# ---------------------------------------------------------------------------
+# top-k selection on given scores (bit-exact: both sides read the same fp32)
+# ---------------------------------------------------------------------------
+SELECT_CASES = [
+    (1, 2, 8, 1, ((0, 8, 4),), 0),
+    (2, 3, 68, 4, ((4, 68, 16),), 0),
+    (1, 2, 68, 4, ((4, 68, 16),), 3),                         # many exact ties
+    (1, 2, 512, 0, ((0, 480, 144), (480, 512, 10)), 0),
+    (1, 1, 1024, 2, ((2, 1024, 300),), 5),
+    (1, 2, 100, 0, ((0, 100, 100), (0, 1, 1)), 0),            # k = width; overlapping groups
+    (1, 2, 70, 70, ((0, 70, 3),), 0),                         # every row is a text row
+]
+
+
+@pytest.mark.parametrize("B,H,nB,tb,groups,ties", SELECT_CASES)
+def test_select_matches_oracle(B, H, nB, tb, groups, ties):
+    S = synth.random_scores(B, H, nB, seed=140 + nB + ties, tie_levels=ties)
+    if ties:
+        S[..., ::7] = -0.0
+        S[..., 1::7] = 0.0
+    rp, ci = bsa.select_topk(torch.from_numpy(S).to(dev()), tb, groups)
+    torch.cuda.synchronize()
+    rpo, cio = oracle.select(S, tb, groups)
+    rp = rp.cpu().numpy()
+    np.testing.assert_array_equal(rp, rpo)
+    np.testing.assert_array_equal(ci.cpu().numpy()[:rp[-1]], cio)
+
+
+# ---------------------------------------------------------------------------
+# block scores
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,N,D,block", [(2, 3, 5 * 64 + 9, 64, 64), (1, 2, 4 * 128, 128, 128),
+                                           (1, 2, 3 * 128 + 1, 64, 128)])
+def test_meanpool_scores_and_selection(B, H, N, D, block):
+    q, k, _ = synth.random_qkv(B, H, N, D, seed=150 + N)
+    w = np.random.default_rng(151).standard_normal((D, 32)).astype(np.float32) / math.sqrt(D)
+    S = bsa.pool_scores(to_dev_bf16(q), to_dev_bf16(k), block, bsa.SCORE_MEANPOOL_PROJ,
+                        w=torch.from_numpy(w).to(dev()))
+    torch.cuda.synchronize()
+    So = oracle.scores_meanpool_proj(q, k, block, w)
+    Sg = S.cpu().numpy().astype(np.float64)
+    scale = np.abs(So).max(axis=-1, keepdims=True)
+    assert np.all(np.abs(Sg - So) <= 1e-5 * scale + 1e-7)
+    nB = So.shape[-1]
+    tb, groups = 1, ((1, nB, max(1, nB // 3)),)
+    rp, ci = bsa.select_topk(S, tb, groups)
+    torch.cuda.synchronize()
+    rpo, cio = oracle.select(So, tb, groups)
+    rp = rp.cpu().numpy()
+    g_rows = csr_rows(rp, ci.cpu().numpy())
+    qb = np.tile(np.arange(nB), B * H)
+    check_selection(g_rows, csr_rows(rpo, cio), So.reshape(-1, nB), qb, tb, groups)
+
+
+@pytest.mark.parametrize("B,H,N,D,block", [(1, 2, 6 * 64 + 10, 64, 64), (1, 2, 5 * 128, 128, 128),
+                                           (2, 1, 3 * 128 + 77, 128, 128)])
+def test_exact_scores_small(B, H, N, D, block):
+    q, k, _ = synth.random_qkv(B, H, N, D, seed=160 + N, scale=1.5)
+    S = bsa.pool_scores(to_dev_bf16(q), to_dev_bf16(k), block, bsa.SCORE_EXACT_AVGPOOL)
+    torch.cuda.synchronize()
+    So = oracle.scores_exact_avgpool(q, k, block)
+    Sg = S.cpu().numpy().astype(np.float64)
+    scale = np.abs(So).max(axis=-1, keepdims=True)
+    err = np.abs(Sg - So) / scale
+    assert err.max() <= 2e-5, f"max rel err {err.max():.2e}"
+    # a workspace of a single slot gives the same bits (persistent workgroups)
+    nB = So.shape[-1]
+    ws = torch.empty(nB * block * 4, dtype=torch.uint8, device=dev())
+    S1 = bsa.pool_scores(to_dev_bf16(q), to_dev_bf16(k), block, bsa.SCORE_EXACT_AVGPOOL, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S1)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+def _workload_forward_check(wl, x, rp, ci, n_sample, seed, must_blocks=(), modes=None):
+    B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
+    kw = {}
+    if modes is not None:
+        kw = dict(head_modes=modes, o_cache=to_dev_bf16(x["o_cache"]) if "o_cache" in x else None,
+                  lse_cache=torch.from_numpy(x["lse_cache"]).to(dev()) if "lse_cache" in x else None)
+    O, L = _run_forward(x["q"], x["k"], x["v"], block, rp, ci, **kw)
+    must = []
+    for (b, h, i) in must_blocks:
+        t0 = i * block
+        must += [((b * H + h) * N + t) for t in range(t0, min(N, t0 + block))]
+    rows = sample_rows(B, H, N, n_sample, seed, must)
+    if modes is not None:
+        rows = rows[modes[(rows // N) % H] != bsa.HEAD_SKIP]
+    Oo, Lo = oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=rows)
+    Og = bf16_to_f64(O).reshape(-1, D)[rows]
+    Lg = L.cpu().numpy().reshape(-1)[rows].astype(np.float64)
+    mx, mean = check_forward(Og, Lg, Oo, Lo, wl.name)
+    _log(f"{wl.name}: {len(rows)} sampled rows, max|dO|={mx:.2e} mean|dO|={mean:.2e}")
+    return O, L
+
+
+@pytest.mark.slow
+def test_workload_c1_full_chain():
+    wl = synth.WORKLOADS["C1"]
+    x = synth.make_inputs(wl)
+    nB, tb = wl.n_blocks, wl.text_blocks
+    qd, kd = to_dev_bf16(x["q"]), to_dev_bf16(x["k"])
+    S = bsa.pool_scores(qd, kd, wl.block, wl.score_mode, w=torch.from_numpy(x["w"]).to(dev()))
+    rp, ci = bsa.select_topk(S, tb, wl.groups)
+    torch.cuda.synchronize()
+    So = oracle.scores_meanpool_proj(x["q"], x["k"], wl.block, x["w"])
+    rpo, cio = oracle.select(So, tb, wl.groups)
+    g_rows = csr_rows(rp.cpu().numpy(), ci.cpu().numpy())
+    qb = np.tile(np.arange(nB), wl.B * wl.H)
+    differ = check_selection(g_rows, csr_rows(rpo, cio), So.reshape(-1, nB), qb, tb, wl.groups)
+    counts = np.diff(rpo)
+    assert counts[0] == nB and set(counts[1:nB].tolist()) <= {4, 5}
+    # forward on the oracle's block list, every row
+    O, L = _run_forward(x["q"], x["k"], x["v"], wl.block, rpo, cio)
+    Oo, Lo = oracle.forward(x["q"], x["k"], x["v"], wl.block, rpo, cio)
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "C1")
+    if differ == 0:   # GPU list identical: the end-to-end GPU chain gives the same bits
+        O2, _ = bsa.forward(qd, kd, to_dev_bf16(x["v"]), wl.block, rp, ci)
+        torch.cuda.synchronize()
+        assert torch.equal(O.view(torch.int16), O2.view(torch.int16))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["C2", "C4"])
+def test_workload_arrow(name):
+    wl = synth.WORKLOADS[name]
+    x = synth.make_inputs(wl)
+    modes, wins = x["head_modes"], x["head_windows"]
+    nB, tb = wl.n_blocks, wl.text_blocks
+    rp, ci = bsa.build_arrow_layout(wl.B, wl.H, wl.N, wl.block, wl.text_len, modes, wins, device=dev())
+    torch.cuda.synchronize()
+    rpo, cio = oracle.arrow(wl.B, wl.H, nB, tb, modes, wins)
+    np.testing.assert_array_equal(rp.cpu().numpy(), rpo)
+    np.testing.assert_array_equal(ci.cpu().numpy(), cio)
+    comp_heads = [h for h in range(wl.H) if modes[h] != bsa.HEAD_SKIP]
+    must = [(0, comp_heads[0], 0), (0, comp_heads[-1], nB - 1), (0, comp_heads[len(comp_heads) // 2], nB // 2)]
+    O, L = _workload_forward_check(wl, x, rpo, cio, 384, seed=170, must_blocks=must, modes=modes)
+    skip = modes == bsa.HEAD_SKIP
+    if skip.any():
+        np.testing.assert_array_equal(bf16_bits(O)[:, skip], x["o_cache"][:, skip])
+        np.testing.assert_array_equal(L.cpu().numpy()[:, skip], x["lse_cache"][:, skip])
+
+
+@pytest.mark.slow
+def test_workload_c3_content_driven():
+    wl = synth.WORKLOADS["C3"]
+    x = synth.make_inputs(wl)
+    nB, tb = wl.n_blocks, wl.text_blocks
+    S = bsa.pool_scores(to_dev_bf16(x["q"]), to_dev_bf16(x["k"]), wl.block, wl.score_mode,
+                        w=torch.from_numpy(x["w"]).to(dev()))
+    rp, ci = bsa.select_topk(S, tb, wl.groups)
+    torch.cuda.synchronize()
+    So = oracle.scores_meanpool_proj(x["q"], x["k"], wl.block, x["w"])
+    Sg = S.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(Sg - So) <= 1e-5 * np.abs(So).max(axis=-1, keepdims=True) + 1e-7)
+    rpo, cio = oracle.select(So, tb, wl.groups)
+    rpg = rp.cpu().numpy()
+    g_rows = csr_rows(rpg, ci.cpu().numpy())
+    qb = np.tile(np.arange(nB), wl.B * wl.H)
+    differ = check_selection(g_rows, csr_rows(rpo, cio), So.reshape(-1, nB), qb, tb, wl.groups)
+    _log(f"C3: {differ} of {len(qb)} rows differ only by near-ties")
+    assert rpo[-1] == wl.B * wl.H * (tb * nB + (nB - tb) * (tb + 16))
+    _workload_forward_check(wl, x, rpo, cio, 512, seed=171, must_blocks=[(1, 15, 0), (0, 3, nB - 1)])
+
+
+@pytest.mark.slow
+def test_workload_c5_exact_selection_and_forward():
+    wl = synth.WORKLOADS["C5"]
+    _log("C5: generating inputs")
+    x = synth.make_inputs(wl)
+    nB, tb = wl.n_blocks, wl.text_blocks
+    qd, kd = to_dev_bf16(x["q"]), to_dev_bf16(x["k"])
+    _log("C5: exact scores on the GPU")
+    S = bsa.pool_scores(qd, kd, wl.block, wl.score_mode)
+    rp, ci = bsa.select_topk(S, tb, wl.groups)
+    torch.cuda.synchronize()
+    rpg, cig = rp.cpu().numpy(), ci.cpu().numpy()
+    check_csr_valid(rpg, cig[:rpg[-1]], nB)
+    assert np.all(np.diff(rpg) == 154)
+    # the oracle scores a sample of query-block rows exactly
+    r = np.random.default_rng(180)
+    rows = sorted(set(r.choice(wl.B * wl.H * nB, size=10, replace=False).tolist()) | {0, nB - 1, 31 * nB + 479})
+    _log(f"C5: oracle exact scores for {len(rows)} query blocks")
+    So = oracle.scores_exact_avgpool(x["q"], x["k"], wl.block, rows=rows)
+    Sg = S.cpu().numpy().reshape(-1, nB)[rows].astype(np.float64)
+    rel = np.abs(Sg - So) / np.abs(So).max(axis=-1, keepdims=True)
+    assert rel.max() <= 2e-5, f"C5 exact score rel err {rel.max():.2e}"
+    np.testing.assert_allclose(So.sum(-1) * wl.block, 1.0, rtol=1e-9)
+    qb = [row % nB for row in rows]
+    rpo, cio = oracle.select_rows(So, qb, tb, wl.groups)
+    g_rows = [cig[rpg[row]:rpg[row + 1]].tolist() for row in rows]
+    differ = check_selection(g_rows, csr_rows(rpo, cio), So, qb, tb, wl.groups)
+    _log(f"C5: {differ} of {len(rows)} sampled rows differ only by near-ties")
+    del S, qd, kd
+    torch.cuda.empty_cache()
+    # forward on a generator-built block list of the same shape
+    rps, cis = synth.block_lists_with_counts(wl.B, wl.H, nB, wl.groups, tb, seed=181)
+    _workload_forward_check(wl, x, rps, cis, 256, seed=182, must_blocks=[(0, 7, 0), (0, 31, nB - 1)])
