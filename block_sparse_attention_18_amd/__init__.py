@@ -256,6 +256,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
     for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if col_idx.numel() == 0:
+        # a block list with no entries: the kernels never read col_idx, but the
+        # C ABI wants a valid pointer
+        col_idx = torch.zeros(1, dtype=torch.int32, device=row_ptr.device)
     modes = None if head_modes is None else _host_i8(head_modes, H)
     dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
     dc = _desc(o_cache, "o_cache")

@@ -71,7 +71,9 @@ def test_forward_random_block_lists(B, H, N, D, block, seed):
 
 def test_forward_scale_and_large_logits():
     B, H, N, D, block = 1, 2, 3 * 128, 128, 128
-    q, k, v = synth.random_qkv(B, H, N, D, seed=110, scale=3.0)
+    # large logits (Q, K with sigma 3), unit-scale V as in every workload
+    q, k, _ = synth.random_qkv(B, H, N, D, seed=110, scale=3.0)
+    _, _, v = synth.random_qkv(B, H, N, D, seed=112)
     nB = N // block
     rp, ci = synth.random_block_lists(B, H, nB, seed=111, density=0.6)
     O, L = _run_forward(q, k, v, block, rp, ci, scale=0.2)
