@@ -34,15 +34,13 @@ template <int BETA, int D>
 struct FwdShape {
     static constexpr int NW = BETA / 32;          // waves per workgroup
     static constexpr int NT = NW * 64;            // threads per workgroup
-    static constexpr int KT = BETA / 32;          // 32-key sub-tiles per block
+    static constexpr int SUB = BETA / 64;         // 64-key sub-tiles per block
     static constexpr int QS = D / 16;             // k-steps of S^T over d
     static constexpr int DT = D / 32;             // 32-row d tiles of O^T
-    static constexpr int KCH = D / 8;             // 16-byte chunks per K row
-    static constexpr int VCH = BETA / 8;          // 16-byte chunks per V^T row
-    static constexpr int K_ITEMS = BETA * KCH;    // 16-byte chunks per K tile
-    static constexpr int V_ITEMS = (BETA / 4) * (D / 8);   // (4 keys x 8 d) items per V tile
-    static constexpr size_t LDS_BYTES = 2u * BETA * D * sizeof(uint16_t);
-    static_assert(K_ITEMS % NT == 0 && V_ITEMS % NT == 0, "tile split");
+    static constexpr int KCH = D / 8;             // 16-byte chunks per K / V row
+    static constexpr int TILE = 64 * D;           // bf16 elements of one 64-key K or V tile
+    static constexpr int DMA = 64 * KCH / NT;     // 16-byte loads per lane per tile
+    static_assert(64 * KCH % NT == 0, "tile split");
 };
 
 // Row of the K tile fed to A-operand row n of a 32-key sub-tile.
@@ -51,22 +49,189 @@ __device__ __forceinline__ int perm_row(int n)
     return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 }
 
-__device__ __forceinline__ uint32_t u4_word(const uint4 &u, int w)
+// XOR swizzles of the 16-byte chunk index within a row of the K and V tiles.
+// K: the 16 rows read by one quarter-wave land on 16 distinct chunk slots.
+// V: the 4 rows x 4 chunks read by one half-wave transpose load land on 16
+// distinct chunk slots.  (Rows are 256 B for D = 128, 128 B for D = 64.)
+template <int D>
+__device__ __forceinline__ int kswz(int row)
 {
-    return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row)
+{
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_desc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Lazy rescaling: the running reference max only moves when a sub-tile's max
+// exceeds it by more than this (log2 units), so the O rescale is skipped for
+// most sub-tiles; probabilities stay below 2^8 relative to the reference.
+constexpr float kRescaleSlack = 8.0f;
+
+// Per-lane state of one wave: its 32 queries' Q^T fragments, O^T
+// accumulators and online-softmax statistics.
+template <int BETA, int D>
+struct WaveState {
+    bf16x8 qf[FwdShape<BETA, D>::QS];
+    f32x16 oacc[FwdShape<BETA, D>::DT];
+    float m_run;   // reference max, log2-scaled domain
+    float l_run;   // running sum over this lane's keys
+};
+
+// Issue the copies of one 64-key sub-tile (K and V, starting at key k0)
+// straight from global memory into LDS.  Lane l of load x writes the 16-byte
+// slot (x*NW + wave)*64 + l; slot s holds row s / KCH, chunk (s % KCH) XOR the
+// row's swizzle.  A partial tile repeats its last key (those scores are
+// masked).
+template <int BETA, int D>
+__device__ __forceinline__ void load_subtile(uint16_t *__restrict__ Kd, uint16_t *__restrict__ Vd,
+                                             __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                             const FwdParams &p, int k0, int wv, int lane)
+{
+    using Sh = FwdShape<BETA, D>;
+    const int rows = min(64, p.N - k0);
+    const uint32_t ks = (uint32_t)((int64_t)k0 * p.k.sn * 2);
+    const uint32_t vs = (uint32_t)((int64_t)k0 * p.v.sn * 2);
+#pragma unroll
+    for (int x = 0; x < Sh::DMA; ++x) {
+        const int slot = (x * Sh::NW + wv) * 64 + lane;
+        const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
+        const int rs = min(r, rows - 1);
+        const int wbase = (x * Sh::NW + wv) * 64 * 8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            krs, (lds_void *)(Kd + wbase), 16, (uint32_t)(rs * p.k.sn * 2 + ((ps ^ kswz<D>(r)) * 16)), ks,
+            0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vrs, (lds_void *)(Vd + wbase), 16, (uint32_t)(rs * p.v.sn * 2 + ((ps ^ vswz<D>(r)) * 16)), vs,
+            0, 0);
+    }
+}
+
+// One pipeline step: start copying the next sub-tile into the other buffer
+// (if there is one), then fold the current sub-tile (keys k0 .. k0+63 in
+// Kc / Vc) into the wave's online softmax.  The restrict-qualified buffers
+// tell the compiler that the copies in flight do not alias the tiles read.
+template <int BETA, int D>
+__device__ __forceinline__ void pipeline_step(
+    const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vc, uint16_t *__restrict__ Kn,
+    uint16_t *__restrict__ Vn, bool prefetch, int k0n, bool compute, int k0,
+    __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const FwdParams &p, int wv, int lane,
+    WaveState<BETA, D> &st)
+{
+    using Sh = FwdShape<BETA, D>;
+    if (prefetch) load_subtile<BETA, D>(Kn, Vn, krs, vrs, p, k0n, wv, lane);
+    if (!compute) return;
+    const int hl = lane >> 5, n = lane & 31;
+    const float c = p.scale_log2;
+
+    // S^T (64 keys x 32 queries)
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+        const int r = kt * 32 + perm_row(n);
+#pragma unroll
+        for (int s = 0; s < Sh::QS; ++s) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8 *>(Kc + r * D + (((2 * s + hl) ^ kswz<D>(r)) * 8));
+            sacc[kt] = mfma32x32x16(a, st.qf[s], sacc[kt]);
+        }
+    }
+    if (k0 + 64 > p.N) {   // partial last tile: keys past N do not exist
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + kt * 32 + perm_row(8 * (r >> 2) + 4 * hl + (r & 3));
+                if (key >= p.N) sacc[kt][r] = -INFINITY;
+            }
+    }
+    // online softmax for this lane's query, lazily rescaled
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    if (__ballot(mx > st.m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(st.m_run, mx);
+        const float alpha = (st.m_run == m_new) ? 1.f : fast_exp2(st.m_run - m_new);
+        st.m_run = m_new;
+        st.l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < Sh::DT; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[d][r] *= alpha;
+    }
+    const float mr = st.m_run;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(__builtin_fmaf(sacc[kt][r], c, -mr));
+            sacc[kt][r] = pr;
+            st.l_run += pr;
+        }
+
+    // O^T += V^T P^T ; V^T fragments come from row-major V by transposing LDS
+    // reads (lane 4r + c of each 16-lane group names row r, columns
+    // 4c..4c+3; lane x of the group receives column x of rows 0..3)
+    const int G = lane >> 4, jl = lane & 15;
+    const int kbase = 8 * (G >> 1), dbase = 16 * (G & 1);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            uint4 pk;
+            pk.x = pack_bf16x2(sacc[kt][8 * u + 0], sacc[kt][8 * u + 1]);
+            pk.y = pack_bf16x2(sacc[kt][8 * u + 2], sacc[kt][8 * u + 3]);
+            pk.z = pack_bf16x2(sacc[kt][8 * u + 4], sacc[kt][8 * u + 5]);
+            pk.w = pack_bf16x2(sacc[kt][8 * u + 6], sacc[kt][8 * u + 7]);
+            const bf16x8 pf = as_bf16x8(pk);
+#pragma unroll
+            for (int d = 0; d < Sh::DT; ++d) {
+                s16x4 h2[2];
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int vr = kt * 32 + 16 * u + kbase + 4 * pp + (jl >> 2);
+                    const int dc = 32 * d + dbase + 4 * (jl & 3);
+                    const int pos = (dc >> 3) ^ vswz<D>(vr);
+                    const uint16_t *src = Vc + vr * D + pos * 8 + (dc & 4);
+                    h2[pp] = __builtin_bit_cast(
+                        s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                   (__attribute__((address_space(3))) bf16x4 *)src));
+                }
+                const bf16x8 a =
+                    __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                st.oacc[d] = mfma32x32x16(a, pf, st.oacc[d]);
+            }
+        }
+    }
 }
 
 template <int BETA, int D>
-__global__ __launch_bounds__(BETA / 32 * 64) void fwd_kernel(const FwdParams p)
+__global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kernel(const FwdParams p)
 {
     using Sh = FwdShape<BETA, D>;
-    extern __shared__ __align__(16) uint16_t lds[];
-    uint16_t *Ks = lds;                 // [BETA][D], chunk c of row r at (c ^ r % KCH)
-    uint16_t *Vt = lds + BETA * D;      // [D][BETA], chunk c of row d at (c ^ d % VCH)
+    // two buffers, each a 64-key K tile followed by a 64-key V tile
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * Sh::TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane >> 5;           // lane half
     const int n = lane & 31;
 
@@ -80,160 +245,77 @@ __global__ __launch_bounds__(BETA / 32 * 64) void fwd_kernel(const FwdParams p)
     const int64_t row = (int64_t)bh * p.nB + i;
     const int e0 = p.row_ptr[row];
     const int e1 = p.row_ptr[row + 1];
+    const int T = (e1 > e0 ? e1 - e0 : 0) * Sh::SUB;   // 64-key sub-tiles to visit
 
     const uint16_t *qb = p.q.p + b * p.q.sb + hh * p.q.sh;
     const uint16_t *kb = p.k.p + b * p.k.sb + hh * p.k.sh;
     const uint16_t *vb = p.v.p + b * p.v.sb + hh * p.v.sh;
 
+    WaveState<BETA, D> st;
     // Q^T fragments: lane (hl, n) holds query row n, d = 16 s + 8 hl .. +7.
     const int qrow = i * BETA + wv * 32 + n;
-    bf16x8 qf[Sh::QS];
 #pragma unroll
     for (int s = 0; s < Sh::QS; ++s) {
         uint4 u = qrow < p.N ? ld_g16(qb + (int64_t)qrow * p.q.sn + 16 * s + 8 * hl) : zero_u4();
-        qf[s] = as_bf16x8(u);
+        st.qf[s] = as_bf16x8(u);
     }
+#pragma unroll
+    for (int d = 0; d < Sh::DT; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.oacc[d][r] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
 
-    f32x16 oacc[Sh::DT];
-#pragma unroll
-    for (int t = 0; t < Sh::DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[t][r] = 0.f;
-    float m_run = -INFINITY;   // running max, log2-scaled domain
-    float l_run = 0.f;         // running sum over this lane's keys
-    const float c = p.scale_log2;
+    const __amdgpu_buffer_rsrc_t krs = buffer_desc(kb, (uint32_t)(((int64_t)(p.N - 1) * p.k.sn + D) * 2));
+    const __amdgpu_buffer_rsrc_t vrs = buffer_desc(vb, (uint32_t)(((int64_t)(p.N - 1) * p.v.sn + D) * 2));
 
-    for (int e = e0; e < e1; ++e) {
-        const int j = p.col_idx[e];
-        if ((unsigned)j >= (unsigned)p.nB) continue;
-        const int key0 = j * BETA;
+    // Sub-tile t: key block col_idx[e0 + t / SUB], keys 64 (t % SUB) .. +63.
+    // An entry outside [0, nB) is ignored: its copy reads block 0 and its
+    // compute is skipped.
+    auto tile_key0 = [&](int t, bool &valid) {
+        const int j = __builtin_amdgcn_readfirstlane(p.col_idx[e0 + t / Sh::SUB]);
+        valid = (unsigned)j < (unsigned)p.nB;
+        return (valid ? j * BETA : 0) + 64 * (t % Sh::SUB);
+    };
 
-        __syncthreads();   // every wave is done reading the previous tile
-#pragma unroll
-        for (int it = 0; it < Sh::K_ITEMS / Sh::NT; ++it) {
-            const int c16 = tid + it * Sh::NT;
-            const int r = c16 / Sh::KCH, cc = c16 % Sh::KCH;
-            const int key = key0 + r;
-            uint4 u = key < p.N ? ld_g16(kb + (int64_t)key * p.k.sn + cc * 8) : zero_u4();
-            *reinterpret_cast<uint4 *>(Ks + r * D + ((cc ^ (r % Sh::KCH)) * 8)) = u;
-        }
-#pragma unroll
-        for (int it = 0; it < Sh::V_ITEMS / Sh::NT; ++it) {
-            const int item = tid + it * Sh::NT;
-            const int q4 = (item % 16) + 16 * (item / (16 * (D / 8)));   // key quad
-            const int cd = (item / 16) % (D / 8);                        // d chunk
-            uint4 x[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int key = key0 + 4 * q4 + a;
-                x[a] = key < p.N ? ld_g16(vb + (int64_t)key * p.v.sn + cd * 8) : zero_u4();
-            }
-#pragma unroll
-            for (int ee = 0; ee < 8; ++ee) {
-                const int wd = ee >> 1;
-                uint32_t lo, hi;
-                if (ee & 1) {
-                    lo = (u4_word(x[0], wd) >> 16) | (u4_word(x[1], wd) & 0xFFFF0000u);
-                    hi = (u4_word(x[2], wd) >> 16) | (u4_word(x[3], wd) & 0xFFFF0000u);
-                } else {
-                    lo = (u4_word(x[0], wd) & 0xFFFFu) | (u4_word(x[1], wd) << 16);
-                    hi = (u4_word(x[2], wd) & 0xFFFFu) | (u4_word(x[3], wd) << 16);
-                }
-                const int d = cd * 8 + ee;
-                const int pos = q4 ^ (2 * (d % Sh::VCH));
-                *reinterpret_cast<uint2 *>(Vt + d * BETA + 4 * pos) = make_uint2(lo, hi);
-            }
-        }
-        __syncthreads();
+    bool valid = false;
+    int k0 = 0;
+    if (T > 0) {
+        k0 = tile_key0(0, valid);
+        load_subtile<BETA, D>(smem, smem + Sh::TILE, krs, vrs, p, k0, wv, lane);
+    }
+    __syncthreads();   // Q in registers; sub-tile 0 in LDS
 
-        // S^T (keys x queries) for the BETA keys of this block
-        f32x16 sacc[Sh::KT];
-#pragma unroll
-        for (int kt = 0; kt < Sh::KT; ++kt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-            const int r = kt * 32 + perm_row(n);
-#pragma unroll
-            for (int s = 0; s < Sh::QS; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    Ks + r * D + (((2 * s + hl) ^ (r % Sh::KCH)) * 8));
-                sacc[kt] = mfma32x32x16(a, qf[s], sacc[kt]);
-            }
-        }
-        if (key0 + BETA > p.N) {   // partial last block: keys past N do not exist
-#pragma unroll
-            for (int kt = 0; kt < Sh::KT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + kt * 32 + perm_row(8 * (r >> 2) + 4 * hl + (r & 3));
-                    if (key >= p.N) sacc[kt][r] = -INFINITY;
-                }
-        }
-
-        // online softmax for this lane's query
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < Sh::KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx * c);
-        const float alpha = (m_run == m_new) ? 1.f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        float ls = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < Sh::KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pr = fast_exp2(__builtin_fmaf(sacc[kt][r], c, -m_new));
-                sacc[kt][r] = pr;
-                ls += pr;
-            }
-        l_run = l_run * alpha + ls;
-#pragma unroll
-        for (int t = 0; t < Sh::DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int kt = 0; kt < Sh::KT; ++kt) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                uint4 pk;
-                pk.x = pack_bf16x2(sacc[kt][8 * u + 0], sacc[kt][8 * u + 1]);
-                pk.y = pack_bf16x2(sacc[kt][8 * u + 2], sacc[kt][8 * u + 3]);
-                pk.z = pack_bf16x2(sacc[kt][8 * u + 4], sacc[kt][8 * u + 5]);
-                pk.w = pack_bf16x2(sacc[kt][8 * u + 6], sacc[kt][8 * u + 7]);
-                const bf16x8 pf = as_bf16x8(pk);
-                const int key8 = 4 * kt + 2 * u + hl;
-#pragma unroll
-                for (int t = 0; t < Sh::DT; ++t) {
-                    const int d = t * 32 + n;
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        Vt + d * BETA + 8 * (key8 ^ (d % Sh::VCH)));
-                    oacc[t] = mfma32x32x16(a, pf, oacc[t]);
-                }
-            }
-        }
+    for (int t = 0; t < T; ++t) {
+        uint16_t *cur = smem + (t & 1) * 2 * Sh::TILE;
+        uint16_t *nxt = smem + ((t & 1) ^ 1) * 2 * Sh::TILE;
+        bool valid_n = false;
+        int k0n = 0;
+        const bool prefetch = t + 1 < T;
+        if (prefetch) k0n = tile_key0(t + 1, valid_n);
+        pipeline_step<BETA, D>(cur, cur + Sh::TILE, nxt, nxt + Sh::TILE, prefetch, k0n, valid, k0, krs,
+                               vrs, p, wv, lane, st);
+        __syncthreads();   // sub-tile t + 1 landed for every wave; buffer of t is free
+        valid = valid_n;
+        k0 = k0n;
     }
 
     // epilogue: normalise and store O (bf16) and LSE (natural log)
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < p.N) {
         uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)qrow * p.o_sn;
 #pragma unroll
-        for (int t = 0; t < Sh::DT; ++t)
+        for (int d = 0; d < Sh::DT; ++d)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                uint2 st;
-                st.x = pack_bf16x2(oacc[t][4 * g + 0] * inv, oacc[t][4 * g + 1] * inv);
-                st.y = pack_bf16x2(oacc[t][4 * g + 2] * inv, oacc[t][4 * g + 3] * inv);
-                *reinterpret_cast<uint2 *>(orow + t * 32 + 8 * g + 4 * hl) = st;
+                uint2 sv;
+                sv.x = pack_bf16x2(st.oacc[d][4 * g + 0] * inv, st.oacc[d][4 * g + 1] * inv);
+                sv.y = pack_bf16x2(st.oacc[d][4 * g + 2] * inv, st.oacc[d][4 * g + 3] * inv);
+                *reinterpret_cast<uint2 *>(orow + d * 32 + 8 * g + 4 * hl) = sv;
             }
         if (p.lse && hl == 0) {
-            const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+            const float lse = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
             p.lse[(int64_t)bh * p.N + qrow] = lse;
         }
     }
@@ -243,14 +325,10 @@ template <int BETA, int D>
 static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s)
 {
     using Sh = FwdShape<BETA, D>;
-    auto kern = fwd_kernel<BETA, D>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)Sh::LDS_BYTES);
-    if (err != hipSuccess) return err;
     const unsigned grid = (unsigned)((int64_t)p.B * p.H * p.nB);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(Sh::NT), Sh::LDS_BYTES, s, p);
+    auto kern = fwd_kernel<BETA, D>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(Sh::NT), 0, s, p);
     return hipGetLastError();
 }
 
