@@ -40,7 +40,11 @@ struct FwdShape {
     static constexpr int KCH = D / 8;             // 16-byte chunks per K / V row
     static constexpr int TILE = 64 * D;           // bf16 elements of one 64-key K or V tile
     static constexpr int DMA = 64 * KCH / NT;     // 16-byte loads per lane per tile
+    static constexpr int ROWS_PER_COPY = NT / KCH; // tile rows covered by one copy of all lanes
     static_assert(64 * KCH % NT == 0, "tile split");
+    // when the swizzles ignore the row bits a copy step changes, the per-lane
+    // source offset of copy x is that of copy 0 plus x rows-per-copy rows
+    static constexpr bool UNIFORM_COPY = ROWS_PER_COPY % 16 == 0;
 };
 
 // Row of the K tile fed to A-operand row n of a 32-key sub-tile.
@@ -81,85 +85,91 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_desc(const void *base, 
 constexpr float kRescaleSlack = 8.0f;
 
 // Per-lane state of one wave: its 32 queries' Q^T fragments, O^T
-// accumulators and online-softmax statistics.
+// accumulators, online-softmax statistics, and the lane's LDS / global byte
+// offsets, which are the same for every sub-tile.
 template <int BETA, int D>
 struct WaveState {
-    bf16x8 qf[FwdShape<BETA, D>::QS];
-    f32x16 oacc[FwdShape<BETA, D>::DT];
-    float m_run;   // reference max, log2-scaled domain
-    float l_run;   // running sum over this lane's keys
+    using Sh = FwdShape<BETA, D>;
+    bf16x8 qf[Sh::QS];
+    f32x16 oacc[Sh::DT];
+    float m_run;                 // reference max, log2-scaled domain
+    float l_run;                 // running sum over this lane's keys
+    uint32_t kread[Sh::QS];      // K operand of k-step s, key sub-tile 0 (bytes in a tile)
+    uint32_t vread[Sh::DT];      // V^T operand of d tile d, keys 0..3 (bytes in a tile)
+    uint32_t kdma, vdma;         // source offset of the lane's first 16-byte copy of a tile
 };
 
-// Issue the copies of one 64-key sub-tile (K and V, starting at key k0)
-// straight from global memory into LDS.  Lane l of load x writes the 16-byte
-// slot (x*NW + wave)*64 + l; slot s holds row s / KCH, chunk (s % KCH) XOR the
-// row's swizzle.  A partial tile repeats its last key (those scores are
-// masked).
 template <int BETA, int D>
-__device__ __forceinline__ void load_subtile(uint16_t *__restrict__ Kd, uint16_t *__restrict__ Vd,
-                                             __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                             const FwdParams &p, int k0, int wv, int lane)
+__device__ __forceinline__ void init_offsets(WaveState<BETA, D> &st, const FwdParams &p, int wv, int lane)
 {
     using Sh = FwdShape<BETA, D>;
-    const int rows = min(64, p.N - k0);
-    const uint32_t ks = (uint32_t)((int64_t)k0 * p.k.sn * 2);
-    const uint32_t vs = (uint32_t)((int64_t)k0 * p.v.sn * 2);
+    const int hl = lane >> 5, n = lane & 31;
+    const int r0 = perm_row(n);
 #pragma unroll
-    for (int x = 0; x < Sh::DMA; ++x) {
-        const int slot = (x * Sh::NW + wv) * 64 + lane;
-        const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
-        const int rs = min(r, rows - 1);
-        const int wbase = (x * Sh::NW + wv) * 64 * 8;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            krs, (lds_void *)(Kd + wbase), 16, (uint32_t)(rs * p.k.sn * 2 + ((ps ^ kswz<D>(r)) * 16)), ks,
-            0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            vrs, (lds_void *)(Vd + wbase), 16, (uint32_t)(rs * p.v.sn * 2 + ((ps ^ vswz<D>(r)) * 16)), vs,
-            0, 0);
+    for (int s = 0; s < Sh::QS; ++s)
+        st.kread[s] = (uint32_t)(r0 * D * 2 + (((2 * s + hl) ^ kswz<D>(r0)) * 16));
+    // transposing V reads: lane 4r + c of each 16-lane group names row r,
+    // columns 4c..4c+3; lane x of the group receives column x of rows 0..3
+    const int G = lane >> 4, jl = lane & 15;
+    const int vr0 = 8 * (G >> 1) + (jl >> 2);
+#pragma unroll
+    for (int d = 0; d < Sh::DT; ++d) {
+        const int dc = 32 * d + 16 * (G & 1) + 4 * (jl & 3);
+        st.vread[d] = (uint32_t)(vr0 * D * 2 + (((dc >> 3) ^ vswz<D>(vr0)) * 16) + (dc & 4) * 2);
     }
+    // copy x of a lane covers tile row r0 + x * ROWS_PER_COPY with the same
+    // chunk: the swizzles only use row bits that the step leaves unchanged
+    const int slot = wv * 64 + lane;
+    const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
+    st.kdma = (uint32_t)(r * p.k.sn * 2 + ((ps ^ kswz<D>(r)) * 16));
+    st.vdma = (uint32_t)(r * p.v.sn * 2 + ((ps ^ vswz<D>(r)) * 16));
 }
 
-// One pipeline step: start copying the next sub-tile into the other buffer
-// (if there is one), then fold the current sub-tile (keys k0 .. k0+63 in
-// Kc / Vc) into the wave's online softmax.  The restrict-qualified buffers
-// tell the compiler that the copies in flight do not alias the tiles read.
+template <typename T>
+__device__ __forceinline__ const T *lds_at(const uint16_t *base, uint32_t byte_off)
+{
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+// S^T (64 keys x 32 queries) of one sub-tile from the K tile Kc.
 template <int BETA, int D>
-__device__ __forceinline__ void pipeline_step(
-    const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vc, uint16_t *__restrict__ Kn,
-    uint16_t *__restrict__ Vn, bool prefetch, int k0n, bool compute, int k0,
-    __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const FwdParams &p, int wv, int lane,
-    WaveState<BETA, D> &st)
+__device__ __forceinline__ void qk_mfma(const uint16_t *__restrict__ Kc, const WaveState<BETA, D> &st,
+                                        f32x16 (&sacc)[2])
 {
     using Sh = FwdShape<BETA, D>;
-    if (prefetch) load_subtile<BETA, D>(Kn, Vn, krs, vrs, p, k0n, wv, lane);
-    if (!compute) return;
-    const int hl = lane >> 5, n = lane & 31;
-    const float c = p.scale_log2;
-
-    // S^T (64 keys x 32 queries)
-    f32x16 sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-        const int r = kt * 32 + perm_row(n);
 #pragma unroll
         for (int s = 0; s < Sh::QS; ++s) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8 *>(Kc + r * D + (((2 * s + hl) ^ kswz<D>(r)) * 8));
+            const bf16x8 a = *lds_at<bf16x8>(Kc + kt * 32 * D, st.kread[s]);
             sacc[kt] = mfma32x32x16(a, st.qf[s], sacc[kt]);
         }
     }
-    if (k0 + 64 > p.N) {   // partial last tile: keys past N do not exist
+}
+
+// Keys past N in a partial last tile do not exist: their scores become -inf.
+template <int BETA, int D>
+__device__ __forceinline__ void mask_tail(int k0, int N, int lane, f32x16 (&sacc)[2])
+{
+    const int hl = lane >> 5;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + kt * 32 + perm_row(8 * (r >> 2) + 4 * hl + (r & 3));
-                if (key >= p.N) sacc[kt][r] = -INFINITY;
-            }
-    }
-    // online softmax for this lane's query, lazily rescaled
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kt * 32 + perm_row(8 * (r >> 2) + 4 * hl + (r & 3));
+            if (key >= N) sacc[kt][r] = -INFINITY;
+        }
+}
+
+// Online softmax, part 1: the sub-tile's row max (both lane halves) and the
+// lazy rescale of the running state when it exceeds the reference by more
+// than the slack.
+template <int BETA, int D>
+__device__ __forceinline__ void softmax_rescale(const f32x16 (&sacc)[2], float c, WaveState<BETA, D> &st)
+{
+    using Sh = FwdShape<BETA, D>;
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -176,58 +186,125 @@ __device__ __forceinline__ void pipeline_step(
 #pragma unroll
             for (int r = 0; r < 16; ++r) st.oacc[d][r] *= alpha;
     }
+}
+
+// Online softmax, part 2: probabilities relative to the reference max,
+// summed and packed to bf16 as the B operand of each 16-key k-step.
+template <int BETA, int D>
+__device__ __forceinline__ void softmax_probs(const f32x16 (&sacc)[2], float c, WaveState<BETA, D> &st,
+                                              bf16x8 (&pf)[2][2])
+{
     const float mr = st.m_run;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pr = fast_exp2(__builtin_fmaf(sacc[kt][r], c, -mr));
-            sacc[kt][r] = pr;
-            st.l_run += pr;
+        for (int u = 0; u < 2; ++u) {
+            float pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pr[e] = fast_exp2(__builtin_fmaf(sacc[kt][8 * u + e], c, -mr));
+                st.l_run += pr[e];
+            }
+            uint4 pk;
+            pk.x = pack_bf16x2(pr[0], pr[1]);
+            pk.y = pack_bf16x2(pr[2], pr[3]);
+            pk.z = pack_bf16x2(pr[4], pr[5]);
+            pk.w = pack_bf16x2(pr[6], pr[7]);
+            pf[kt][u] = as_bf16x8(pk);
         }
+}
 
-    // O^T += V^T P^T ; V^T fragments come from row-major V by transposing LDS
-    // reads (lane 4r + c of each 16-lane group names row r, columns
-    // 4c..4c+3; lane x of the group receives column x of rows 0..3)
-    const int G = lane >> 4, jl = lane & 15;
-    const int kbase = 8 * (G >> 1), dbase = 16 * (G & 1);
+// O^T += V^T P^T with the V tile Vc.  V^T operands come from row-major V by
+// transposing LDS reads.
+template <int BETA, int D>
+__device__ __forceinline__ void pv_mfma(const uint16_t *__restrict__ Vc, const bf16x8 (&pf)[2][2],
+                                        WaveState<BETA, D> &st)
+{
+    using Sh = FwdShape<BETA, D>;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            uint4 pk;
-            pk.x = pack_bf16x2(sacc[kt][8 * u + 0], sacc[kt][8 * u + 1]);
-            pk.y = pack_bf16x2(sacc[kt][8 * u + 2], sacc[kt][8 * u + 3]);
-            pk.z = pack_bf16x2(sacc[kt][8 * u + 4], sacc[kt][8 * u + 5]);
-            pk.w = pack_bf16x2(sacc[kt][8 * u + 6], sacc[kt][8 * u + 7]);
-            const bf16x8 pf = as_bf16x8(pk);
 #pragma unroll
             for (int d = 0; d < Sh::DT; ++d) {
                 s16x4 h2[2];
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp) {
-                    const int vr = kt * 32 + 16 * u + kbase + 4 * pp + (jl >> 2);
-                    const int dc = 32 * d + dbase + 4 * (jl & 3);
-                    const int pos = (dc >> 3) ^ vswz<D>(vr);
-                    const uint16_t *src = Vc + vr * D + pos * 8 + (dc & 4);
+                    const uint16_t *rowp = Vc + (kt * 32 + 16 * u + 4 * pp) * D;
                     h2[pp] = __builtin_bit_cast(
                         s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                   (__attribute__((address_space(3))) bf16x4 *)src));
+                                   (__attribute__((address_space(3))) bf16x4 *)lds_at<uint16_t>(rowp, st.vread[d])));
                 }
                 const bf16x8 a =
                     __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                st.oacc[d] = mfma32x32x16(a, pf, st.oacc[d]);
+                st.oacc[d] = mfma32x32x16(a, pf[kt][u], st.oacc[d]);
             }
         }
     }
+}
+
+// Issue the copy of one 64-key tile (K or V rows from key k0) into LDS.
+// Lane l of copy x writes the 16-byte slot (x*NW + wave)*64 + l; slot s holds
+// tile row s / KCH, chunk (s % KCH) XOR the row's swizzle.  A partial tile
+// repeats its last key (those scores are masked).
+template <int BETA, int D>
+__device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t rs, int64_t sn,
+                                          uint32_t off0, bool is_v, const FwdParams &p, int k0, int wv,
+                                          int lane)
+{
+    using Sh = FwdShape<BETA, D>;
+    const int rows = p.N - k0;
+    const uint32_t so = (uint32_t)((int64_t)k0 * sn * 2);
+    const uint32_t step = (uint32_t)((int64_t)Sh::ROWS_PER_COPY * sn * 2);
+#pragma unroll
+    for (int x = 0; x < Sh::DMA; ++x) {
+        uint32_t o = off0, sx = so + x * step;
+        if (rows < 64 || !Sh::UNIFORM_COPY) {
+            const int slot = (x * Sh::NW + wv) * 64 + lane;
+            const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
+            const int rr = min(r, rows - 1);
+            o = (uint32_t)(rr * sn * 2 + ((ps ^ (is_v ? vswz<D>(r) : kswz<D>(r))) * 16));
+            sx = so;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16,
+                                                 o, sx, 0, 0);
+    }
+}
+
+// One pipeline step: start copying the next sub-tile (K and V) into the
+// other buffer pair, then fold the current sub-tile (keys k0 .. k0+63 in
+// Kc / Vc) into the wave's online softmax.  The restrict-qualified buffers
+// tell the compiler that the copies in flight do not alias the tiles read.
+template <int BETA, int D>
+__device__ __forceinline__ void pipeline_step(
+    const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vc, uint16_t *__restrict__ Kn,
+    uint16_t *__restrict__ Vn, bool prefetch, int k0n, bool compute, int k0,
+    __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const FwdParams &p, int wv, int lane,
+    WaveState<BETA, D> &st)
+{
+    if (prefetch) {
+        load_tile<BETA, D>(Kn, krs, p.k.sn, st.kdma, false, p, k0n, wv, lane);
+        load_tile<BETA, D>(Vn, vrs, p.v.sn, st.vdma, true, p, k0n, wv, lane);
+    }
+    if (!compute) return;
+    const float c = p.scale_log2;
+    f32x16 sacc[2];
+    qk_mfma<BETA, D>(Kc, st, sacc);
+    if (k0 + 64 > p.N) mask_tail<BETA, D>(k0, p.N, lane, sacc);
+    softmax_rescale<BETA, D>(sacc, c, st);
+    bf16x8 pf[2][2];
+    softmax_probs<BETA, D>(sacc, c, st, pf);
+    pv_mfma<BETA, D>(Vc, pf, st);
 }
 
 template <int BETA, int D>
 __global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kernel(const FwdParams p)
 {
     using Sh = FwdShape<BETA, D>;
-    // two buffers, each a 64-key K tile followed by a 64-key V tile
+    // two buffers, each a 64-key K tile and a 64-key V tile
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * Sh::TILE];
+    uint16_t *const K0 = smem, *const V0 = smem + Sh::TILE;
+    uint16_t *const K1 = smem + 2 * Sh::TILE, *const V1 = smem + 3 * Sh::TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -265,12 +342,13 @@ __global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kerne
         for (int r = 0; r < 16; ++r) st.oacc[d][r] = 0.f;
     st.m_run = -INFINITY;
     st.l_run = 0.f;
+    init_offsets<BETA, D>(st, p, wv, lane);
 
     const __amdgpu_buffer_rsrc_t krs = buffer_desc(kb, (uint32_t)(((int64_t)(p.N - 1) * p.k.sn + D) * 2));
     const __amdgpu_buffer_rsrc_t vrs = buffer_desc(vb, (uint32_t)(((int64_t)(p.N - 1) * p.v.sn + D) * 2));
 
     // Sub-tile t: key block col_idx[e0 + t / SUB], keys 64 (t % SUB) .. +63.
-    // An entry outside [0, nB) is ignored: its copy reads block 0 and its
+    // An entry outside [0, nB) is ignored: its copies read block 0 and its
     // compute is skipped.
     auto tile_key0 = [&](int t, bool &valid) {
         const int j = __builtin_amdgcn_readfirstlane(p.col_idx[e0 + t / Sh::SUB]);
@@ -282,20 +360,28 @@ __global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kerne
     int k0 = 0;
     if (T > 0) {
         k0 = tile_key0(0, valid);
-        load_subtile<BETA, D>(smem, smem + Sh::TILE, krs, vrs, p, k0, wv, lane);
+        load_tile<BETA, D>(K0, krs, p.k.sn, st.kdma, false, p, k0, wv, lane);
+        load_tile<BETA, D>(V0, vrs, p.v.sn, st.vdma, true, p, k0, wv, lane);
     }
     __syncthreads();   // Q in registers; sub-tile 0 in LDS
 
-    for (int t = 0; t < T; ++t) {
-        uint16_t *cur = smem + (t & 1) * 2 * Sh::TILE;
-        uint16_t *nxt = smem + ((t & 1) ^ 1) * 2 * Sh::TILE;
+    // Even sub-tiles live in buffer 0, odd ones in buffer 1; the loop is
+    // unrolled by two so that every LDS address is a per-lane offset plus a
+    // compile-time constant.
+    for (int t = 0; t < T; t += 2) {
         bool valid_n = false;
         int k0n = 0;
-        const bool prefetch = t + 1 < T;
+        bool prefetch = t + 1 < T;
         if (prefetch) k0n = tile_key0(t + 1, valid_n);
-        pipeline_step<BETA, D>(cur, cur + Sh::TILE, nxt, nxt + Sh::TILE, prefetch, k0n, valid, k0, krs,
-                               vrs, p, wv, lane, st);
-        __syncthreads();   // sub-tile t + 1 landed for every wave; buffer of t is free
+        pipeline_step<BETA, D>(K0, V0, K1, V1, prefetch, k0n, valid, k0, krs, vrs, p, wv, lane, st);
+        __syncthreads();   // sub-tile t + 1 landed for every wave; buffer 0 is free
+        if (!prefetch) break;
+        valid = valid_n;
+        k0 = k0n;
+        prefetch = t + 2 < T;
+        if (prefetch) k0n = tile_key0(t + 2, valid_n);
+        pipeline_step<BETA, D>(K1, V1, K0, V0, prefetch, k0n, valid, k0, krs, vrs, p, wv, lane, st);
+        __syncthreads();   // sub-tile t + 2 landed for every wave; buffer 1 is free
         valid = valid_n;
         k0 = k0n;
     }
