@@ -47,38 +47,6 @@ struct FwdShape {
     static constexpr bool UNIFORM_COPY = ROWS_PER_COPY % 16 == 0;
 };
 
-// Row of the K tile fed to A-operand row n of a 32-key sub-tile.
-__device__ __forceinline__ int perm_row(int n)
-{
-    return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
-}
-
-// XOR swizzles of the 16-byte chunk index within a row of the K and V tiles.
-// K: the 16 rows read by one quarter-wave land on 16 distinct chunk slots.
-// V: the 4 rows x 4 chunks read by one half-wave transpose load land on 16
-// distinct chunk slots.  (Rows are 256 B for D = 128, 128 B for D = 64.)
-template <int D>
-__device__ __forceinline__ int kswz(int row)
-{
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int vswz(int row)
-{
-    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Raw buffer resource over `bytes` bytes from `base` (gfx9 format word).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_desc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
 // Lazy rescaling: the running reference max only moves when a sub-tile's max
 // exceeds it by more than this (log2 units), so the O rescale is skipped for
 // most sub-tiles; probabilities stay below 2^8 relative to the reference.
@@ -125,11 +93,6 @@ __device__ __forceinline__ void init_offsets(WaveState<BETA, D> &st, const FwdPa
     st.vdma = (uint32_t)(r * p.v.sn * 2 + ((ps ^ vswz<D>(r)) * 16));
 }
 
-template <typename T>
-__device__ __forceinline__ const T *lds_at(const uint16_t *base, uint32_t byte_off)
-{
-    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
-}
 
 // S^T (64 keys x 32 queries) of one sub-tile from the K tile Kc.
 template <int BETA, int D>

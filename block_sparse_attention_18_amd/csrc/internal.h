@@ -11,7 +11,7 @@ namespace bsa {
 constexpr int kMaxSkipHeads = 1024;   // bitmask of SKIP heads carried in kernel args
 constexpr int kMaxArrowHeads = 256;   // per-head modes/windows carried in kernel args
 constexpr int kMaxSelectBlocks = 1024;
-constexpr int kExactSlots = 512;      // persistent workgroups of the exact-score kernel
+constexpr int kExactSlots = 1024;     // persistent workgroups of the exact-score kernel
 
 struct Tensor4 {
     const uint16_t *p;

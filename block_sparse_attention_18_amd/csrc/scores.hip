@@ -117,37 +117,143 @@ hipError_t launch_scores(const ScoreParams &p, hipStream_t s)
 // ---------------------------------------------------------------------------
 template <int BETA, int D>
 struct ExactShape {
-    static constexpr int NW = BETA / 32;
+    static constexpr int NW = BETA / 32;            // waves, 32 query rows each
     static constexpr int NT = NW * 64;
-    static constexpr int KT = BETA / 32;
-    static constexpr int QS = D / 16;
-    static constexpr int KCH = D / 8;
-    static constexpr int K_ITEMS = BETA * KCH;
-    static constexpr size_t LDS_BYTES = (size_t)BETA * D * sizeof(uint16_t) + BETA * sizeof(float);
-    static_assert(K_ITEMS % NT == 0, "tile split");
+    static constexpr int SUB = BETA / 64;           // 64-key sub-tiles per key block
+    static constexpr int QS = D / 16;               // k-steps over d
+    static constexpr int KCH = D / 8;               // 16-byte chunks per K row
+    static constexpr int TILE = 64 * D;             // bf16 elements of one 64-key K tile
+    static constexpr int DMA = 64 * KCH / NT;       // 16-byte copies per lane per tile
+    static constexpr int ROWS_PER_COPY = NT / KCH;
+    static constexpr bool UNIFORM_COPY = ROWS_PER_COPY % 16 == 0;
+    static_assert(64 * KCH % NT == 0, "tile split");
 };
 
-__device__ __forceinline__ int exact_perm_row(int n)
+// Copy one 64-key K tile (rows from key k0) straight into LDS; lane l of
+// copy x writes slot (x*NW + wave)*64 + l = (row, chunk XOR the row's
+// swizzle).  A partial tile repeats its last key (those scores are masked).
+template <int BETA, int D>
+__device__ __forceinline__ void exact_load_k(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t rs,
+                                             int64_t sn, uint32_t off0, int N, int k0, int wv, int lane)
 {
-    return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+    using Sh = ExactShape<BETA, D>;
+    const int rows = N - k0;
+    const uint32_t so = (uint32_t)((int64_t)k0 * sn * 2);
+    const uint32_t step = (uint32_t)((int64_t)Sh::ROWS_PER_COPY * sn * 2);
+#pragma unroll
+    for (int x = 0; x < Sh::DMA; ++x) {
+        uint32_t o = off0, sx = so + x * step;
+        if (rows < 64 || !Sh::UNIFORM_COPY) {
+            const int slot = (x * Sh::NW + wv) * 64 + lane;
+            const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
+            o = (uint32_t)(min(r, rows - 1) * sn * 2 + ((ps ^ kswz<D>(r)) * 16));
+            sx = so;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16, o,
+                                                 sx, 0, 0);
+    }
+}
+
+// Per-lane state: the 32 queries' Q^T fragments, the running log2-sum-exp
+// over key blocks (M, L), the current key block's partial (bm, bl), and
+// the lane's constant LDS / global offsets.
+template <int BETA, int D>
+struct ExactState {
+    bf16x8 qf[ExactShape<BETA, D>::QS];
+    float M, L, bm, bl;
+    uint32_t kread[ExactShape<BETA, D>::QS];
+    uint32_t kdma;
+};
+
+// One step: copy the next sub-tile into the other buffer, then fold the
+// current 64 keys (starting at k0) into the block partial; at the end of a
+// key block, park its log2-sum-exp in the scratch slot and update (M, L).
+template <int BETA, int D>
+__device__ __forceinline__ void exact_step(const uint16_t *__restrict__ Kc, uint16_t *__restrict__ Kn,
+                                           bool prefetch, int k0n, int k0, bool first_half, bool last_half,
+                                           int j, __amdgpu_buffer_rsrc_t krs, const ExactParams &p,
+                                           float *slot, int wv, int lane, ExactState<BETA, D> &st)
+{
+    using Sh = ExactShape<BETA, D>;
+    if (prefetch) exact_load_k<BETA, D>(Kn, krs, p.k.sn, st.kdma, p.N, k0n, wv, lane);
+    const int hl = lane >> 5, n = lane & 31;
+    const float c = p.scale_log2;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < Sh::QS; ++s) {
+            const bf16x8 a = *lds_at<bf16x8>(Kc + kt * 32 * D, st.kread[s]);
+            sacc[kt] = mfma32x32x16(a, st.qf[s], sacc[kt]);
+        }
+    }
+    if (k0 + 64 > p.N) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + kt * 32 + perm_row(8 * (r >> 2) + 4 * hl + (r & 3));
+                if (key >= p.N) sacc[kt][r] = -INFINITY;
+            }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;   // at least one key of a tile exists
+    float ls = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ls += fast_exp2(__builtin_fmaf(sacc[kt][r], c, -mx));
+    ls += __shfl_xor(ls, 32, 64);
+    if (first_half) {
+        st.bm = mx;
+        st.bl = ls;
+    } else {
+        const float m2 = fmaxf(st.bm, mx);
+        st.bl = st.bl * fast_exp2(st.bm - m2) + ls * fast_exp2(mx - m2);
+        st.bm = m2;
+    }
+    if (last_half) {
+        const float lj = st.bm + __log2f(st.bl);   // block log2-sum-exp of this token
+        const float Mn = fmaxf(st.M, lj);
+        st.L = st.L * ((st.M == Mn) ? 1.f : fast_exp2(st.M - Mn)) + fast_exp2(lj - Mn);
+        st.M = Mn;
+        if (hl == 0) slot[(int64_t)j * BETA + wv * 32 + n] = lj;
+    }
 }
 
 template <int BETA, int D>
-__global__ __launch_bounds__(BETA / 32 * 64) void exact_scores_kernel(const ExactParams p)
+__global__ __launch_bounds__(BETA / 32 * 64, 4) void exact_scores_kernel(const ExactParams p)
 {
     using Sh = ExactShape<BETA, D>;
-    extern __shared__ __align__(16) uint16_t lds[];
-    uint16_t *Ks = lds;
-    float *lse2 = reinterpret_cast<float *>(lds + BETA * D);
+    __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * Sh::TILE];
+    __shared__ float lse2[BETA];
+    uint16_t *const K0 = kbuf, *const K1 = kbuf + Sh::TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane >> 5;
     const int n = lane & 31;
-    const float c = p.scale_log2;
     float *slot = p.scratch + (int64_t)blockIdx.x * p.nB * BETA;   // [nB][BETA]
     const int64_t items = (int64_t)p.B * p.H * p.nB;
+    const int T = p.nB * Sh::SUB;   // 64-key sub-tiles per item
+
+    ExactState<BETA, D> st;
+    {
+        const int r0 = perm_row(n);
+#pragma unroll
+        for (int s = 0; s < Sh::QS; ++s)
+            st.kread[s] = (uint32_t)(r0 * D * 2 + (((2 * s + hl) ^ kswz<D>(r0)) * 16));
+        const int sl = wv * 64 + lane;
+        const int r = sl / Sh::KCH, ps = sl % Sh::KCH;
+        st.kdma = (uint32_t)(r * p.k.sn * 2 + ((ps ^ kswz<D>(r)) * 16));
+    }
 
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const int bh = (int)(item / p.nB);
@@ -155,85 +261,47 @@ __global__ __launch_bounds__(BETA / 32 * 64) void exact_scores_kernel(const Exac
         const int b = bh / p.H, hh = bh - b * p.H;
         const uint16_t *qb = p.q.p + b * p.q.sb + hh * p.q.sh;
         const uint16_t *kb = p.k.p + b * p.k.sb + hh * p.k.sh;
-        const int tq = wv * 32 + n;           // query token within the block
-        const int qrow = i * BETA + tq;
-
-        bf16x8 qf[Sh::QS];
+        const __amdgpu_buffer_rsrc_t krs =
+            buffer_desc(kb, (uint32_t)(((int64_t)(p.N - 1) * p.k.sn + D) * 2));
+        const int qrow = i * BETA + wv * 32 + n;
 #pragma unroll
         for (int s = 0; s < Sh::QS; ++s) {
             uint4 u = qrow < p.N ? ld_g16(qb + (int64_t)qrow * p.q.sn + 16 * s + 8 * hl) : zero_u4();
-            qf[s] = as_bf16x8(u);
+            st.qf[s] = as_bf16x8(u);
         }
-        float M = -INFINITY, L = 0.f;     // running log2-sum-exp over key blocks
+        st.M = -INFINITY;
+        st.L = 0.f;
 
-        for (int j = 0; j < p.nB; ++j) {
-            const int key0 = j * BETA;
+        __syncthreads();   // the previous item is done with K0 / K1 and lse2
+        exact_load_k<BETA, D>(K0, krs, p.k.sn, st.kdma, p.N, 0, wv, lane);
+        __syncthreads();   // sub-tile 0 in LDS
+        // even sub-tiles in K0, odd in K1 (the loop is unrolled by two)
+        for (int t = 0; t < T; t += 2) {
+            const int k0 = t * 64;
+            exact_step<BETA, D>(K0, K1, t + 1 < T, k0 + 64, k0, (t % Sh::SUB) == 0,
+                                (t % Sh::SUB) == Sh::SUB - 1, t / Sh::SUB, krs, p, slot, wv, lane, st);
             __syncthreads();
-#pragma unroll
-            for (int it = 0; it < Sh::K_ITEMS / Sh::NT; ++it) {
-                const int c16 = tid + it * Sh::NT;
-                const int r = c16 / Sh::KCH, cc = c16 % Sh::KCH;
-                const int key = key0 + r;
-                uint4 u = key < p.N ? ld_g16(kb + (int64_t)key * p.k.sn + cc * 8) : zero_u4();
-                *reinterpret_cast<uint4 *>(Ks + r * D + ((cc ^ (r % Sh::KCH)) * 8)) = u;
-            }
+            if (t + 1 >= T) break;
+            exact_step<BETA, D>(K1, K0, t + 2 < T, k0 + 128, k0 + 64, ((t + 1) % Sh::SUB) == 0,
+                                ((t + 1) % Sh::SUB) == Sh::SUB - 1, (t + 1) / Sh::SUB, krs, p, slot, wv,
+                                lane, st);
             __syncthreads();
-
-            f32x16 sacc[Sh::KT];
-#pragma unroll
-            for (int kt = 0; kt < Sh::KT; ++kt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-                const int r = kt * 32 + exact_perm_row(n);
-#pragma unroll
-                for (int s = 0; s < Sh::QS; ++s) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        Ks + r * D + (((2 * s + hl) ^ (r % Sh::KCH)) * 8));
-                    sacc[kt] = mfma32x32x16(a, qf[s], sacc[kt]);
-                }
-            }
-            if (key0 + BETA > p.N) {
-#pragma unroll
-                for (int kt = 0; kt < Sh::KT; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + kt * 32 + exact_perm_row(8 * (r >> 2) + 4 * hl + (r & 3));
-                        if (key >= p.N) sacc[kt][r] = -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < Sh::KT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mb = mx * c;
-            float ls = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < Sh::KT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) ls += fast_exp2(__builtin_fmaf(sacc[kt][r], c, -mb));
-            ls += __shfl_xor(ls, 32, 64);
-            const float lj = mb + __log2f(ls);        // block log2-sum-exp of this token
-            const float Mn = fmaxf(M, lj);
-            L = L * ((M == Mn) ? 1.f : fast_exp2(M - Mn)) + fast_exp2(lj - Mn);
-            M = Mn;
-            if (hl == 0) slot[(int64_t)j * BETA + tq] = lj;
         }
-        if (hl == 0) lse2[tq] = M + __log2f(L);
+        if (hl == 0) lse2[wv * 32 + n] = st.M + __log2f(st.L);
         __syncthreads();   // slot and lse2 complete for this item
 
+        // S_ij = 1/(n_i n_j) sum_t 2^(l_tj - L_t), one wave per key block j
         const int n_i = min(BETA, p.N - i * BETA);
         for (int j = wv; j < p.nB; j += Sh::NW) {
-            float s = 0.f;
+            float sum = 0.f;
 #pragma unroll
             for (int t = lane; t < BETA; t += 64)
-                if (t < n_i) s += fast_exp2(slot[(int64_t)j * BETA + t] - lse2[t]);
+                if (t < n_i) sum += fast_exp2(slot[(int64_t)j * BETA + t] - lse2[t]);
 #pragma unroll
-            for (int d = 32; d > 0; d >>= 1) s += __shfl_xor(s, d, 64);
+            for (int d = 32; d > 0; d >>= 1) sum += __shfl_xor(sum, d, 64);
             if (lane == 0) {
                 const int n_j = min(BETA, p.N - j * BETA);
-                p.S[item * p.nB + j] = s / ((float)n_i * (float)n_j);
+                p.S[item * p.nB + j] = sum / ((float)n_i * (float)n_j);
             }
         }
     }
@@ -244,11 +312,7 @@ static hipError_t launch_exact_t(const ExactParams &p, int slots, hipStream_t s)
 {
     using Sh = ExactShape<BETA, D>;
     auto kern = exact_scores_kernel<BETA, D>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)Sh::LDS_BYTES);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(slots), dim3(Sh::NT), Sh::LDS_BYTES, s, p);
+    hipLaunchKernelGGL(kern, dim3(slots), dim3(Sh::NT), 0, s, p);
     return hipGetLastError();
 }
 
