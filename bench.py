@@ -56,10 +56,11 @@ def _traffic(workload: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--window", type=int, default=None, help="override the arrow window")
+    ap.add_argument("--no-split", action="store_true", help="run every row in one workgroup")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -122,6 +123,7 @@ def main():
             bsa.build_arrow_layout(B, H, N, block, wl.text_len, modes, wins, device=dev,
                                    row_ptr=row_ptr, col_idx=col_idx)
         fwd_kw = dict(head_modes=modes, o_cache=o_cache, lse_cache=lse_cache)
+        split = bsa.arrow_split_policy(B, H, N, block, wl.text_len, modes, wins)
     else:
         w = torch.from_numpy(x["w"]).to(dev) if "w" in x else None
         scores = torch.empty((B, H, nB, nB), dtype=torch.float32, device=dev)
@@ -140,6 +142,14 @@ def main():
                             workspace=ws_sel)
         fwd_kw = {}
         computed_heads = B * H
+        split = bsa.select_split_policy(B, H, nB, wl.text_blocks, wl.groups, block=block)
+    if args.no_split:
+        split = None
+    if split is not None:   # workspace allocated once, outside the timed region
+        split["workspace"] = torch.empty(
+            bsa.split_workspace_size(B, H, N, D, block, split["max_chunks"], split["max_split_rows"]),
+            dtype=torch.uint8, device=dev)
+        fwd_kw["split"] = split
 
     def forward():
         bsa.forward(q, k, v, block, row_ptr, col_idx, out=out, lse=lse, **fwd_kw)
@@ -198,6 +208,8 @@ def main():
                        else f"select groups={list(wl.groups)} text_blocks={wl.text_blocks}"),
             "kept_pairs": kept_pairs,
             "kept_fraction": round(kept_pairs / (B * H * nB * nB), 4),
+            "long_row_split": (None if split is None else
+                               {k2: split[k2] for k2 in ("chunk_blocks", "max_chunks", "max_split_rows")}),
             "parallelism": "single GPU",
         },
         "dense_equiv_tflops": round(dense_flop / (ms_step * 1e-3) / 1e12, 2),
@@ -207,7 +219,7 @@ def main():
         "step_wall_ms": round(wall * 1e3 / args.steps, 4),
         "roofline": {
             "bound": "mfma",
-            "kernel": "bsa::fwd_kernel",
+            "kernel": "bsa::fwd_kernel (+ split plan / combine when long rows are split)",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -19,6 +19,7 @@ The four calls mirror the C ABI:
 from __future__ import annotations
 
 import ctypes
+import heapq
 import math
 import os
 import threading
@@ -48,6 +49,12 @@ class BsaTensor(ctypes.Structure):
                 ("N", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
                 ("stride_n", ctypes.c_int64)]
+
+
+class BsaSplit(ctypes.Structure):
+    _fields_ = [("chunk_blocks", ctypes.c_int32), ("max_chunks", ctypes.c_int32),
+                ("max_split_rows", ctypes.c_int64), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class BsaGroup(ctypes.Structure):
@@ -81,7 +88,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_select_topk": (I32, [V, I64, I64, I32, I32, GP, I32, V, V, I64, V, SZ, V]),
             "bsa_arrow_capacity": (I64, [I64, I64, I64, I32, I64, V, V]),
             "bsa_build_arrow_layout": (I32, [I64, I64, I64, I32, I64, V, V, V, V, I64, V]),
-            "bsa_forward": (I32, [TP, TP, TP, I32, V, V, V, TP, V, F, TP, V, V]),
+            "bsa_forward": (I32, [TP, TP, TP, I32, V, V, V, TP, V, F, TP, V,
+                                  ctypes.POINTER(BsaSplit), V]),
+            "bsa_forward_split_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32, I64]),
             "bsa_status_string": (ctypes.c_char_p, [I32]),
             "bsa_last_error": (ctypes.c_char_p, []),
             "bsa_version": (ctypes.c_char_p, []),
@@ -236,13 +245,108 @@ def build_arrow_layout(B: int, H: int, N: int, block: int, text_len: int, head_m
     return row_ptr, col_idx[:cap] if cap > 0 else col_idx[:0]
 
 
+def split_workspace_size(B, H, N, D, block, max_chunks, max_split_rows) -> int:
+    return int(load().bsa_forward_split_workspace_size(B, H, N, D, block, max_chunks, max_split_rows))
+
+
+def _makespan(costs, slots: int) -> float:
+    """Greedy list schedule of work items (in dispatch order) onto `slots`
+    concurrent workgroups; returns the finishing time of the last one."""
+    if not costs:
+        return 0.0
+    if len(costs) <= slots:
+        return float(max(costs))
+    heap = [0.0] * slots
+    for c in costs:
+        t = heapq.heappop(heap)
+        heapq.heappush(heap, t + c)
+    return max(heap)
+
+
+# Cost model of the split decision, in units of one kept block's compute:
+# a workgroup's prologue / epilogue, the extra plan and combine launches, and
+# the predicted gain a split must reach (the list-schedule model ignores that
+# the last workgroups run faster on an emptier chip, so it is optimistic).
+_ITEM_OVERHEAD = 0.5
+_SPLIT_OVERHEAD = 8.0
+_SPLIT_GAIN = 0.8
+
+
+def _split_from_rows(nB: int, lens, typical: int, target_chunks: int, slots: int):
+    """Split plan from per-row block counts given in dispatch order.  Rows longer
+    than L = max(typical, ceil(nB / target_chunks)) would be cut into at most
+    ceil(nB / L) chunks; the plan is returned only when the list-schedule
+    makespan with splitting (plus the plan / combine cost) beats the makespan
+    without it by a clear margin."""
+    L = max(1, typical, -(-nB // target_chunks))
+    S = min(64, max(2, -(-nB // L)))
+    long_rows = sum(1 for x in lens if x > L)
+    if long_rows == 0:
+        return None
+    whole = [x + _ITEM_OVERHEAD for x in lens]
+    cut = []
+    for x in lens:
+        c = min(S, -(-x // L)) if x > L else 1
+        cut += [x / c + _ITEM_OVERHEAD] * c
+    if _makespan(cut, slots) + _SPLIT_OVERHEAD >= _SPLIT_GAIN * _makespan(whole, slots):
+        return None
+    return {"chunk_blocks": L, "max_chunks": S, "max_split_rows": long_rows}
+
+
+def _slots(block: int) -> int:
+    # concurrent forward workgroups on the 256 CUs: two per CU at block 128,
+    # about four at block 64 (smaller LDS tiles, two waves each)
+    return 512 if block == 128 else 1024
+
+
+def arrow_split_policy(B: int, H: int, N: int, block: int, text_len: int, head_modes, head_windows,
+                       target_chunks: int = 4):
+    """Long-row split for an arrow layout (text rows and full heads next to
+    short windowed rows), or None when splitting would not pay."""
+    nB = n_blocks(N, block)
+    tb = -(-text_len // block)
+    per_head, typical = [], 1
+    for h in range(H):
+        m, w = int(head_modes[h]), int(head_windows[h])
+        row = []
+        for i in range(nB):
+            if m == HEAD_SKIP:
+                ln = 0
+            elif m == HEAD_FULL or i < tb:
+                ln = nB
+            else:
+                lo, hi = max(tb, i - w), min(nB - 1, i + w)
+                ln = tb + max(0, hi - lo + 1)
+                typical = max(typical, ln)
+            row.append(ln)
+        per_head.append(row)
+    if all(int(m) == HEAD_FULL for m in head_modes):
+        typical = -(-nB // target_chunks)
+    # dispatch order of the forward: query-block-major, then batch and head
+    lens = [per_head[h][i] for i in range(nB) for _ in range(B) for h in range(H)]
+    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block))
+
+
+def select_split_policy(B: int, H: int, nB: int, text_blocks: int, groups, target_chunks: int = 4,
+                        block: int = 128):
+    """Long-row split for a top-k selection (dense text rows next to rows of
+    text + k blocks), or None when splitting would not pay."""
+    typical = min(nB, text_blocks + sum(int(g[2]) for g in groups))
+    lens = [nB if i < text_blocks else typical for i in range(nB) for _ in range(B * H)]
+    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block))
+
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
             row_ptr: torch.Tensor, col_idx: torch.Tensor, head_modes=None,
             o_cache: Optional[torch.Tensor] = None, lse_cache: Optional[torch.Tensor] = None,
             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None,
-            return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Block-sparse attention forward.  Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N])."""
+            lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+            split: Optional[dict] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Block-sparse attention forward.  Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N]).
+
+    split: None, or {"chunk_blocks", "max_chunks", "max_split_rows"[, "workspace"]}
+    to cut long rows over several workgroups (see arrow_split_policy /
+    select_split_policy).  A missing workspace is allocated here."""
     lib = load()
     B, H, N, D = q.shape
     if out is None:
@@ -263,9 +367,19 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
     modes = None if head_modes is None else _host_i8(head_modes, H)
     dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
     dc = _desc(o_cache, "o_cache")
+    sp = None
+    if split is not None:
+        ws = split.get("workspace")
+        if ws is None:
+            need = split_workspace_size(B, H, N, D, block, split["max_chunks"], split["max_split_rows"])
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+            split["workspace"] = ws
+        sp = BsaSplit(int(split["chunk_blocks"]), int(split["max_chunks"]), int(split["max_split_rows"]),
+                      ws.data_ptr(), ws.numel() * ws.element_size())
     _check(lib.bsa_forward(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), block,
                            _ptr(row_ptr), _ptr(col_idx), modes, _ref(dc), _ptr(lse_cache),
-                           float(scale or 0.0), ctypes.byref(do), _ptr(lse), _stream(q.device)))
+                           float(scale or 0.0), ctypes.byref(do), _ptr(lse),
+                           None if sp is None else ctypes.byref(sp), _stream(q.device)))
     return out, lse
 
 

@@ -7,9 +7,10 @@
 //   ARROW : keep(i, j) = i < T_b or j < T_b or |i - j| <= w
 //   FULL  : keep every (i, j)
 //   SKIP  : nothing is computed (empty rows)
-// Everything is closed form, so one workgroup per (b, h) computes its row
-// lengths, scans them, writes row_ptr and then the ascending columns.  The
-// offset of a head is the closed-form nnz of every head before it.
+// Everything is closed form, so every row is independent: one wavefront per
+// row computes its offset (closed-form nnz of the heads before it plus the
+// lengths of the earlier rows of its head), writes row_ptr and then its
+// ascending columns.
 #include "common.h"
 #include "internal.h"
 
@@ -37,63 +38,46 @@ __device__ __forceinline__ int64_t arrow_head_nnz(int mode, int w, int nB, int t
     return (int64_t)tb * nB + ni * tb + band;
 }
 
+// One wavefront per row (b, h, i).  The row's offset is the closed-form nnz
+// of the batch entries and heads before it plus the lengths of the earlier
+// rows of its head; lane 0 of row 0 also writes row_ptr[0].
 __global__ __launch_bounds__(256) void arrow_kernel(const ArrowParams p)
 {
-    __shared__ int64_t wsum[4];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int bh = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t rows = (int64_t)p.B * p.H * p.nB;
+    if (row >= rows) return;
+    const int bh = (int)(row / p.nB), i = (int)(row - (int64_t)bh * p.nB);
     const int b = bh / p.H, hh = bh - b * p.H;
     const int mode = p.mode[hh], w = p.window[hh];
 
-    int64_t base = (int64_t)b * p.per_batch;
-    for (int h2 = 0; h2 < hh; ++h2) base += arrow_head_nnz(p.mode[h2], p.window[h2], p.nB, p.text_blocks);
-
-    int32_t *rp = p.row_ptr + (int64_t)bh * p.nB;
-    int64_t carry = 0;
-    for (int i0 = 0; i0 < p.nB; i0 += 256) {
-        const int i = i0 + tid;
-        const int64_t len = i < p.nB ? arrow_row_len(mode, w, p.nB, p.text_blocks, i) : 0;
-        // inclusive scan of 64-bit lengths across the workgroup
-        int64_t x = len;
+    // prefix: batch entries and heads before this one, then earlier rows of
+    // this head (summed by the lanes, then reduced)
+    int64_t part = 0;
+    for (int h2 = lane; h2 < hh; h2 += 64) part += arrow_head_nnz(p.mode[h2], p.window[h2], p.nB, p.text_blocks);
+    for (int i2 = lane; i2 < i; i2 += 64) part += arrow_row_len(mode, w, p.nB, p.text_blocks, i2);
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int64_t y = __shfl_up(x, d, 64);
-            if (lane >= d) x += y;
-        }
-        if (lane == 63) wsum[wv] = x;
-        __syncthreads();
-        int64_t pre = 0, tot = 0;
-        for (int v = 0; v < 4; ++v) {
-            if (v < wv) pre += wsum[v];
-            tot += wsum[v];
-        }
-        if (i < p.nB) rp[i + 1] = (int32_t)(base + carry + pre + x);
-        carry += tot;
-        __syncthreads();
-    }
-    if (bh == 0 && tid == 0) p.row_ptr[0] = 0;
-    __syncthreads();   // row_ptr of this head is written (workgroup scope)
+    for (int d = 32; d > 0; d >>= 1) part += __shfl_xor(part, d, 64);
+    const int64_t base = (int64_t)b * p.per_batch + part;
 
-    // columns: one wavefront per row
-    for (int i = wv; i < p.nB; i += 4) {
-        const int64_t start = (i == 0) ? base : (int64_t)rp[i];
-        const int64_t len = arrow_row_len(mode, w, p.nB, p.text_blocks, i);
-        const bool dense = (mode == 0) || (i < p.text_blocks);
-        const int lo = max(p.text_blocks, i - w);
-        for (int64_t e = lane; e < len; e += 64) {
-            int col;
-            if (dense || e < p.text_blocks) col = (int)e;
-            else col = lo + (int)(e - p.text_blocks);
-            if (start + e < p.capacity) p.col_idx[start + e] = col;
-        }
+    const int64_t len = arrow_row_len(mode, w, p.nB, p.text_blocks, i);
+    if (lane == 0) {
+        p.row_ptr[row + 1] = (int32_t)(base + len);
+        if (row == 0) p.row_ptr[0] = 0;
+    }
+    const bool dense = (mode == 0) || (i < p.text_blocks);
+    const int lo = max(p.text_blocks, i - w);
+    for (int64_t e = lane; e < len; e += 64) {
+        const int col = (dense || e < p.text_blocks) ? (int)e : lo + (int)(e - p.text_blocks);
+        if (base + e < p.capacity) p.col_idx[base + e] = col;
     }
 }
 
 hipError_t launch_arrow(const ArrowParams &p, hipStream_t s)
 {
-    const int64_t grid = (int64_t)p.B * p.H;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(arrow_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
+    const int64_t rows = (int64_t)p.B * p.H * p.nB;
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(arrow_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

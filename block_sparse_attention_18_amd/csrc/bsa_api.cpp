@@ -77,6 +77,25 @@ int64_t select_row_bound(int64_t nB, int64_t tb, const bsa_group *g, int32_t ng)
     return k < nB ? k : nB;
 }
 
+// Byte layout of the long-row splitting workspace: counts, work list, split
+// rows, partial-result slots (each region 256-byte aligned).
+struct SplitLayout {
+    size_t items, split_rows, partials, total;
+};
+
+SplitLayout split_layout(int64_t rows, int32_t block, int64_t D, int32_t max_chunks, int64_t max_split_rows)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    SplitLayout l;
+    const int64_t n_items = rows + max_split_rows * (max_chunks - 1);
+    l.items = 256;
+    l.split_rows = l.items + up((size_t)n_items * 16);
+    l.partials = l.split_rows + up((size_t)max_split_rows * 8);
+    l.total = l.partials + (size_t)max_split_rows * max_chunks *
+                               (size_t)bsa::partial_slot_floats(block, (int)D) * sizeof(float);
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,10 +346,20 @@ bsa_status bsa_build_arrow_layout(int64_t B, int64_t H, int64_t N, int32_t block
 }
 
 // ---------------------------------------------------------------------------
+size_t bsa_forward_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int32_t block,
+                                        int32_t max_chunks, int64_t max_split_rows)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || (D != 64 && D != 128) || !block_ok(block) || max_chunks < 2 ||
+        max_chunks > 64 || max_split_rows < 1)
+        return 0;
+    const int64_t rows = B * H * ceil_div(N, block);
+    return split_layout(rows, block, D, max_chunks, std::min(max_split_rows, rows)).total;
+}
+
 bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,
                        const int32_t *row_ptr, const int32_t *col_idx, const int8_t *head_modes,
                        const bsa_tensor *o_cache, const float *lse_cache, float scale,
-                       const bsa_tensor *o, float *lse, void *stream)
+                       const bsa_tensor *o, float *lse, const bsa_split *split, void *stream)
 {
     bsa_status st;
     if ((st = check_tensor(q, "q")) != BSA_OK) return st;
@@ -382,10 +411,64 @@ bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tenso
     const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
     fp.scale_log2 = sc * 1.4426950408889634f;
 
+    const int64_t rows = q->B * H * nB;
+    int64_t grid = rows, split_rows = 0;
+    SplitLayout sl{};
+    if (split) {
+        if (split->chunk_blocks < 1 || split->max_chunks < 2 || split->max_chunks > 64 ||
+            split->max_split_rows < 1)
+            return fail(BSA_ERR_INVALID_ARG,
+                        "split: chunk_blocks >= 1, max_chunks in 2..64 and max_split_rows >= 1 required");
+        split_rows = std::min<int64_t>(split->max_split_rows, rows);
+        sl = split_layout(rows, block, q->D, split->max_chunks, split_rows);
+        if (!split->workspace || !aligned16(split->workspace) || split->workspace_bytes < sl.total)
+            return fail(BSA_ERR_WORKSPACE, "split workspace needs %zu bytes (16-byte aligned)", sl.total);
+        grid = rows + split_rows * (split->max_chunks - 1);
+        if (grid >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "split work list too long");
+    }
+
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if ((e = bsa::launch_forward(fp, block, (int)q->D, s)) != hipSuccess)
+    if (split) {
+        char *ws = static_cast<char *>(split->workspace);
+        bsa::PlanParams pp{};
+        pp.row_ptr = row_ptr;
+        pp.items = reinterpret_cast<int4 *>(ws + sl.items);
+        pp.counts = reinterpret_cast<int32_t *>(ws);
+        pp.split_rows = reinterpret_cast<int2 *>(ws + sl.split_rows);
+        pp.BH = (int32_t)(q->B * H);
+        pp.H = (int32_t)H;
+        pp.nB = (int32_t)nB;
+        std::memcpy(pp.skip_bits, fp.skip_bits, sizeof pp.skip_bits);
+        pp.chunk_blocks = split->chunk_blocks;
+        pp.max_chunks = split->max_chunks;
+        pp.max_split_rows = split_rows;
+        if ((e = bsa::launch_plan(pp, s)) != hipSuccess) return hip_fail(e, "plan launch");
+        fp.items = pp.items;
+        fp.counts = pp.counts;
+        fp.partials = reinterpret_cast<float *>(ws + sl.partials);
+        fp.max_chunks = split->max_chunks;
+    }
+    if ((e = bsa::launch_forward(fp, block, (int)q->D, grid, s)) != hipSuccess)
         return hip_fail(e, "forward launch");
+    if (split) {
+        bsa::CombineParams cp{};
+        cp.partials = fp.partials;
+        cp.counts = fp.counts;
+        cp.split_rows = reinterpret_cast<const int2 *>(static_cast<char *>(split->workspace) + sl.split_rows);
+        cp.o = fp.o;
+        cp.o_sb = fp.o_sb;
+        cp.o_sh = fp.o_sh;
+        cp.o_sn = fp.o_sn;
+        cp.lse = lse;
+        cp.H = (int32_t)H;
+        cp.N = (int32_t)q->N;
+        cp.nB = (int32_t)nB;
+        cp.D = (int32_t)q->D;
+        cp.block = block;
+        cp.max_chunks = split->max_chunks;
+        if ((e = bsa::launch_combine(cp, split_rows, s)) != hipSuccess) return hip_fail(e, "combine launch");
+    }
     if (any_skip) {
         bsa::SkipCopyParams cp{};
         cp.src = t4(o_cache);

@@ -276,15 +276,33 @@ __global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kerne
     const int n = lane & 31;
 
     const int BH = p.B * p.H;
-    const int i = blockIdx.x / BH;
-    const int bh = blockIdx.x - i * BH;
+    int i, bh, chunk = 0, chunks = 1, rank = -1;
+    if (p.items) {   // one item of the long-row splitting work list
+        if ((int)blockIdx.x >= p.counts[0]) return;
+        const int4 it = p.items[blockIdx.x];
+        bh = it.x / p.nB;
+        i = it.x - bh * p.nB;
+        chunk = it.y;
+        chunks = it.z;
+        rank = it.w;
+    } else {         // query-block-major: every head's text rows first
+        i = blockIdx.x / BH;
+        bh = blockIdx.x - i * BH;
+    }
     const int b = bh / p.H;
     const int hh = bh - b * p.H;
     if ((p.skip_bits[hh >> 5] >> (hh & 31)) & 1u) return;
 
     const int64_t row = (int64_t)bh * p.nB + i;
-    const int e0 = p.row_ptr[row];
-    const int e1 = p.row_ptr[row + 1];
+    int e0 = p.row_ptr[row];
+    int e1 = p.row_ptr[row + 1];
+    if (chunks > 1) {   // this workgroup takes one contiguous chunk of the row
+        const int len = e1 > e0 ? e1 - e0 : 0;
+        const int cs = (len + chunks - 1) / chunks;
+        const int lo = e0 + min(len, chunk * cs);
+        e1 = e0 + min(len, (chunk + 1) * cs);
+        e0 = lo;
+    }
     const int T = (e1 > e0 ? e1 - e0 : 0) * Sh::SUB;   // 64-key sub-tiles to visit
 
     const uint16_t *qb = p.q.p + b * p.q.sb + hh * p.q.sh;
@@ -349,8 +367,26 @@ __global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kerne
         k0 = k0n;
     }
 
-    // epilogue: normalise and store O (bf16) and LSE (natural log)
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+    if (rank >= 0) {
+        // a chunk of a split row: park the unnormalised output and the
+        // (reference max, sum) of every query for the combine step
+        float *slot = p.partials + ((int64_t)rank * p.max_chunks + chunk) * partial_slot_floats(BETA, D);
+        const int tq = wv * 32 + n;
+#pragma unroll
+        for (int d = 0; d < Sh::DT; ++d)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4 *>(slot + tq * D + d * 32 + 8 * g + 4 * hl) =
+                    make_float4(st.oacc[d][4 * g + 0], st.oacc[d][4 * g + 1], st.oacc[d][4 * g + 2],
+                                st.oacc[d][4 * g + 3]);
+        if (hl == 0) {
+            slot[BETA * D + tq] = st.m_run;
+            slot[BETA * D + BETA + tq] = l_tot;
+        }
+        return;
+    }
+    // epilogue: normalise and store O (bf16) and LSE (natural log)
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < p.N) {
         uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)qrow * p.o_sn;
@@ -371,23 +407,159 @@ __global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kerne
 }
 
 template <int BETA, int D>
-static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s)
+static hipError_t launch_fwd_t(const FwdParams &p, int64_t grid, hipStream_t s)
 {
     using Sh = FwdShape<BETA, D>;
-    const unsigned grid = (unsigned)((int64_t)p.B * p.H * p.nB);
     if (grid == 0) return hipSuccess;
     auto kern = fwd_kernel<BETA, D>;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(Sh::NT), 0, s, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdParams &p, int block, int D, hipStream_t s)
+hipError_t launch_forward(const FwdParams &p, int block, int D, int64_t grid, hipStream_t s)
 {
-    if (block == 128 && D == 128) return launch_fwd_t<128, 128>(p, s);
-    if (block == 128 && D == 64) return launch_fwd_t<128, 64>(p, s);
-    if (block == 64 && D == 128) return launch_fwd_t<64, 128>(p, s);
-    if (block == 64 && D == 64) return launch_fwd_t<64, 64>(p, s);
+    if (block == 128 && D == 128) return launch_fwd_t<128, 128>(p, grid, s);
+    if (block == 128 && D == 64) return launch_fwd_t<128, 64>(p, grid, s);
+    if (block == 64 && D == 128) return launch_fwd_t<64, 128>(p, grid, s);
+    if (block == 64 && D == 64) return launch_fwd_t<64, 64>(p, grid, s);
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Long-row splitting.  One workgroup walks the rows query-block-major (the
+// order the forward dispatches them in), cuts every row longer than
+// chunk_blocks into min(max_chunks, ceil(len / chunk_blocks)) chunks, ranks
+// the split rows (at most max_split_rows; later long rows stay whole) and
+// writes the work list.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void plan_kernel(const PlanParams p)
+{
+    __shared__ int ws_split[16], ws_items[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t rows = (int64_t)p.BH * p.nB;
+    int carry_split = 0, carry_items = 0;
+    for (int64_t base = 0; base < rows; base += 1024) {
+        const int64_t g = base + tid;   // query-block-major position
+        int len = 0, row = 0;
+        if (g < rows) {
+            const int i = (int)(g / p.BH), bh = (int)(g % p.BH);
+            row = bh * p.nB + i;
+            len = max(0, p.row_ptr[row + 1] - p.row_ptr[row]);
+        }
+        int want = 1;
+        const int hh = (int)((g % p.BH) % p.H);
+        const bool skip_head = (p.skip_bits[hh >> 5] >> (hh & 31)) & 1u;
+        if (g < rows && !skip_head && len > p.chunk_blocks)
+            want = min(p.max_chunks, (len + p.chunk_blocks - 1) / p.chunk_blocks);
+        int split = (g < rows && want > 1) ? 1 : 0;
+        // rank of this split row
+        int incl = wave_incl_scan(split);
+        if (lane == 63) ws_split[wv] = incl;
+        __syncthreads();
+        int pre = 0, tot_split = 0;
+        for (int x = 0; x < 16; ++x) {
+            if (x < wv) pre += ws_split[x];
+            tot_split += ws_split[x];
+        }
+        const int rank = carry_split + pre + incl - split;
+        if (split && rank >= p.max_split_rows) {   // pool full: run this row whole
+            split = 0;
+            want = 1;
+        }
+        const int items = g < rows ? want : 0;
+        int incl2 = wave_incl_scan(items);
+        if (lane == 63) ws_items[wv] = incl2;
+        __syncthreads();
+        int pre2 = 0, tot_items = 0;
+        for (int x = 0; x < 16; ++x) {
+            if (x < wv) pre2 += ws_items[x];
+            tot_items += ws_items[x];
+        }
+        const int first = carry_items + pre2 + incl2 - items;
+        for (int c = 0; c < items; ++c) p.items[first + c] = make_int4(row, c, want, split ? rank : -1);
+        if (split) p.split_rows[rank] = make_int2(row, want);
+        carry_split += tot_split;
+        carry_items += tot_items;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        p.counts[0] = carry_items;
+        p.counts[1] = (int)min((int64_t)carry_split, p.max_split_rows);
+    }
+}
+
+hipError_t launch_plan(const PlanParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, p);
+    return hipGetLastError();
+}
+
+// Merge the chunks of one split row: with reference maxima m_c and sums l_c,
+// M = max m_c, L = sum l_c 2^(m_c - M), O = sum O_c 2^(m_c - M) / L and
+// LSE = (M + log2 L) ln 2.  One workgroup per split row, two threads per
+// query (half the head dimension each).
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const CombineParams p)
+{
+    constexpr int HALF = D / 2;
+    if ((int)blockIdx.x >= p.counts[1]) return;
+    const int2 sr = p.split_rows[blockIdx.x];
+    const int row = sr.x, chunks = sr.y;
+    const int bh = row / p.nB, i = row - bh * p.nB;
+    const int b = bh / p.H, hh = bh - b * p.H;
+    const int64_t slot_floats = partial_slot_floats(p.block, D);
+    const float *base = p.partials + (int64_t)blockIdx.x * p.max_chunks * slot_floats;
+    for (int x = threadIdx.x; x < 2 * p.block; x += blockDim.x) {
+        const int tq = x >> 1, d0 = (x & 1) * HALF;
+        const int t = i * p.block + tq;
+        if (t >= p.N) continue;
+        float M = -INFINITY;
+        for (int c = 0; c < chunks; ++c) M = fmaxf(M, base[c * slot_floats + p.block * D + tq]);
+        float L = 0.f;
+        float acc[HALF];
+#pragma unroll
+        for (int d = 0; d < HALF; ++d) acc[d] = 0.f;
+        for (int c = 0; c < chunks; ++c) {
+            const float *slot = base + c * slot_floats;
+            const float mc = slot[p.block * D + tq];
+            const float w = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
+            L += slot[p.block * D + p.block + tq] * w;
+            const float *src = slot + tq * D + d0;
+#pragma unroll
+            for (int d = 0; d < HALF; d += 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(src + d);
+                acc[d] += a.x * w;
+                acc[d + 1] += a.y * w;
+                acc[d + 2] += a.z * w;
+                acc[d + 3] += a.w * w;
+            }
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)t * p.o_sn + d0;
+#pragma unroll
+        for (int d = 0; d < HALF; d += 8) {
+            uint4 st;
+            st.x = pack_bf16x2(acc[d] * inv, acc[d + 1] * inv);
+            st.y = pack_bf16x2(acc[d + 2] * inv, acc[d + 3] * inv);
+            st.z = pack_bf16x2(acc[d + 4] * inv, acc[d + 5] * inv);
+            st.w = pack_bf16x2(acc[d + 6] * inv, acc[d + 7] * inv);
+            *reinterpret_cast<uint4 *>(orow + d) = st;
+        }
+        if (p.lse && (x & 1) == 0)
+            p.lse[(int64_t)bh * p.N + t] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    }
+}
+
+hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s)
+{
+    if (grid <= 0) return hipSuccess;
+    if (p.D == 128)
+        hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    else if (p.D == 64)
+        hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 // SKIP heads: copy the cached output (and LSE) of the head unchanged

@@ -28,6 +28,35 @@ struct FwdParams {
     int32_t B, H, N, nB;
     float scale_log2;           // softmax scale * log2(e)
     uint32_t skip_bits[kMaxSkipHeads / 32];
+    // long-row splitting (items == null: one workgroup per row)
+    const int4 *items;          // {row, chunk, chunks, split rank or -1}
+    const int32_t *counts;      // [0] items, [1] split rows
+    float *partials;            // [split rank * max_chunks + chunk] slots
+    int32_t max_chunks;
+};
+
+// Work-list builder for long-row splitting.
+struct PlanParams {
+    const int32_t *row_ptr;
+    int4 *items;
+    int32_t *counts;
+    int2 *split_rows;           // [rank] = {row, chunks}
+    int32_t BH, H, nB;
+    int32_t chunk_blocks, max_chunks;
+    int64_t max_split_rows;
+    uint32_t skip_bits[kMaxSkipHeads / 32];   // rows of SKIP heads are never split
+};
+
+// Merges the partial results of split rows.
+struct CombineParams {
+    const float *partials;
+    const int32_t *counts;
+    const int2 *split_rows;
+    uint16_t *o;
+    int64_t o_sb, o_sh, o_sn;
+    float *lse;
+    int32_t H, N, nB, D, block;
+    int32_t max_chunks;
 };
 
 struct SkipCopyParams {
@@ -89,8 +118,12 @@ struct ArrowParams {
     int32_t window[kMaxArrowHeads];
 };
 
-hipError_t launch_forward(const FwdParams &p, int block, int D, hipStream_t s);
+hipError_t launch_forward(const FwdParams &p, int block, int D, int64_t grid, hipStream_t s);
 hipError_t launch_skip_copy(const SkipCopyParams &p, hipStream_t s);
+hipError_t launch_plan(const PlanParams &p, hipStream_t s);
+hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s);
+// bytes of one partial-result slot (O [block][D] fp32, then max and sum [block])
+__host__ __device__ inline int64_t partial_slot_floats(int block, int D) { return (int64_t)block * D + 2 * block; }
 hipError_t launch_pool_proj(const PoolParams &p, int block, int D, hipStream_t s);
 hipError_t launch_scores(const ScoreParams &p, hipStream_t s);
 hipError_t launch_exact_scores(const ExactParams &p, int block, int D, int slots, hipStream_t s);

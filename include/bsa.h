@@ -160,6 +160,29 @@ bsa_status bsa_build_arrow_layout(int64_t B, int64_t H, int64_t N, int32_t block
                                   int32_t *col_idx, int64_t capacity, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Long-row splitting for bsa_forward (optional).  Rows with more than
+ * chunk_blocks kept blocks are cut into at most max_chunks contiguous chunks
+ * of their block list; each chunk runs in its own workgroup and the partial
+ * results (unnormalised output, running max and sum per query) are merged
+ * afterwards, which is exact up to rounding order.  At most max_split_rows
+ * rows are split (in the order text-like long rows are met: query-block
+ * major, then batch and head); further long rows run unsplit.  This is a
+ * scheduling device only: it balances rows of very different lengths (text
+ * rows and full heads next to short windowed rows, [W] 4.3 on the cost of
+ * irregular block sets); it does not change the result beyond rounding.
+ * ---------------------------------------------------------------------- */
+typedef struct bsa_split {
+    int32_t chunk_blocks;   /* split rows longer than this (>= 1)            */
+    int32_t max_chunks;     /* chunks per split row, 2..64                    */
+    int64_t max_split_rows; /* capacity of the partial-result pool, >= 1      */
+    void *workspace;        /* device, >= bsa_forward_split_workspace_size()  */
+    size_t workspace_bytes;
+} bsa_split;
+
+size_t bsa_forward_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int32_t block,
+                                        int32_t max_chunks, int64_t max_split_rows);
+
+/* ------------------------------------------------------------------------
  * bsa_forward -- block-sparse attention forward ([W] 3.1, [D] fused
  * kernel, [S] sparse attention with a precomputed mask).  For every token
  * t of a computed head, with i = t / block:
@@ -178,14 +201,16 @@ bsa_status bsa_build_arrow_layout(int64_t B, int64_t H, int64_t N, int32_t block
  * untouched ([D] head-wise caching).  o_cache is required iff some head is
  * SKIP.
  * scale <= 0 selects 1/sqrt(D).  lse: device fp32 [B][H][N] or NULL.
+ * split: NULL (every row in one workgroup) or the long-row splitting above.
  * Errors: INVALID_ARG (null pointers, shape mismatch, misalignment, SKIP
- * without o_cache), UNSUPPORTED (D or block size).
+ * without o_cache, bad split parameters), UNSUPPORTED (D or block size),
+ * WORKSPACE (split workspace too small).
  * ---------------------------------------------------------------------- */
 bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
                        int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
                        const int8_t *head_modes, const bsa_tensor *o_cache,
                        const float *lse_cache, float scale, const bsa_tensor *o, float *lse,
-                       void *stream);
+                       const bsa_split *split, void *stream);
 
 /* Name of a status code (static string). */
 const char *bsa_status_string(bsa_status status);

@@ -53,7 +53,7 @@ def _t(B=1, H=2, N=256, D=64, data=FAKE, sb=None, sh=None, sn=None):
 
 
 def _fwd(q=None, k=None, v=None, o=None, block=64, rp=FAKE, ci=FAKE, modes=None, oc=None,
-         scale=0.0):
+         scale=0.0, split=None):
     lib = bsa.load()
     q = q or _t()
     k = k or _t()
@@ -62,7 +62,8 @@ def _fwd(q=None, k=None, v=None, o=None, block=64, rp=FAKE, ci=FAKE, modes=None,
     ref = lambda d: None if d is None else ctypes.byref(d)
     return lib.bsa_forward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), block,
                            ctypes.c_void_p(rp) if rp else None, ctypes.c_void_p(ci) if ci else None,
-                           modes, ref(oc), None, scale, ctypes.byref(o), None, None)
+                           modes, ref(oc), None, scale, ctypes.byref(o), None,
+                           None if split is None else ctypes.byref(split), None)
 
 
 def _err():
@@ -91,6 +92,50 @@ def test_forward_skip_requires_cache_and_known_modes():
     assert _fwd(modes=modes, oc=_t(N=128)) == 1 and "o_cache" in _err()
     bad = (ctypes.c_int8 * 2)(0, 7)
     assert _fwd(modes=bad) == 1 and "unknown mode" in _err()
+
+
+def test_forward_split_validation_and_workspace_size():
+    lib = bsa.load()
+    # 1 x 2 heads x 4 query blocks = 8 rows; 3 split rows of 4 chunks
+    need = lib.bsa_forward_split_workspace_size(1, 2, 256, 64, 64, 4, 3)
+    items = 8 + 3 * 3
+    slot_floats = 64 * 64 + 2 * 64
+    up = lambda x: (x + 255) // 256 * 256
+    assert need == 256 + up(items * 16) + up(3 * 8) + 3 * 4 * slot_floats * 4
+    # the split-row pool is capped at the number of rows
+    assert lib.bsa_forward_split_workspace_size(1, 2, 256, 64, 64, 4, 100) == \
+        lib.bsa_forward_split_workspace_size(1, 2, 256, 64, 64, 4, 8)
+    assert lib.bsa_forward_split_workspace_size(1, 2, 256, 64, 64, 1, 3) == 0
+    mk = lambda cb=8, mc=4, msr=3, ws=FAKE, wsb=1 << 30: bsa.BsaSplit(cb, mc, msr, ws, wsb)
+    assert _fwd(split=mk(cb=0)) == 1 and "split" in _err()
+    assert _fwd(split=mk(mc=1)) == 1
+    assert _fwd(split=mk(mc=65)) == 1
+    assert _fwd(split=mk(msr=0)) == 1
+    assert _fwd(split=mk(wsb=need - 1)) == 4 and "split workspace" in _err()
+    assert _fwd(split=mk(ws=0)) == 4
+    assert _fwd(split=mk(ws=FAKE + 4)) == 4
+
+
+def test_split_policies():
+    # 2K MMDiT arrow, w = 8: text rows (132 blocks) are shorter than the average
+    # work per workgroup slot, so splitting does not pay
+    modes = [bsa.HEAD_ARROW] * 24
+    assert bsa.arrow_split_policy(1, 24, 16896, 128, 512, modes, [8] * 24) is None
+    # w = 0: the text rows dominate; they are cut into 4 chunks of <= 33 blocks
+    plan = bsa.arrow_split_policy(1, 24, 16896, 128, 512, modes, [0] * 24)
+    assert plan == {"chunk_blocks": 33, "max_chunks": 4, "max_split_rows": 96}
+    # FLUX 1024^2 mix (12 arrow w=1 / 8 full / 4 skip): the predicted gain is
+    # marginal, so the policy keeps rows whole
+    modes2 = [1] * 12 + [0] * 8 + [2] * 4
+    assert bsa.arrow_split_policy(1, 24, 4608, 128, 512, modes2, [1] * 24) is None
+    # with a single long head among many windowed ones the split pays
+    modes3 = [0] + [1] * 63
+    plan3 = bsa.arrow_split_policy(1, 64, 4608, 128, 512, modes3, [0] * 64)
+    assert plan3 is not None and plan3["max_split_rows"] == 36 + 63 * 4
+    # uniform rows: nothing to split
+    assert bsa.select_split_policy(1, 32, 512, 0, ((0, 480, 144), (480, 512, 10))) is None
+    # the list schedule itself
+    assert bsa._makespan([3, 1, 1, 1], 2) == 3 and bsa._makespan([1, 1, 1, 1], 2) == 2
 
 
 def test_pool_scores_validation():

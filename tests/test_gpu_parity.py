@@ -119,6 +119,66 @@ def test_forward_strided_skip_and_alias():
     np.testing.assert_array_equal(bf16_bits(O2)[:, comp], Ob[:, comp])
 
 
+SPLIT_CASES = [
+    # B, H, N, D, block, chunk_blocks, max_chunks, max_split_rows, seed
+    (2, 3, 9 * 128 + 40, 128, 128, 2, 4, 64, 200),     # many split rows, ragged tail
+    (1, 2, 12 * 64, 64, 64, 3, 3, 4, 201),             # pool smaller than the long rows
+    (1, 2, 10 * 128, 64, 128, 4, 2, 100, 202),
+    (2, 2, 7 * 64 + 3, 128, 64, 1, 64, 1000, 203),     # a chunk per block, empty chunks
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,block,cb,mc,msr,seed", SPLIT_CASES)
+def test_forward_split_long_rows(B, H, N, D, block, cb, mc, msr, seed):
+    _log(f"split B={B} H={H} N={N} D={D} block={block} chunk={cb} chunks={mc} pool={msr}")
+    q, k, v = synth.random_qkv(B, H, N, D, seed=seed)
+    nB = -(-N // block)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=seed + 1, density=0.6, empty_rows=2, full_rows=4)
+    split = {"chunk_blocks": cb, "max_chunks": mc, "max_split_rows": msr}
+    O, L = _run_forward(q, k, v, block, rp, ci, split=split)
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci)
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "split")
+    O1, L1 = _run_forward(q, k, v, block, rp, ci)
+    assert float((O.float() - O1.float()).abs().max()) <= 2e-2
+    # the plan's bookkeeping: items and split rows as the host expects
+    lens = np.diff(rp)
+    order = [(bh * nB + i) for i in range(nB) for bh in range(B * H)]
+    want = [min(mc, -(-int(lens[r]) // cb)) if lens[r] > cb else 1 for r in order]
+    n_split = min(msr, sum(1 for x in want if x > 1))
+    counts = split["workspace"][:8].view(torch.int32).cpu().numpy()
+    assert counts[1] == n_split
+    ranked = 0
+    n_items = 0
+    for x in want:
+        if x > 1 and ranked < msr:
+            ranked += 1
+            n_items += x
+        else:
+            n_items += 1
+    assert counts[0] == n_items
+
+
+def test_forward_split_with_skip_heads_keeps_lse():
+    B, H, N, D, block = 1, 3, 6 * 128, 128, 128
+    q, k, v = synth.random_qkv(B, H, N, D, seed=210)
+    nB = N // block
+    rp, ci = synth.random_block_lists(B, H, nB, seed=211, density=0.9, empty_rows=0, full_rows=6)
+    modes = np.array([bsa.HEAD_FULL, bsa.HEAD_SKIP, bsa.HEAD_ARROW], np.int8)
+    cache = synth.random_qkv(B, H, N, D, seed=212)[0]
+    lse = torch.full((B, H, N), 123.0, dtype=torch.float32, device=dev())
+    split = {"chunk_blocks": 1, "max_chunks": 6, "max_split_rows": 100}
+    O, L = _run_forward(q, k, v, block, rp, ci, head_modes=modes, o_cache=to_dev_bf16(cache), lse=lse,
+                        split=split)
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci)
+    comp = modes != bsa.HEAD_SKIP
+    check_forward(bf16_to_f64(O)[:, comp], L.cpu().numpy()[:, comp].astype(np.float64), Oo[:, comp],
+                  Lo[:, comp], "split+skip")
+    np.testing.assert_array_equal(bf16_bits(O)[:, ~comp], cache[:, ~comp])
+    assert torch.all(L[:, 1] == 123.0)
+    # rows of the skip head are never split
+    assert split["workspace"][:8].view(torch.int32).cpu().numpy()[1] == 2 * nB
+
+
 def test_forward_is_deterministic():
     B, H, N, D, block = 1, 4, 8 * 128, 128, 128
     q, k, v = synth.random_qkv(B, H, N, D, seed=130)
@@ -228,11 +288,11 @@ def test_exact_scores_small(B, H, N, D, block):
 # ---------------------------------------------------------------------------
 # the five workloads at full size
 # ---------------------------------------------------------------------------
-def _workload_forward_check(wl, x, rp, ci, n_sample, seed, must_blocks=(), modes=None):
+def _workload_forward_check(wl, x, rp, ci, n_sample, seed, must_blocks=(), modes=None, split=None):
     B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
-    kw = {}
+    kw = {} if split is None else {"split": split}
     if modes is not None:
-        kw = dict(head_modes=modes, o_cache=to_dev_bf16(x["o_cache"]) if "o_cache" in x else None,
+        kw.update(head_modes=modes, o_cache=to_dev_bf16(x["o_cache"]) if "o_cache" in x else None,
                   lse_cache=torch.from_numpy(x["lse_cache"]).to(dev()) if "lse_cache" in x else None)
     O, L = _run_forward(x["q"], x["k"], x["v"], block, rp, ci, **kw)
     must = []
@@ -291,6 +351,14 @@ def test_workload_arrow(name):
     comp_heads = [h for h in range(wl.H) if modes[h] != bsa.HEAD_SKIP]
     must = [(0, comp_heads[0], 0), (0, comp_heads[-1], nB - 1), (0, comp_heads[len(comp_heads) // 2], nB // 2)]
     O, L = _workload_forward_check(wl, x, rpo, cio, 384, seed=170, must_blocks=must, modes=modes)
+    # the same forward with long rows split over several workgroups
+    # the same forward with long rows split over several workgroups (forced:
+    # the policy may judge a split not worth it for this workload)
+    plan = bsa.arrow_split_policy(wl.B, wl.H, wl.N, wl.block, wl.text_len, modes, wins) or \
+        {"chunk_blocks": 33 if name == "C4" else 9, "max_chunks": 4, "max_split_rows": 1000}
+    O2, L2 = _workload_forward_check(wl, x, rpo, cio, 384, seed=171, must_blocks=must, modes=modes,
+                                     split=plan)
+    assert float((O.float() - O2.float()).abs().max()) <= 2e-2
     skip = modes == bsa.HEAD_SKIP
     if skip.any():
         np.testing.assert_array_equal(bf16_bits(O)[:, skip], x["o_cache"][:, skip])
@@ -317,6 +385,8 @@ def test_workload_c3_content_driven():
     _log(f"C3: {differ} of {len(qb)} rows differ only by near-ties")
     assert rpo[-1] == wl.B * wl.H * (tb * nB + (nB - tb) * (tb + 16))
     _workload_forward_check(wl, x, rpo, cio, 512, seed=171, must_blocks=[(1, 15, 0), (0, 3, nB - 1)])
+    plan = {"chunk_blocks": 20, "max_chunks": 4, "max_split_rows": 128}
+    _workload_forward_check(wl, x, rpo, cio, 512, seed=172, must_blocks=[(1, 15, 0), (0, 3, 1)], split=plan)
 
 
 @pytest.mark.slow
