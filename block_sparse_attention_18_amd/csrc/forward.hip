@@ -21,10 +21,14 @@
 //    B operand (16 keys x 32 queries) of O^T = V^T P^T.  Each lane therefore
 //    owns one query: the running max, running sum and the O rescale are
 //    lane-local, and only the max needs one cross-half exchange per block.
-//  * K is staged row-major and V transposed ([d][key]) in LDS with XOR
-//    swizzles of 16-byte chunks, so the 128-bit operand reads and the
-//    staging writes stay (near) conflict-free without padding.
-//  * exp is exp2 with scale*log2(e) folded into one FMA.
+//  * K and V are copied row-major into LDS by buffer loads that write LDS
+//    directly, double-buffered in 64-key sub-tiles, with XOR swizzles of
+//    16-byte chunks so that the 128-bit K reads and the transposing V reads
+//    are conflict-free without padding.
+//  * Software pipeline: step t computes S^T of sub-tile t while it finishes
+//    the softmax and O update of sub-tile t-1, and the vector work (exp2
+//    with scale*log2(e) folded into one FMA, row sums, bf16 packing, row
+//    max) is spread between the MFMAs of the same wave.
 #include "common.h"
 #include "internal.h"
 
@@ -62,10 +66,15 @@ struct WaveState {
     f32x16 oacc[Sh::DT];
     float m_run;                 // reference max, log2-scaled domain
     float l_run;                 // running sum over this lane's keys
-    uint32_t kread[Sh::QS];      // K operand of k-step s, key sub-tile 0 (bytes in a tile)
-    uint32_t vread[Sh::DT];      // V^T operand of d tile d, keys 0..3 (bytes in a tile)
+    uint32_t kread;              // K operand of k-step 0 (bytes in a tile); k-step s: ^ KSTEP * s
+    uint32_t vread;              // V^T operand of d tile 0, keys 0..3; d tile d: ^ VSTEP * d
     uint32_t kdma, vdma;         // source offset of the lane's first 16-byte copy of a tile
 };
+
+// The swizzles XOR the chunk index with row bits, so stepping the chunk by
+// a power of two that the swizzle also touches is an XOR of the byte offset:
+// K k-step s moves 2 chunks (32 bytes), V d tile d moves 4 chunks (64 bytes).
+constexpr uint32_t KSTEP = 32, VSTEP = 64;
 
 template <int BETA, int D>
 __device__ __forceinline__ void init_offsets(WaveState<BETA, D> &st, const FwdParams &p, int wv, int lane)
@@ -73,18 +82,13 @@ __device__ __forceinline__ void init_offsets(WaveState<BETA, D> &st, const FwdPa
     using Sh = FwdShape<BETA, D>;
     const int hl = lane >> 5, n = lane & 31;
     const int r0 = perm_row(n);
-#pragma unroll
-    for (int s = 0; s < Sh::QS; ++s)
-        st.kread[s] = (uint32_t)(r0 * D * 2 + (((2 * s + hl) ^ kswz<D>(r0)) * 16));
+    st.kread = (uint32_t)(r0 * D * 2 + ((hl ^ kswz<D>(r0)) * 16));
     // transposing V reads: lane 4r + c of each 16-lane group names row r,
     // columns 4c..4c+3; lane x of the group receives column x of rows 0..3
     const int G = lane >> 4, jl = lane & 15;
     const int vr0 = 8 * (G >> 1) + (jl >> 2);
-#pragma unroll
-    for (int d = 0; d < Sh::DT; ++d) {
-        const int dc = 32 * d + 16 * (G & 1) + 4 * (jl & 3);
-        st.vread[d] = (uint32_t)(vr0 * D * 2 + (((dc >> 3) ^ vswz<D>(vr0)) * 16) + (dc & 4) * 2);
-    }
+    const int dc = 16 * (G & 1) + 4 * (jl & 3);
+    st.vread = (uint32_t)(vr0 * D * 2 + (((dc >> 3) ^ vswz<D>(vr0)) * 16) + (dc & 4) * 2);
     // copy x of a lane covers tile row r0 + x * ROWS_PER_COPY with the same
     // chunk: the swizzles only use row bits that the step leaves unchanged
     const int slot = wv * 64 + lane;
@@ -94,51 +98,63 @@ __device__ __forceinline__ void init_offsets(WaveState<BETA, D> &st, const FwdPa
 }
 
 
-// S^T (64 keys x 32 queries) of one sub-tile from the K tile Kc.
+// S^T (64 keys x 32 queries) of one sub-tile from the K tile Kc; the two
+// 32-key accumulator chains alternate so consecutive MFMAs are independent.
 template <int BETA, int D>
 __device__ __forceinline__ void qk_mfma(const uint16_t *__restrict__ Kc, const WaveState<BETA, D> &st,
                                         f32x16 (&sacc)[2])
 {
     using Sh = FwdShape<BETA, D>;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < Sh::QS; ++s) {
-            const bf16x8 a = *lds_at<bf16x8>(Kc + kt * 32 * D, st.kread[s]);
+    for (int s = 0; s < Sh::QS; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const bf16x8 a = *lds_at<bf16x8>(Kc + kt * 32 * D, st.kread ^ (KSTEP * s));
             sacc[kt] = mfma32x32x16(a, st.qf[s], sacc[kt]);
         }
-    }
 }
 
 // Keys past N in a partial last tile do not exist: their scores become -inf.
+// Accumulator row r of half-wave hl is key 8 hl + koff(r) of its 32-key tile
+// (the permuted order of the K rows).
+__device__ __forceinline__ constexpr int koff(int r) { return (r & 3) + 4 * ((r >> 2) & 1) + 16 * ((r >> 3) & 1); }
+
 template <int BETA, int D>
 __device__ __forceinline__ void mask_tail(int k0, int N, int lane, f32x16 (&sacc)[2])
 {
-    const int hl = lane >> 5;
+    const int lim = N - k0 - 8 * (lane >> 5);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kt * 32 + perm_row(8 * (r >> 2) + 4 * hl + (r & 3));
-            if (key >= N) sacc[kt][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+            if (kt * 32 + koff(r) >= lim) sacc[kt][r] = -INFINITY;
 }
 
-// Online softmax, part 1: the sub-tile's row max (both lane halves) and the
-// lazy rescale of the running state when it exceeds the reference by more
-// than the slack.
+// Online softmax, part 1: the sub-tile's row max (the two lane halves hold
+// the two key halves of every query, exchanged by a lane swap) and the lazy
+// rescale of the running state when it exceeds the reference by more than
+// the slack.
+__device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2], float c)
+{
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        m0 = fmaxf(m0, sacc[0][r]);
+        m1 = fmaxf(m1, sacc[1][r]);
+    }
+    const float mx = fmaxf(m0, m1);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+}
+
 template <int BETA, int D>
-__device__ __forceinline__ void softmax_rescale(const f32x16 (&sacc)[2], float c, WaveState<BETA, D> &st)
+__device__ __forceinline__ void lazy_rescale(float mx, WaveState<BETA, D> &st)
 {
     using Sh = FwdShape<BETA, D>;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
     if (__ballot(mx > st.m_run + kRescaleSlack)) {
         const float m_new = fmaxf(st.m_run, mx);
         const float alpha = (st.m_run == m_new) ? 1.f : fast_exp2(st.m_run - m_new);
@@ -152,40 +168,40 @@ __device__ __forceinline__ void softmax_rescale(const f32x16 (&sacc)[2], float c
 }
 
 // Online softmax, part 2: probabilities relative to the reference max,
-// summed and packed to bf16 as the B operand of each 16-key k-step.
-template <int BETA, int D>
+// summed and packed to bf16 as the B operand of each 16-key k-step.  Groups
+// G0 .. G1-1 of the four (kt, u) groups are done.
+template <int BETA, int D, int G0 = 0, int G1 = 4>
 __device__ __forceinline__ void softmax_probs(const f32x16 (&sacc)[2], float c, WaveState<BETA, D> &st,
                                               bf16x8 (&pf)[2][2])
 {
     const float mr = st.m_run;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int g = G0; g < G1; ++g) {
+        const int kt = g >> 1, u = g & 1;
+        float pr[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float pr[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pr[e] = fast_exp2(__builtin_fmaf(sacc[kt][8 * u + e], c, -mr));
-                st.l_run += pr[e];
-            }
-            uint4 pk;
-            pk.x = pack_bf16x2(pr[0], pr[1]);
-            pk.y = pack_bf16x2(pr[2], pr[3]);
-            pk.z = pack_bf16x2(pr[4], pr[5]);
-            pk.w = pack_bf16x2(pr[6], pr[7]);
-            pf[kt][u] = as_bf16x8(pk);
+        for (int e = 0; e < 8; ++e) {
+            pr[e] = fast_exp2(__builtin_fmaf(sacc[kt][8 * u + e], c, -mr));
+            st.l_run += pr[e];
         }
+        uint4 pk;
+        pk.x = pack_bf16x2(pr[0], pr[1]);
+        pk.y = pack_bf16x2(pr[2], pr[3]);
+        pk.z = pack_bf16x2(pr[4], pr[5]);
+        pk.w = pack_bf16x2(pr[6], pr[7]);
+        pf[kt][u] = as_bf16x8(pk);
+    }
 }
 
 // O^T += V^T P^T with the V tile Vc.  V^T operands come from row-major V by
 // transposing LDS reads.
-template <int BETA, int D>
+template <int BETA, int D, int KT0 = 0, int KT1 = 2>
 __device__ __forceinline__ void pv_mfma(const uint16_t *__restrict__ Vc, const bf16x8 (&pf)[2][2],
                                         WaveState<BETA, D> &st)
 {
     using Sh = FwdShape<BETA, D>;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = KT0; kt < KT1; ++kt) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -196,7 +212,7 @@ __device__ __forceinline__ void pv_mfma(const uint16_t *__restrict__ Vc, const b
                     const uint16_t *rowp = Vc + (kt * 32 + 16 * u + 4 * pp) * D;
                     h2[pp] = __builtin_bit_cast(
                         s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                   (__attribute__((address_space(3))) bf16x4 *)lds_at<uint16_t>(rowp, st.vread[d])));
+                                   (__attribute__((address_space(3))) bf16x4 *)lds_at<uint16_t>(rowp, st.vread ^ (VSTEP * d))));
                 }
                 const bf16x8 a =
                     __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -218,46 +234,117 @@ __device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_b
     using Sh = FwdShape<BETA, D>;
     const int rows = p.N - k0;
     const uint32_t so = (uint32_t)((int64_t)k0 * sn * 2);
-    const uint32_t step = (uint32_t)((int64_t)Sh::ROWS_PER_COPY * sn * 2);
+    if (Sh::UNIFORM_COPY && rows >= 64) {
+        // full tile: copy x is copy 0 moved by x * ROWS_PER_COPY rows
+        const uint32_t step = (uint32_t)((int64_t)Sh::ROWS_PER_COPY * sn * 2);
+#pragma unroll
+        for (int x = 0; x < Sh::DMA; ++x)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16,
+                                                     off0, so + x * step, 0, 0);
+        return;
+    }
 #pragma unroll
     for (int x = 0; x < Sh::DMA; ++x) {
-        uint32_t o = off0, sx = so + x * step;
-        if (rows < 64 || !Sh::UNIFORM_COPY) {
-            const int slot = (x * Sh::NW + wv) * 64 + lane;
-            const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
-            const int rr = min(r, rows - 1);
-            o = (uint32_t)(rr * sn * 2 + ((ps ^ (is_v ? vswz<D>(r) : kswz<D>(r))) * 16));
-            sx = so;
-        }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16,
-                                                 o, sx, 0, 0);
+        const int slot = (x * Sh::NW + wv) * 64 + lane;
+        const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
+        const int rr = min(r, rows - 1);
+        const uint32_t o = (uint32_t)(rr * sn * 2 + ((ps ^ (is_v ? vswz<D>(r) : kswz<D>(r))) * 16));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16, o, so,
+                                                 0, 0);
     }
 }
 
-// One pipeline step: start copying the next sub-tile (K and V) into the
-// other buffer pair, then fold the current sub-tile (keys k0 .. k0+63 in
-// Kc / Vc) into the wave's online softmax.  The restrict-qualified buffers
-// tell the compiler that the copies in flight do not alias the tiles read.
-template <int BETA, int D>
-__device__ __forceinline__ void pipeline_step(
-    const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vc, uint16_t *__restrict__ Kn,
-    uint16_t *__restrict__ Vn, bool prefetch, int k0n, bool compute, int k0,
-    __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const FwdParams &p, int wv, int lane,
-    WaveState<BETA, D> &st)
+// Instruction interleave of one region: NPRE LDS reads first, then NM
+// groups of one MFMA, NR LDS reads, NV vector and NE transcendental
+// instructions.  A waiting MFMA holds the SIMD's issue stage, so the
+// softmax's vector work is spread between the MFMAs of the same wave rather
+// than run beside a back-to-back MFMA chain.
+template <int NPRE, int NM, int NR, int NV, int NE>
+__device__ __forceinline__ void interleave()
 {
-    if (prefetch) {
-        load_tile<BETA, D>(Kn, krs, p.k.sn, st.kdma, false, p, k0n, wv, lane);
-        load_tile<BETA, D>(Vn, vrs, p.v.sn, st.vdma, true, p, k0n, wv, lane);
+    __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
+#pragma unroll
+    for (int x = 0; x < NM; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+        __builtin_amdgcn_sched_group_barrier(0x400, NE, 0);
     }
-    if (!compute) return;
+}
+
+// Scores of a sub-tile whose block index is invalid, or of keys past N in
+// the last tile, are masked out (valid tiles always keep key k0 < N).
+template <int BETA, int D>
+__device__ __forceinline__ void mask_scores(bool valid, int k0, int N, int lane, f32x16 (&sacc)[2])
+{
+    if (!valid || k0 + 64 > N) mask_tail<BETA, D>(k0, valid ? N : k0, lane, sacc);
+}
+
+// Steady-state step t: S^T of sub-tile t (K tile Kc) and the softmax and O
+// update of sub-tile t-1 (scores s_prev, V tile Vp).  Copies of K(t+1) into
+// Kn (when there is one) and V(t) into Vn are issued first.  Three scheduled
+// regions:
+//   A: QK^T(t)               with probabilities of keys 0..47 of t-1
+//   B: PV(t-1), keys 0..31   with probabilities of keys 48..63 of t-1
+//   C: PV(t-1), keys 32..63  with the row max of t
+// then the lazy rescale for t.  t's scores are masked at the next step.
+template <int BETA, int D>
+__device__ __forceinline__ void fused_step(
+    const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vp, uint16_t *__restrict__ Kn,
+    uint16_t *__restrict__ Vn, bool valid, int k0, bool valid_p, int k0_p, bool load_k, int k0_k,
+    __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const FwdParams &p, int wv, int lane,
+    WaveState<BETA, D> &st, f32x16 (&s_cur)[2], f32x16 (&s_prev)[2])
+{
+    using Sh = FwdShape<BETA, D>;
+    // masking of t-1's scores first: a branch here does not split the
+    // scheduled regions, and t's scores are not live yet
+    mask_scores<BETA, D>(valid_p, k0_p, p.N, lane, s_prev);
+    if (load_k) load_tile<BETA, D>(Kn, krs, p.k.sn, st.kdma, false, p, k0_k, wv, lane);
+    load_tile<BETA, D>(Vn, vrs, p.v.sn, st.vdma, true, p, k0, wv, lane);
     const float c = p.scale_log2;
-    f32x16 sacc[2];
-    qk_mfma<BETA, D>(Kc, st, sacc);
-    if (k0 + 64 > p.N) mask_tail<BETA, D>(k0, p.N, lane, sacc);
-    softmax_rescale<BETA, D>(sacc, c, st);
     bf16x8 pf[2][2];
-    softmax_probs<BETA, D>(sacc, c, st, pf);
-    pv_mfma<BETA, D>(Vc, pf, st);
+    constexpr int PV_HALF = 2 * Sh::DT;        // MFMAs of PV over 32 keys
+    constexpr int QK = 2 * Sh::QS;             // MFMAs of QK^T
+    qk_mfma<BETA, D>(Kc, st, s_cur);
+    softmax_probs<BETA, D, 0, 3>(s_prev, c, st, pf);       // 24 exp, ~60 other
+    interleave<3, QK, 1, (60 + QK - 1) / QK, (24 + QK - 1) / QK>();
+    __builtin_amdgcn_sched_barrier(0);
+    pv_mfma<BETA, D, 0, 1>(Vp, pf, st);
+    softmax_probs<BETA, D, 3, 4>(s_prev, c, st, pf);       // 8 exp, ~20 other
+    interleave<4, PV_HALF, 2, (20 + PV_HALF - 1) / PV_HALF, (8 + PV_HALF - 1) / PV_HALF>();
+    __builtin_amdgcn_sched_barrier(0);
+    pv_mfma<BETA, D, 1, 2>(Vp, pf, st);
+    // the rows of a partial tile past N repeat its last key, so the max over
+    // the unmasked scores is the max over the keys that exist
+    const float mx = tile_max(s_cur, c) + (valid ? 0.f : -INFINITY);   // no branch
+    interleave<4, PV_HALF, 2, (24 + PV_HALF - 1) / PV_HALF, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    lazy_rescale<BETA, D>(mx, st);
+}
+
+// First step: S^T of sub-tile 0 and its row max; copies K(1) and V(0).
+template <int BETA, int D>
+__device__ __forceinline__ void first_step(
+    const uint16_t *__restrict__ Kc, uint16_t *__restrict__ Kn, uint16_t *__restrict__ Vn, bool valid,
+    int k0, bool load_k, int k0_k, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+    const FwdParams &p, int wv, int lane, WaveState<BETA, D> &st, f32x16 (&s_cur)[2])
+{
+    if (load_k) load_tile<BETA, D>(Kn, krs, p.k.sn, st.kdma, false, p, k0_k, wv, lane);
+    load_tile<BETA, D>(Vn, vrs, p.v.sn, st.vdma, true, p, k0, wv, lane);
+    qk_mfma<BETA, D>(Kc, st, s_cur);
+    lazy_rescale<BETA, D>(valid ? tile_max(s_cur, p.scale_log2) : -INFINITY, st);
+}
+
+// Last step: softmax and O update of the last sub-tile.
+template <int BETA, int D>
+__device__ __forceinline__ void last_step(const uint16_t *__restrict__ Vp, bool valid_p, int k0_p,
+                                          const FwdParams &p, int lane, WaveState<BETA, D> &st,
+                                          f32x16 (&s_prev)[2])
+{
+    mask_scores<BETA, D>(valid_p, k0_p, p.N, lane, s_prev);
+    bf16x8 pf[2][2];
+    softmax_probs<BETA, D>(s_prev, p.scale_log2, st, pf);
+    pv_mfma<BETA, D>(Vp, pf, st);
 }
 
 template <int BETA, int D>
@@ -321,7 +408,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kerne
     for (int d = 0; d < Sh::DT; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.oacc[d][r] = 0.f;
-    st.m_run = -INFINITY;
+    st.m_run = -1.0e30f;   // finite: a fully masked tile gives p = 0, never NaN
     st.l_run = 0.f;
     init_offsets<BETA, D>(st, p, wv, lane);
 
@@ -329,42 +416,59 @@ __global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kerne
     const __amdgpu_buffer_rsrc_t vrs = buffer_desc(vb, (uint32_t)(((int64_t)(p.N - 1) * p.v.sn + D) * 2));
 
     // Sub-tile t: key block col_idx[e0 + t / SUB], keys 64 (t % SUB) .. +63.
-    // An entry outside [0, nB) is ignored: its copies read block 0 and its
-    // compute is skipped.
+    // The index is wave-uniform, so it is read through the constant address
+    // space (a scalar load, which leaves the vector memory counter to the
+    // tile copies).  An entry outside [0, nB) is ignored: its copies read
+    // block 0 and its scores are masked.
+    const __attribute__((address_space(4))) int32_t *cidx =
+        (const __attribute__((address_space(4))) int32_t *)(p.col_idx + e0);
     auto tile_key0 = [&](int t, bool &valid) {
-        const int j = __builtin_amdgcn_readfirstlane(p.col_idx[e0 + t / Sh::SUB]);
+        const int j = cidx[t / Sh::SUB];
         valid = (unsigned)j < (unsigned)p.nB;
         return (valid ? j * BETA : 0) + 64 * (t % Sh::SUB);
     };
 
-    bool valid = false;
-    int k0 = 0;
+    // Step t computes S^T of sub-tile t and finishes sub-tile t-1.  K(t) sits
+    // in K[t&1], V(t) in V[t&1]; step t copies K(t+1) and V(t), so a V tile
+    // lands one step after its K tile.  Steps 0 and T are peeled; the loop
+    // is unrolled by two so that every LDS address is a per-lane offset plus
+    // a compile-time constant.  An entry whose block index is invalid is
+    // read from block 0 and fully masked.
+    f32x16 sa[2], sb[2];
     if (T > 0) {
-        k0 = tile_key0(0, valid);
-        load_tile<BETA, D>(K0, krs, p.k.sn, st.kdma, false, p, k0, wv, lane);
-        load_tile<BETA, D>(V0, vrs, p.v.sn, st.vdma, true, p, k0, wv, lane);
-    }
-    __syncthreads();   // Q in registers; sub-tile 0 in LDS
-
-    // Even sub-tiles live in buffer 0, odd ones in buffer 1; the loop is
-    // unrolled by two so that every LDS address is a per-lane offset plus a
-    // compile-time constant.
-    for (int t = 0; t < T; t += 2) {
-        bool valid_n = false;
-        int k0n = 0;
-        bool prefetch = t + 1 < T;
-        if (prefetch) k0n = tile_key0(t + 1, valid_n);
-        pipeline_step<BETA, D>(K0, V0, K1, V1, prefetch, k0n, valid, k0, krs, vrs, p, wv, lane, st);
-        __syncthreads();   // sub-tile t + 1 landed for every wave; buffer 0 is free
-        if (!prefetch) break;
-        valid = valid_n;
-        k0 = k0n;
-        prefetch = t + 2 < T;
-        if (prefetch) k0n = tile_key0(t + 2, valid_n);
-        pipeline_step<BETA, D>(K1, V1, K0, V0, prefetch, k0n, valid, k0, krs, vrs, p, wv, lane, st);
-        __syncthreads();   // sub-tile t + 2 landed for every wave; buffer 1 is free
-        valid = valid_n;
-        k0 = k0n;
+        // (valid, first key) of sub-tiles t-1 (prv), t (cur), t+1 (nxt); the
+        // index of t+2 is read during step t, a full step before its use
+        bool v_cur = false, v_nxt = false, v_prv;
+        int k_cur = tile_key0(0, v_cur), k_nxt = 0, k_prv;
+        if (T > 1) k_nxt = tile_key0(1, v_nxt);
+        load_tile<BETA, D>(K0, krs, p.k.sn, st.kdma, false, p, k_cur, wv, lane);
+        __syncthreads();   // Q in registers; K(0) in LDS
+        first_step<BETA, D>(K0, K1, V0, v_cur, k_cur, T > 1, k_nxt, krs, vrs, p, wv, lane, st, sa);
+        __syncthreads();
+        v_prv = v_cur; k_prv = k_cur;
+        v_cur = v_nxt; k_cur = k_nxt;
+        for (int t = 1; t < T; t += 2) {
+            // odd step t: K(t) in K1, V(t-1) in V0; copies K(t+1) -> K0, V(t) -> V1
+            v_nxt = false; k_nxt = 0;
+            if (t + 1 < T) k_nxt = tile_key0(t + 1, v_nxt);
+            fused_step<BETA, D>(K1, V0, K0, V1, v_cur, k_cur, v_prv, k_prv, t + 1 < T, k_nxt, krs, vrs, p, wv,
+                                lane, st, sb, sa);
+            __syncthreads();
+            v_prv = v_cur; k_prv = k_cur;
+            v_cur = v_nxt; k_cur = k_nxt;
+            if (t + 1 >= T) break;
+            // even step t+1: K(t+1) in K0, V(t) in V1; copies K(t+2) -> K1, V(t+1) -> V0
+            v_nxt = false; k_nxt = 0;
+            if (t + 2 < T) k_nxt = tile_key0(t + 2, v_nxt);
+            fused_step<BETA, D>(K0, V1, K1, V0, v_cur, k_cur, v_prv, k_prv, t + 2 < T, k_nxt, krs, vrs, p, wv,
+                                lane, st, sa, sb);
+            __syncthreads();
+            v_prv = v_cur; k_prv = k_cur;
+            v_cur = v_nxt; k_cur = k_nxt;
+        }
+        // finish sub-tile T-1 (V(T-1) in V[(T-1)&1])
+        if (T & 1) last_step<BETA, D>(V0, v_prv, k_prv, p, lane, st, sa);
+        else last_step<BETA, D>(V1, v_prv, k_prv, p, lane, st, sb);
     }
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
