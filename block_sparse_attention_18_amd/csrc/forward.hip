@@ -347,8 +347,13 @@ __device__ __forceinline__ void last_step(const uint16_t *__restrict__ Vp, bool 
     pv_mfma<BETA, D>(Vp, pf, st);
 }
 
+// Occupancy: two waves per SIMD (β=128: two 4-wave workgroups per CU; β=64,
+// D=64: four 2-wave workgroups, whose 32 KB of tiles fit the LDS four times).
 template <int BETA, int D>
-__global__ __launch_bounds__(BETA / 32 * 64, BETA == 128 ? 2 : 1) void fwd_kernel(const FwdParams p)
+constexpr int fwd_min_blocks() { return BETA == 128 ? 2 : (D == 64 ? 4 : 2); }
+
+template <int BETA, int D>
+__global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void fwd_kernel(const FwdParams p)
 {
     using Sh = FwdShape<BETA, D>;
     // two buffers, each a 64-key K tile and a 64-key V tile
