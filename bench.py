@@ -65,6 +65,9 @@ def main():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the kept-pairs sweep of the forward at the C4 shape "
+                         "(arrow windows 0..127 and all-FULL) with a least-squares fit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -93,6 +96,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": max(args.steps, 1)}))
         return
     bsa.load()
+    if args.sweep:
+        print(json.dumps(sweep(torch, bsa, synth, dev)), flush=True)
+        return
 
     wl = synth.WORKLOADS[args.workload]
     if args.window is not None:
@@ -119,9 +125,10 @@ def main():
         kept_pairs = cap
         computed_heads = B * int((modes != bsa.HEAD_SKIP).sum())
 
-        def layout():
+        def layout(mark=None):
             bsa.build_arrow_layout(B, H, N, block, wl.text_len, modes, wins, device=dev,
                                    row_ptr=row_ptr, col_idx=col_idx)
+        layout_parts = ("arrow",)
         fwd_kw = dict(head_modes=modes, o_cache=o_cache, lse_cache=lse_cache)
         split = bsa.arrow_split_policy(B, H, N, block, wl.text_len, modes, wins)
     else:
@@ -136,10 +143,13 @@ def main():
         ws_sel = torch.empty(max(int(bsa.load().bsa_select_workspace_size(B, H, nB)), 16),
                              dtype=torch.uint8, device=dev)
 
-        def layout():
+        def layout(mark=None):
             bsa.pool_scores(q, k, block, wl.score_mode, w=w, out=scores, workspace=ws_s)
+            if mark is not None:
+                mark()
             bsa.select_topk(scores, wl.text_blocks, wl.groups, row_ptr=row_ptr, col_idx=col_idx,
                             workspace=ws_sel)
+        layout_parts = ("pool_scores", "select")
         fwd_kw = {}
         computed_heads = B * H
         split = bsa.select_split_policy(B, H, nB, wl.text_blocks, wl.groups, block=block)
@@ -166,25 +176,34 @@ def main():
     actual_flop = flop_pair * kept_pairs
     dense_flop = 4.0 * N * N * D * B * H
 
-    # timed region: K steps, per-forward events on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    # timed region: K steps; events on the launch stream mark the start of the
+    # step, the boundary between the layout parts, and the forward
+    def new_ev():
+        return torch.cuda.Event(enable_timing=True)
+    ev = [[new_ev() for _ in range(len(layout_parts) + 2)] for _ in range(args.steps)]
+    t0, t1 = new_ev(), new_ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
     for s in range(args.steps):
-        layout()
-        ev[s][0].record(stream)
+        e = ev[s]
+        e[0].record(stream)
+        layout(mark=lambda: e[1].record(stream))
+        e[-2].record(stream)
         forward()
-        ev[s][1].record(stream)
+        e[-1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
-    fwd_ms = [a.elapsed_time(b) for a, b in ev]
+    fwd_ms = [e[-2].elapsed_time(e[-1]) for e in ev]
     fwd_avg = float(np.mean(fwd_ms))
+    part_ms = {name: float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev]))
+               for j, name in enumerate(layout_parts)}
+    cold = None
+    if wl.layout != "arrow":
+        cold = cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr,
+                                 wl.score_mode == synth.SCORE_EXACT_AVGPOOL)
 
     value = actual_flop / (ms_step * 1e-3) / 1e12
     achieved = actual_flop / (fwd_avg * 1e-3) / 1e12
@@ -215,6 +234,9 @@ def main():
         "dense_equiv_tflops": round(dense_flop / (ms_step * 1e-3) / 1e12, 2),
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "forward_ms": round(fwd_avg, 4),
+        "forward_ms_p10_p50_p90": [round(float(np.percentile(fwd_ms, q_)), 4) for q_ in (10, 50, 90)],
+        "layout_ms": {k2: round(v2, 4) for k2, v2 in part_ms.items()},
+        "layout_cold_cache": cold,
         "forward_dense_equiv_tflops": round(dense_flop / (fwd_avg * 1e-3) / 1e12, 2),
         "step_wall_ms": round(wall * 1e3 / args.steps, 4),
         "roofline": {
@@ -234,6 +256,88 @@ def main():
         res["cpu_baseline"] = cpu_baseline(wl, x, row_ptr, col_idx, args.cpu_seconds,
                                            fwd_kw.get("head_modes"))
     print(json.dumps(res), flush=True)
+
+
+def cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr, exact: bool, iters: int = 10):
+    """pool_scores and select timed with a 512 MB scratch write before every
+    call, so the 256 MB last-level cache does not serve their inputs.  Rates
+    against the algorithmic work: mean-pool scores are HBM-bound (Q and K
+    read once); exact scores are MFMA-bound (one Q K^T over all pairs, plus
+    one exp per pair); select reads the score matrix once and writes the
+    CSR once."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    pool, sel = [], []
+    for _ in range(iters):
+        scratch.fill_(1)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        layout(mark=lambda: e[1].record(stream))
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        pool.append(e[0].elapsed_time(e[1]))
+        sel.append(e[1].elapsed_time(e[2]))
+    pool_ms, sel_ms = float(np.median(pool)), float(np.median(sel))
+    nnz = int(row_ptr[-1].item())
+    sel_bytes = 4.0 * B * H * nB * nB + 4.0 * (nnz + B * H * nB + 1)
+    res = {"pool_scores_ms": round(pool_ms, 4)}
+    if exact:
+        flop = 2.0 * B * H * N * N * D
+        res["pool_scores_tflops"] = round(flop / (pool_ms * 1e-3) / 1e12, 1)
+        res["pool_scores_frac_mfma_peak"] = round(flop / (pool_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    else:
+        res["pool_GBps"] = round(2.0 * B * H * N * D * 2 / (pool_ms * 1e-3) / 1e9, 1)
+        res["hbm_peak_GBps"] = PEAK_HBM_GBS
+    res["select_ms"] = round(sel_ms, 4)
+    res["select_GBps"] = round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1)
+    return res
+
+
+def sweep(torch, bsa, synth, dev, windows=(0, 1, 2, 4, 8, 18, 32, 64, 127), reps: int = 30):
+    """Forward time against kept pairs at the C4 shape: arrow windows plus
+    all-FULL heads; least-squares fit t = a + b * pairs."""
+    base = synth.WORKLOADS["C4"]
+    x = synth.make_inputs(base)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = d(x["q"]), d(x["k"]), d(x["v"])
+    B, H, N, D, block = base.B, base.H, base.N, base.D, base.block
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    pts = []
+    for w in list(windows) + ["full"]:
+        modes = np.full(H, bsa.HEAD_FULL if w == "full" else bsa.HEAD_ARROW, dtype=np.int8)
+        wins = np.full(H, 0 if w == "full" else w, dtype=np.int32)
+        rp, ci = bsa.build_arrow_layout(B, H, N, block, base.text_len, modes, wins, device=dev)
+        pairs = bsa.arrow_capacity(B, H, N, block, base.text_len, modes, wins)
+        for _ in range(10):
+            bsa.forward(q, k, v, block, rp, ci, out=out, lse=lse)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            bsa.forward(q, k, v, block, rp, ci, out=out, lse=lse)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        t = float(np.median(ts))
+        pts.append({"window": w, "kept_pairs": pairs, "forward_ms": round(t, 4),
+                    "tflops": round(4.0 * block * block * D * pairs / (t * 1e-3) / 1e12, 1)})
+    xs = np.array([p_["kept_pairs"] for p_ in pts], dtype=np.float64)
+    ys = np.array([p_["forward_ms"] for p_ in pts], dtype=np.float64)
+    A = np.stack([np.ones_like(xs), xs], axis=1)
+    (a, b), *_ = np.linalg.lstsq(A, ys, rcond=None)
+    r2 = 1.0 - float(((ys - (a + b * xs)) ** 2).sum() / ((ys - ys.mean()) ** 2).sum())
+    full = pts[-1]
+    for p_ in pts:
+        realised = full["forward_ms"] / p_["forward_ms"]
+        theoretical = full["kept_pairs"] / p_["kept_pairs"]
+        p_["speedup_realised_over_theoretical"] = round(realised / theoretical, 3)
+    return {"sweep": "forward time vs kept pairs, C4 shape (B1 H24 N16896 D128 block 128)",
+            "fit_ms": {"intercept": round(float(a), 4), "us_per_kept_pair": round(float(b) * 1e3, 6),
+                       "r2": round(r2, 5)},
+            "points": pts}
 
 
 def cpu_baseline(wl, x, row_ptr, col_idx, seconds, modes):
@@ -262,13 +366,21 @@ def cpu_baseline(wl, x, row_ptr, col_idx, seconds, modes):
     t = time.perf_counter()
     oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=probe)
     dt = max(time.perf_counter() - t, 1e-3)
-    n = int(min(max(64 * seconds / dt, 64), 200000))
+    n = int(min(max(64 * seconds / dt, 64), 1000000))
     rows = rows_of(n)
     t = time.perf_counter()
     oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=rows)
     dt = time.perf_counter() - t
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(flop(rows) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"{n} random query rows of the {wl.name} forward (fp64, kept blocks only), "
                       f"{dt:.1f} s"}
 
