@@ -97,4 +97,65 @@ __device__ __forceinline__ const T *lds_at(const uint16_t *base, uint32_t byte_o
     return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
+// The swizzles XOR the chunk index with row bits, so stepping the chunk by
+// a power of two that the swizzle also touches is an XOR of the byte offset:
+// K k-step s moves 2 chunks (32 bytes), V d tile d moves 4 chunks (64 bytes).
+constexpr uint32_t KSTEP = 32, VSTEP = 64;
+
+// Accumulator row r of half-wave hl of a 32x32 S^T tile (K rows fed in the
+// perm_row order) holds key 8 hl + koff(r) of its 32 keys.
+__device__ __forceinline__ constexpr int koff(int r) { return (r & 3) + 4 * ((r >> 2) & 1) + 16 * ((r >> 3) & 1); }
+
+// Scores of keys at offset >= lim (per lane: key offset within the 64-key
+// sub-tile minus 8 hl) become -inf.
+__device__ __forceinline__ void mask_keys(f32x16 (&sacc)[2], int lim)
+{
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (kt * 32 + koff(r) >= lim) sacc[kt][r] = -INFINITY;
+}
+
+// Max over a 64-key sub-tile of S^T for the lane's query, times c: the two
+// lane halves hold the two key halves of every query and are combined by a
+// lane swap (a VALU op, no LDS round trip).
+__device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2], float c)
+{
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        m0 = fmaxf(m0, sacc[0][r]);
+        m1 = fmaxf(m1, sacc[1][r]);
+    }
+    const float mx = fmaxf(m0, m1);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+}
+
+// Sum of a value over the two lane halves (lanes l and l ^ 32).
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// Instruction interleave of one scheduled region: NPRE LDS reads first, then
+// NM groups of one MFMA, NR LDS reads, NV vector and NE transcendental
+// instructions.  A waiting MFMA holds the SIMD's issue stage, so vector work
+// is spread between the MFMAs of the same wave rather than run beside a
+// back-to-back MFMA chain.
+template <int NPRE, int NM, int NR, int NV, int NE>
+__device__ __forceinline__ void interleave()
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
+#pragma unroll
+    for (int x = 0; x < NM; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+        __builtin_amdgcn_sched_group_barrier(0x400, NE, 0);
+    }
+}
+
 }  // namespace bsa

@@ -71,11 +71,6 @@ struct WaveState {
     uint32_t kdma, vdma;         // source offset of the lane's first 16-byte copy of a tile
 };
 
-// The swizzles XOR the chunk index with row bits, so stepping the chunk by
-// a power of two that the swizzle also touches is an XOR of the byte offset:
-// K k-step s moves 2 chunks (32 bytes), V d tile d moves 4 chunks (64 bytes).
-constexpr uint32_t KSTEP = 32, VSTEP = 64;
-
 template <int BETA, int D>
 __device__ __forceinline__ void init_offsets(WaveState<BETA, D> &st, const FwdParams &p, int wv, int lane)
 {
@@ -119,38 +114,14 @@ __device__ __forceinline__ void qk_mfma(const uint16_t *__restrict__ Kc, const W
 }
 
 // Keys past N in a partial last tile do not exist: their scores become -inf.
-// Accumulator row r of half-wave hl is key 8 hl + koff(r) of its 32-key tile
-// (the permuted order of the K rows).
-__device__ __forceinline__ constexpr int koff(int r) { return (r & 3) + 4 * ((r >> 2) & 1) + 16 * ((r >> 3) & 1); }
-
 template <int BETA, int D>
 __device__ __forceinline__ void mask_tail(int k0, int N, int lane, f32x16 (&sacc)[2])
 {
-    const int lim = N - k0 - 8 * (lane >> 5);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (kt * 32 + koff(r) >= lim) sacc[kt][r] = -INFINITY;
+    mask_keys(sacc, N - k0 - 8 * (lane >> 5));
 }
 
-// Online softmax, part 1: the sub-tile's row max (the two lane halves hold
-// the two key halves of every query, exchanged by a lane swap) and the lazy
-// rescale of the running state when it exceeds the reference by more than
-// the slack.
-__device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2], float c)
-{
-    float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        m0 = fmaxf(m0, sacc[0][r]);
-        m1 = fmaxf(m1, sacc[1][r]);
-    }
-    const float mx = fmaxf(m0, m1);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-}
-
+// Online softmax, part 1: the lazy rescale of the running state when the
+// sub-tile's row max (tile_max) exceeds the reference by more than the slack.
 template <int BETA, int D>
 __device__ __forceinline__ void lazy_rescale(float mx, WaveState<BETA, D> &st)
 {
@@ -254,26 +225,8 @@ __device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_b
     }
 }
 
-// Instruction interleave of one region: NPRE LDS reads first, then NM
-// groups of one MFMA, NR LDS reads, NV vector and NE transcendental
-// instructions.  A waiting MFMA holds the SIMD's issue stage, so the
-// softmax's vector work is spread between the MFMAs of the same wave rather
-// than run beside a back-to-back MFMA chain.
-template <int NPRE, int NM, int NR, int NV, int NE>
-__device__ __forceinline__ void interleave()
-{
-    __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
-#pragma unroll
-    for (int x = 0; x < NM; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
-        __builtin_amdgcn_sched_group_barrier(0x400, NE, 0);
-    }
-}
-
 // Scores of a sub-tile whose block index is invalid, or of keys past N in
-// the last tile, are masked out (valid tiles always keep key k0 < N).
+// the last tile, are masked out.
 template <int BETA, int D>
 __device__ __forceinline__ void mask_scores(bool valid, int k0, int N, int lane, f32x16 (&sacc)[2])
 {
@@ -315,8 +268,11 @@ __device__ __forceinline__ void fused_step(
     __builtin_amdgcn_sched_barrier(0);
     pv_mfma<BETA, D, 1, 2>(Vp, pf, st);
     // the rows of a partial tile past N repeat its last key, so the max over
-    // the unmasked scores is the max over the keys that exist
-    const float mx = tile_max(s_cur, c) + (valid ? 0.f : -INFINITY);   // no branch
+    // the unmasked scores is the max over the keys that exist; a sub-tile
+    // with no key below N (the second half of a last block of <= 64 keys)
+    // or with an invalid block index has none
+    const bool has_keys = valid && k0 < p.N;
+    const float mx = tile_max(s_cur, c) + (has_keys ? 0.f : -INFINITY);   // no branch
     interleave<4, PV_HALF, 2, (24 + PV_HALF - 1) / PV_HALF, 0>();
     __builtin_amdgcn_sched_barrier(0);
     lazy_rescale<BETA, D>(mx, st);
@@ -332,7 +288,7 @@ __device__ __forceinline__ void first_step(
     if (load_k) load_tile<BETA, D>(Kn, krs, p.k.sn, st.kdma, false, p, k0_k, wv, lane);
     load_tile<BETA, D>(Vn, vrs, p.v.sn, st.vdma, true, p, k0, wv, lane);
     qk_mfma<BETA, D>(Kc, st, s_cur);
-    lazy_rescale<BETA, D>(valid ? tile_max(s_cur, p.scale_log2) : -INFINITY, st);
+    lazy_rescale<BETA, D>((valid && k0 < p.N) ? tile_max(s_cur, p.scale_log2) : -INFINITY, st);
 }
 
 // Last step: softmax and O update of the last sub-tile.

@@ -12,10 +12,12 @@
 // without materialising A.  One pass over the key blocks: for every query
 // token t and key block j the kernel forms the block log-sum-exp
 //   l_tj = log2 sum_{s in j} 2^{c z_ts}   (c = scale * log2 e)
-// with QK^T on bf16 MFMA, keeps a running log-sum-exp over j, and parks
-// l_tj in a per-workgroup scratch slot.  Once the row's full log-sum-exp
-// L_t is known, S_ij = 1/(n_i n_j) sum_t 2^{l_tj - L_t}.  The QK^T product is
-// therefore done once, not twice.
+// with QK^T on bf16 MFMA.  Sums are kept against a per-query reference that
+// only moves when a score exceeds it by about 2^6 (log2 units); l_tj is
+// parked in a per-workgroup scratch slot and the running total gives the
+// row's log-sum-exp L_t.  Then S_ij = 1/(n_i n_j) sum_t 2^{l_tj - L_t}.  The
+// QK^T product is done once, not twice; the exp2 / sum work of one 32-key
+// half runs between the MFMAs of the next half, four waves per SIMD.
 #include "common.h"
 #include "internal.h"
 
@@ -131,7 +133,8 @@ struct ExactShape {
 
 // Copy one 64-key K tile (rows from key k0) straight into LDS; lane l of
 // copy x writes slot (x*NW + wave)*64 + l = (row, chunk XOR the row's
-// swizzle).  A partial tile repeats its last key (those scores are masked).
+// swizzle).  A partial tile repeats its last key (those scores are masked);
+// a full tile is copy 0 moved by x * ROWS_PER_COPY rows.
 template <int BETA, int D>
 __device__ __forceinline__ void exact_load_k(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t rs,
                                              int64_t sn, uint32_t off0, int N, int k0, int wv, int lane)
@@ -139,92 +142,173 @@ __device__ __forceinline__ void exact_load_k(uint16_t *__restrict__ dst, __amdgp
     using Sh = ExactShape<BETA, D>;
     const int rows = N - k0;
     const uint32_t so = (uint32_t)((int64_t)k0 * sn * 2);
-    const uint32_t step = (uint32_t)((int64_t)Sh::ROWS_PER_COPY * sn * 2);
+    if (Sh::UNIFORM_COPY && rows >= 64) {
+        const uint32_t step = (uint32_t)((int64_t)Sh::ROWS_PER_COPY * sn * 2);
+#pragma unroll
+        for (int x = 0; x < Sh::DMA; ++x)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16,
+                                                     off0, so + x * step, 0, 0);
+        return;
+    }
 #pragma unroll
     for (int x = 0; x < Sh::DMA; ++x) {
-        uint32_t o = off0, sx = so + x * step;
-        if (rows < 64 || !Sh::UNIFORM_COPY) {
-            const int slot = (x * Sh::NW + wv) * 64 + lane;
-            const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
-            o = (uint32_t)(min(r, rows - 1) * sn * 2 + ((ps ^ kswz<D>(r)) * 16));
-            sx = so;
-        }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16, o,
-                                                 sx, 0, 0);
+        const int slot = (x * Sh::NW + wv) * 64 + lane;
+        const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
+        const uint32_t o = (uint32_t)(min(r, rows - 1) * sn * 2 + ((ps ^ kswz<D>(r)) * 16));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16, o, so,
+                                                 0, 0);
     }
 }
 
-// Per-lane state: the 32 queries' Q^T fragments, the running log2-sum-exp
-// over key blocks (M, L), the current key block's partial (bm, bl), and
-// the lane's constant LDS / global offsets.
+// Per-lane state: the 32 queries' Q^T fragments; the reference max m_ref
+// (log2 domain, equal in both lane halves of a query); bl, the current key
+// block's sum of 2^(c z - m_ref) over this lane's keys; L, the sum over the
+// finished key blocks (both halves), relative to m_ref; the lane's constant
+// LDS / global offsets.
 template <int BETA, int D>
 struct ExactState {
     bf16x8 qf[ExactShape<BETA, D>::QS];
-    float M, L, bm, bl;
-    uint32_t kread[ExactShape<BETA, D>::QS];
+    float m_ref, bl, L;
+    uint32_t kread;              // K operand of k-step 0; k-step s: ^ KSTEP * s
     uint32_t kdma;
 };
 
-// One step: copy the next sub-tile into the other buffer, then fold the
-// current 64 keys (starting at k0) into the block partial; at the end of a
-// key block, park its log2-sum-exp in the scratch slot and update (M, L).
+// S^T of one 32-key half (kt) of a 64-key sub-tile: 32 keys x 32 queries.
 template <int BETA, int D>
-__device__ __forceinline__ void exact_step(const uint16_t *__restrict__ Kc, uint16_t *__restrict__ Kn,
-                                           bool prefetch, int k0n, int k0, bool first_half, bool last_half,
-                                           int j, __amdgpu_buffer_rsrc_t krs, const ExactParams &p,
-                                           float *slot, int wv, int lane, ExactState<BETA, D> &st)
+__device__ __forceinline__ void exact_qk_half(const uint16_t *__restrict__ Kc, int kt, const ExactState<BETA, D> &st,
+                                              f32x16 &acc)
 {
     using Sh = ExactShape<BETA, D>;
-    if (prefetch) exact_load_k<BETA, D>(Kn, krs, p.k.sn, st.kdma, p.N, k0n, wv, lane);
-    const int hl = lane >> 5, n = lane & 31;
-    const float c = p.scale_log2;
-    f32x16 sacc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+    for (int s = 0; s < Sh::QS; ++s) {
+        const bf16x8 a = *lds_at<bf16x8>(Kc + kt * 32 * D, st.kread ^ (KSTEP * s));
+        acc = mfma32x32x16(a, st.qf[s], acc);
+    }
+}
+
+// Fold the scores of one 32-key half into the current block's sum.  The
+// common path has no max: it sums 2^(c z - m_ref) against the current
+// reference and returns that partial; exact_fold_fix, taken (wave-uniform)
+// when some lane's partial exceeds 2^64 or overflowed, recomputes the half
+// against the exact max and rescales the running sums.  The reference thus
+// only moves when a score exceeds it by about 2^6 log2 units, and the sums
+// stay far from the fp32 range.
+template <int BETA, int D>
+__device__ __forceinline__ float exact_fold_sum(const f32x16 &sv, float c, const ExactState<BETA, D> &st)
+{
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int s = 0; s < Sh::QS; ++s) {
-            const bf16x8 a = *lds_at<bf16x8>(Kc + kt * 32 * D, st.kread[s]);
-            sacc[kt] = mfma32x32x16(a, st.qf[s], sacc[kt]);
+    for (int r = 0; r < 16; r += 2) {
+        s0 += fast_exp2(__builtin_fmaf(sv[r], c, -st.m_ref));
+        s1 += fast_exp2(__builtin_fmaf(sv[r + 1], c, -st.m_ref));
+    }
+    return s0 + s1;
+}
+
+constexpr float kExactBig = 18446744073709551616.0f;   // 2^64
+
+// One region with an explicit instruction order: S^T of half kt of the
+// sub-tile in Kc into acc, and the fold sum of the scores sv of another half.
+// Slot s issues the K read of k-step s+2, the MFMA of k-step s, and the
+// fma / exp2 / add of scores 2s and 2s+1; a full scheduling barrier between
+// slots keeps the order, so the vector work runs under the MFMAs.
+template <int BETA, int D>
+__device__ __forceinline__ float exact_region(const uint16_t *__restrict__ Kc, int kt, const ExactState<BETA, D> &st,
+                                              f32x16 &acc, const f32x16 &sv, float c)
+{
+    using Sh = ExactShape<BETA, D>;
+    static_assert(Sh::QS == 8 || Sh::QS == 4, "k-steps");
+    constexpr int PER = 16 / Sh::QS;   // scores folded per slot
+    const uint16_t *kt_base = Kc + kt * 32 * D;
+    bf16x8 a[Sh::QS];
+    a[0] = *lds_at<bf16x8>(kt_base, st.kread);
+    a[1] = *lds_at<bf16x8>(kt_base, st.kread ^ KSTEP);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    float s0 = 0.f, s1 = 0.f;
+    const float m = st.m_ref;
+#pragma unroll
+    for (int s = 0; s < Sh::QS; ++s) {
+        if (s + 2 < Sh::QS) a[s + 2] = *lds_at<bf16x8>(kt_base, st.kread ^ (KSTEP * (s + 2)));
+        acc = mfma32x32x16(a[s], st.qf[s], acc);
+#pragma unroll
+        for (int e = 0; e < PER; e += 2) {
+            s0 += fast_exp2(__builtin_fmaf(sv[PER * s + e], c, -m));
+            s1 += fast_exp2(__builtin_fmaf(sv[PER * s + e + 1], c, -m));
         }
+        // pin the partial sums to this slot: pure arithmetic is otherwise
+        // free to move past the scheduling barrier towards its only use
+        asm volatile("" ::"v"(s0), "v"(s1));
+        __builtin_amdgcn_sched_barrier(0);
     }
-    if (k0 + 64 > p.N) {
+    return s0 + s1;
+}
+
+
+template <int BETA, int D>
+__device__ __forceinline__ void exact_fold_commit(float part, const f32x16 &sv, float c, ExactState<BETA, D> &st)
+{
+    if (__ballot(!(part <= kExactBig))) {
+        float m = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + kt * 32 + perm_row(8 * (r >> 2) + 4 * hl + (r & 3));
-                if (key >= p.N) sacc[kt][r] = -INFINITY;
-            }
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sv[r]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+        const float m_new = fmaxf(st.m_ref, mx);
+        const float alpha = fast_exp2(st.m_ref - m_new);
+        st.bl *= alpha;
+        st.L *= alpha;
+        st.m_ref = m_new;
+        part = exact_fold_sum<BETA, D>(sv, c, st);
     }
-    float mx = -INFINITY;
+    st.bl += part;
+}
+
+// End of key block j: its log2-sum-exp l_tj = m_ref + log2(bl over both
+// halves) is parked in the scratch slot and the block joins L.
+template <int BETA, int D>
+__device__ __forceinline__ void exact_finish_block(int j, float *slot, int wv, int lane, ExactState<BETA, D> &st)
+{
+    const float bt = half_sum(st.bl);
+    st.L += bt;
+    st.bl = 0.f;
+    if ((lane >> 5) == 0) slot[(int64_t)j * BETA + wv * 32 + (lane & 31)] = st.m_ref + __log2f(bt);
+}
+
+// Keys of half kt of the sub-tile at k0 that lie past N become -inf.
+__device__ __forceinline__ void exact_mask_half(int k0, int kt, int N, int lane, f32x16 &sv)
+{
+    if (k0 + 64 > N) {
+        const int lim = N - k0 - 32 * kt - 8 * (lane >> 5);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;   // at least one key of a tile exists
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ls += fast_exp2(__builtin_fmaf(sacc[kt][r], c, -mx));
-    ls += __shfl_xor(ls, 32, 64);
-    if (first_half) {
-        st.bm = mx;
-        st.bl = ls;
-    } else {
-        const float m2 = fmaxf(st.bm, mx);
-        st.bl = st.bl * fast_exp2(st.bm - m2) + ls * fast_exp2(mx - m2);
-        st.bm = m2;
+        for (int r = 0; r < 16; ++r)
+            if (koff(r) >= lim) sv[r] = -INFINITY;
     }
-    if (last_half) {
-        const float lj = st.bm + __log2f(st.bl);   // block log2-sum-exp of this token
-        const float Mn = fmaxf(st.M, lj);
-        st.L = st.L * ((st.M == Mn) ? 1.f : fast_exp2(st.M - Mn)) + fast_exp2(lj - Mn);
-        st.M = Mn;
-        if (hl == 0) slot[(int64_t)j * BETA + wv * 32 + n] = lj;
-    }
+}
+
+// Step t over the 64-key sub-tile in Kc (keys from k0), pipelined at
+// 32-key granularity: region 1 computes S^T of half 0 of t while folding
+// half 1 of t-1 (sb, carried over from the previous step); region 2
+// computes S^T of half 1 of t (into sb) while folding half 0 of t (sa).
+// Both halves' scores are 16 registers each.  Masks and the end of a key
+// block are handled between the regions, so no branch splits a region.
+template <int BETA, int D>
+__device__ __forceinline__ void exact_step(const uint16_t *__restrict__ Kc, uint16_t *__restrict__ Kn, bool load_k,
+                                           int k0_k, int k0, bool finish_prev, int j_prev,
+                                           __amdgpu_buffer_rsrc_t krs, const ExactParams &p, float *slot, int wv,
+                                           int lane, ExactState<BETA, D> &st, f32x16 &sa, f32x16 &sb)
+{
+    const float c = p.scale_log2;
+    if (load_k) exact_load_k<BETA, D>(Kn, krs, p.k.sn, st.kdma, p.N, k0_k, wv, lane);
+    exact_mask_half(k0 - 64, 1, p.N, lane, sb);
+    float part = exact_region<BETA, D>(Kc, 0, st, sa, sb, c);
+    exact_fold_commit<BETA, D>(part, sb, c, st);
+    if (finish_prev) exact_finish_block<BETA, D>(j_prev, slot, wv, lane, st);
+    exact_mask_half(k0, 0, p.N, lane, sa);
+    part = exact_region<BETA, D>(Kc, 1, st, sb, sa, c);
+    exact_fold_commit<BETA, D>(part, sa, c, st);
 }
 
 template <int BETA, int D>
@@ -247,9 +331,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 4) void exact_scores_kernel(const E
     ExactState<BETA, D> st;
     {
         const int r0 = perm_row(n);
-#pragma unroll
-        for (int s = 0; s < Sh::QS; ++s)
-            st.kread[s] = (uint32_t)(r0 * D * 2 + (((2 * s + hl) ^ kswz<D>(r0)) * 16));
+        st.kread = (uint32_t)(r0 * D * 2 + ((hl ^ kswz<D>(r0)) * 16));
         const int sl = wv * 64 + lane;
         const int r = sl / Sh::KCH, ps = sl % Sh::KCH;
         st.kdma = (uint32_t)(r * p.k.sn * 2 + ((ps ^ kswz<D>(r)) * 16));
@@ -269,25 +351,36 @@ __global__ __launch_bounds__(BETA / 32 * 64, 4) void exact_scores_kernel(const E
             uint4 u = qrow < p.N ? ld_g16(qb + (int64_t)qrow * p.q.sn + 16 * s + 8 * hl) : zero_u4();
             st.qf[s] = as_bf16x8(u);
         }
-        st.M = -INFINITY;
+        st.m_ref = -1.0e30f;   // finite: the first sub-tile moves it with alpha = 0
+        st.bl = 0.f;
         st.L = 0.f;
 
         __syncthreads();   // the previous item is done with K0 / K1 and lse2
         exact_load_k<BETA, D>(K0, krs, p.k.sn, st.kdma, p.N, 0, wv, lane);
-        __syncthreads();   // sub-tile 0 in LDS
-        // even sub-tiles in K0, odd in K1 (the loop is unrolled by two)
-        for (int t = 0; t < T; t += 2) {
-            const int k0 = t * 64;
-            exact_step<BETA, D>(K0, K1, t + 1 < T, k0 + 64, k0, (t % Sh::SUB) == 0,
-                                (t % Sh::SUB) == Sh::SUB - 1, t / Sh::SUB, krs, p, slot, wv, lane, st);
+        __syncthreads();   // K(0) in LDS
+        // sub-tile t in K[t&1]; step t copies K(t+1) into the other buffer.
+        // Step 0 (no previous half to fold) is peeled.
+        f32x16 sa, sb;
+        if (T > 1) exact_load_k<BETA, D>(K1, krs, p.k.sn, st.kdma, p.N, 64, wv, lane);
+        exact_qk_half<BETA, D>(K0, 0, st, sa);
+        exact_mask_half(0, 0, p.N, lane, sa);
+        exact_qk_half<BETA, D>(K0, 1, st, sb);
+        exact_fold_commit<BETA, D>(exact_fold_sum<BETA, D>(sa, p.scale_log2, st), sa, p.scale_log2, st);
+        __syncthreads();
+        for (int t = 1; t < T; t += 2) {
+            exact_step<BETA, D>(K1, K0, t + 1 < T, (t + 1) * 64, t * 64, ((t - 1) % Sh::SUB) == Sh::SUB - 1,
+                                (t - 1) / Sh::SUB, krs, p, slot, wv, lane, st, sa, sb);
             __syncthreads();
             if (t + 1 >= T) break;
-            exact_step<BETA, D>(K1, K0, t + 2 < T, k0 + 128, k0 + 64, ((t + 1) % Sh::SUB) == 0,
-                                ((t + 1) % Sh::SUB) == Sh::SUB - 1, (t + 1) / Sh::SUB, krs, p, slot, wv,
-                                lane, st);
+            exact_step<BETA, D>(K0, K1, t + 2 < T, (t + 2) * 64, (t + 1) * 64, (t % Sh::SUB) == Sh::SUB - 1,
+                                t / Sh::SUB, krs, p, slot, wv, lane, st, sa, sb);
             __syncthreads();
         }
-        if (hl == 0) lse2[wv * 32 + n] = st.M + __log2f(st.L);
+        // half 1 of the last sub-tile, then the last key block
+        exact_mask_half((T - 1) * 64, 1, p.N, lane, sb);
+        exact_fold_commit<BETA, D>(exact_fold_sum<BETA, D>(sb, p.scale_log2, st), sb, p.scale_log2, st);
+        exact_finish_block<BETA, D>(p.nB - 1, slot, wv, lane, st);
+        if (hl == 0) lse2[wv * 32 + n] = st.m_ref + __log2f(st.L);
         __syncthreads();   // slot and lse2 complete for this item
 
         // S_ij = 1/(n_i n_j) sum_t 2^(l_tj - L_t), one wave per key block j
@@ -295,8 +388,8 @@ __global__ __launch_bounds__(BETA / 32 * 64, 4) void exact_scores_kernel(const E
         for (int j = wv; j < p.nB; j += Sh::NW) {
             float sum = 0.f;
 #pragma unroll
-            for (int t = lane; t < BETA; t += 64)
-                if (t < n_i) sum += fast_exp2(slot[(int64_t)j * BETA + t] - lse2[t]);
+            for (int tq = lane; tq < BETA; tq += 64)
+                if (tq < n_i) sum += fast_exp2(slot[(int64_t)j * BETA + tq] - lse2[tq]);
 #pragma unroll
             for (int d = 32; d > 0; d >>= 1) sum += __shfl_xor(sum, d, 64);
             if (lane == 0) {

@@ -81,6 +81,25 @@ def test_forward_scale_and_large_logits():
     check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "scale 0.2")
 
 
+def test_forward_very_negative_logits_and_empty_last_subtile():
+    """Every logit far below zero (about -260 in log2 units) with a last block
+    of 40 keys, whose second 64-key sub-tile holds no key: that sub-tile must
+    not raise the running reference max, or every probability underflows."""
+    B, H, N, D, block = 1, 2, 2 * 128 + 40, 128, 128
+    rng = np.random.default_rng(115)
+    u = rng.choice([-1.0, 1.0], size=(B, H, 1, D))
+    q = synth.f32_to_bf16((4.0 * u + 0.3 * rng.standard_normal((B, H, N, D))).astype(np.float32))
+    k = synth.f32_to_bf16((-4.0 * u + 0.3 * rng.standard_normal((B, H, N, D))).astype(np.float32))
+    v = synth.f32_to_bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
+    nB = -(-N // block)
+    rp = np.arange(0, B * H * nB * nB + 1, nB, dtype=np.int32)        # every row dense
+    ci = np.tile(np.arange(nB, dtype=np.int32), B * H * nB)
+    O, L = _run_forward(q, k, v, block, rp, ci)
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci)
+    assert np.all(np.isfinite(Lo)) and Lo.max() < -150.0
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "negative logits")
+
+
 def test_forward_strided_skip_and_alias():
     B, H, N, D, block = 2, 4, 3 * 64 + 5, 64, 64
     q, k, v = synth.random_qkv(B, H, N, D, seed=120)
@@ -267,7 +286,9 @@ def test_meanpool_scores_and_selection(B, H, N, D, block):
 
 
 @pytest.mark.parametrize("B,H,N,D,block", [(1, 2, 6 * 64 + 10, 64, 64), (1, 2, 5 * 128, 128, 128),
-                                           (2, 1, 3 * 128 + 77, 128, 128)])
+                                           (2, 1, 3 * 128 + 77, 128, 128),
+                                           # last block of 40 keys: its second 64-key sub-tile is empty
+                                           (1, 2, 3 * 128 + 40, 128, 128)])
 def test_exact_scores_small(B, H, N, D, block):
     q, k, _ = synth.random_qkv(B, H, N, D, seed=160 + N, scale=1.5)
     S = bsa.pool_scores(to_dev_bf16(q), to_dev_bf16(k), block, bsa.SCORE_EXACT_AVGPOOL)
