@@ -72,6 +72,12 @@ def _load():
         lib.oracle_forward.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, D, P, I, P, P]
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
+        lib.oracle_e4m3_encode_array.argtypes = [P, I, P]
+        lib.oracle_e4m3_encode_array.restype = None
+        lib.oracle_e4m3_decode_array.argtypes = [P, I, P]
+        lib.oracle_e4m3_decode_array.restype = None
+        lib.oracle_quantize_fp8.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, P]
+        lib.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, P, I, P, P]
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -225,4 +231,66 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, block: int,
                                 _ptr(col_idx), _ptr(modes_a), _ptr(oc), _ptr(lc), scale,
                                 _ptr(r), len(r), _ptr(O), _ptr(L))
     _check(rc, "forward")
+    return O, L
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) quantisation and the forward on the quantised inputs
+# ---------------------------------------------------------------------------
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """OCP E4M3 codes (uint8) of float32 values, round to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().oracle_e4m3_encode_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(c: np.ndarray) -> np.ndarray:
+    """Values (float64) of OCP E4M3 codes."""
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().oracle_e4m3_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def quantize_fp8(q: np.ndarray, k: np.ndarray, v: np.ndarray):
+    """(q8 [B,H,N,D], q_scale [B,H,N], k8 [B,H,N,D], k_scale [B,H,ceil(N/64)],
+    v8 [B,H,N,D], v_scale [B,H,D]): per-token Q, per-64-key-tile K and
+    per-channel V max-abs scaling to E4M3 (codes decided in fp32)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, H, N, D = q.shape
+    NT = (N + 63) // 64
+    q8 = np.empty((B, H, N, D), np.uint8); k8 = np.empty_like(q8); v8 = np.empty_like(q8)
+    qs = np.empty((B, H, N), np.float32); ks = np.empty((B, H, NT), np.float32)
+    vs = np.empty((B, H, D), np.float32)
+    _check(_load().oracle_quantize_fp8(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, _ptr(q8), _ptr(qs),
+                                       _ptr(k8), _ptr(ks), _ptr(v8), _ptr(vs)), "quantize_fp8")
+    return q8, qs, k8, ks, v8, vs
+
+
+def forward_fp8(q8, q_scale, k8, k_scale, v8, v_scale, block: int, row_ptr, col_idx,
+                scale: Optional[float] = None, rows: Optional[Sequence[int]] = None):
+    """The block-sparse forward on the dequantised inputs (see quantize_fp8)."""
+    q8 = np.ascontiguousarray(q8, np.uint8); k8 = np.ascontiguousarray(k8, np.uint8)
+    v8 = np.ascontiguousarray(v8, np.uint8)
+    qs = np.ascontiguousarray(q_scale, np.float32); ks = np.ascontiguousarray(k_scale, np.float32)
+    vs = np.ascontiguousarray(v_scale, np.float32)
+    B, H, N, D = q8.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if col_idx.size == 0:
+        col_idx = np.zeros(1, dtype=np.int32)
+    lib = _load()
+    if rows is None:
+        O = np.empty((B, H, N, D), np.float64); L = np.empty((B, H, N), np.float64)
+        rc = lib.oracle_forward_fp8(_ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(v8), _ptr(vs), B, H, N, D,
+                                    block, _ptr(row_ptr), _ptr(col_idx), scale, None, 0, _ptr(O), _ptr(L))
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        O = np.empty((len(r), D), np.float64); L = np.empty((len(r),), np.float64)
+        rc = lib.oracle_forward_fp8(_ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(v8), _ptr(vs), B, H, N, D,
+                                    block, _ptr(row_ptr), _ptr(col_idx), scale, _ptr(r), len(r), _ptr(O),
+                                    _ptr(L))
+    _check(rc, "forward_fp8")
     return O, L

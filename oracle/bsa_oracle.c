@@ -410,6 +410,207 @@ int oracle_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     return rc;
 }
 
+/* ------------------------------------------------------------------------
+ * FP8 (OCP E4M3) quantisation and the forward on quantised inputs.
+ *
+ * E4M3, by its definition: 1 sign bit, 4 exponent bits (bias 7), 3
+ * mantissa bits; exponent field 0 holds subnormals m * 2^-9; field 15 with
+ * mantissa 7 is NaN (no infinities); the largest finite value is
+ * 1.75 * 2^8 = 448.  Encoding rounds to nearest, ties to even mantissa.
+ *
+ * Scaled quantisation of a group of values x with amax = max |x| (all in
+ * fp32, the precision the codes are decided in):
+ *   scale = amax / 448,  inv = 448 / amax   (both 0 when amax == 0),
+ *   code  = E4M3(x * inv),   dequantised value = decode(code) * scale.
+ * Groups: Q per token (over d); K per 64-key tile of a head (64 keys x d,
+ * the last tile holding the keys that exist); V per channel d over all N
+ * keys of a head.
+ * ---------------------------------------------------------------------- */
+double oracle_e4m3_decode(uint8_t c)
+{
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+uint8_t oracle_e4m3_encode(float x)
+{
+    if (isnan(x)) return 0x7F;
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs((double)x);
+    if (a > 464.0) return (uint8_t)(sign | 0x7F);   /* past the rounding range of 448: NaN */
+    /* the finite non-negative codes 0x00 .. 0x7E are increasing in value:
+       find the first code >= a, then take the nearer neighbour, ties to the
+       even code (even mantissa) */
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (oracle_e4m3_decode((uint8_t)mid) < a) lo = mid + 1;
+        else hi = mid;
+    }
+    int c = lo;
+    if (c > 0) {
+        const double up = oracle_e4m3_decode((uint8_t)c) - a;
+        const double dn = a - oracle_e4m3_decode((uint8_t)(c - 1));
+        if (dn < up || (dn == up && ((c - 1) & 1) == 0)) c = c - 1;
+    }
+    return (uint8_t)(sign | c);
+}
+
+void oracle_e4m3_encode_array(const float *x, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+}
+
+void oracle_e4m3_decode_array(const uint8_t *c, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+
+static void quant_group_scale(float amax, float *scale, float *inv)
+{
+    if (amax > 0.f) {
+        *scale = amax / 448.0f;
+        *inv = 448.0f / amax;
+    } else {
+        *scale = 0.f;
+        *inv = 0.f;
+    }
+}
+
+static float widen_bf16_f(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+int oracle_quantize_fp8(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int64_t B, int64_t H, int64_t N, int64_t D,
+                        uint8_t *q8, float *q_scale, uint8_t *k8, float *k_scale,
+                        uint8_t *v8, float *v_scale)
+{
+    if (!q || !k || !v || !q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || B <= 0 || H <= 0 ||
+        N <= 0 || D <= 0)
+        return OR_EINVAL;
+    const int64_t NT = (N + 63) / 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        for (int64_t t = 0; t < N; ++t) {   /* Q: per token */
+            const uint16_t *x = q + (bh * N + t) * D;
+            float amax = 0.f;
+            for (int64_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(widen_bf16_f(x[d])));
+            float sc, inv;
+            quant_group_scale(amax, &sc, &inv);
+            q_scale[bh * N + t] = sc;
+            for (int64_t d = 0; d < D; ++d) q8[(bh * N + t) * D + d] = oracle_e4m3_encode(widen_bf16_f(x[d]) * inv);
+        }
+        for (int64_t T = 0; T < NT; ++T) {   /* K: per 64-key tile */
+            const int64_t t0 = T * 64, t1 = (t0 + 64 < N) ? t0 + 64 : N;
+            float amax = 0.f;
+            for (int64_t t = t0; t < t1; ++t)
+                for (int64_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(widen_bf16_f(k[(bh * N + t) * D + d])));
+            float sc, inv;
+            quant_group_scale(amax, &sc, &inv);
+            k_scale[bh * NT + T] = sc;
+            for (int64_t t = t0; t < t1; ++t)
+                for (int64_t d = 0; d < D; ++d)
+                    k8[(bh * N + t) * D + d] = oracle_e4m3_encode(widen_bf16_f(k[(bh * N + t) * D + d]) * inv);
+        }
+        for (int64_t d = 0; d < D; ++d) {   /* V: per channel */
+            float amax = 0.f;
+            for (int64_t t = 0; t < N; ++t) amax = fmaxf(amax, fabsf(widen_bf16_f(v[(bh * N + t) * D + d])));
+            float sc, inv;
+            quant_group_scale(amax, &sc, &inv);
+            v_scale[bh * D + d] = sc;
+            for (int64_t t = 0; t < N; ++t)
+                v8[(bh * N + t) * D + d] = oracle_e4m3_encode(widen_bf16_f(v[(bh * N + t) * D + d]) * inv);
+        }
+    }
+    return OR_OK;
+}
+
+/* The forward of oracle_forward on the dequantised inputs
+ * q = decode(q8) * q_scale[token], k = decode(k8) * k_scale[tile],
+ * v = decode(v8) * v_scale[channel]; every head computed (no modes). */
+int oracle_forward_fp8(const uint8_t *q8, const float *q_scale, const uint8_t *k8, const float *k_scale,
+                       const uint8_t *v8, const float *v_scale, int64_t B, int64_t H, int64_t N, int64_t D,
+                       int64_t beta, const int32_t *row_ptr, const int32_t *col_idx, double scale,
+                       const int64_t *rows, int64_t n_rows, double *O, double *LSE)
+{
+    if (!q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !row_ptr || !O || !LSE || B <= 0 ||
+        H <= 0 || N <= 0 || D <= 0 || beta <= 0)
+        return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta), NT = (N + 63) / 64;
+    if (row_ptr[0] != 0) return OR_EINVAL;
+    for (int64_t r = 0; r < B * H * nB; ++r) {
+        if (row_ptr[r + 1] < row_ptr[r]) return OR_EINVAL;
+        for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e)
+            if (!col_idx || col_idx[e] < 0 || col_idx[e] >= nB) return OR_EINVAL;
+    }
+    if (!rows) n_rows = B * H * N;
+    for (int64_t x = 0; x < n_rows; ++x) {
+        const int64_t row = rows ? rows[x] : x;
+        if (row < 0 || row >= B * H * N) return OR_EINVAL;
+    }
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *z = malloc(sizeof(double) * N);
+        unsigned char *kept = malloc((size_t)nB);
+        if (!z || !kept) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t x = 0; x < n_rows; ++x) {
+                const int64_t row = rows ? rows[x] : x;
+                const int64_t bh = row / N, t = row % N;
+                double *o = O + x * D;
+                const int64_t r = bh * nB + t / beta;
+                memset(kept, 0, (size_t)nB);
+                for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) kept[col_idx[e]] = 1;
+                const double qs = q_scale[row];
+                double m = -INFINITY;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (!kept[s / beta]) { z[s] = -INFINITY; continue; }
+                    const double ks = k_scale[bh * NT + s / 64];
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        acc += (oracle_e4m3_decode(q8[row * D + d]) * qs) *
+                               (oracle_e4m3_decode(k8[(bh * N + s) * D + d]) * ks);
+                    z[s] = scale * acc;
+                    if (z[s] > m) m = z[s];
+                }
+                if (m == -INFINITY) {
+                    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                    LSE[x] = -INFINITY;
+                    continue;
+                }
+                double l = 0.0;
+                for (int64_t s = 0; s < N; ++s)
+                    if (z[s] != -INFINITY) l += exp(z[s] - m);
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (z[s] == -INFINITY) continue;
+                    const double pw = exp(z[s] - m);
+                    for (int64_t d = 0; d < D; ++d)
+                        o[d] += pw * (oracle_e4m3_decode(v8[(bh * N + s) * D + d]) * v_scale[bh * D + d]);
+                }
+                for (int64_t d = 0; d < D; ++d) o[d] /= l;
+                LSE[x] = m + log(l);
+            }
+        }
+        free(z);
+        free(kept);
+    }
+    return rc;
+}
+
 int oracle_threads(void)
 {
 #ifdef _OPENMP
