@@ -15,6 +15,11 @@ The four calls mirror the C ABI:
   build_arrow_layout   CSR block list of the arrow / full / skip layout
   forward              online-softmax attention over the CSR block list,
                        returning O (bf16) and LSE (fp32, natural log)
+
+and the FP8 (E4M3) mode of the forward:
+
+  quantize_fp8         E4M3 codes and scales of Q, K, V
+  forward_fp8          the forward on those codes (FP8 matrix cores)
 """
 from __future__ import annotations
 
@@ -62,6 +67,14 @@ class BsaGroup(ctypes.Structure):
                 ("k", ctypes.c_int32)]
 
 
+class BsaFp8Qkv(ctypes.Structure):
+    _fields_ = [("q8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+                ("k8", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v8t", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("D", ctypes.c_int64)]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -91,6 +104,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_forward": (I32, [TP, TP, TP, I32, V, V, V, TP, V, F, TP, V,
                                   ctypes.POINTER(BsaSplit), V]),
             "bsa_forward_split_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32, I64]),
+            "bsa_quantize_fp8_workspace_size": (SZ, [I64, I64, I64, I64]),
+            "bsa_quantize_fp8": (I32, [TP, TP, TP, ctypes.POINTER(BsaFp8Qkv), V, SZ, V]),
+            "bsa_forward_fp8": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, F, TP, V, V]),
             "bsa_status_string": (ctypes.c_char_p, [I32]),
             "bsa_last_error": (ctypes.c_char_p, []),
             "bsa_version": (ctypes.c_char_p, []),
@@ -380,6 +396,86 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
                            _ptr(row_ptr), _ptr(col_idx), modes, _ref(dc), _ptr(lse_cache),
                            float(scale or 0.0), ctypes.byref(do), _ptr(lse),
                            None if sp is None else ctypes.byref(sp), _stream(q.device)))
+    return out, lse
+
+
+class Fp8QKV:
+    """E4M3 codes and scales of Q, K, V (the layout of bsa_quantize_fp8):
+    q8 / k8 uint8 [B,H,N,D], q_scale fp32 [B,H,N], k_scale fp32 [B,H,ceil(N/64)],
+    v8t uint8 [B,H,D,64*ceil(N/64)] (V transposed, keys permuted inside each
+    64-key group), v_scale fp32 [B,H,D]."""
+
+    def __init__(self, B: int, H: int, N: int, D: int, device):
+        NT = (N + 63) // 64
+        u8 = dict(dtype=torch.uint8, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.shape = (B, H, N, D)
+        self.q8 = torch.empty((B, H, N, D), **u8)
+        self.q_scale = torch.empty((B, H, N), **f32)
+        self.k8 = torch.empty((B, H, N, D), **u8)
+        self.k_scale = torch.empty((B, H, NT), **f32)
+        self.v8t = torch.empty((B, H, D, 64 * NT), **u8)
+        self.v_scale = torch.empty((B, H, D), **f32)
+
+    def desc(self) -> BsaFp8Qkv:
+        arrays = (self.q8, self.q_scale, self.k8, self.k_scale, self.v8t, self.v_scale)
+        for a in arrays:
+            if not a.is_cuda or not a.is_contiguous():
+                raise ValueError("fp8 operands must be contiguous device tensors")
+        return BsaFp8Qkv(*[a.data_ptr() for a in arrays], *self.shape)
+
+
+def v8t_key_column(key: int) -> int:
+    """Column of V^T (inside the padded array) that holds key `key`."""
+    t, k = divmod(key, 64)
+    a, g, h, e = k >> 5, (k >> 3) & 3, (k >> 2) & 1, k & 3
+    return 64 * t + 32 * h + 16 * a + 4 * g + e
+
+
+def quantize_fp8_workspace_size(B, H, N, D) -> int:
+    return int(load().bsa_quantize_fp8_workspace_size(B, H, N, D))
+
+
+def quantize_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[Fp8QKV] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Fp8QKV:
+    """E4M3 codes with max-abs scales: per token for Q, per 64-key tile for K,
+    per channel for V."""
+    lib = load()
+    B, H, N, D = q.shape
+    if out is None:
+        out = Fp8QKV(B, H, N, D, q.device)
+    if workspace is None:
+        workspace = torch.empty(max(quantize_fp8_workspace_size(B, H, N, D), 16), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk, dv = _desc(q, "q"), _desc(k, "k"), _desc(v, "v")
+    d8 = out.desc()
+    _check(lib.bsa_quantize_fp8(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(d8),
+                                _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out
+
+
+def forward_fp8(qkv: Fp8QKV, block: int, row_ptr: torch.Tensor, col_idx: torch.Tensor,
+                scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None,
+                return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Block-sparse attention forward on E4M3 operands.  Returns (O bf16, LSE fp32)."""
+    lib = load()
+    B, H, N, D = qkv.shape
+    dev = qkv.q8.device
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if col_idx.numel() == 0:
+        col_idx = torch.zeros(1, dtype=torch.int32, device=row_ptr.device)
+    d8, do = qkv.desc(), _desc(out, "out")
+    _check(lib.bsa_forward_fp8(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx), float(scale or 0.0),
+                               ctypes.byref(do), _ptr(lse), _stream(dev)))
     return out, lse
 
 

@@ -96,6 +96,28 @@ SplitLayout split_layout(int64_t rows, int32_t block, int64_t D, int32_t max_chu
     return l;
 }
 
+// FP8 operands: shape of the descriptor and alignment of its arrays.
+bsa_status check_fp8(const bsa_fp8_qkv *t, const char *name)
+{
+    if (!t) return fail(BSA_ERR_INVALID_ARG, "%s: null descriptor", name);
+    if (!t->q8 || !t->q_scale || !t->k8 || !t->k_scale || !t->v8t || !t->v_scale)
+        return fail(BSA_ERR_INVALID_ARG, "%s: null array", name);
+    if (t->B <= 0 || t->H <= 0 || t->N <= 0 || t->D <= 0)
+        return fail(BSA_ERR_INVALID_ARG, "%s: shape must be positive", name);
+    if (t->D != 64 && t->D != 128)
+        return fail(BSA_ERR_UNSUPPORTED, "%s: head dim %lld not supported (64 or 128)", name, (long long)t->D);
+    if (t->N > (1ll << 24) || t->B * t->H > (1ll << 30))
+        return fail(BSA_ERR_UNSUPPORTED, "%s: N above 2^24 or B*H too large", name);
+    if (!aligned16(t->q8) || !aligned16(t->q_scale) || !aligned16(t->k8) || !aligned16(t->k_scale) ||
+        !aligned16(t->v8t) || !aligned16(t->v_scale))
+        return fail(BSA_ERR_INVALID_ARG, "%s: arrays must be 16-byte aligned", name);
+    return BSA_OK;
+}
+
+// Quantisation workspace: reciprocal channel scales [B*H][D], then the
+// channel maxima of 256-key chunks [B*H][ceil(N/256)][D] (256-byte aligned).
+size_t fp8_ws_inv_bytes(int64_t BH, int64_t D) { return ((size_t)(BH * D) * sizeof(float) + 255) & ~(size_t)255; }
+
 }  // namespace
 
 extern "C" {
@@ -488,6 +510,97 @@ bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tenso
         if (cp.copy_o || (lse_cache && lse && lse_cache != lse))
             if ((e = bsa::launch_skip_copy(cp, s)) != hipSuccess) return hip_fail(e, "skip copy launch");
     }
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t bsa_quantize_fp8_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || (D != 64 && D != 128)) return 0;
+    const int64_t BH = B * H;
+    return fp8_ws_inv_bytes(BH, D) + (size_t)(BH * ceil_div(N, 256) * D) * sizeof(float);
+}
+
+bsa_status bsa_quantize_fp8(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_fp8_qkv *out,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSA_OK) return st;
+    if ((st = check_tensor(v, "v")) != BSA_OK) return st;
+    if (!same_shape(q, k) || !same_shape(q, v)) return fail(BSA_ERR_INVALID_ARG, "q, k and v shapes differ");
+    if ((st = check_fp8(out, "out")) != BSA_OK) return st;
+    if (out->B != q->B || out->H != q->H || out->N != q->N || out->D != q->D)
+        return fail(BSA_ERR_INVALID_ARG, "out shape differs from q");
+    const size_t need = bsa_quantize_fp8_workspace_size(q->B, q->H, q->N, q->D);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        return fail(BSA_ERR_WORKSPACE, "quantisation workspace needs %zu bytes (16-byte aligned)", need);
+    const int64_t BH = q->B * q->H;
+    if (BH * ceil_div(q->N, 64) >= (1ll << 31) || ceil_div(q->N, 256) > 65535)
+        return fail(BSA_ERR_UNSUPPORTED, "too many tiles");
+
+    bsa::Fp8QuantParams p{};
+    p.q = t4(q);
+    p.k = t4(k);
+    p.v = t4(v);
+    p.q8 = static_cast<uint8_t *>(out->q8);
+    p.k8 = static_cast<uint8_t *>(out->k8);
+    p.v8t = static_cast<uint8_t *>(out->v8t);
+    p.q_scale = out->q_scale;
+    p.k_scale = out->k_scale;
+    p.v_scale = out->v_scale;
+    p.v_inv = static_cast<float *>(workspace);
+    p.vmax_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + fp8_ws_inv_bytes(BH, q->D));
+    p.BHN = BH * q->N;
+    p.B = (int32_t)q->B;
+    p.H = (int32_t)q->H;
+    p.N = (int32_t)q->N;
+    p.NT = (int32_t)ceil_div(q->N, 64);
+    p.NP = 64 * p.NT;
+    p.S = (int32_t)ceil_div(q->N, 256);
+    hipError_t e = bsa::launch_quantize_fp8(p, (int)q->D, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fp8 quantisation launch");
+    return BSA_OK;
+}
+
+bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                           float scale, const bsa_tensor *o, float *lse, void *stream)
+{
+    bsa_status st;
+    if ((st = check_fp8(in, "in")) != BSA_OK) return st;
+    if ((st = check_tensor(o, "o")) != BSA_OK) return st;
+    if (o->B != in->B || o->H != in->H || o->N != in->N || o->D != in->D)
+        return fail(BSA_ERR_INVALID_ARG, "o shape differs from the fp8 inputs");
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    if (!row_ptr || !col_idx) return fail(BSA_ERR_INVALID_ARG, "row_ptr / col_idx null");
+    if (std::isnan(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
+    const int64_t nB = ceil_div(in->N, block);
+    if (in->B * in->H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many query blocks");
+
+    bsa::Fp8FwdParams p{};
+    p.q8 = static_cast<const uint8_t *>(in->q8);
+    p.k8 = static_cast<const uint8_t *>(in->k8);
+    p.v8t = static_cast<const uint8_t *>(in->v8t);
+    p.q_scale = in->q_scale;
+    p.k_scale = in->k_scale;
+    p.v_scale = in->v_scale;
+    p.o = static_cast<uint16_t *>(o->data);
+    p.o_sb = o->stride_b;
+    p.o_sh = o->stride_h;
+    p.o_sn = o->stride_n;
+    p.lse = lse;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.B = (int32_t)in->B;
+    p.H = (int32_t)in->H;
+    p.N = (int32_t)in->N;
+    p.nB = (int32_t)nB;
+    p.NT = (int32_t)ceil_div(in->N, 64);
+    p.NP = 64 * p.NT;
+    const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)in->D);
+    p.scale_log2 = sc * 1.4426950408889634f;
+    hipError_t e = bsa::launch_forward_fp8(p, block, (int)in->D, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fp8 forward launch");
     return BSA_OK;
 }
 

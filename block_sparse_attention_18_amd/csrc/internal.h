@@ -118,7 +118,33 @@ struct ArrowParams {
     int32_t window[kMaxArrowHeads];
 };
 
+// FP8 (E4M3) quantisation of Q, K, V (see bsa_quantize_fp8).
+struct Fp8QuantParams {
+    Tensor4 q, k, v;
+    uint8_t *q8, *k8, *v8t;
+    float *q_scale, *k_scale, *v_scale;
+    float *vmax_part;           // [B*H][S][D] channel maxima of 256-key chunks
+    float *v_inv;               // [B*H][D] 448 / amax
+    int64_t BHN;
+    int32_t B, H, N, NT, NP, S;
+};
+
+// FP8 forward (see bsa_forward_fp8).
+struct Fp8FwdParams {
+    const uint8_t *q8, *k8, *v8t;
+    const float *q_scale, *k_scale, *v_scale;
+    uint16_t *o;
+    int64_t o_sb, o_sh, o_sn;
+    float *lse;
+    const int32_t *row_ptr;
+    const int32_t *col_idx;
+    int32_t B, H, N, nB, NT, NP;
+    float scale_log2;
+};
+
 hipError_t launch_forward(const FwdParams &p, int block, int D, int64_t grid, hipStream_t s);
+hipError_t launch_quantize_fp8(const Fp8QuantParams &p, int D, hipStream_t s);
+hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, hipStream_t s);
 hipError_t launch_skip_copy(const SkipCopyParams &p, hipStream_t s);
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s);

@@ -150,7 +150,7 @@ bsa_status bsa_select_topk(const float *scores, int64_t B, int64_t H, int32_t n_
  * head_modes int8 [H] and head_windows int32 [H] are host arrays shared by
  * every batch entry.  capacity must be at least bsa_arrow_capacity().
  * Errors: INVALID_ARG (unknown mode, negative window, text_len outside
- * [0, N]), UNSUPPORTED (H > 1024 or nB > 65536), CAPACITY.
+ * [0, N]), UNSUPPORTED (H > 256 or nB > 65536), CAPACITY.
  * ---------------------------------------------------------------------- */
 int64_t bsa_arrow_capacity(int64_t B, int64_t H, int64_t N, int32_t block, int64_t text_len,
                            const int8_t *head_modes, const int32_t *head_windows);
@@ -212,6 +212,60 @@ bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tenso
                        const float *lse_cache, float scale, const bsa_tensor *o, float *lse,
                        const bsa_split *split, void *stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 forward (OCP E4M3 operands on the gfx950 FP8 matrix cores).
+ *
+ * The same operation as bsa_forward -- the dense softmax restricted to the
+ * kept key blocks of every query block -- with Q, K, V held as E4M3 codes
+ * and a scale per group, and P rounded to E4M3 for the P.V product.  This
+ * is the FP8 throughput mode of block-sparse attention kernels (GNA sparse
+ * attention write-up, section 2.1, mixed-precision support, and section
+ * 1.2 for its FP16 / FP8 rates); results carry FP8 rounding error.
+ *
+ * bsa_quantize_fp8 fills a bsa_fp8_qkv from bf16 Q, K, V (same shapes and
+ * conventions as bsa_forward), with max-abs scaling to +-448:
+ *   q8 [B][H][N][D] uint8,  q_scale [B][H][N]        one scale per token,
+ *   k8 [B][H][N][D] uint8,  k_scale [B][H][NT]       one per 64-key tile
+ *                                                    (NT = ceil(N/64)),
+ *   v8t [B][H][D][NP] uint8, v_scale [B][H][D]       one per channel,
+ * with NP = 64*NT; v8t is V transposed, keys permuted inside each 64-key
+ * group: key 64T + 32a + 8g + 4h + e (a, h in {0,1}, g, e in 0..3) sits at
+ * column 64T + 32h + 16a + 4g + e; padding columns are 0.  For each group
+ * scale = amax / 448 and code = E4M3(x * (448 / amax)), rounded to nearest
+ * even, decided in fp32 (all 0 for an all-zero group).  All arrays are
+ * caller-owned device memory, 16-byte aligned, contiguous as shown.  The
+ * workspace (bsa_quantize_fp8_workspace_size bytes, 16-byte aligned) holds
+ * the per-channel maxima.  Errors: INVALID_ARG, UNSUPPORTED (D not in
+ * {64, 128}), WORKSPACE.
+ *
+ * bsa_forward_fp8 computes O (bf16, any strides as in bsa_forward) and LSE
+ * (natural log, fp32 [B][H][N] or NULL) from a bsa_fp8_qkv with the CSR of
+ * bsa_forward; scale <= 0 means 1/sqrt(D).  Every head is computed (no
+ * head modes, no long-row splitting).  The row sum that normalises O and
+ * gives LSE is the sum of the E4M3-rounded probabilities.  Errors:
+ * INVALID_ARG, UNSUPPORTED (D not in {64, 128}, block not in {64, 128}).
+ * ---------------------------------------------------------------------- */
+typedef struct bsa_fp8_qkv {
+    void *q8;
+    float *q_scale;
+    void *k8;
+    float *k_scale;
+    void *v8t;
+    float *v_scale;
+    int64_t B, H, N, D;
+} bsa_fp8_qkv;
+
+size_t bsa_quantize_fp8_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D);
+bsa_status bsa_quantize_fp8(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                            const bsa_fp8_qkv *out, void *workspace, size_t workspace_bytes,
+                            void *stream);
+bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
+                           const int32_t *col_idx, float scale, const bsa_tensor *o, float *lse,
+                           void *stream);
+
+/* ------------------------------------------------------------------------
+ * Utilities.
+ * ---------------------------------------------------------------------- */
 /* Name of a status code (static string). */
 const char *bsa_status_string(bsa_status status);
 /* Message describing the most recent failure on the calling thread. */

@@ -215,6 +215,46 @@ def test_arrow_validation_and_capacity():
                                       ctypes.c_void_p(FAKE), 10 ** 7, None) == 2
 
 
+def _fp8(B=1, H=2, N=256, D=64, base=FAKE):
+    return bsa.BsaFp8Qkv(base, base + 0x100000, base + 0x200000, base + 0x300000, base + 0x400000,
+                         base + 0x500000, B, H, N, D)
+
+
+def test_fp8_workspace_and_quantize_validation():
+    lib = bsa.load()
+    up = lambda x: (x + 255) // 256 * 256
+    # reciprocal channel scales, then channel maxima of 256-key chunks
+    assert lib.bsa_quantize_fp8_workspace_size(1, 2, 600, 64) == up(2 * 64 * 4) + 2 * 3 * 64 * 4
+    assert lib.bsa_quantize_fp8_workspace_size(1, 2, 600, 96) == 0
+    need = lib.bsa_quantize_fp8_workspace_size(1, 2, 256, 64)
+    call = lambda out=None, ws=FAKE, wsb=need, q=None: lib.bsa_quantize_fp8(
+        ctypes.byref(q or _t()), ctypes.byref(_t()), ctypes.byref(_t()),
+        None if out is False else ctypes.byref(out or _fp8()),
+        ctypes.c_void_p(ws) if ws else None, wsb, None)
+    assert call(out=False) == 1 and "null descriptor" in _err()
+    assert call(out=_fp8(N=128)) == 1 and "shape" in _err()
+    assert call(out=_fp8(base=FAKE + 4)) == 1 and "aligned" in _err()
+    assert call(wsb=need - 1) == 4 and "workspace" in _err()
+    assert call(ws=0) == 4
+    assert call(q=_t(D=128)) == 1
+    bad = _fp8()
+    bad.k_scale = None
+    assert call(out=bad) == 1 and "null array" in _err()
+
+
+def test_fp8_forward_validation():
+    lib = bsa.load()
+    call = lambda inp=None, block=64, rp=FAKE, ci=FAKE, scale=0.0, o=None: lib.bsa_forward_fp8(
+        ctypes.byref(inp or _fp8()), block, ctypes.c_void_p(rp) if rp else None,
+        ctypes.c_void_p(ci) if ci else None, scale, ctypes.byref(o or _t()), None, None)
+    assert call(block=32) == 2 and "block size" in _err()
+    assert call(inp=_fp8(D=96), o=_t(D=96)) == 2
+    assert call(o=_t(N=128)) == 1 and "shape" in _err()
+    assert call(rp=0) == 1 and "row_ptr" in _err()
+    assert call(scale=float("nan")) == 1 and "NaN" in _err()
+    assert call(inp=_fp8(N=(1 << 24) + 1), o=_t(N=(1 << 24) + 1)) == 2 and "2^24" in _err()
+
+
 def test_binding_refuses_host_tensors():
     import torch
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
