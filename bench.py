@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "block-sparse attn fwd TFLOP/s (actual + dense-equiv) and % bf16 MFMA peak"
 
@@ -65,6 +66,9 @@ def main():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="run the forward in the FP8 (E4M3) mode on inputs quantised once "
+                         "before the timed region (quantisation timed separately)")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the kept-pairs sweep of the forward at the C4 shape "
                          "(arrow windows 0..127 and all-FULL) with a least-squares fit")
@@ -153,7 +157,7 @@ def main():
         fwd_kw = {}
         computed_heads = B * H
         split = bsa.select_split_policy(B, H, nB, wl.text_blocks, wl.groups, block=block)
-    if args.no_split:
+    if args.no_split or args.fp8:
         split = None
     if split is not None:   # workspace allocated once, outside the timed region
         split["workspace"] = torch.empty(
@@ -161,8 +165,24 @@ def main():
             dtype=torch.uint8, device=dev)
         fwd_kw["split"] = split
 
-    def forward():
-        bsa.forward(q, k, v, block, row_ptr, col_idx, out=out, lse=lse, **fwd_kw)
+    quant = None
+    if args.fp8:
+        if "head_modes" in fwd_kw and np.any(fwd_kw["head_modes"] == bsa.HEAD_SKIP):
+            print("the FP8 forward computes every head: pick a workload without SKIP heads",
+                  file=sys.stderr)
+            sys.exit(2)
+        qkv8 = bsa.quantize_fp8(q, k, v)
+        ws_q = torch.empty(max(bsa.quantize_fp8_workspace_size(B, H, N, D), 16), dtype=torch.uint8,
+                           device=dev)
+
+        def forward():
+            bsa.forward_fp8(qkv8, block, row_ptr, col_idx, out=out, lse=lse)
+
+        def quantize():
+            bsa.quantize_fp8(q, k, v, out=qkv8, workspace=ws_q)
+    else:
+        def forward():
+            bsa.forward(q, k, v, block, row_ptr, col_idx, out=out, lse=lse, **fwd_kw)
 
     # warmup (also fixes kept_pairs for content-driven selection)
     for _ in range(max(args.warmup, 1)):
@@ -200,6 +220,21 @@ def main():
     fwd_avg = float(np.mean(fwd_ms))
     part_ms = {name: float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev]))
                for j, name in enumerate(layout_parts)}
+    if args.fp8:
+        # quantisation of Q, K, V: reads them (V twice: channel maxima, then
+        # codes) and writes the codes; the scales are negligible
+        for _ in range(3):
+            quantize()
+        qe = [new_ev() for _ in range(11)]
+        for j in range(10):
+            qe[j].record(stream)
+            quantize()
+        qe[10].record(stream)
+        torch.cuda.synchronize()
+        q_ms = float(np.median([qe[j].elapsed_time(qe[j + 1]) for j in range(10)]))
+        elems = B * H * N * D
+        quant = {"ms": round(q_ms, 4), "hbm_bytes": 4 * 2 * elems + 3 * elems,
+                 "GBps": round((4 * 2 * elems + 3 * elems) / (q_ms * 1e-3) / 1e9, 1)}
     cold = None
     if wl.layout != "arrow":
         cold = cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr,
@@ -218,7 +253,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {wl.description}",
@@ -230,6 +265,9 @@ def main():
             "long_row_split": (None if split is None else
                                {k2: split[k2] for k2 in ("chunk_blocks", "max_chunks", "max_split_rows")}),
             "parallelism": "single GPU",
+            "precision": ("E4M3 Q (per-token scale), K (per-64-key-tile scale), V (per-channel "
+                          "scale) and P; fp32 accumulation; bf16 O" if args.fp8 else
+                          "bf16 Q, K, V, P; fp32 accumulation; bf16 O"),
         },
         "dense_equiv_tflops": round(dense_flop / (ms_step * 1e-3) / 1e12, 2),
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
@@ -239,20 +277,22 @@ def main():
         "layout_cold_cache": cold,
         "forward_dense_equiv_tflops": round(dense_flop / (fwd_avg * 1e-3) / 1e12, 2),
         "step_wall_ms": round(wall * 1e3 / args.steps, 4),
+        "fp8_quantize": quant,
         "roofline": {
             "bound": "mfma",
-            "kernel": "bsa::fwd_kernel (+ split plan / combine when long rows are split)",
+            "kernel": ("bsa::fwd8_kernel" if args.fp8 else
+                       "bsa::fwd_kernel (+ split plan / combine when long rows are split)"),
             "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic(wl.name),
+            "frac": round(achieved / (PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS), 4),
+            "traffic": None if args.fp8 else _traffic(wl.name),
             "algorithmic_flop_per_launch": actual_flop,
         },
         "cpu_baseline": None,
     }
 
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.fp8:
         res["cpu_baseline"] = cpu_baseline(wl, x, row_ptr, col_idx, args.cpu_seconds,
                                            fwd_kw.get("head_modes"))
     print(json.dumps(res), flush=True)

@@ -38,10 +38,12 @@ __device__ __forceinline__ void fp8_group_scale(float amax, float &scale, float 
     }
 }
 
-// Four floats -> four E4M3 bytes (byte 0 = a).
+// Four floats -> four E4M3 bytes (byte 0 = a).  The first conversion keeps
+// the upper half of its destination, which the second one overwrites: any
+// dying value serves as that destination (no zeroing move).
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -279,6 +281,7 @@ struct F8State {
     i32x8 qf[Sh::KS];            // Q^T codes: query n, channels 64 ks + 32 h .. +31
     f32x16 oacc[Sh::DT];         // O^T in V code units
     f32x16 lacc;                 // row sums of the E4M3 probabilities (all 16 equal)
+    i32x8 ones;                  // E4M3 1.0 in every byte: A operand of the row sums
     float m_run;                 // reference max, log2-scaled domain
     float cq;                    // scale * log2(e) * q_scale of the lane's query
     uint32_t kread;              // K operand, k-step 0, first 16 bytes; (ks, x): ^ (64 ks + 16 x)
@@ -333,36 +336,36 @@ __device__ __forceinline__ void mask_scores8(bool valid, int k0, int N, int lane
 }
 
 template <int BETA, int D>
-__device__ __forceinline__ void lazy_rescale8(float mx, F8State<BETA, D> &st)
+__device__ __forceinline__ bool lazy_rescale8(float mx, F8State<BETA, D> &st)
 {
     using Sh = F8Shape<BETA, D>;
-    if (__ballot(mx > st.m_run + 8.0f)) {
-        const float m_new = fmaxf(st.m_run, mx);
-        const float alpha = (st.m_run == m_new) ? 1.f : fast_exp2(st.m_run - m_new);
-        st.m_run = m_new;
+    if (!__ballot(mx > st.m_run + 8.0f)) return false;
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = (st.m_run == m_new) ? 1.f : fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st.lacc[r] *= alpha;
+    for (int r = 0; r < 16; ++r) st.lacc[r] *= alpha;
 #pragma unroll
-        for (int d = 0; d < Sh::DT; ++d)
+    for (int d = 0; d < Sh::DT; ++d)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st.oacc[d][r] *= alpha;
-    }
+        for (int r = 0; r < 16; ++r) st.oacc[d][r] *= alpha;
+    return true;
 }
 
-// Probabilities relative to the reference max (at most 2^8 under the lazy
-// rescale, inside the E4M3 range), rounded to E4M3 and packed as the B
-// operand of O^T += V^T P^T: byte 16 a + r of the lane.
-__device__ __forceinline__ void probs8(const f32x16 (&sacc)[2], float c, float m, i32x8 &pf)
+// Probabilities of accumulator tile A of a sub-tile (keys 32 A + 8 g + 4 h
+// + e) relative to the reference max (at most 2^8 under the lazy rescale,
+// inside the E4M3 range), rounded to E4M3 and packed into bytes 16 A + r of
+// the B operand of O^T += V^T P^T.
+template <int A>
+__device__ __forceinline__ void probs_half(const f32x16 (&sacc)[2], float c, float m, i32x8 &pf)
 {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int g = 0; g < 4; ++g) {
+        float x[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float x[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = fast_exp2(__builtin_fmaf(sacc[a][4 * g + e], c, -m));
-            pf[4 * a + g] = (int)pack_fp8x4(x[0], x[1], x[2], x[3]);
-        }
+        for (int e = 0; e < 4; ++e) x[e] = fast_exp2(__builtin_fmaf(sacc[A][4 * g + e], c, -m));
+        pf[4 * A + g] = (int)pack_fp8x4(x[0], x[1], x[2], x[3]);
+    }
 }
 
 // O^T += V^T P^T (one MFMA per 32-row d tile) and the row sums of P (an
@@ -378,10 +381,7 @@ __device__ __forceinline__ void pv8(const uint8_t *__restrict__ Vc, const i32x8 
         const i32x8 v = lds_i32x8(t, st.vread, st.vread ^ 16);
         st.oacc[d] = mfma_fp8(v, pf, st.oacc[d]);
     }
-    i32x8 ones;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ones[j] = 0x38383838;   // E4M3 1.0
-    st.lacc = mfma_fp8(ones, pf, st.lacc);
+    st.lacc = mfma_fp8(st.ones, pf, st.lacc);
 }
 
 // Copy of one 64-key K tile (keys from k0; rows past N repeat key N-1) into
@@ -431,32 +431,43 @@ struct F8Tile {
     float c;       // scale * log2(e) * q_scale * k_scale of the tile (> 0)
 };
 
-// Steady-state step t: S^T of sub-tile t (K tile Kc) while the
-// probabilities of t-1 are formed, then O^T += V^T P^T of t-1 (V tile Vp)
-// while the row max of t is taken, then the lazy rescale for t.
+// Steady-state step t, two scheduled regions of MFMAs with the vector work
+// spread between them:
+//   A: S^T(t) = K(t) Q^T            with the probabilities of keys 32..63 of t-1
+//   B: O^T += V^T(t-1) P^T(t-1)     with the row max of t and the
+//                                   probabilities of keys 0..31 of t
+// Keys 0..31 of t are exponentiated against the reference max before the
+// max of t is known; when the lazy rescale then moves the reference (rare:
+// the first sub-tile of a row, or a max that grows by more than 2^8) they
+// are recomputed.  Masking of t's scores sits between the two regions.
 template <int BETA, int D>
 __device__ __forceinline__ void step8(const uint8_t *__restrict__ Kc, const uint8_t *__restrict__ Vp,
                                       uint8_t *__restrict__ Kn, uint8_t *__restrict__ Vn, const F8Tile &cur,
                                       const F8Tile &prv, bool load_k, int k0_k, __amdgpu_buffer_rsrc_t krs,
                                       __amdgpu_buffer_rsrc_t vrs, uint32_t vstep, const Fp8FwdParams &p, int wv,
-                                      int lane, F8State<BETA, D> &st, f32x16 (&s_cur)[2], f32x16 (&s_prev)[2])
+                                      int lane, F8State<BETA, D> &st, f32x16 (&s_cur)[2], f32x16 (&s_prev)[2],
+                                      i32x8 &pf_prev, i32x8 &pf_cur)
 {
     using Sh = F8Shape<BETA, D>;
-    mask_scores8(prv.valid, prv.k0, p.N, lane, s_prev);
     if (load_k) load_k8<BETA, D>(Kn, krs, st.kdma, p.N, k0_k, wv, lane);
     load_v8<BETA, D>(Vn, vrs, st.vdma, vstep, p.NP, cur.k0, wv);
-    constexpr int QK = 2 * Sh::KS;
-    i32x8 pf;
+    constexpr int QK = 2 * Sh::KS, PV = Sh::DT + 1;
     qk8<BETA, D>(Kc, st, s_cur);
-    probs8(s_prev, prv.c, st.m_run, pf);   // 32 exp, ~48 other
-    interleave<2, QK, 2, (48 + QK - 1) / QK, (32 + QK - 1) / QK>();
+    probs_half<1>(s_prev, prv.c, st.m_run, pf_prev);        // 16 exp, ~24 other
+    interleave<2, QK, 2, (24 + QK - 1) / QK, (16 + QK - 1) / QK>();
     __builtin_amdgcn_sched_barrier(0);
-    pv8<BETA, D>(Vp, pf, st);
+    // the packed probabilities are used after the masking branch; without
+    // this use the compiler sinks their computation past it, out of region A
+    asm volatile("" ::"v"(pf_prev));
+    mask_scores8(cur.valid, cur.k0, p.N, lane, s_cur);
+    pv8<BETA, D>(Vp, pf_prev, st);
     const bool has_keys = cur.valid && cur.k0 < p.N;
     const float mx = tile_max(s_cur, cur.c) + (has_keys ? 0.f : -INFINITY);
-    interleave<2, Sh::DT + 1, 2, (24 + Sh::DT) / (Sh::DT + 1), 0>();
+    probs_half<0>(s_cur, cur.c, st.m_run, pf_cur);           // 16 exp, ~44 other with the max
+    interleave<2, PV, 2, (44 + PV - 1) / PV, (16 + PV - 1) / PV>();
     __builtin_amdgcn_sched_barrier(0);
-    lazy_rescale8<BETA, D>(mx, st);
+    asm volatile("" ::"v"(pf_cur), "v"(mx));
+    if (lazy_rescale8<BETA, D>(mx, st)) probs_half<0>(s_cur, cur.c, st.m_run, pf_cur);
 }
 
 // Occupancy target (waves per SIMD): two, so that a wave's accumulators,
@@ -507,6 +518,11 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
         for (int r = 0; r < 16; ++r) st.oacc[d][r] = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.lacc[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.ones[j] = 0x38383838;
+    // opaque to the compiler: otherwise it keeps one copy and rebuilds the
+    // 8-register operand before every row-sum MFMA
+    asm volatile("" : "+v"(st.ones));
     st.m_run = -1.0e30f;
 
     st.kread = (uint32_t)(n * D + 16 * (k8swz<D>(n) ^ (2 * hl)));
@@ -542,40 +558,49 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
     const F8Tile none = {0, false, 1.f};
 
     f32x16 sa[2], sb[2];
+    i32x8 pa, pb;
     if (T > 0) {
         F8Tile cur = tile(0), nxt = none, prv;
         if (T > 1) nxt = tile(1);
         load_k8<BETA, D>(K0, krs, st.kdma, p.N, cur.k0, wv, lane);
         __syncthreads();
-        // first step: S^T(0) and its max; copies K(1) and V(0)
+        // first step: S^T(0), its max and the probabilities of keys 0..31;
+        // copies K(1) and V(0)
         if (T > 1) load_k8<BETA, D>(K1, krs, st.kdma, p.N, nxt.k0, wv, lane);
         load_v8<BETA, D>(V0, vrs, st.vdma, vstep, p.NP, cur.k0, wv);
         qk8<BETA, D>(K0, st, sa);
+        mask_scores8(cur.valid, cur.k0, p.N, lane, sa);
         lazy_rescale8<BETA, D>((cur.valid && cur.k0 < p.N) ? tile_max(sa, cur.c) : -INFINITY, st);
+        probs_half<0>(sa, cur.c, st.m_run, pa);
         __syncthreads();
         prv = cur;
         cur = nxt;
         for (int t = 1; t < T; t += 2) {
             nxt = none;
             if (t + 1 < T) nxt = tile(t + 1);
-            step8<BETA, D>(K1, V0, K0, V1, cur, prv, t + 1 < T, nxt.k0, krs, vrs, vstep, p, wv, lane, st, sb, sa);
+            step8<BETA, D>(K1, V0, K0, V1, cur, prv, t + 1 < T, nxt.k0, krs, vrs, vstep, p, wv, lane, st, sb, sa,
+                           pa, pb);
             __syncthreads();
             prv = cur;
             cur = nxt;
             if (t + 1 >= T) break;
             nxt = none;
             if (t + 2 < T) nxt = tile(t + 2);
-            step8<BETA, D>(K0, V1, K1, V0, cur, prv, t + 2 < T, nxt.k0, krs, vrs, vstep, p, wv, lane, st, sa, sb);
+            step8<BETA, D>(K0, V1, K1, V0, cur, prv, t + 2 < T, nxt.k0, krs, vrs, vstep, p, wv, lane, st, sa, sb,
+                           pb, pa);
             __syncthreads();
             prv = cur;
             cur = nxt;
         }
-        // last sub-tile: probabilities and O update (V(T-1) in V[(T-1)&1])
-        f32x16 (&sl)[2] = (T & 1) ? sa : sb;
-        mask_scores8(prv.valid, prv.k0, p.N, lane, sl);
-        i32x8 pf;
-        probs8(sl, prv.c, st.m_run, pf);
-        pv8<BETA, D>((T & 1) ? V0 : V1, pf, st);
+        // last sub-tile: keys 32..63 of its probabilities and the O update
+        // (V(T-1) in V[(T-1)&1], scores already masked)
+        if (T & 1) {
+            probs_half<1>(sa, prv.c, st.m_run, pa);
+            pv8<BETA, D>(V0, pa, st);
+        } else {
+            probs_half<1>(sb, prv.c, st.m_run, pb);
+            pv8<BETA, D>(V1, pb, st);
+        }
     }
 
     const float l_tot = st.lacc[0];
