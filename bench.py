@@ -34,22 +34,23 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "block-sparse attn fwd TFLOP/s (actual + dense-equiv) and % bf16 MFMA peak"
 
 
-def _src_hash() -> str:
+def _src_hash(fp8: bool) -> str:
     h = hashlib.sha256()
-    p = os.path.join(ROOT, "block_sparse_attention_18_amd", "csrc", "forward.hip")
+    p = os.path.join(ROOT, "block_sparse_attention_18_amd", "csrc", "fp8.hip" if fp8 else "forward.hip")
     h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str):
+def _traffic(workload: str, fp8: bool = False):
     """HBM bytes per forward launch from committed rocprofv3 counter runs, if they
-    were taken on the current forward kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"forward_{workload.lower()}_traffic.json")
+    were taken on the current kernel source; else None."""
+    name = "forward_fp8" if fp8 else "forward"
+    p = os.path.join(ROOT, "profiles", f"{name}_{workload.lower()}_traffic.json")
     try:
         d = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if d.get("forward_src_sha") != _src_hash():
+    if d.get("forward_src_sha") != _src_hash(fp8):
         return None
     return d.get("bytes_per_launch")
 
@@ -286,7 +287,7 @@ def main():
             "peak": PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / (PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS), 4),
-            "traffic": None if args.fp8 else _traffic(wl.name),
+            "traffic": _traffic(wl.name, args.fp8),
             "algorithmic_flop_per_launch": actual_flop,
         },
         "cpu_baseline": None,
