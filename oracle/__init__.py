@@ -16,6 +16,10 @@ Every function follows the definitions stated in ``bsa_oracle.c``:
                           column group with lower-index tie-break
   arrow                   closed-form arrow / full / skip layout
   forward                 dense softmax restricted to the kept blocks
+  quantize_fp8 / forward_fp8   E4M3 codes with max-abs scales; the forward
+                          on the dequantised inputs
+  output_rse              per-head relative squared error of an output
+  mask_jaccard            per-head Jaccard similarity of two block masks
 """
 from __future__ import annotations
 
@@ -294,3 +298,55 @@ def forward_fp8(q8, q_scale, k8, k_scale, v8, v_scale, block: int, row_ptr, col_
                                     _ptr(L))
     _check(rc, "forward_fp8")
     return O, L
+
+
+# ---------------------------------------------------------------------------
+# Diagnostics of sparse against full attention and of mask reuse
+# ---------------------------------------------------------------------------
+def output_rse(y_test: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
+    """Per-(b, h) relative squared error of an attention output against a
+    reference (DiTFastAttnV2, "Headwise Arrow Attention", single-layer RSE):
+
+        RSE = sum (y_test - y_ref)^2 / sum (y_ref - mean(y_ref))^2
+
+    over the head's N x D elements, mean over the same elements.  Inputs are
+    [B, H, N, D] (bf16 bit patterns as uint16, or floats); returns fp64
+    [B, H].  A reference with no spread gives +inf (0/0 gives 0)."""
+    t = _widen(y_test)
+    r = _widen(y_ref)
+    B, H = r.shape[:2]
+    out = np.empty((B, H), np.float64)
+    for b in range(B):
+        for h in range(H):
+            ref = r[b, h].reshape(-1)
+            num = float(np.sum((t[b, h].reshape(-1) - ref) ** 2))
+            den = float(np.sum((ref - ref.mean()) ** 2))
+            out[b, h] = (0.0 if num == 0.0 else math.inf) if den == 0.0 else num / den
+    return out
+
+
+def mask_jaccard(B: int, H: int, n_blocks: int, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b) -> np.ndarray:
+    """Per-(b, h) Jaccard similarity |A & B| / |A | B| of two block masks
+    given as CSR over rows (b*H + h)*nB + i (SparseD, "sparse reuse": the
+    stability of the reused mask against each step's own selection).
+    Entries outside [0, nB) are ignored; repeated entries count once; two
+    empty masks have similarity 1."""
+    out = np.empty((B, H), np.float64)
+    for b in range(B):
+        for h in range(H):
+            inter = union = 0
+            for i in range(n_blocks):
+                r = (b * H + h) * n_blocks + i
+                a = {int(j) for j in col_idx_a[row_ptr_a[r]:row_ptr_a[r + 1]] if 0 <= j < n_blocks}
+                c = {int(j) for j in col_idx_b[row_ptr_b[r]:row_ptr_b[r + 1]] if 0 <= j < n_blocks}
+                inter += len(a & c)
+                union += len(a | c)
+            out[b, h] = 1.0 if union == 0 else inter / union
+    return out
+
+
+def _widen(a: np.ndarray) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
