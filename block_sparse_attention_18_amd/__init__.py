@@ -20,6 +20,13 @@ and the FP8 (E4M3) mode of the forward:
 
   quantize_fp8         E4M3 codes and scales of Q, K, V
   forward_fp8          the forward on those codes (FP8 matrix cores)
+
+diagnostics of sparse against full attention, and the step schedule of a
+mask that is selected once and reused:
+
+  output_rse           per-head relative squared error of an output
+  mask_jaccard         per-head Jaccard similarity of two block masks
+  ReuseSchedule        full / select / sparse action of each step
 """
 from __future__ import annotations
 
@@ -107,6 +114,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_quantize_fp8_workspace_size": (SZ, [I64, I64, I64, I64]),
             "bsa_quantize_fp8": (I32, [TP, TP, TP, ctypes.POINTER(BsaFp8Qkv), V, SZ, V]),
             "bsa_forward_fp8": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, F, TP, V, V]),
+            "bsa_output_rse_workspace_size": (SZ, [I64, I64, I64, I64]),
+            "bsa_output_rse": (I32, [TP, TP, V, V, SZ, V]),
+            "bsa_mask_jaccard": (I32, [I64, I64, I32, V, V, V, V, V, V]),
             "bsa_status_string": (ctypes.c_char_p, [I32]),
             "bsa_last_error": (ctypes.c_char_p, []),
             "bsa_version": (ctypes.c_char_p, []),
@@ -477,6 +487,82 @@ def forward_fp8(qkv: Fp8QKV, block: int, row_ptr: torch.Tensor, col_idx: torch.T
     _check(lib.bsa_forward_fp8(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx), float(scale or 0.0),
                                ctypes.byref(do), _ptr(lse), _stream(dev)))
     return out, lse
+
+
+def output_rse(test: torch.Tensor, ref: torch.Tensor, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-head sum (test - ref)^2 / sum (ref - mean ref)^2 over each head's
+    N x D elements; fp64 [B, H] on the device."""
+    lib = load()
+    B, H, N, D = ref.shape
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.float64, device=ref.device)
+    if out.dtype != torch.float64 or not out.is_contiguous() or out.numel() < B * H:
+        raise ValueError("out must be a contiguous fp64 tensor of B*H elements")
+    if workspace is None:
+        need = int(lib.bsa_output_rse_workspace_size(B, H, N, D))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=ref.device)
+    dt, dr = _desc(test, "test"), _desc(ref, "ref")
+    _check(lib.bsa_output_rse(ctypes.byref(dt), ctypes.byref(dr), _ptr(out), _ptr(workspace),
+                              workspace.numel(), _stream(ref.device)))
+    return out
+
+
+def mask_jaccard(B: int, H: int, n_blocks: int, row_ptr_a: torch.Tensor, col_idx_a: torch.Tensor,
+                 row_ptr_b: torch.Tensor, col_idx_b: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-head Jaccard similarity of two CSR block masks; fp64 [B, H]."""
+    lib = load()
+    dev = row_ptr_a.device
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.float64, device=dev)
+    if out.dtype != torch.float64 or not out.is_contiguous() or out.numel() < B * H:
+        raise ValueError("out must be a contiguous fp64 tensor of B*H elements")
+    arrs = []
+    for name, t in (("row_ptr_a", row_ptr_a), ("col_idx_a", col_idx_a), ("row_ptr_b", row_ptr_b),
+                    ("col_idx_b", col_idx_b)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+        arrs.append(t if t.numel() else torch.zeros(1, dtype=torch.int32, device=dev))
+    _check(lib.bsa_mask_jaccard(B, H, n_blocks, *[_ptr(a) for a in arrs], _ptr(out), _stream(dev)))
+    return out
+
+
+class ReuseSchedule:
+    """Which attention each of T denoising steps runs when a block mask is
+    selected once and reused (SparseD, "skipping sparse" and "sparse
+    reuse"): steps 0 .. n_full-1 run full attention, n_full = floor(T *
+    skip); step n_full selects the mask (exact avgpool scores and isolated
+    top-k) and runs sparse attention with it; every later step reuses it."""
+
+    FULL, SELECT, SPARSE = "full", "select", "sparse"
+
+    def __init__(self, steps: int, skip: float = 0.2):
+        if steps < 1 or not (0.0 <= skip <= 1.0):
+            raise ValueError("steps >= 1 and 0 <= skip <= 1 required")
+        self.steps = int(steps)
+        self.skip = float(skip)
+        # floor, with a guard against T * skip landing a rounding error below an integer
+        self.n_full = min(self.steps, int(math.floor(self.steps * self.skip + 1e-9)))
+
+    def action(self, step: int) -> str:
+        if not 0 <= step < self.steps:
+            raise IndexError(step)
+        if step < self.n_full:
+            return self.FULL
+        return self.SELECT if step == self.n_full else self.SPARSE
+
+    def counts(self) -> dict:
+        n_sel = 1 if self.n_full < self.steps else 0
+        return {self.FULL: self.n_full, self.SELECT: n_sel,
+                self.SPARSE: self.steps - self.n_full - n_sel}
+
+    def amortised_speedup(self, t_full: float, t_select: float, t_sparse: float) -> float:
+        """Time of T full steps over the time of this schedule, given the time
+        of a full step, of the selection (scores + top-k) and of a sparse step."""
+        c = self.counts()
+        t = c[self.FULL] * t_full + c[self.SELECT] * (t_select + t_sparse) + c[self.SPARSE] * t_sparse
+        return self.steps * t_full / t
 
 
 def version() -> str:

@@ -118,6 +118,13 @@ bsa_status check_fp8(const bsa_fp8_qkv *t, const char *name)
 // channel maxima of 256-key chunks [B*H][ceil(N/256)][D] (256-byte aligned).
 size_t fp8_ws_inv_bytes(int64_t BH, int64_t D) { return ((size_t)(BH * D) * sizeof(float) + 255) & ~(size_t)255; }
 
+// RSE chunks: about 64 K elements per workgroup, at most 1024 per head.
+int32_t rse_chunks(int64_t N, int64_t D)
+{
+    int64_t c = ceil_div(N * D, 65536);
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(c, 1024));
+}
+
 }  // namespace
 
 extern "C" {
@@ -601,6 +608,62 @@ bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *
     p.scale_log2 = sc * 1.4426950408889634f;
     hipError_t e = bsa::launch_forward_fp8(p, block, (int)in->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fp8 forward launch");
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t bsa_output_rse_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || (D != 64 && D != 128)) return 0;
+    return (size_t)(B * H) * rse_chunks(N, D) * 3 * sizeof(double);
+}
+
+bsa_status bsa_output_rse(const bsa_tensor *test, const bsa_tensor *ref, double *rse, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(test, "test")) != BSA_OK) return st;
+    if ((st = check_tensor(ref, "ref")) != BSA_OK) return st;
+    if (!same_shape(test, ref)) return fail(BSA_ERR_INVALID_ARG, "test and ref shapes differ");
+    if (!rse) return fail(BSA_ERR_INVALID_ARG, "rse null");
+    const size_t need = bsa_output_rse_workspace_size(ref->B, ref->H, ref->N, ref->D);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        return fail(BSA_ERR_WORKSPACE, "rse workspace needs %zu bytes (16-byte aligned)", need);
+    bsa::RseParams p{};
+    p.test = t4(test);
+    p.ref = t4(ref);
+    p.partials = static_cast<double *>(workspace);
+    p.rse = rse;
+    p.B = (int32_t)ref->B;
+    p.H = (int32_t)ref->H;
+    p.N = (int32_t)ref->N;
+    p.D = (int32_t)ref->D;
+    p.chunks = rse_chunks(ref->N, ref->D);
+    p.rows_per_chunk = (int32_t)ceil_div(ref->N, p.chunks);
+    hipError_t e = bsa::launch_output_rse(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "rse launch");
+    return BSA_OK;
+}
+
+bsa_status bsa_mask_jaccard(int64_t B, int64_t H, int32_t n_blocks, const int32_t *row_ptr_a,
+                            const int32_t *col_idx_a, const int32_t *row_ptr_b, const int32_t *col_idx_b,
+                            double *jaccard, void *stream)
+{
+    if (B <= 0 || H <= 0 || n_blocks <= 0) return fail(BSA_ERR_INVALID_ARG, "B, H, n_blocks must be positive");
+    if (!row_ptr_a || !col_idx_a || !row_ptr_b || !col_idx_b || !jaccard)
+        return fail(BSA_ERR_INVALID_ARG, "null array");
+    if (n_blocks > 65536 || B * H > INT32_MAX) return fail(BSA_ERR_UNSUPPORTED, "n_blocks above 65536 or B*H too large");
+    bsa::JaccardParams p{};
+    p.row_ptr_a = row_ptr_a;
+    p.col_idx_a = col_idx_a;
+    p.row_ptr_b = row_ptr_b;
+    p.col_idx_b = col_idx_b;
+    p.jaccard = jaccard;
+    p.B = (int32_t)B;
+    p.H = (int32_t)H;
+    p.nB = n_blocks;
+    hipError_t e = bsa::launch_mask_jaccard(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "jaccard launch");
     return BSA_OK;
 }
 

@@ -142,7 +142,24 @@ struct Fp8FwdParams {
     float scale_log2;
 };
 
+// Per-head RSE of an output against a reference (see bsa_output_rse).
+struct RseParams {
+    Tensor4 test, ref;
+    double *partials;           // [B*H][chunks][3]
+    double *rse;                // [B*H]
+    int32_t B, H, N, D, chunks, rows_per_chunk;
+};
+
+// Per-head Jaccard similarity of two block masks (see bsa_mask_jaccard).
+struct JaccardParams {
+    const int32_t *row_ptr_a, *col_idx_a, *row_ptr_b, *col_idx_b;
+    double *jaccard;            // [B*H]
+    int32_t B, H, nB;
+};
+
 hipError_t launch_forward(const FwdParams &p, int block, int D, int64_t grid, hipStream_t s);
+hipError_t launch_output_rse(const RseParams &p, hipStream_t s);
+hipError_t launch_mask_jaccard(const JaccardParams &p, hipStream_t s);
 hipError_t launch_quantize_fp8(const Fp8QuantParams &p, int D, hipStream_t s);
 hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, hipStream_t s);
 hipError_t launch_skip_copy(const SkipCopyParams &p, hipStream_t s);

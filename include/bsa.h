@@ -264,6 +264,36 @@ bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *
                            void *stream);
 
 /* ------------------------------------------------------------------------
+ * Diagnostics of sparse attention.
+ *
+ * bsa_output_rse: per-(b, h) relative squared error of an attention output
+ * against a reference output (DiTFastAttnV2, head-wise arrow attention:
+ * the single-layer RSE by which its compression plans are judged):
+ *     rse[b*H + h] = sum (test - ref)^2 / sum (ref - mean(ref))^2
+ * with sums and the mean over the head's N x D elements, accumulated in
+ * fp64.  A reference with no spread gives +inf (0 when test == ref).  test
+ * and ref are bf16 tensors as in bsa_forward (same shape, any strides);
+ * rse is device memory, fp64 [B*H].  The workspace
+ * (bsa_output_rse_workspace_size bytes, 16-byte aligned) holds per-chunk
+ * partial sums.  Errors: INVALID_ARG, UNSUPPORTED (D not in {64, 128}),
+ * WORKSPACE.
+ *
+ * bsa_mask_jaccard: per-(b, h) Jaccard similarity |A & B| / |A | B| of two
+ * block masks given as CSR over rows (b*H + h)*n_blocks + i, n_blocks key
+ * blocks per row (SparseD, sparse reuse: the stability of the reused mask
+ * against each step's own selection).  Entries outside [0, n_blocks) are
+ * ignored, repeated entries count once, two empty masks give 1.  All
+ * arrays are device memory; jaccard is fp64 [B*H].  Errors: INVALID_ARG,
+ * UNSUPPORTED (n_blocks > 65536 or B*H > 2^31 - 1).
+ * ---------------------------------------------------------------------- */
+size_t bsa_output_rse_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D);
+bsa_status bsa_output_rse(const bsa_tensor *test, const bsa_tensor *ref, double *rse, void *workspace,
+                          size_t workspace_bytes, void *stream);
+bsa_status bsa_mask_jaccard(int64_t B, int64_t H, int32_t n_blocks, const int32_t *row_ptr_a,
+                            const int32_t *col_idx_a, const int32_t *row_ptr_b, const int32_t *col_idx_b,
+                            double *jaccard, void *stream);
+
+/* ------------------------------------------------------------------------
  * Utilities.
  * ---------------------------------------------------------------------- */
 /* Name of a status code (static string). */

@@ -255,6 +255,29 @@ def test_fp8_forward_validation():
     assert call(inp=_fp8(N=(1 << 24) + 1), o=_t(N=(1 << 24) + 1)) == 2 and "2^24" in _err()
 
 
+def test_diagnostics_validation_and_workspace():
+    lib = bsa.load()
+    # per-chunk partial sums: 3 doubles per chunk, ~64 K elements per chunk
+    assert lib.bsa_output_rse_workspace_size(1, 2, 4096, 128) == 2 * 8 * 3 * 8
+    assert lib.bsa_output_rse_workspace_size(1, 2, 10, 64) == 2 * 1 * 3 * 8
+    assert lib.bsa_output_rse_workspace_size(1, 2, 10, 96) == 0
+    need = lib.bsa_output_rse_workspace_size(1, 2, 256, 64)
+    call = lambda t=None, r=None, out=FAKE, ws=FAKE, wsb=need: lib.bsa_output_rse(
+        ctypes.byref(t or _t()), ctypes.byref(r or _t()), ctypes.c_void_p(out) if out else None,
+        ctypes.c_void_p(ws) if ws else None, wsb, None)
+    assert call(r=_t(N=128)) == 1 and "shapes differ" in _err()
+    assert call(out=0) == 1
+    assert call(wsb=need - 1) == 4 and "workspace" in _err()
+    assert call(t=_t(D=96)) == 2
+    jac = lambda B=1, H=2, nb=8, rp=FAKE, out=FAKE: lib.bsa_mask_jaccard(
+        B, H, nb, ctypes.c_void_p(rp) if rp else None, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(out) if out else None, None)
+    assert jac(nb=0) == 1
+    assert jac(rp=0) == 1 and "null" in _err()
+    assert jac(out=0) == 1
+    assert jac(nb=70000) == 2
+
+
 def test_binding_refuses_host_tensors():
     import torch
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)

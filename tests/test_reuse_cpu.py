@@ -1,0 +1,33 @@
+"""Host logic of the select-once / reuse step schedule (SparseD)."""
+import pytest
+
+import block_sparse_attention_18_amd as bsa
+
+
+def test_schedule_follows_the_skip_fraction():
+    s = bsa.ReuseSchedule(128, 0.2)        # 128 * 0.2 = 25.6 -> 25 full steps
+    assert s.n_full == 25
+    assert [s.action(i) for i in (0, 24, 25, 26, 127)] == ["full", "full", "select", "sparse", "sparse"]
+    assert s.counts() == {"full": 25, "select": 1, "sparse": 102}
+    assert bsa.ReuseSchedule(1024, 0.2).n_full == 204
+    assert bsa.ReuseSchedule(10, 0.3).n_full == 3      # 10 * 0.3 is 2.9999999999999996 in binary
+    with pytest.raises(IndexError):
+        s.action(128)
+
+
+def test_schedule_edge_cases():
+    s = bsa.ReuseSchedule(5, 0.0)
+    assert s.action(0) == "select" and s.counts() == {"full": 0, "select": 1, "sparse": 4}
+    f = bsa.ReuseSchedule(5, 1.0)
+    assert all(f.action(i) == "full" for i in range(5)) and f.counts()["select"] == 0
+    assert f.amortised_speedup(2.0, 9.0, 1.0) == pytest.approx(1.0)
+    with pytest.raises(ValueError):
+        bsa.ReuseSchedule(0)
+    with pytest.raises(ValueError):
+        bsa.ReuseSchedule(10, 1.5)
+
+
+def test_amortised_speedup():
+    s = bsa.ReuseSchedule(10, 0.2)          # 2 full, 1 select + sparse, 7 sparse
+    # 10 * 4 / (2 * 4 + (3 + 1) + 7 * 1) = 40 / 19
+    assert s.amortised_speedup(4.0, 3.0, 1.0) == pytest.approx(40 / 19)
