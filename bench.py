@@ -70,6 +70,14 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="run the forward in the FP8 (E4M3) mode on inputs quantised once "
                          "before the timed region (quantisation timed separately)")
+    ap.add_argument("--reuse", type=int, default=0, metavar="T",
+                    help="only run a T-step select-once / reuse loop (full attention for the first "
+                         "T*skip steps, one selection, then the reused mask) with RSE and Jaccard "
+                         "diagnostics, on --reuse-workload")
+    ap.add_argument("--reuse-workload", default="C5")
+    ap.add_argument("--reuse-skip", type=float, default=0.2)
+    ap.add_argument("--reuse-diag-every", type=int, default=16,
+                    help="diagnose every this many sparse steps (and the selection step)")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the kept-pairs sweep of the forward at the C4 shape "
                          "(arrow windows 0..127 and all-FULL) with a least-squares fit")
@@ -103,6 +111,9 @@ def main():
     bsa.load()
     if args.sweep:
         print(json.dumps(sweep(torch, bsa, synth, dev)), flush=True)
+        return
+    if args.reuse:
+        print(json.dumps(reuse_loop(torch, bsa, synth, dev, args)), flush=True)
         return
 
     wl = synth.WORKLOADS[args.workload]
@@ -379,6 +390,125 @@ def sweep(torch, bsa, synth, dev, windows=(0, 1, 2, 4, 8, 18, 32, 64, 127), reps
             "fit_ms": {"intercept": round(float(a), 4), "us_per_kept_pair": round(float(b) * 1e3, 6),
                        "r2": round(r2, 5)},
             "points": pts}
+
+
+def reuse_loop(torch, bsa, synth, dev, args):
+    """Select-once / reuse over T denoising steps (SparseD's schedule) on a
+    content-driven workload.  Step s runs on X_s = X + a_s Z for X = the
+    workload's Q, K, V, Z a seeded N(0, 1) drift and a_s = 0.5 (1 - s / T)
+    (inputs that change less and less from step to step); the inputs of a
+    step are formed before its timed region.  Full steps run the forward on
+    the dense block list; the selection step runs scoring + top-k + the
+    sparse forward; later steps reuse the mask.  At sampled steps the sparse
+    output is compared with full attention (per-head RSE) and the reused
+    mask with that step's own selection (per-head Jaccard); those extra
+    computations are not timed."""
+    wl = synth.WORKLOADS[args.reuse_workload]
+    if wl.layout != "select":
+        raise SystemExit("--reuse needs a content-driven (select) workload")
+    T = args.reuse
+    sched = bsa.ReuseSchedule(T, args.reuse_skip)
+    B, H, N, D, block, nB = wl.B, wl.H, wl.N, wl.D, wl.block, wl.n_blocks
+    x = synth.make_inputs(wl)
+    z = synth.random_qkv(B, H, N, D, seed=wl.seed + 1000)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    base = [d(x["q"]), d(x["k"]), d(x["v"])]
+    drift = [d(a) for a in z]
+    w = torch.from_numpy(x["w"]).to(dev) if "w" in x else None
+    del x, z
+    cur = [torch.empty_like(t) for t in base]
+
+    def set_inputs(s):
+        a = 0.5 * (1.0 - s / T)
+        for c, b0, z0 in zip(cur, base, drift):
+            torch.add(b0, z0, alpha=a, out=c)
+
+    full_modes = np.zeros(H, np.int8)
+    rp_full, ci_full = bsa.build_arrow_layout(B, H, N, block, 0, full_modes, np.zeros(H, np.int32), device=dev)
+    cap = bsa.select_capacity(B, H, nB, wl.text_blocks, wl.groups)
+    rp_s = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+    ci_s = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    rp_f = torch.empty_like(rp_s)
+    ci_f = torch.empty_like(ci_s)
+    scores = torch.empty((B, H, nB, nB), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(bsa.pool_scores_workspace_size(B, H, N, D, block, wl.score_mode,
+                                                        wl.r if w is not None else 0), 16),
+                     dtype=torch.uint8, device=dev)
+    ws_sel = torch.empty(max(int(bsa.load().bsa_select_workspace_size(B, H, nB)), 16), dtype=torch.uint8,
+                         device=dev)
+    out = torch.empty_like(cur[0])
+    out_full = torch.empty_like(cur[0])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def select(rp, ci):
+        bsa.pool_scores(cur[0], cur[1], block, wl.score_mode, w=w, out=scores, workspace=ws)
+        bsa.select_topk(scores, wl.text_blocks, wl.groups, row_ptr=rp, col_idx=ci, workspace=ws_sel)
+
+    def fwd(rp, ci, o):
+        bsa.forward(cur[0], cur[1], cur[2], block, rp, ci, out=o, lse=lse)
+
+    # warm-up of every kernel the loop uses
+    set_inputs(0)
+    select(rp_s, ci_s)
+    fwd(rp_s, ci_s, out)
+    fwd(rp_full, ci_full, out_full)
+    torch.cuda.synchronize()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+    times = {"full": [], "select": [], "sparse": []}
+    diag = []
+    for s in range(T):
+        set_inputs(s)
+        act = sched.action(s)
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        if act == "select":
+            select(rp_s, ci_s)
+        e1.record(stream)
+        if act == "full":
+            fwd(rp_full, ci_full, out)
+        else:
+            fwd(rp_s, ci_s, out)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        if act == "full":
+            times["full"].append(e0.elapsed_time(e2))
+        else:
+            times["sparse"].append(e1.elapsed_time(e2))
+            if act == "select":
+                times["select"].append(e0.elapsed_time(e1))
+        if act != "full" and (s - sched.n_full) % args.reuse_diag_every == 0 or (act == "sparse" and s == T - 1):
+            fwd(rp_full, ci_full, out_full)
+            rse = bsa.output_rse(out, out_full).cpu().numpy().reshape(-1)
+            select(rp_f, ci_f)
+            jac = bsa.mask_jaccard(B, H, nB, rp_s, ci_s, rp_f, ci_f).cpu().numpy().reshape(-1)
+            diag.append({"step": s, "rse_mean": round(float(rse.mean()), 5),
+                         "rse_max": round(float(rse.max()), 5),
+                         "jaccard_mean": round(float(jac.mean()), 4),
+                         "jaccard_min": round(float(jac.min()), 4)})
+    med = {k2: (float(np.median(v2)) if v2 else None) for k2, v2 in times.items()}
+    total = sum(sum(v2) for v2 in times.values())
+    t_full = med["full"] if med["full"] is not None else None
+    kept = int(rp_s[-1].item())
+    res = {
+        "mode": "reuse",
+        "workload": f"{wl.name}: {wl.description}",
+        "steps": T, "skip": args.reuse_skip, "schedule": sched.counts(),
+        "step_ms_median": {k2: (round(v2, 3) if v2 is not None else None) for k2, v2 in med.items()},
+        "attention_ms_total": round(total, 2),
+        "kept_fraction": round(kept / (B * H * nB * nB), 4),
+        "data": "synthetic: workload inputs plus a seeded drift that shrinks over the steps",
+    }
+    if t_full is not None and med["sparse"] is not None:
+        res["full_every_step_ms"] = round(T * t_full, 2)
+        res["amortised_speedup"] = round(sched.amortised_speedup(t_full, med["select"] or 0.0, med["sparse"]), 3)
+        res["amortised_speedup_measured"] = round(T * t_full / total, 3)
+    res["diagnostics"] = diag
+    return res
 
 
 def cpu_baseline(wl, x, row_ptr, col_idx, seconds, modes):
