@@ -18,6 +18,10 @@ Every function follows the definitions stated in ``bsa_oracle.c``:
   forward                 dense softmax restricted to the kept blocks
   quantize_fp8 / forward_fp8   E4M3 codes with max-abs scales; the forward
                           on the dequantised inputs
+  na_start / forward_neighborhood / tile_permutation / neighborhood_layout
+                          2-D neighbourhood (GNA) attention on the latent
+                          grid: window start, the masked forward, tile-major
+                          token order, block layout with full / partial flags
   output_rse              per-head relative squared error of an output
   mask_jaccard            per-head Jaccard similarity of two block masks
 """
@@ -81,6 +85,11 @@ def _load():
         lib.oracle_e4m3_decode_array.argtypes = [P, I, P]
         lib.oracle_e4m3_decode_array.restype = None
         lib.oracle_quantize_fp8.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, P]
+        lib.oracle_na_start.argtypes = [I, I, I, I]
+        lib.oracle_na_start.restype = I
+        lib.oracle_forward_neighborhood.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, D, P, I, P, P]
+        lib.oracle_tile_permutation.argtypes = [I, I, I, I, I, P]
+        lib.oracle_neighborhood_layout.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, I]
         lib.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, P, I, P, P]
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -350,3 +359,58 @@ def _widen(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# 2-D neighbourhood attention (GNA)
+# ---------------------------------------------------------------------------
+def na_start(i: int, L: int, k: int, s: int) -> int:
+    """First position of the window of position i on an axis of length L
+    (window k, stride s)."""
+    return int(_load().oracle_na_start(i, L, k, s))
+
+
+def forward_neighborhood(q, k, v, text_len: int, grid: Tuple[int, int], window: Tuple[int, int],
+                         stride: Tuple[int, int] = (1, 1), scale: Optional[float] = None,
+                         rows: Optional[Sequence[int]] = None):
+    """Softmax attention under the 2-D neighbourhood mask, natural token order
+    (text tokens, then the image grid row-major)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    (R, C), (kh, kw), (sh, sw) = grid, window, stride
+    lib = _load()
+    if rows is None:
+        O = np.empty((B, H, N, D), np.float64); L = np.empty((B, H, N), np.float64)
+        rc = lib.oracle_forward_neighborhood(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, text_len, R, C, kh, kw, sh, sw,
+                                             scale, None, 0, _ptr(O), _ptr(L))
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        O = np.empty((len(r), D), np.float64); L = np.empty((len(r),), np.float64)
+        rc = lib.oracle_forward_neighborhood(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, text_len, R, C, kh, kw, sh, sw,
+                                             scale, _ptr(r), len(r), _ptr(O), _ptr(L))
+    _check(rc, "forward_neighborhood")
+    return O, L
+
+
+def tile_permutation(text_len: int, grid: Tuple[int, int], tile: Tuple[int, int]) -> np.ndarray:
+    """perm[p] = natural index of the token at tile-major position p."""
+    (R, C), (th, tw) = grid, tile
+    perm = np.empty(text_len + R * C, np.int64)
+    _check(_load().oracle_tile_permutation(text_len, R, C, th, tw, _ptr(perm)), "tile_permutation")
+    return perm
+
+
+def neighborhood_layout(text_len: int, grid: Tuple[int, int], tile: Tuple[int, int], window: Tuple[int, int],
+                        stride: Tuple[int, int] = (1, 1)):
+    """Block layout of one head in tile-major order: (row_ptr, col_idx, flags),
+    flag 0 = every (query, key) pair of the block pair kept, 1 = some."""
+    (R, C), (th, tw), (kh, kw), (sh, sw) = grid, tile, window, stride
+    nB = (text_len + R * C) // (th * tw)
+    row_ptr = np.empty(nB + 1, np.int32)
+    col_idx = np.empty(nB * nB, np.int32)
+    flags = np.empty(nB * nB, np.uint8)
+    _check(_load().oracle_neighborhood_layout(text_len, R, C, th, tw, kh, kw, sh, sw, _ptr(row_ptr), _ptr(col_idx),
+                                              _ptr(flags), nB * nB), "neighborhood_layout")
+    n = int(row_ptr[-1])
+    return row_ptr, col_idx[:n].copy(), flags[:n].copy()

@@ -620,3 +620,160 @@ int oracle_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------
+ * Two-dimensional neighbourhood attention (GNA notes, section 1.1: a
+ * window around each query on the latent grid, with a stride by which
+ * groups of queries share one window; stride 1 is the sliding window, a
+ * stride equal to the window gives blocked attention).  Per axis of length
+ * L with window k and stride s, query position i sees the k positions from
+ *     start(i) = clamp(s * floor(i / s) + floor(s / 2) - floor(k / 2), 0, L - k),
+ * the window of the centre of i's stride group, shifted inside the axis.
+ * The sequence is text_len text tokens, then the R x C image grid in
+ * row-major order; text queries see every key and every query sees the
+ * text keys (regions involving text stay dense).
+ * ---------------------------------------------------------------------- */
+int64_t oracle_na_start(int64_t i, int64_t L, int64_t k, int64_t s)
+{
+    int64_t a = s * (i / s) + s / 2 - k / 2;
+    if (a > L - k) a = L - k;
+    if (a < 0) a = 0;
+    return a;
+}
+
+typedef struct {
+    int64_t T, R, C, kh, kw, sh, sw;
+} na_geom;
+
+/* natural-order tokens: does query tq see key tk */
+static int na_token_keep(int64_t tq, int64_t tk, const na_geom *g)
+{
+    if (tq < g->T || tk < g->T) return 1;
+    const int64_t pq = tq - g->T, pk = tk - g->T;
+    const int64_t rq = pq / g->C, cq = pq % g->C, rk = pk / g->C, ck = pk % g->C;
+    const int64_t r0 = oracle_na_start(rq, g->R, g->kh, g->sh), c0 = oracle_na_start(cq, g->C, g->kw, g->sw);
+    return rk >= r0 && rk < r0 + g->kh && ck >= c0 && ck < c0 + g->kw;
+}
+
+static int na_check(int64_t N, int64_t T, int64_t R, int64_t C, int64_t kh, int64_t kw, int64_t sh, int64_t sw)
+{
+    return T >= 0 && R > 0 && C > 0 && N == T + R * C && kh >= 1 && kh <= R && kw >= 1 && kw <= C && sh >= 1 &&
+           sw >= 1;
+}
+
+/* Dense softmax attention under the neighbourhood mask, natural token order. */
+int oracle_forward_neighborhood(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t B, int64_t H,
+                                int64_t N, int64_t D, int64_t text_len, int64_t R, int64_t C, int64_t kh,
+                                int64_t kw, int64_t sh, int64_t sw, double scale, const int64_t *rows,
+                                int64_t n_rows, double *O, double *LSE)
+{
+    if (!q || !k || !v || !O || !LSE || B <= 0 || H <= 0 || D <= 0 || !na_check(N, text_len, R, C, kh, kw, sh, sw))
+        return OR_EINVAL;
+    if (!rows) n_rows = B * H * N;
+    for (int64_t x = 0; x < n_rows; ++x) {
+        const int64_t row = rows ? rows[x] : x;
+        if (row < 0 || row >= B * H * N) return OR_EINVAL;
+    }
+    const na_geom g = {text_len, R, C, kh, kw, sh, sw};
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *z = malloc(sizeof(double) * N);
+        if (!z) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t x = 0; x < n_rows; ++x) {
+                const int64_t row = rows ? rows[x] : x;
+                const int64_t bh = row / N, t = row % N;
+                double *o = O + x * D;
+                double m = -INFINITY;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (!na_token_keep(t, s, &g)) { z[s] = -INFINITY; continue; }
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        acc += widen_bf16(q[row * D + d]) * widen_bf16(k[(bh * N + s) * D + d]);
+                    z[s] = scale * acc;
+                    if (z[s] > m) m = z[s];
+                }
+                double l = 0.0;
+                for (int64_t s = 0; s < N; ++s)
+                    if (z[s] != -INFINITY) l += exp(z[s] - m);
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (z[s] == -INFINITY) continue;
+                    const double p = exp(z[s] - m);
+                    for (int64_t d = 0; d < D; ++d) o[d] += p * widen_bf16(v[(bh * N + s) * D + d]);
+                }
+                for (int64_t d = 0; d < D; ++d) o[d] /= l;
+                LSE[x] = m + log(l);
+            }
+        }
+        free(z);
+    }
+    return rc;
+}
+
+/* Tile-major order (GNA notes, section 2.2, token permutation): text
+ * tokens first and unchanged, then the image tiles of th x tw tokens in
+ * row-major order of tiles, each tile's tokens row-major.  perm[p] is the
+ * natural index of the token at permuted position p. */
+int oracle_tile_permutation(int64_t text_len, int64_t R, int64_t C, int64_t th, int64_t tw, int64_t *perm)
+{
+    if (!perm || text_len < 0 || R <= 0 || C <= 0 || th <= 0 || tw <= 0 || R % th || C % tw) return OR_EINVAL;
+    for (int64_t t = 0; t < text_len; ++t) perm[t] = t;
+    const int64_t tpr = C / tw;
+    for (int64_t p = 0; p < R * C; ++p) {
+        const int64_t tile = p / (th * tw), o = p % (th * tw);
+        const int64_t r = (tile / tpr) * th + o / tw, c = (tile % tpr) * tw + o % tw;
+        perm[text_len + p] = text_len + r * C + c;
+    }
+    return OR_OK;
+}
+
+/* Block layout of one head in tile-major order, by brute force over token
+ * pairs: block pair (i, j) is absent when no query of block i sees a key of
+ * block j, "full" (flag 0) when every query sees every key, else "partial"
+ * (flag 1).  Blocks are th*tw tokens; text_len must be a multiple of that.
+ * Columns ascend within a row. */
+int oracle_neighborhood_layout(int64_t text_len, int64_t R, int64_t C, int64_t th, int64_t tw, int64_t kh,
+                               int64_t kw, int64_t sh, int64_t sw, int32_t *row_ptr, int32_t *col_idx,
+                               uint8_t *flags, int64_t capacity)
+{
+    const int64_t beta = th * tw, N = text_len + R * C;
+    if (!row_ptr || !col_idx || !flags || text_len % beta || !na_check(N, text_len, R, C, kh, kw, sh, sw) ||
+        R % th || C % tw)
+        return OR_EINVAL;
+    const int64_t nB = N / beta;
+    int64_t *perm = malloc(sizeof(int64_t) * N);
+    int64_t *cnt = malloc(sizeof(int64_t) * nB * nB);
+    if (!perm || !cnt) { free(perm); free(cnt); return OR_ENOMEM; }
+    oracle_tile_permutation(text_len, R, C, th, tw, perm);
+    const na_geom g = {text_len, R, C, kh, kw, sh, sw};
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nB; ++i)
+        for (int64_t j = 0; j < nB; ++j) {
+            int64_t c = 0;
+            for (int64_t a = 0; a < beta; ++a)
+                for (int64_t b = 0; b < beta; ++b) c += na_token_keep(perm[i * beta + a], perm[j * beta + b], &g);
+            cnt[i * nB + j] = c;
+        }
+    int64_t nnz = 0;
+    int rc = OR_OK;
+    row_ptr[0] = 0;
+    for (int64_t i = 0; i < nB && rc == OR_OK; ++i) {
+        for (int64_t j = 0; j < nB; ++j) {
+            const int64_t c = cnt[i * nB + j];
+            if (c == 0) continue;
+            if (nnz >= capacity) { rc = OR_ECAPACITY; break; }
+            col_idx[nnz] = (int32_t)j;
+            flags[nnz] = c == beta * beta ? 0 : 1;
+            ++nnz;
+        }
+        row_ptr[i + 1] = (int32_t)nnz;
+    }
+    free(perm);
+    free(cnt);
+    return rc;
+}
