@@ -21,6 +21,12 @@ and the FP8 (E4M3) mode of the forward:
   quantize_fp8         E4M3 codes and scales of Q, K, V
   forward_fp8          the forward on those codes (FP8 matrix cores)
 
+2-D neighbourhood (GNA) attention on the latent grid:
+
+  permute_tokens             natural <-> tile-major token order
+  build_neighborhood_layout  block list + full / partial flag per entry
+  forward_neighborhood       the forward, masking partial tiles per token
+
 diagnostics of sparse against full attention, and the step schedule of a
 mask that is selected once and reused:
 
@@ -82,6 +88,13 @@ class BsaFp8Qkv(ctypes.Structure):
                 ("N", ctypes.c_int64), ("D", ctypes.c_int64)]
 
 
+class BsaNeighborhood(ctypes.Structure):
+    _fields_ = [("text_len", ctypes.c_int64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("tile_rows", ctypes.c_int32), ("tile_cols", ctypes.c_int32),
+                ("window_rows", ctypes.c_int32), ("window_cols", ctypes.c_int32),
+                ("stride_rows", ctypes.c_int32), ("stride_cols", ctypes.c_int32)]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -117,6 +130,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_output_rse_workspace_size": (SZ, [I64, I64, I64, I64]),
             "bsa_output_rse": (I32, [TP, TP, V, V, SZ, V]),
             "bsa_mask_jaccard": (I32, [I64, I64, I32, V, V, V, V, V, V]),
+            "bsa_permute_tokens": (I32, [TP, TP, V, V, I32, ctypes.POINTER(BsaNeighborhood), I32, V]),
+            "bsa_neighborhood_capacity": (I64, [I64, I64, I32, ctypes.POINTER(BsaNeighborhood)]),
+            "bsa_build_neighborhood_layout": (I32, [I64, I64, I32, ctypes.POINTER(BsaNeighborhood), V, V, V, I64,
+                                                    V]),
+            "bsa_forward_neighborhood": (I32, [TP, TP, TP, I32, V, V, V, ctypes.POINTER(BsaNeighborhood), F, TP, V,
+                                               ctypes.POINTER(BsaSplit), V]),
             "bsa_status_string": (ctypes.c_char_p, [I32]),
             "bsa_last_error": (ctypes.c_char_p, []),
             "bsa_version": (ctypes.c_char_p, []),
@@ -486,6 +505,92 @@ def forward_fp8(qkv: Fp8QKV, block: int, row_ptr: torch.Tensor, col_idx: torch.T
     d8, do = qkv.desc(), _desc(out, "out")
     _check(lib.bsa_forward_fp8(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx), float(scale or 0.0),
                                ctypes.byref(do), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def neighborhood(text_len: int, grid: Tuple[int, int], tile: Tuple[int, int], window: Tuple[int, int],
+                 stride: Tuple[int, int] = (1, 1)) -> BsaNeighborhood:
+    """Geometry of 2-D neighbourhood attention: text_len text tokens, then a
+    grid = (rows, cols) image in row-major order, cut into tile = (tile_rows,
+    tile_cols) tiles of one block each; window and stride per axis."""
+    return BsaNeighborhood(int(text_len), int(grid[0]), int(grid[1]), int(tile[0]), int(tile[1]),
+                           int(window[0]), int(window[1]), int(stride[0]), int(stride[1]))
+
+
+def permute_tokens(x: torch.Tensor, nb: BsaNeighborhood, inverse: bool = False,
+                   lse: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   lse_out: Optional[torch.Tensor] = None):
+    """Natural -> tile-major token order (inverse: back).  Returns out, or
+    (out, lse_out) when lse is given."""
+    lib = load()
+    if out is None:
+        out = torch.empty_like(x)
+    if lse is not None and lse_out is None:
+        lse_out = torch.empty_like(lse)
+    for name, t in (("lse", lse), ("lse_out", lse_out)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 [B, H, N] tensor")
+    block = nb.tile_rows * nb.tile_cols
+    di, do = _desc(x, "in"), _desc(out, "out")
+    _check(lib.bsa_permute_tokens(ctypes.byref(di), ctypes.byref(do), _ptr(lse), _ptr(lse_out), block,
+                                  ctypes.byref(nb), 1 if inverse else 0, _stream(x.device)))
+    return out if lse is None else (out, lse_out)
+
+
+def neighborhood_capacity(B: int, H: int, nb: BsaNeighborhood) -> int:
+    return int(load().bsa_neighborhood_capacity(B, H, nb.tile_rows * nb.tile_cols, ctypes.byref(nb)))
+
+
+def build_neighborhood_layout(B: int, H: int, nb: BsaNeighborhood, device=None):
+    """(row_ptr, col_idx, entry_flags) int32 device tensors of the tile-major
+    block list; flag 1 marks a partially covered key tile."""
+    lib = load()
+    dev = device or torch.device("cuda")
+    cap = neighborhood_capacity(B, H, nb)
+    if cap < 0:
+        _check(lib.bsa_build_neighborhood_layout(B, H, nb.tile_rows * nb.tile_cols, ctypes.byref(nb), None, None,
+                                                 None, 0, None))
+    block = nb.tile_rows * nb.tile_cols
+    nB = (nb.text_len + nb.rows * nb.cols) // block
+    row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    flags = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    _check(lib.bsa_build_neighborhood_layout(B, H, block, ctypes.byref(nb), _ptr(row_ptr), _ptr(col_idx),
+                                             _ptr(flags), cap, _stream(dev)))
+    return row_ptr, col_idx, flags
+
+
+def forward_neighborhood(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                         col_idx: torch.Tensor, entry_flags: torch.Tensor, nb: BsaNeighborhood,
+                         scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                         split: Optional[dict] = None):
+    """Block-sparse forward on tile-major Q, K, V, masking the partially
+    covered key tiles per token.  Returns (O, LSE) in tile-major order."""
+    lib = load()
+    B, H, N, D = q.shape
+    block = nb.tile_rows * nb.tile_cols
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx), ("entry_flags", entry_flags)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    sp = None
+    if split is not None:
+        ws = split.get("workspace")
+        if ws is None:
+            need = split_workspace_size(B, H, N, D, block, split["max_chunks"], split["max_split_rows"])
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+            split["workspace"] = ws
+        sp = BsaSplit(int(split["chunk_blocks"]), int(split["max_chunks"]), int(split["max_split_rows"]),
+                      ws.data_ptr(), ws.numel() * ws.element_size())
+    dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
+    _check(lib.bsa_forward_neighborhood(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), block, _ptr(row_ptr),
+                                        _ptr(col_idx), _ptr(entry_flags), ctypes.byref(nb), float(scale or 0.0),
+                                        ctypes.byref(do), _ptr(lse), None if sp is None else ctypes.byref(sp),
+                                        _stream(q.device)))
     return out, lse
 
 

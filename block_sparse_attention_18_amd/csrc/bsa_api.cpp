@@ -385,10 +385,11 @@ size_t bsa_forward_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t
     return split_layout(rows, block, D, max_chunks, std::min(max_split_rows, rows)).total;
 }
 
-bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,
-                       const int32_t *row_ptr, const int32_t *col_idx, const int8_t *head_modes,
-                       const bsa_tensor *o_cache, const float *lse_cache, float scale,
-                       const bsa_tensor *o, float *lse, const bsa_split *split, void *stream)
+static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,
+                               const int32_t *row_ptr, const int32_t *col_idx, const int8_t *head_modes,
+                               const bsa_tensor *o_cache, const float *lse_cache, float scale,
+                               const bsa_tensor *o, float *lse, const bsa_split *split, void *stream,
+                               const int32_t *entry_flags, const bsa::NbGeom *nb)
 {
     bsa_status st;
     if ((st = check_tensor(q, "q")) != BSA_OK) return st;
@@ -426,6 +427,8 @@ bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tenso
     fp.q = t4(q);
     fp.k = t4(k);
     fp.v = t4(v);
+    fp.flags = entry_flags;
+    if (nb) fp.nb = *nb;
     fp.o = static_cast<uint16_t *>(o->data);
     fp.o_sb = o->stride_b;
     fp.o_sh = o->stride_h;
@@ -518,6 +521,146 @@ bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tenso
             if ((e = bsa::launch_skip_copy(cp, s)) != hipSuccess) return hip_fail(e, "skip copy launch");
     }
     return BSA_OK;
+}
+
+bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,
+                       const int32_t *row_ptr, const int32_t *col_idx, const int8_t *head_modes,
+                       const bsa_tensor *o_cache, const float *lse_cache, float scale,
+                       const bsa_tensor *o, float *lse, const bsa_split *split, void *stream)
+{
+    return forward_impl(q, k, v, block, row_ptr, col_idx, head_modes, o_cache, lse_cache, scale, o, lse, split,
+                        stream, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// 2-D neighbourhood attention
+// ---------------------------------------------------------------------------
+static bsa_status check_nb(const bsa_neighborhood *g, int64_t N, int32_t block, bsa::NbGeom *out)
+{
+    if (!g) return fail(BSA_ERR_INVALID_ARG, "neighborhood: null descriptor");
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    if (g->rows <= 0 || g->cols <= 0 || g->tile_rows <= 0 || g->tile_cols <= 0 || g->text_len < 0)
+        return fail(BSA_ERR_INVALID_ARG, "neighborhood: grid and tile must be positive");
+    if ((int64_t)g->tile_rows * g->tile_cols != block || (g->tile_cols & (g->tile_cols - 1)))
+        return fail(BSA_ERR_INVALID_ARG, "neighborhood: tile_rows * tile_cols must equal the block, tile_cols a power of two");
+    if (g->rows % g->tile_rows || g->cols % g->tile_cols || g->text_len % block)
+        return fail(BSA_ERR_INVALID_ARG, "neighborhood: grid not a whole number of tiles, or text_len not a whole number of blocks");
+    if (g->text_len + (int64_t)g->rows * g->cols != N)
+        return fail(BSA_ERR_INVALID_ARG, "neighborhood: text_len + rows * cols must equal N");
+    if (g->window_rows < 1 || g->window_rows > g->rows || g->window_cols < 1 || g->window_cols > g->cols ||
+        g->stride_rows < 1 || g->stride_cols < 1)
+        return fail(BSA_ERR_INVALID_ARG, "neighborhood: window must lie in 1..grid and strides be >= 1");
+    if (N / block > 65536) return fail(BSA_ERR_UNSUPPORTED, "neighborhood: more than 65536 blocks");
+    bsa::NbGeom x{};
+    x.T = (int32_t)g->text_len;
+    x.Tb = (int32_t)(g->text_len / block);
+    x.R = g->rows;
+    x.C = g->cols;
+    x.th = g->tile_rows;
+    x.tw = g->tile_cols;
+    x.tw_log2 = 0;
+    while ((1 << x.tw_log2) < x.tw) ++x.tw_log2;
+    x.tpr = g->cols / g->tile_cols;
+    x.kh = g->window_rows;
+    x.kw = g->window_cols;
+    x.sh = g->stride_rows;
+    x.sw = g->stride_cols;
+    *out = x;
+    return BSA_OK;
+}
+
+static int64_t nb_head_nnz(const bsa::NbGeom &g, int32_t nB)
+{
+    int64_t n = 0;
+    for (int32_t i = 0; i < nB; ++i) n += bsa::nb_row_len(g, nB, i);
+    return n;
+}
+
+int64_t bsa_neighborhood_capacity(int64_t B, int64_t H, int32_t block, const bsa_neighborhood *nb)
+{
+    if (B <= 0 || H <= 0 || !nb) return -1;
+    bsa::NbGeom g;
+    const int64_t N = nb->text_len + (int64_t)nb->rows * nb->cols;
+    if (check_nb(nb, N, block, &g) != BSA_OK) return -1;
+    return B * H * nb_head_nnz(g, (int32_t)(N / block));
+}
+
+bsa_status bsa_build_neighborhood_layout(int64_t B, int64_t H, int32_t block, const bsa_neighborhood *nb,
+                                         int32_t *row_ptr, int32_t *col_idx, int32_t *entry_flags,
+                                         int64_t capacity, void *stream)
+{
+    if (B <= 0 || H <= 0) return fail(BSA_ERR_INVALID_ARG, "B and H must be positive");
+    if (!nb) return fail(BSA_ERR_INVALID_ARG, "neighborhood: null descriptor");
+    bsa::NbGeom g;
+    bsa_status st;
+    const int64_t N = nb->text_len + (int64_t)nb->rows * nb->cols;
+    if ((st = check_nb(nb, N, block, &g)) != BSA_OK) return st;
+    if (!row_ptr || !col_idx || !entry_flags) return fail(BSA_ERR_INVALID_ARG, "row_ptr / col_idx / entry_flags null");
+    const int32_t nB = (int32_t)(N / block);
+    const int64_t per_head = nb_head_nnz(g, nB);
+    if (B * H * nB >= (1ll << 31) || B * H * per_head >= (1ll << 31))
+        return fail(BSA_ERR_UNSUPPORTED, "layout too large for int32 indices");
+    if (capacity < B * H * per_head)
+        return fail(BSA_ERR_CAPACITY, "capacity %lld below %lld", (long long)capacity, (long long)(B * H * per_head));
+    bsa::NbLayoutParams p{};
+    p.nb = g;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.flags = entry_flags;
+    p.capacity = capacity;
+    p.per_head = per_head;
+    p.B = (int32_t)B;
+    p.H = (int32_t)H;
+    p.nB = nB;
+    hipError_t e = bsa::launch_neighborhood_layout(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "neighborhood layout launch");
+    return BSA_OK;
+}
+
+bsa_status bsa_permute_tokens(const bsa_tensor *in, const bsa_tensor *out, const float *lse_in, float *lse_out,
+                              int32_t block, const bsa_neighborhood *nb, int32_t inverse, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(in, "in")) != BSA_OK) return st;
+    if ((st = check_tensor(out, "out")) != BSA_OK) return st;
+    if (!same_shape(in, out)) return fail(BSA_ERR_INVALID_ARG, "in and out shapes differ");
+    if (in->data == out->data) return fail(BSA_ERR_INVALID_ARG, "permutation cannot run in place");
+    if ((lse_in == nullptr) != (lse_out == nullptr) || (lse_in && lse_in == lse_out))
+        return fail(BSA_ERR_INVALID_ARG, "lse_in and lse_out: both or neither, distinct");
+    bsa::NbGeom g;
+    if ((st = check_nb(nb, in->N, block, &g)) != BSA_OK) return st;
+    bsa::PermuteParams p{};
+    p.in = t4(in);
+    p.out = static_cast<uint16_t *>(out->data);
+    p.o_sb = out->stride_b;
+    p.o_sh = out->stride_h;
+    p.o_sn = out->stride_n;
+    p.lse_in = lse_in;
+    p.lse_out = lse_out;
+    p.nb = g;
+    p.B = (int32_t)in->B;
+    p.H = (int32_t)in->H;
+    p.N = (int32_t)in->N;
+    p.D = (int32_t)in->D;
+    p.inverse = inverse ? 1 : 0;
+    if (in->B * in->H > 65535) return fail(BSA_ERR_UNSUPPORTED, "B*H above 65535");
+    hipError_t e = bsa::launch_permute_tokens(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    return BSA_OK;
+}
+
+bsa_status bsa_forward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,
+                                    const int32_t *row_ptr, const int32_t *col_idx, const int32_t *entry_flags,
+                                    const bsa_neighborhood *nb, float scale, const bsa_tensor *o, float *lse,
+                                    const bsa_split *split, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if (!entry_flags) return fail(BSA_ERR_INVALID_ARG, "entry_flags null");
+    bsa::NbGeom g;
+    if ((st = check_nb(nb, q->N, block, &g)) != BSA_OK) return st;
+    return forward_impl(q, k, v, block, row_ptr, col_idx, nullptr, nullptr, nullptr, scale, o, lse, split, stream,
+                        entry_flags, &g);
 }
 
 // ---------------------------------------------------------------------------

@@ -225,8 +225,35 @@ __device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_b
     }
 }
 
+// 2-D neighbourhood masking of a partially covered key tile: the score of
+// (query, key) survives when the key's grid position lies in the query's
+// window.  Text queries and text keys are never masked.
+template <int BETA, int D>
+__device__ __forceinline__ void mask_window(const FwdParams &p, int k0, int qrow, int lane, f32x16 (&sacc)[2])
+{
+    const NbGeom &g = p.nb;
+    const int j = k0 / BETA;
+    if (j < g.Tb || qrow < g.T || qrow >= p.N) return;
+    const int pq = qrow - g.T, tq = pq / BETA, oq = pq - tq * BETA;
+    const int aq = tq / g.tpr;
+    const int rq = aq * g.th + (oq >> g.tw_log2), cq = (tq - aq * g.tpr) * g.tw + (oq & (g.tw - 1));
+    const int rs = nb_start(rq, g.R, g.kh, g.sh), cs = nb_start(cq, g.C, g.kw, g.sw);
+    const int tk = j - g.Tb, ak = tk / g.tpr;
+    const int kr0 = ak * g.th - rs, kc0 = (tk - ak * g.tpr) * g.tw - cs;
+    const int o0 = (k0 - j * BETA) + 8 * (lane >> 5);   // key offset in the tile of register 0
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int o = o0 + kt * 32 + koff(r);
+            const int dr = kr0 + (o >> g.tw_log2), dc = kc0 + (o & (g.tw - 1));
+            if ((unsigned)dr >= (unsigned)g.kh || (unsigned)dc >= (unsigned)g.kw) sacc[kt][r] = -INFINITY;
+        }
+}
+
 // Scores of a sub-tile whose block index is invalid, or of keys past N in
-// the last tile, are masked out.
+// the last tile, are masked out; so are those outside the windows in a
+// partially covered tile of a neighbourhood layout.
 template <int BETA, int D>
 __device__ __forceinline__ void mask_scores(bool valid, int k0, int N, int lane, f32x16 (&sacc)[2])
 {
@@ -241,17 +268,18 @@ __device__ __forceinline__ void mask_scores(bool valid, int k0, int N, int lane,
 //   B: PV(t-1), keys 0..31   with probabilities of keys 48..63 of t-1
 //   C: PV(t-1), keys 32..63  with the row max of t
 // then the lazy rescale for t.  t's scores are masked at the next step.
-template <int BETA, int D>
+template <int BETA, int D, bool NBM>
 __device__ __forceinline__ void fused_step(
     const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vp, uint16_t *__restrict__ Kn,
     uint16_t *__restrict__ Vn, bool valid, int k0, bool valid_p, int k0_p, bool load_k, int k0_k,
     __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const FwdParams &p, int wv, int lane,
-    WaveState<BETA, D> &st, f32x16 (&s_cur)[2], f32x16 (&s_prev)[2])
+    WaveState<BETA, D> &st, f32x16 (&s_cur)[2], f32x16 (&s_prev)[2], bool partial_p, int qrow)
 {
     using Sh = FwdShape<BETA, D>;
     // masking of t-1's scores first: a branch here does not split the
     // scheduled regions, and t's scores are not live yet
     mask_scores<BETA, D>(valid_p, k0_p, p.N, lane, s_prev);
+    if (NBM && partial_p) mask_window<BETA, D>(p, k0_p, qrow, lane, s_prev);
     if (load_k) load_tile<BETA, D>(Kn, krs, p.k.sn, st.kdma, false, p, k0_k, wv, lane);
     load_tile<BETA, D>(Vn, vrs, p.v.sn, st.vdma, true, p, k0, wv, lane);
     const float c = p.scale_log2;
@@ -292,12 +320,13 @@ __device__ __forceinline__ void first_step(
 }
 
 // Last step: softmax and O update of the last sub-tile.
-template <int BETA, int D>
+template <int BETA, int D, bool NBM>
 __device__ __forceinline__ void last_step(const uint16_t *__restrict__ Vp, bool valid_p, int k0_p,
                                           const FwdParams &p, int lane, WaveState<BETA, D> &st,
-                                          f32x16 (&s_prev)[2])
+                                          f32x16 (&s_prev)[2], bool partial_p, int qrow)
 {
     mask_scores<BETA, D>(valid_p, k0_p, p.N, lane, s_prev);
+    if (NBM && partial_p) mask_window<BETA, D>(p, k0_p, qrow, lane, s_prev);
     bf16x8 pf[2][2];
     softmax_probs<BETA, D>(s_prev, p.scale_log2, st, pf);
     pv_mfma<BETA, D>(Vp, pf, st);
@@ -308,7 +337,8 @@ __device__ __forceinline__ void last_step(const uint16_t *__restrict__ Vp, bool 
 template <int BETA, int D>
 constexpr int fwd_min_blocks() { return BETA == 128 ? 2 : (D == 64 ? 4 : 2); }
 
-template <int BETA, int D>
+// NBM: neighbourhood masking of the tiles the layout flags as partial.
+template <int BETA, int D, bool NBM>
 __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void fwd_kernel(const FwdParams p)
 {
     using Sh = FwdShape<BETA, D>;
@@ -388,6 +418,10 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
         valid = (unsigned)j < (unsigned)p.nB;
         return (valid ? j * BETA : 0) + 64 * (t % Sh::SUB);
     };
+    // neighbourhood layouts: per-entry flag of a partially covered key tile
+    const __attribute__((address_space(4))) int32_t *cflag =
+        (const __attribute__((address_space(4))) int32_t *)(NBM ? p.flags + e0 : p.col_idx + e0);
+    auto tile_partial = [&](int t, bool valid) { return NBM && valid && cflag[t / Sh::SUB] != 0; };
 
     // Step t computes S^T of sub-tile t and finishes sub-tile t-1.  K(t) sits
     // in K[t&1], V(t) in V[t&1]; step t copies K(t+1) and V(t), so a V tile
@@ -402,34 +436,41 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
         bool v_cur = false, v_nxt = false, v_prv;
         int k_cur = tile_key0(0, v_cur), k_nxt = 0, k_prv;
         if (T > 1) k_nxt = tile_key0(1, v_nxt);
+        bool f_cur = tile_partial(0, v_cur), f_nxt = T > 1 && tile_partial(1, v_nxt), f_prv;
         load_tile<BETA, D>(K0, krs, p.k.sn, st.kdma, false, p, k_cur, wv, lane);
         __syncthreads();   // Q in registers; K(0) in LDS
         first_step<BETA, D>(K0, K1, V0, v_cur, k_cur, T > 1, k_nxt, krs, vrs, p, wv, lane, st, sa);
         __syncthreads();
-        v_prv = v_cur; k_prv = k_cur;
-        v_cur = v_nxt; k_cur = k_nxt;
+        v_prv = v_cur; k_prv = k_cur; f_prv = f_cur;
+        v_cur = v_nxt; k_cur = k_nxt; f_cur = f_nxt;
         for (int t = 1; t < T; t += 2) {
             // odd step t: K(t) in K1, V(t-1) in V0; copies K(t+1) -> K0, V(t) -> V1
-            v_nxt = false; k_nxt = 0;
-            if (t + 1 < T) k_nxt = tile_key0(t + 1, v_nxt);
-            fused_step<BETA, D>(K1, V0, K0, V1, v_cur, k_cur, v_prv, k_prv, t + 1 < T, k_nxt, krs, vrs, p, wv,
-                                lane, st, sb, sa);
+            v_nxt = false; k_nxt = 0; f_nxt = false;
+            if (t + 1 < T) {
+                k_nxt = tile_key0(t + 1, v_nxt);
+                f_nxt = tile_partial(t + 1, v_nxt);
+            }
+            fused_step<BETA, D, NBM>(K1, V0, K0, V1, v_cur, k_cur, v_prv, k_prv, t + 1 < T, k_nxt, krs, vrs, p, wv,
+                                lane, st, sb, sa, f_prv, qrow);
             __syncthreads();
-            v_prv = v_cur; k_prv = k_cur;
-            v_cur = v_nxt; k_cur = k_nxt;
+            v_prv = v_cur; k_prv = k_cur; f_prv = f_cur;
+            v_cur = v_nxt; k_cur = k_nxt; f_cur = f_nxt;
             if (t + 1 >= T) break;
             // even step t+1: K(t+1) in K0, V(t) in V1; copies K(t+2) -> K1, V(t+1) -> V0
-            v_nxt = false; k_nxt = 0;
-            if (t + 2 < T) k_nxt = tile_key0(t + 2, v_nxt);
-            fused_step<BETA, D>(K0, V1, K1, V0, v_cur, k_cur, v_prv, k_prv, t + 2 < T, k_nxt, krs, vrs, p, wv,
-                                lane, st, sa, sb);
+            v_nxt = false; k_nxt = 0; f_nxt = false;
+            if (t + 2 < T) {
+                k_nxt = tile_key0(t + 2, v_nxt);
+                f_nxt = tile_partial(t + 2, v_nxt);
+            }
+            fused_step<BETA, D, NBM>(K0, V1, K1, V0, v_cur, k_cur, v_prv, k_prv, t + 2 < T, k_nxt, krs, vrs, p, wv,
+                                lane, st, sa, sb, f_prv, qrow);
             __syncthreads();
-            v_prv = v_cur; k_prv = k_cur;
-            v_cur = v_nxt; k_cur = k_nxt;
+            v_prv = v_cur; k_prv = k_cur; f_prv = f_cur;
+            v_cur = v_nxt; k_cur = k_nxt; f_cur = f_nxt;
         }
         // finish sub-tile T-1 (V(T-1) in V[(T-1)&1])
-        if (T & 1) last_step<BETA, D>(V0, v_prv, k_prv, p, lane, st, sa);
-        else last_step<BETA, D>(V1, v_prv, k_prv, p, lane, st, sb);
+        if (T & 1) last_step<BETA, D, NBM>(V0, v_prv, k_prv, p, lane, st, sa, f_prv, qrow);
+        else last_step<BETA, D, NBM>(V1, v_prv, k_prv, p, lane, st, sb, f_prv, qrow);
     }
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
@@ -476,8 +517,10 @@ static hipError_t launch_fwd_t(const FwdParams &p, int64_t grid, hipStream_t s)
 {
     using Sh = FwdShape<BETA, D>;
     if (grid == 0) return hipSuccess;
-    auto kern = fwd_kernel<BETA, D>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
+    if (p.flags)
+        hipLaunchKernelGGL((fwd_kernel<BETA, D, true>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<BETA, D, false>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
     return hipGetLastError();
 }
 

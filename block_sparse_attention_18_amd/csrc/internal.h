@@ -18,6 +18,55 @@ struct Tensor4 {
     int64_t sb, sh, sn;
 };
 
+// Geometry of 2-D neighbourhood attention in tile-major token order: T text
+// tokens (Tb blocks), then an R x C image grid cut into th x tw tiles (one
+// block each, tw a power of two, tpr tiles per tile row), window kh x kw,
+// stride sh x sw.
+struct NbGeom {
+    int32_t T, Tb, R, C, th, tw, tw_log2, tpr, kh, kw, sh, sw;
+};
+
+// First position of the window of position i on an axis of length L
+// (window k, stride s): the window of the centre of i's stride group,
+// shifted inside the axis.
+__host__ __device__ inline int32_t nb_start(int32_t i, int32_t L, int32_t k, int32_t s)
+{
+    const int32_t a = s * (i / s) + s / 2 - k / 2;
+    return a < 0 ? 0 : (a > L - k ? L - k : a);
+}
+
+// Image query tile i (i >= Tb): the key tile ranges its queries' windows
+// touch ([r0, r1) x [c0, c1) in tiles) and the token ranges every one of
+// its queries sees ([ir0, ir1) x [ic0, ic1), possibly empty).
+struct NbRow {
+    int32_t r0, r1, c0, c1, ir0, ir1, ic0, ic1;
+};
+
+__host__ __device__ inline NbRow nb_row(const NbGeom &g, int32_t i)
+{
+    const int32_t tile = i - g.Tb, a = tile / g.tpr, b = tile - a * g.tpr;
+    const int32_t q0 = a * g.th, q1 = q0 + g.th - 1, p0 = b * g.tw, p1 = p0 + g.tw - 1;
+    NbRow w;
+    const int32_t ur0 = nb_start(q0, g.R, g.kh, g.sh), ur1 = nb_start(q1, g.R, g.kh, g.sh) + g.kh;
+    const int32_t uc0 = nb_start(p0, g.C, g.kw, g.sw), uc1 = nb_start(p1, g.C, g.kw, g.sw) + g.kw;
+    w.r0 = ur0 / g.th;
+    w.r1 = (ur1 + g.th - 1) / g.th;
+    w.c0 = uc0 / g.tw;
+    w.c1 = (uc1 + g.tw - 1) / g.tw;
+    w.ir0 = nb_start(q1, g.R, g.kh, g.sh);
+    w.ir1 = nb_start(q0, g.R, g.kh, g.sh) + g.kh;
+    w.ic0 = nb_start(p1, g.C, g.kw, g.sw);
+    w.ic1 = nb_start(p0, g.C, g.kw, g.sw) + g.kw;
+    return w;
+}
+
+__host__ __device__ inline int64_t nb_row_len(const NbGeom &g, int32_t nB, int32_t i)
+{
+    if (i < g.Tb) return nB;
+    const NbRow w = nb_row(g, i);
+    return (int64_t)g.Tb + (int64_t)(w.r1 - w.r0) * (w.c1 - w.c0);
+}
+
 struct FwdParams {
     Tensor4 q, k, v;
     uint16_t *o;
@@ -33,6 +82,29 @@ struct FwdParams {
     const int32_t *counts;      // [0] items, [1] split rows
     float *partials;            // [split rank * max_chunks + chunk] slots
     int32_t max_chunks;
+    // 2-D neighbourhood masking (flags == null: none): per CSR entry 0 = every
+    // (query, key) pair of the block pair kept, 1 = masked per token
+    const int32_t *flags;
+    NbGeom nb;
+};
+
+// Tile-major token permutation (see bsa_permute_tokens).
+struct PermuteParams {
+    Tensor4 in;
+    uint16_t *out;
+    int64_t o_sb, o_sh, o_sn;
+    const float *lse_in;
+    float *lse_out;
+    NbGeom nb;
+    int32_t B, H, N, D, inverse;
+};
+
+// 2-D neighbourhood block layout (see bsa_build_neighborhood_layout).
+struct NbLayoutParams {
+    NbGeom nb;
+    int32_t *row_ptr, *col_idx, *flags;
+    int64_t capacity, per_head;  // per_head: entries of one head
+    int32_t B, H, nB;
 };
 
 // Work-list builder for long-row splitting.
@@ -159,6 +231,8 @@ struct JaccardParams {
 
 hipError_t launch_forward(const FwdParams &p, int block, int D, int64_t grid, hipStream_t s);
 hipError_t launch_output_rse(const RseParams &p, hipStream_t s);
+hipError_t launch_permute_tokens(const PermuteParams &p, hipStream_t s);
+hipError_t launch_neighborhood_layout(const NbLayoutParams &p, hipStream_t s);
 hipError_t launch_mask_jaccard(const JaccardParams &p, hipStream_t s);
 hipError_t launch_quantize_fp8(const Fp8QuantParams &p, int D, hipStream_t s);
 hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, hipStream_t s);

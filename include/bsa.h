@@ -213,6 +213,63 @@ bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tenso
                        const bsa_split *split, void *stream);
 
 /* ------------------------------------------------------------------------
+ * 2-D neighbourhood attention (GNA notes, 1.1: a window around each query
+ * on the latent grid with a stride by which groups of queries share one
+ * window; 2.1: fine-grained masking only where a key tile is partially
+ * inside the windows; 2.2: token permutation into tiles).
+ *
+ * The sequence is text_len text tokens, then an rows x cols image grid in
+ * row-major ("natural") order.  Text queries see every key and every query
+ * sees the text keys.  On an axis of length L with window k and stride s,
+ * the image query at position i sees positions
+ *     start(i) .. start(i) + k - 1,
+ *     start(i) = clamp(s * floor(i / s) + floor(s / 2) - floor(k / 2), 0, L - k),
+ * on both axes (s = 1: a sliding window; s = k: blocked attention).
+ *
+ * Kernels work in tile-major order: text tokens first, then the image cut
+ * into tile_rows x tile_cols tiles (tile_rows * tile_cols = block,
+ * tile_cols a power of two), tiles row-major, tokens row-major within a
+ * tile, so each block is one tile.  text_len must be a whole number of
+ * blocks and the grid a whole number of tiles; N = text_len + rows * cols.
+ *
+ * bsa_permute_tokens moves a bf16 [B][H][N][D] tensor (and optionally an
+ * fp32 [B][H][N] LSE) from natural to tile-major order, or back when
+ * inverse != 0 (for O and LSE); not in place.
+ *
+ * bsa_build_neighborhood_layout writes the CSR block list of every
+ * (b, h) (all heads alike) in tile-major order plus a flag per entry:
+ * 0 = every query of the query tile sees every key of the key tile,
+ * 1 = partially covered, masked per token by the forward.  Columns ascend.
+ * capacity >= bsa_neighborhood_capacity() entries (-1 on a bad geometry).
+ *
+ * bsa_forward_neighborhood: bsa_forward (every head computed, no head
+ * modes) on tile-major Q, K, V with that block list and its flags; O and
+ * LSE come out in tile-major order.  The row max of a partial tile is taken
+ * over all its keys (an upper bound of the kept ones): the result is exact
+ * unless masked logits exceed every kept one by more than ~87 (natural
+ * units), where the kept probabilities would underflow.
+ * Errors: INVALID_ARG (geometry, shapes, nulls), UNSUPPORTED, CAPACITY.
+ * ---------------------------------------------------------------------- */
+typedef struct bsa_neighborhood {
+    int64_t text_len;
+    int32_t rows, cols;
+    int32_t tile_rows, tile_cols;
+    int32_t window_rows, window_cols;
+    int32_t stride_rows, stride_cols;
+} bsa_neighborhood;
+
+bsa_status bsa_permute_tokens(const bsa_tensor *in, const bsa_tensor *out, const float *lse_in, float *lse_out,
+                              int32_t block, const bsa_neighborhood *nb, int32_t inverse, void *stream);
+int64_t bsa_neighborhood_capacity(int64_t B, int64_t H, int32_t block, const bsa_neighborhood *nb);
+bsa_status bsa_build_neighborhood_layout(int64_t B, int64_t H, int32_t block, const bsa_neighborhood *nb,
+                                         int32_t *row_ptr, int32_t *col_idx, int32_t *entry_flags,
+                                         int64_t capacity, void *stream);
+bsa_status bsa_forward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,
+                                    const int32_t *row_ptr, const int32_t *col_idx, const int32_t *entry_flags,
+                                    const bsa_neighborhood *nb, float scale, const bsa_tensor *o, float *lse,
+                                    const bsa_split *split, void *stream);
+
+/* ------------------------------------------------------------------------
  * FP8 forward (OCP E4M3 operands on the gfx950 FP8 matrix cores).
  *
  * The same operation as bsa_forward -- the dense softmax restricted to the

@@ -72,13 +72,17 @@ class Workload:
     D: int
     block: int
     text_len: int
-    layout: str                     # "select" or "arrow"
+    layout: str                     # "select", "arrow" or "neighborhood"
     seed: int
     score_mode: int = SCORE_MEANPOOL_PROJ
     r: int = 32                     # projection width (meanpool mode)
     groups: Tuple[Tuple[int, int, int], ...] = ()   # (col_begin, col_end, k)
     arrow_counts: Tuple[int, int, int] = (0, 0, 0)  # (#arrow, #full, #skip) heads
     arrow_window: int = 0
+    nb_grid: Tuple[int, int] = (0, 0)      # neighbourhood: image grid (rows, cols)
+    nb_tile: Tuple[int, int] = (0, 0)      # tile (rows, cols), one block each
+    nb_window: Tuple[int, int] = (0, 0)
+    nb_stride: Tuple[int, int] = (1, 1)
     structure: str = "none"
     description: str = ""
 
@@ -122,6 +126,14 @@ WORKLOADS = {
         structure="dlm",
         description="64k bidirectional diffusion LM: exact avgpool scores, "
                     "top-30% prefill and generation columns"),
+    # 2-D neighbourhood attention (GNA) on the FLUX.1 2048^2 shape: window
+    # side a quarter of the 128 x 128 latent grid, 8 x 16 tiles of one block
+    "G1": Workload(
+        name="G1", B=1, H=24, N=16896, D=128, block=128, text_len=512, layout="neighborhood",
+        seed=6, nb_grid=(128, 128), nb_tile=(8, 16), nb_window=(32, 32), nb_stride=(1, 1),
+        structure="pos2d",
+        description="2K MMDiT, FLUX.1 2048^2: 512 text + 128x128 image, 2-D neighbourhood window "
+                    "32x32 (GNA), 8x16 tiles"),
 }
 
 

@@ -278,6 +278,53 @@ def test_diagnostics_validation_and_workspace():
     assert jac(nb=70000) == 2
 
 
+@pytest.mark.parametrize("T,grid,tile,window,stride", [
+    (512, (128, 128), (8, 16), (32, 32), (1, 1)),
+    (128, (32, 64), (8, 16), (9, 17), (3, 4)),
+    (0, (16, 32), (4, 16), (16, 32), (16, 32)),
+    (64, (24, 40), (8, 8), (8, 16), (8, 16)),
+])
+def test_neighborhood_capacity_matches_oracle_layout(T, grid, tile, window, stride):
+    """The host's closed-form entry count of the neighbourhood layout equals the
+    nnz of the oracle's brute-force layout."""
+    import oracle
+    lib = bsa.load()
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    rp, ci, fl = oracle.neighborhood_layout(T, grid, tile, window, stride)
+    block = tile[0] * tile[1]
+    assert lib.bsa_neighborhood_capacity(2, 3, block, ctypes.byref(nb)) == 6 * int(rp[-1])
+
+
+def test_neighborhood_validation():
+    lib = bsa.load()
+    cap = lambda **kw: lib.bsa_neighborhood_capacity(1, 1, 128, ctypes.byref(bsa.neighborhood(
+        kw.get("T", 512), kw.get("grid", (128, 128)), kw.get("tile", (8, 16)), kw.get("window", (32, 32)),
+        kw.get("stride", (1, 1)))))
+    assert cap() > 0
+    assert cap(tile=(8, 8)) == -1            # 64 tokens: not the block
+    assert cap(tile=(16, 8), grid=(128, 120)) > 0   # any grid of whole tiles
+    assert cap(tile=(4, 32), grid=(128, 112)) == -1   # grid not a whole number of tiles
+    assert cap(T=500) == -1                  # text not a whole number of blocks
+    assert cap(window=(0, 32)) == -1 and cap(window=(129, 32)) == -1
+    assert cap(stride=(0, 1)) == -1
+    nb = bsa.neighborhood(512, (128, 128), (8, 16), (32, 32))
+    t = lambda N=16896: _t(B=1, H=2, N=N, D=128, data=FAKE)
+    fwd = lambda N=16896, fl=FAKE: lib.bsa_forward_neighborhood(
+        ctypes.byref(t(N)), ctypes.byref(t(N)), ctypes.byref(t(N)), 128, ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(fl) if fl else None, ctypes.byref(nb), 0.0, ctypes.byref(t(N)),
+        None, None, None)
+    assert fwd(N=16895) == 1 and "N" in _err()
+    assert fwd(fl=0) == 1 and "entry_flags" in _err()
+    perm = lambda inp, outp, inv=0: lib.bsa_permute_tokens(ctypes.byref(inp), ctypes.byref(outp), None, None, 128,
+                                                            ctypes.byref(nb), inv, None)
+    assert perm(t(), t()) == 1 and "in place" in _err()
+    lay = lambda capacity: lib.bsa_build_neighborhood_layout(1, 2, 128, ctypes.byref(nb), ctypes.c_void_p(FAKE),
+                                                             ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                                             capacity, None)
+    need = lib.bsa_neighborhood_capacity(1, 2, 128, ctypes.byref(nb))
+    assert lay(need - 1) == 3
+
+
 def test_binding_refuses_host_tensors():
     import torch
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
