@@ -63,6 +63,8 @@ def main():
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--window", type=int, default=None, help="override the arrow window")
     ap.add_argument("--no-split", action="store_true", help="run every row in one workgroup")
+    ap.add_argument("--stride", default=None, help="neighbourhood workloads: stride 'rows,cols'")
+    ap.add_argument("--nb-window", default=None, help="neighbourhood workloads: window 'rows,cols'")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -131,7 +133,42 @@ def main():
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    if wl.layout == "arrow":
+    post = None
+    token_pairs = None
+    if wl.layout == "neighborhood":
+        # inputs arrive in natural order: the step permutes Q, K, V to tile-major
+        # order, builds the layout, runs the forward and permutes O, LSE back
+        stride = tuple(int(v2) for v2 in args.stride.split(",")) if args.stride else wl.nb_stride
+        window = tuple(int(v2) for v2 in args.nb_window.split(",")) if args.nb_window else wl.nb_window
+        wl = wl.replace(nb_stride=stride, nb_window=window)
+        nb = bsa.neighborhood(wl.text_len, wl.nb_grid, wl.nb_tile, wl.nb_window, wl.nb_stride)
+        cap = bsa.neighborhood_capacity(B, H, nb)
+        row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        flags = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        kept_pairs = cap
+        computed_heads = B * H
+        qn, kn, vn = q, k, v
+        q, k, v = torch.empty_like(qn), torch.empty_like(kn), torch.empty_like(vn)
+        out_t = torch.empty_like(q)
+        lse_t = torch.empty_like(lse)
+        R_, C_ = wl.nb_grid
+        token_pairs = B * H * (wl.text_len * N + R_ * C_ * (wl.text_len + wl.nb_window[0] * wl.nb_window[1]))
+
+        def layout(mark=None):
+            for src, dst in ((qn, q), (kn, k), (vn, v)):
+                bsa.permute_tokens(src, nb, out=dst)
+            if mark is not None:
+                mark()
+            bsa.build_neighborhood_layout(B, H, nb, row_ptr=row_ptr, col_idx=col_idx, flags=flags)
+        layout_parts = ("permute_in", "layout")
+        split = bsa.arrow_split_policy(B, H, N, block, wl.text_len, [bsa.HEAD_ARROW] * H,
+                                       [max(wl.nb_window) // max(wl.nb_tile)] * H)
+        fwd_kw = {}
+
+        def post():
+            bsa.permute_tokens(out_t, nb, inverse=True, lse=lse_t, out=out, lse_out=lse)
+    elif wl.layout == "arrow":
         modes, wins = x["head_modes"], x["head_windows"]
         cap = bsa.arrow_capacity(B, H, N, block, wl.text_len, modes, wins)
         row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
@@ -192,6 +229,10 @@ def main():
 
         def quantize():
             bsa.quantize_fp8(q, k, v, out=qkv8, workspace=ws_q)
+    elif wl.layout == "neighborhood":
+        def forward():
+            bsa.forward_neighborhood(q, k, v, row_ptr, col_idx, flags, nb, out=out_t, lse=lse_t,
+                                     **({"split": fwd_kw["split"]} if "split" in fwd_kw else {}))
     else:
         def forward():
             bsa.forward(q, k, v, block, row_ptr, col_idx, out=out, lse=lse, **fwd_kw)
@@ -200,6 +241,8 @@ def main():
     for _ in range(max(args.warmup, 1)):
         layout()
         forward()
+        if post is not None:
+            post()
     torch.cuda.synchronize()
     if wl.layout != "arrow":
         kept_pairs = int(row_ptr[-1].item())
@@ -212,7 +255,7 @@ def main():
     # step, the boundary between the layout parts, and the forward
     def new_ev():
         return torch.cuda.Event(enable_timing=True)
-    ev = [[new_ev() for _ in range(len(layout_parts) + 2)] for _ in range(args.steps)]
+    ev = [[new_ev() for _ in range(len(layout_parts) + 3)] for _ in range(args.steps)]
     t0, t1 = new_ev(), new_ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -221,14 +264,18 @@ def main():
         e = ev[s]
         e[0].record(stream)
         layout(mark=lambda: e[1].record(stream))
-        e[-2].record(stream)
+        e[-3].record(stream)
         forward()
+        e[-2].record(stream)
+        if post is not None:
+            post()
         e[-1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
-    fwd_ms = [e[-2].elapsed_time(e[-1]) for e in ev]
+    fwd_ms = [e[-3].elapsed_time(e[-2]) for e in ev]
+    post_ms = float(np.median([e[-2].elapsed_time(e[-1]) for e in ev])) if post is not None else None
     fwd_avg = float(np.mean(fwd_ms))
     part_ms = {name: float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev]))
                for j, name in enumerate(layout_parts)}
@@ -270,8 +317,11 @@ def main():
         "config": {
             "workload": f"{wl.name}: {wl.description}",
             "B": B, "H": H, "N": N, "D": D, "block": block,
-            "layout": (f"arrow w={wl.arrow_window}" if wl.layout == "arrow"
-                       else f"select groups={list(wl.groups)} text_blocks={wl.text_blocks}"),
+            "layout": (f"arrow w={wl.arrow_window}" if wl.layout == "arrow" else
+                       (f"neighbourhood grid={list(wl.nb_grid)} tile={list(wl.nb_tile)} "
+                        f"window={list(wl.nb_window)} stride={list(wl.nb_stride)}"
+                        if wl.layout == "neighborhood" else
+                        f"select groups={list(wl.groups)} text_blocks={wl.text_blocks}")),
             "kept_pairs": kept_pairs,
             "kept_fraction": round(kept_pairs / (B * H * nB * nB), 4),
             "long_row_split": (None if split is None else
@@ -286,6 +336,10 @@ def main():
         "forward_ms": round(fwd_avg, 4),
         "forward_ms_p10_p50_p90": [round(float(np.percentile(fwd_ms, q_)), 4) for q_ in (10, 50, 90)],
         "layout_ms": {k2: round(v2, 4) for k2, v2 in part_ms.items()},
+        "permute_out_ms": None if post_ms is None else round(post_ms, 4),
+        "token_pairs": token_pairs,
+        "token_level_tflops": (None if token_pairs is None else
+                               round(4.0 * D * token_pairs / (fwd_avg * 1e-3) / 1e12, 2)),
         "layout_cold_cache": cold,
         "forward_dense_equiv_tflops": round(dense_flop / (fwd_avg * 1e-3) / 1e12, 2),
         "step_wall_ms": round(wall * 1e3 / args.steps, 4),
@@ -527,20 +581,36 @@ def cpu_baseline(wl, x, row_ptr, col_idx, seconds, modes):
         t = rng.integers(0, N, n)
         return ((b * H + h) * N + t).astype(np.int64)
 
+    if wl.layout == "neighborhood":
+        # the block list is in tile-major order; the oracle works in natural order
+        perm = oracle.tile_permutation(wl.text_len, wl.nb_grid, wl.nb_tile)
+        pos = np.empty_like(perm)
+        pos[perm] = np.arange(N)
+
+        def run(rows):
+            oracle.forward_neighborhood(x["q"], x["k"], x["v"], wl.text_len, wl.nb_grid, wl.nb_window,
+                                        wl.nb_stride, rows=rows)
+    else:
+        pos = np.arange(N)
+
+        def run(rows):
+            oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=rows)
+
     def flop(rows):
+        # the metric's unit: 4 * block * D per kept block of the row's block row
         bh = rows // N
-        r = bh * nB + (rows % N) // block
+        r = bh * nB + pos[rows % N] // block
         kept = (rp[r + 1] - rp[r]).astype(np.float64)
         return float((4.0 * block * D * kept).sum())
 
     probe = rows_of(64)
     t = time.perf_counter()
-    oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=probe)
+    run(probe)
     dt = max(time.perf_counter() - t, 1e-3)
     n = int(min(max(64 * seconds / dt, 64), 1000000))
     rows = rows_of(n)
     t = time.perf_counter()
-    oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=rows)
+    run(rows)
     dt = time.perf_counter() - t
     cpu_model = ""
     try:

@@ -541,22 +541,28 @@ def neighborhood_capacity(B: int, H: int, nb: BsaNeighborhood) -> int:
     return int(load().bsa_neighborhood_capacity(B, H, nb.tile_rows * nb.tile_cols, ctypes.byref(nb)))
 
 
-def build_neighborhood_layout(B: int, H: int, nb: BsaNeighborhood, device=None):
+def build_neighborhood_layout(B: int, H: int, nb: BsaNeighborhood, device=None,
+                              row_ptr: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None,
+                              flags: Optional[torch.Tensor] = None):
     """(row_ptr, col_idx, entry_flags) int32 device tensors of the tile-major
     block list; flag 1 marks a partially covered key tile."""
     lib = load()
-    dev = device or torch.device("cuda")
+    dev = device or (row_ptr.device if row_ptr is not None else torch.device("cuda"))
     cap = neighborhood_capacity(B, H, nb)
-    if cap < 0:
-        _check(lib.bsa_build_neighborhood_layout(B, H, nb.tile_rows * nb.tile_cols, ctypes.byref(nb), None, None,
-                                                 None, 0, None))
     block = nb.tile_rows * nb.tile_cols
+    if cap < 0:
+        _check(lib.bsa_build_neighborhood_layout(B, H, block, ctypes.byref(nb), None, None, None, 0, None))
     nB = (nb.text_len + nb.rows * nb.cols) // block
-    row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
-    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
-    flags = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if row_ptr is None:
+        row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if flags is None:
+        flags = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if min(col_idx.numel(), flags.numel()) < cap or row_ptr.numel() < B * H * nB + 1:
+        raise ValueError("layout buffers too small")
     _check(lib.bsa_build_neighborhood_layout(B, H, block, ctypes.byref(nb), _ptr(row_ptr), _ptr(col_idx),
-                                             _ptr(flags), cap, _stream(dev)))
+                                             _ptr(flags), min(col_idx.numel(), flags.numel()), _stream(dev)))
     return row_ptr, col_idx, flags
 
 

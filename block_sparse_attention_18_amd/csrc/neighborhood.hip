@@ -8,8 +8,8 @@
 //    row-major to tile-major order (th x tw tiles, one block each; tiles
 //    row-major, tokens row-major inside a tile), or back.  Then every block
 //    of the sequence is one 2-D tile, and a window covers whole tiles plus
-//    a rim of partially covered ones.  One 16-byte chunk per thread; each
-//    tile row is a contiguous run of tw tokens on both sides.
+//    a rim of partially covered ones.  One workgroup per tile; each tile
+//    row is a contiguous run of tw tokens on both sides.
 //  * layout_kernel: the block list of that order, closed form per query
 //    tile.  A key tile is kept when some query of the query tile sees some
 //    key of it (the windows of a tile's queries span the product of their
@@ -20,36 +20,65 @@
 
 namespace bsa {
 
-__device__ __forceinline__ int nb_natural(const NbGeom &g, int beta, int t)
-{
-    if (t < g.T) return t;
-    const int q = t - g.T, tile = q / beta, o = q - tile * beta;
-    const int a = tile / g.tpr, b = tile - a * g.tpr;
-    return g.T + (a * g.th + (o >> g.tw_log2)) * g.C + b * g.tw + (o & (g.tw - 1));
-}
-
-// Grid (chunks / 256, B*H): chunk x of a head is token x / (D/8), 16 bytes
-// at channel 8 (x % (D/8)).
+// Grid (blocks of the sequence, B*H): workgroup (i, bh) moves block i of
+// head bh -- a text block unchanged, or image tile i - Tb -- as 16-byte
+// chunks, 8 per thread.  Tile coordinates are worked out once per
+// workgroup; inside a tile, token o sits at grid row o / tw, column o % tw
+// (shifts: tw and D / 8 are powers of two).
+template <int D>
 __global__ __launch_bounds__(256) void permute_kernel(const PermuteParams p)
 {
-    const int bh = blockIdx.y, b = bh / p.H, h = bh - b * p.H;
-    const int cpt = p.D / 8;
-    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (x >= (int64_t)p.N * cpt) return;
-    const int t = (int)(x / cpt), c = (int)(x - (int64_t)t * cpt);
-    const int nat = nb_natural(p.nb, p.nb.th * p.nb.tw, t);
-    const int src = p.inverse ? t : nat, dst = p.inverse ? nat : t;
-    const uint4 v = ld_g16(p.in.p + b * p.in.sb + h * p.in.sh + (int64_t)src * p.in.sn + 8 * c);
-    *reinterpret_cast<uint4 *>(p.out + b * p.o_sb + h * p.o_sh + (int64_t)dst * p.o_sn + 8 * c) = v;
-    if (c == 0 && p.lse_in && p.lse_out)
-        p.lse_out[(int64_t)bh * p.N + dst] = p.lse_in[(int64_t)bh * p.N + src];
+    constexpr int CPT = D / 8;                      // chunks per token
+    const NbGeom &g = p.nb;
+    const int beta = g.th * g.tw;
+    const int i = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh - b * p.H;
+    int base;                                       // natural index of the block's token 0
+    int tile_row_stride;                            // natural-index step between the tile's rows
+    if (i < g.Tb) {
+        base = i * beta;
+        tile_row_stride = g.tw;                     // a text block: contiguous
+    } else {
+        const int tile = i - g.Tb, a = tile / g.tpr;
+        base = g.T + a * g.th * g.C + (tile - a * g.tpr) * g.tw;
+        tile_row_stride = g.C;
+    }
+    const uint16_t *__restrict__ inb = p.in.p + b * p.in.sb + h * p.in.sh;
+    uint16_t *__restrict__ outb = p.out + b * p.o_sb + h * p.o_sh;
+    // all loads of the thread first, then the stores (up to 8 chunks in flight)
+    constexpr int MAXU = 128 * CPT / 256;
+    const int nu = beta * CPT / 256;
+    uint4 v[MAXU];
+    int dst[MAXU];
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        if (u < nu) {
+            const int x = threadIdx.x + 256 * u;
+            const int o = x / CPT, c = x - o * CPT;
+            const int t = i * beta + o;                                         // tile-major index
+            const int nat = base + (o >> g.tw_log2) * tile_row_stride + (o & (g.tw - 1));
+            const int src = p.inverse ? t : nat;
+            dst[u] = p.inverse ? nat : t;
+            v[u] = ld_g16(inb + (int64_t)src * p.in.sn + 8 * c);
+            if (c == 0 && p.lse_in && p.lse_out)
+                p.lse_out[(int64_t)bh * p.N + dst[u]] = p.lse_in[(int64_t)bh * p.N + src];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        if (u < nu) {
+            const int c = (threadIdx.x + 256 * u) % CPT;
+            *reinterpret_cast<uint4 *>(outb + (int64_t)dst[u] * p.o_sn + 8 * c) = v[u];
+        }
+    }
 }
 
 hipError_t launch_permute_tokens(const PermuteParams &p, hipStream_t s)
 {
-    const int64_t chunks = (int64_t)p.N * (p.D / 8);
-    hipLaunchKernelGGL(permute_kernel, dim3((unsigned)((chunks + 255) / 256), (unsigned)(p.B * p.H)), dim3(256), 0,
-                       s, p);
+    const int nblk = p.N / (p.nb.th * p.nb.tw);
+    const dim3 grid((unsigned)nblk, (unsigned)(p.B * p.H));
+    if (p.D == 128) hipLaunchKernelGGL(permute_kernel<128>, grid, dim3(256), 0, s, p);
+    else if (p.D == 64) hipLaunchKernelGGL(permute_kernel<64>, grid, dim3(256), 0, s, p);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
