@@ -22,6 +22,8 @@ Every function follows the definitions stated in ``bsa_oracle.c``:
                           2-D neighbourhood (GNA) attention on the latent
                           grid: window start, the masked forward, tile-major
                           token order, block layout with full / partial flags
+  forward_f64 / backward  the forward on fp64 inputs and its gradient
+                          (dQ, dK, dV of the kept-block softmax)
   output_rse              per-head relative squared error of an output
   mask_jaccard            per-head Jaccard similarity of two block masks
 """
@@ -90,6 +92,8 @@ def _load():
         lib.oracle_forward_neighborhood.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, D, P, I, P, P]
         lib.oracle_tile_permutation.argtypes = [I, I, I, I, I, P]
         lib.oracle_neighborhood_layout.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, I]
+        lib.oracle_forward_f64.argtypes = [P, P, P, I, I, I, I, I, P, P, D, P, P]
+        lib.oracle_backward_f64.argtypes = [P, P, P, P, I, I, I, I, I, P, P, D, P, P, P]
         lib.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, D, P, I, P, P]
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -414,3 +418,46 @@ def neighborhood_layout(text_len: int, grid: Tuple[int, int], tile: Tuple[int, i
                                               _ptr(flags), nB * nB), "neighborhood_layout")
     n = int(row_ptr[-1])
     return row_ptr, col_idx[:n].copy(), flags[:n].copy()
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+def _f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return np.ascontiguousarray(_widen(a))
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _csr(row_ptr, col_idx):
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if ci.size == 0:
+        ci = np.zeros(1, dtype=np.int32)
+    return rp, ci
+
+
+def forward_f64(q, k, v, block: int, row_ptr, col_idx, scale: Optional[float] = None):
+    """The block-sparse forward on fp64 (or bf16-bit) inputs: (O, LSE) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rp, ci = _csr(row_ptr, col_idx)
+    O = np.empty((B, H, N, D), np.float64); L = np.empty((B, H, N), np.float64)
+    _check(_load().oracle_forward_f64(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, block, _ptr(rp), _ptr(ci), scale,
+                                      _ptr(O), _ptr(L)), "forward_f64")
+    return O, L
+
+
+def backward(q, k, v, dO, block: int, row_ptr, col_idx, scale: Optional[float] = None):
+    """(dQ, dK, dV) in fp64 of the block-sparse forward at (q, k, v) for the
+    output gradient dO (fp64 or bf16-bit inputs)."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rp, ci = _csr(row_ptr, col_idx)
+    dQ = np.empty_like(q); dK = np.empty_like(q); dV = np.empty_like(q)
+    _check(_load().oracle_backward_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), B, H, N, D, block, _ptr(rp), _ptr(ci),
+                                       scale, _ptr(dQ), _ptr(dK), _ptr(dV)), "backward")
+    return dQ, dK, dV

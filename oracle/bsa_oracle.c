@@ -777,3 +777,142 @@ int oracle_neighborhood_layout(int64_t text_len, int64_t R, int64_t C, int64_t t
     free(cnt);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the block-sparse forward (the gradient of the dense softmax
+ * restricted to the kept blocks), fp64 throughout, on fp64 inputs.
+ * With z_ts = scale * Q_t.K_s on kept (t, s), P = softmax_s(z), O = P V:
+ *   dV_s  = sum_t P_ts dO_t
+ *   dP_ts = dO_t . V_s,   Delta_t = sum_s P_ts dP_ts  (= dO_t . O_t)
+ *   dS_ts = P_ts (dP_ts - Delta_t)
+ *   dQ_t  = scale * sum_s dS_ts K_s,   dK_s = scale * sum_t dS_ts Q_t
+ * A row with no kept key contributes nothing.  oracle_forward_f64 is the
+ * forward on the same fp64 inputs (for finite-difference checks).
+ * ---------------------------------------------------------------------- */
+static int bw_check_csr(int64_t rows, int64_t nB, const int32_t *row_ptr, const int32_t *col_idx)
+{
+    if (!row_ptr || row_ptr[0] != 0) return 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        if (row_ptr[r + 1] < row_ptr[r]) return 0;
+        for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e)
+            if (!col_idx || col_idx[e] < 0 || col_idx[e] >= nB) return 0;
+    }
+    return 1;
+}
+
+/* probabilities of row t of head bh: p[s] (0 where not kept); returns 0 for
+ * a row with no kept key */
+static int bw_row_probs(const double *q, const double *k, int64_t N, int64_t D, int64_t beta, int64_t nB,
+                        int64_t bh, int64_t t, const int32_t *row_ptr, const int32_t *col_idx, double scale,
+                        unsigned char *kept, double *p, double *lse)
+{
+    const int64_t r = bh * nB + t / beta;
+    memset(kept, 0, (size_t)nB);
+    for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) kept[col_idx[e]] = 1;
+    double m = -INFINITY;
+    for (int64_t s = 0; s < N; ++s) {
+        if (!kept[s / beta]) { p[s] = -INFINITY; continue; }
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc += q[(bh * N + t) * D + d] * k[(bh * N + s) * D + d];
+        p[s] = scale * acc;
+        if (p[s] > m) m = p[s];
+    }
+    if (m == -INFINITY) return 0;
+    double l = 0.0;
+    for (int64_t s = 0; s < N; ++s) l += p[s] == -INFINITY ? 0.0 : exp(p[s] - m);
+    for (int64_t s = 0; s < N; ++s) p[s] = p[s] == -INFINITY ? 0.0 : exp(p[s] - m) / l;
+    if (lse) *lse = m + log(l);
+    return 1;
+}
+
+int oracle_forward_f64(const double *q, const double *k, const double *v, int64_t B, int64_t H, int64_t N,
+                       int64_t D, int64_t beta, const int32_t *row_ptr, const int32_t *col_idx, double scale,
+                       double *O, double *LSE)
+{
+    if (!q || !k || !v || !O || !LSE || B <= 0 || H <= 0 || N <= 0 || D <= 0 || beta <= 0) return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta);
+    if (!bw_check_csr(B * H * nB, nB, row_ptr, col_idx)) return OR_EINVAL;
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *p = malloc(sizeof(double) * N);
+        unsigned char *kept = malloc((size_t)nB);
+        if (!p || !kept) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t row = 0; row < B * H * N; ++row) {
+                const int64_t bh = row / N, t = row % N;
+                double *o = O + row * D;
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                if (!bw_row_probs(q, k, N, D, beta, nB, bh, t, row_ptr, col_idx, scale, kept, p, &LSE[row])) {
+                    LSE[row] = -INFINITY;
+                    continue;
+                }
+                for (int64_t s = 0; s < N; ++s)
+                    if (p[s] != 0.0)
+                        for (int64_t d = 0; d < D; ++d) o[d] += p[s] * v[(bh * N + s) * D + d];
+            }
+        }
+        free(p);
+        free(kept);
+    }
+    return rc;
+}
+
+int oracle_backward_f64(const double *q, const double *k, const double *v, const double *dO, int64_t B, int64_t H,
+                        int64_t N, int64_t D, int64_t beta, const int32_t *row_ptr, const int32_t *col_idx,
+                        double scale, double *dQ, double *dK, double *dV)
+{
+    if (!q || !k || !v || !dO || !dQ || !dK || !dV || B <= 0 || H <= 0 || N <= 0 || D <= 0 || beta <= 0)
+        return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta);
+    if (!bw_check_csr(B * H * nB, nB, row_ptr, col_idx)) return OR_EINVAL;
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *p = malloc(sizeof(double) * N);
+        double *dp = malloc(sizeof(double) * N);
+        unsigned char *kept = malloc((size_t)nB);
+        if (!p || !dp || !kept) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+            /* one (b, h) per iteration: dK, dV of a head are touched by its rows only */
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < B * H; ++bh) {
+                memset(dK + bh * N * D, 0, sizeof(double) * N * D);
+                memset(dV + bh * N * D, 0, sizeof(double) * N * D);
+                for (int64_t t = 0; t < N; ++t) {
+                    double *dq = dQ + (bh * N + t) * D;
+                    for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
+                    if (!bw_row_probs(q, k, N, D, beta, nB, bh, t, row_ptr, col_idx, scale, kept, p, NULL))
+                        continue;
+                    const double *go = dO + (bh * N + t) * D;
+                    double delta = 0.0;
+                    for (int64_t s = 0; s < N; ++s) {
+                        if (p[s] == 0.0) { dp[s] = 0.0; continue; }
+                        double acc = 0.0;
+                        for (int64_t d = 0; d < D; ++d) acc += go[d] * v[(bh * N + s) * D + d];
+                        dp[s] = acc;
+                        delta += p[s] * acc;
+                    }
+                    for (int64_t s = 0; s < N; ++s) {
+                        if (p[s] == 0.0) continue;
+                        const double ds = p[s] * (dp[s] - delta);
+                        for (int64_t d = 0; d < D; ++d) {
+                            dV[(bh * N + s) * D + d] += p[s] * go[d];
+                            dq[d] += scale * ds * k[(bh * N + s) * D + d];
+                            dK[(bh * N + s) * D + d] += scale * ds * q[(bh * N + t) * D + d];
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(dp);
+        free(kept);
+    }
+    return rc;
+}
