@@ -15,6 +15,7 @@ The four calls mirror the C ABI:
   build_arrow_layout   CSR block list of the arrow / full / skip layout
   forward              online-softmax attention over the CSR block list,
                        returning O (bf16) and LSE (fp32, natural log)
+  backward             dQ, dK, dV of that forward
 
 and the FP8 (E4M3) mode of the forward:
 
@@ -136,6 +137,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                     V]),
             "bsa_forward_neighborhood": (I32, [TP, TP, TP, I32, V, V, V, ctypes.POINTER(BsaNeighborhood), F, TP, V,
                                                ctypes.POINTER(BsaSplit), V]),
+            "bsa_backward_workspace_size": (SZ, [I64, I64, I64]),
+            "bsa_backward": (I32, [TP, TP, TP, TP, TP, I32, V, V, V, F, TP, TP, TP, V, SZ, V]),
             "bsa_status_string": (ctypes.c_char_p, [I32]),
             "bsa_last_error": (ctypes.c_char_p, []),
             "bsa_version": (ctypes.c_char_p, []),
@@ -506,6 +509,35 @@ def forward_fp8(qkv: Fp8QKV, block: int, row_ptr: torch.Tensor, col_idx: torch.T
     _check(lib.bsa_forward_fp8(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx), float(scale or 0.0),
                                ctypes.byref(do), _ptr(lse), _stream(dev)))
     return out, lse
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dO: torch.Tensor, block: int,
+             row_ptr: torch.Tensor, col_idx: torch.Tensor, lse: torch.Tensor, scale: Optional[float] = None,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """(dQ, dK, dV) bf16 of the block-sparse forward, given its output O and
+    LSE and the output gradient dO."""
+    lib = load()
+    B, H, N, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if col_idx.numel() == 0:
+        col_idx = torch.zeros(1, dtype=torch.int32, device=row_ptr.device)
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.bsa_backward_workspace_size(B, H, N)), 16), dtype=torch.uint8,
+                                device=q.device)
+    ds = [_desc(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"), (dq, "dq"), (dk, "dk"),
+                                   (dv, "dv"))]
+    _check(lib.bsa_backward(*[ctypes.byref(d) for d in ds[:5]], block, _ptr(row_ptr), _ptr(col_idx), _ptr(lse),
+                            float(scale or 0.0), *[ctypes.byref(d) for d in ds[5:]], _ptr(workspace),
+                            workspace.numel(), _stream(q.device)))
+    return dq, dk, dv
 
 
 def neighborhood(text_len: int, grid: Tuple[int, int], tile: Tuple[int, int], window: Tuple[int, int],

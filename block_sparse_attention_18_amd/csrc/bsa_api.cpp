@@ -664,6 +664,63 @@ bsa_status bsa_forward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, co
 }
 
 // ---------------------------------------------------------------------------
+size_t bsa_backward_workspace_size(int64_t B, int64_t H, int64_t N)
+{
+    if (B <= 0 || H <= 0 || N <= 0) return 0;
+    return 2 * (((size_t)(B * H * N) * sizeof(float) + 255) & ~(size_t)255);
+}
+
+bsa_status bsa_backward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_tensor *o,
+                        const bsa_tensor *dO, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                        const float *lse, float scale, const bsa_tensor *dq, const bsa_tensor *dk,
+                        const bsa_tensor *dv, void *workspace, size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    const bsa_tensor *ts[] = {q, k, v, o, dO, dq, dk, dv};
+    const char *names[] = {"q", "k", "v", "o", "dO", "dq", "dk", "dv"};
+    for (int x = 0; x < 8; ++x) {
+        if ((st = check_tensor(ts[x], names[x])) != BSA_OK) return st;
+        if (!same_shape(q, ts[x])) return fail(BSA_ERR_INVALID_ARG, "%s shape differs from q", names[x]);
+    }
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    if (!row_ptr || !col_idx || !lse) return fail(BSA_ERR_INVALID_ARG, "row_ptr / col_idx / lse null");
+    if (std::isnan(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
+    const int64_t nB = ceil_div(q->N, block);
+    if (nB > 8192) return fail(BSA_ERR_UNSUPPORTED, "more than 8192 blocks");
+    if (q->B * q->H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many blocks");
+    const size_t need = bsa_backward_workspace_size(q->B, q->H, q->N);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        return fail(BSA_ERR_WORKSPACE, "backward workspace needs %zu bytes (16-byte aligned)", need);
+    bsa::BwdParams p{};
+    p.q = t4(q);
+    p.k = t4(k);
+    p.v = t4(v);
+    p.o = t4(o);
+    p.dO = t4(dO);
+    p.lse = lse;
+    p.lse2 = static_cast<float *>(workspace);
+    p.delta = reinterpret_cast<float *>(static_cast<char *>(workspace) + need / 2);
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.dq = static_cast<uint16_t *>(dq->data);
+    p.dk = static_cast<uint16_t *>(dk->data);
+    p.dv = static_cast<uint16_t *>(dv->data);
+    p.dq_sb = dq->stride_b; p.dq_sh = dq->stride_h; p.dq_sn = dq->stride_n;
+    p.dk_sb = dk->stride_b; p.dk_sh = dk->stride_h; p.dk_sn = dk->stride_n;
+    p.dv_sb = dv->stride_b; p.dv_sh = dv->stride_h; p.dv_sn = dv->stride_n;
+    p.B = (int32_t)q->B;
+    p.H = (int32_t)q->H;
+    p.N = (int32_t)q->N;
+    p.D = (int32_t)q->D;
+    p.nB = (int32_t)nB;
+    p.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
+    p.scale_log2 = p.scale * 1.4426950408889634f;
+    hipError_t e = bsa::launch_backward(p, block, (int)q->D, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
 size_t bsa_quantize_fp8_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D)
 {
     if (B <= 0 || H <= 0 || N <= 0 || (D != 64 && D != 128)) return 0;

@@ -213,6 +213,28 @@ bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tenso
                        const bsa_split *split, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Backward of bsa_forward (the gradient a training step needs; the
+ * multimodal-DiT write-up trains its selection projection jointly with the
+ * model, section 2.2).  For the softmax restricted to the kept blocks,
+ *   dV = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K,
+ *   dS = P * (dO V^T - rowsum(dO * O)),
+ * with P recomputed from Q, K and the forward's LSE.  q, k, v, o, dO, dq, dk,
+ * dv are bf16 tensors as in bsa_forward (same shape, any strides); lse is
+ * the forward's fp32 [B][H][N] (natural log).  The block list is the
+ * forward's; its columns must ascend within each row (as every layout
+ * builder here writes them).  Every head is computed (rows of a head with
+ * no kept block give zero gradients).  The workspace
+ * (bsa_backward_workspace_size bytes, 16-byte aligned) holds two fp32
+ * [B][H][N] arrays.  Results are deterministic.  Errors: INVALID_ARG,
+ * UNSUPPORTED (D, block, more than 8192 blocks), WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t bsa_backward_workspace_size(int64_t B, int64_t H, int64_t N);
+bsa_status bsa_backward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_tensor *o,
+                        const bsa_tensor *dO, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                        const float *lse, float scale, const bsa_tensor *dq, const bsa_tensor *dk,
+                        const bsa_tensor *dv, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * 2-D neighbourhood attention (GNA notes, 1.1: a window around each query
  * on the latent grid with a stride by which groups of queries share one
  * window; 2.1: fine-grained masking only where a key tile is partially
