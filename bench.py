@@ -69,6 +69,9 @@ def main():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward (dQ, dK, dV) of the forward on the workload's "
+                         "layout, for a synthetic output gradient")
     ap.add_argument("--fp8", action="store_true",
                     help="run the forward in the FP8 (E4M3) mode on inputs quantised once "
                          "before the timed region (quantisation timed separately)")
@@ -358,6 +361,11 @@ def main():
         "cpu_baseline": None,
     }
 
+    if args.backward:
+        if wl.layout == "neighborhood" or args.fp8 or ("head_modes" in fwd_kw and fwd_kw["head_modes"] is not None
+                                                       and np.any(fwd_kw["head_modes"] == bsa.HEAD_SKIP)):
+            raise SystemExit("--backward: block layouts without SKIP heads, bf16 only")
+        res["backward"] = backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx, kept_pairs)
     if args.cpu_seconds > 0 and not args.fp8:
         res["cpu_baseline"] = cpu_baseline(wl, x, row_ptr, col_idx, args.cpu_seconds,
                                            fwd_kw.get("head_modes"))
@@ -563,6 +571,40 @@ def reuse_loop(torch, bsa, synth, dev, args):
         res["amortised_speedup_measured"] = round(T * t_full / total, 3)
     res["diagnostics"] = diag
     return res
+
+
+def backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx, kept_pairs, reps=20):
+    """Times bsa_backward (Delta/LSE prep, dQ kernel, dK/dV kernel) after one
+    forward, for a seeded N(0, 1) output gradient.  Algorithmic work: the five
+    products of the backward (S recomputed, dP, dV, dK, dQ), 10 * block^2 * D
+    FLOP per kept block pair; the dQ and dK/dV kernels each recompute S and
+    dP, so 14 * block^2 * D are executed."""
+    B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
+    g = synth.random_qkv(B, H, N, D, seed=wl.seed + 2000)[0]
+    gd = torch.from_numpy(np.ascontiguousarray(g).view(np.int16)).view(torch.bfloat16).to(dev)
+    O, L = bsa.forward(q, k, v, block, row_ptr, col_idx)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(int(bsa.load().bsa_backward_workspace_size(B, H, N)), dtype=torch.uint8, device=dev)
+
+    def run():
+        bsa.backward(q, k, v, O, gd, block, row_ptr, col_idx, L, dq=dq, dk=dk, dv=dv, workspace=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for r in range(reps):
+        ev[r].record(stream)
+        run()
+    ev[reps].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
+    med = float(np.median(ms))
+    alg = 10.0 * block * block * D * kept_pairs
+    return {"ms": round(med, 4), "ms_p10_p50_p90": [round(float(np.percentile(ms, x)), 4) for x in (10, 50, 90)],
+            "algorithmic_tflops": round(alg / (med * 1e-3) / 1e12, 2),
+            "executed_tflops": round(1.4 * alg / (med * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(alg / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "flop_per_pair": "10 * block^2 * D (dQ, dK, dV, dP, S); 14 executed"}
 
 
 def cpu_baseline(wl, x, row_ptr, col_idx, seconds, modes):
