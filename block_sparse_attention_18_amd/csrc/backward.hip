@@ -361,6 +361,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 1) void bwd_dkdv_kernel(const BwdPa
     const float *lse2 = p.lse2 + (int64_t)bh * p.N;
     const float *delta = p.delta + (int64_t)bh * p.N;
     auto qstart = [&](int t) { return qlist[t / Sh::SUB] * BETA + 64 * (t % Sh::SUB); };
+    const bool vec_stats = ((int64_t)bh * p.N) % 4 == 0;   // 16-byte aligned rows of lse2, delta
 
     if (T > 0) {
         int q0 = qstart(0);
@@ -378,32 +379,43 @@ __global__ __launch_bounds__(BETA / 32 * 64, 1) void bwd_dkdv_kernel(const BwdPa
             }
             // row statistics of the lane's 32 accumulator rows: query
             // q0 + 32 kt + 8 hl + koff(r), in groups of 4 consecutive rows
-            float l2[2][16], dl[2][16];
+            // (16-byte loads when the head's rows are 16-byte aligned)
+            float4 l2[2][4], dl[2][4];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int r0 = q0 + 32 * kt + 8 * hl + koff(4 * g);
-                    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), d4 = a;
-                    if (r0 + 0 < p.N) { a.x = lse2[r0 + 0]; d4.x = delta[r0 + 0]; }
-                    if (r0 + 1 < p.N) { a.y = lse2[r0 + 1]; d4.y = delta[r0 + 1]; }
-                    if (r0 + 2 < p.N) { a.z = lse2[r0 + 2]; d4.z = delta[r0 + 2]; }
-                    if (r0 + 3 < p.N) { a.w = lse2[r0 + 3]; d4.w = delta[r0 + 3]; }
-                    l2[kt][4 * g + 0] = a.x; l2[kt][4 * g + 1] = a.y; l2[kt][4 * g + 2] = a.z; l2[kt][4 * g + 3] = a.w;
-                    dl[kt][4 * g + 0] = d4.x; dl[kt][4 * g + 1] = d4.y; dl[kt][4 * g + 2] = d4.z; dl[kt][4 * g + 3] = d4.w;
+                    if (vec_stats && r0 + 4 <= p.N) {
+                        l2[kt][g] = *reinterpret_cast<const float4 *>(lse2 + r0);
+                        dl[kt][g] = *reinterpret_cast<const float4 *>(delta + r0);
+                    } else {
+                        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), d4 = a;
+                        if (r0 + 0 < p.N) { a.x = lse2[r0 + 0]; d4.x = delta[r0 + 0]; }
+                        if (r0 + 1 < p.N) { a.y = lse2[r0 + 1]; d4.y = delta[r0 + 1]; }
+                        if (r0 + 2 < p.N) { a.z = lse2[r0 + 2]; d4.z = delta[r0 + 2]; }
+                        if (r0 + 3 < p.N) { a.w = lse2[r0 + 3]; d4.w = delta[r0 + 3]; }
+                        l2[kt][g] = a;
+                        dl[kt][g] = d4;
+                    }
                 }
             f32x16 s[2], dp[2];
             bw_rows_mfma<D>(Qc, off.rows, kf, s);
             bw_rows_mfma<D>(Gc, off.rows, vf, dp);
             if (q0 + 64 > p.N) mask_keys(s, p.N - q0 - 8 * hl);   // query rows past N
-            f32x16 ds[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pr = fast_exp2(__builtin_fmaf(s[kt][r], c, -l2[kt][r]));
-                    s[kt][r] = pr;
-                    ds[kt][r] = pr * (dp[kt][r] - dl[kt][r]);
+                for (int g = 0; g < 4; ++g) {
+                    const float lv[4] = {l2[kt][g].x, l2[kt][g].y, l2[kt][g].z, l2[kt][g].w};
+                    const float dv4[4] = {dl[kt][g].x, dl[kt][g].y, dl[kt][g].z, dl[kt][g].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g + e;
+                        const float pr = fast_exp2(__builtin_fmaf(s[kt][r], c, -lv[e]));
+                        s[kt][r] = pr;                              // P
+                        dp[kt][r] = pr * (dp[kt][r] - dv4[e]);      // dS
+                    }
                 }
             bf16x8 pp[2][2], ps[2][2];
 #pragma unroll
@@ -411,7 +423,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 1) void bwd_dkdv_kernel(const BwdPa
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     pp[kt][u] = pack8(s, kt, u);
-                    ps[kt][u] = pack8(ds, kt, u);
+                    ps[kt][u] = pack8(dp, kt, u);
                 }
             bw_tr_mfma<D>(Gc, off, pp, dv);
             bw_tr_mfma<D>(Qc, off, ps, dk);
