@@ -205,12 +205,17 @@ __device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_b
     using Sh = FwdShape<BETA, D>;
     const int rows = p.N - k0;
     const uint32_t so = (uint32_t)((int64_t)k0 * sn * 2);
+    // the LDS destination of the wave's first copy, opaque to the compiler
+    // so that every copy's address is this base plus a constant (one scalar
+    // add), rather than a loop-invariant value of its own kept in a register
+    __attribute__((address_space(3))) char *lbase = (__attribute__((address_space(3))) char *)(lds_void *)(dst + wv * 64 * 8);
+    asm volatile("" : "+s"(lbase));
     if (Sh::UNIFORM_COPY && rows >= 64) {
         // full tile: copy x is copy 0 moved by x * ROWS_PER_COPY rows
         const uint32_t step = (uint32_t)((int64_t)Sh::ROWS_PER_COPY * sn * 2);
 #pragma unroll
         for (int x = 0; x < Sh::DMA; ++x)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16,
                                                      off0, so + x * step, 0, 0);
         return;
     }
@@ -220,8 +225,7 @@ __device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_b
         const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
         const int rr = min(r, rows - 1);
         const uint32_t o = (uint32_t)(rr * sn * 2 + ((ps ^ (is_v ? vswz<D>(r) : kswz<D>(r))) * 16));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16, o, so,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16, o, so, 0, 0);
     }
 }
 
