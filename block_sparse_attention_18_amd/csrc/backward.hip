@@ -87,13 +87,16 @@ __device__ __forceinline__ void bw_load_tile(uint16_t *__restrict__ dst, __amdgp
                                              int r0, int N, int wv, int lane)
 {
     using Sh = BwShape<BETA, D>;
+    // one opaque LDS base per call: each copy's destination is a scalar add
+    __attribute__((address_space(3))) char *lbase = (__attribute__((address_space(3))) char *)(lds_void *)(dst + wv * 64 * 8);
+    asm volatile("" : "+s"(lbase));
 #pragma unroll
     for (int x = 0; x < Sh::DMA; ++x) {
         const int slot = (x * Sh::NW + wv) * 64 + lane;
         const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
         const int src = max(0, min(r0 + r, N - 1));
         const uint32_t o = (uint32_t)(src * sn * 2 + ((ps ^ bswz<D>(r)) * 16));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 8), 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16, o, 0, 0, 0);
     }
 }
 

@@ -393,10 +393,13 @@ __device__ __forceinline__ void load_k8(uint8_t *__restrict__ dst, __amdgpu_buff
 {
     using Sh = F8Shape<BETA, D>;
     constexpr int RPC = Sh::NT / Sh::KCH;   // rows per copy
+    // one opaque LDS base per call: each copy's destination is a scalar add
+    __attribute__((address_space(3))) char *lbase = (__attribute__((address_space(3))) char *)(lds_void *)(dst + wv * 64 * 16);
+    asm volatile("" : "+s"(lbase));
     if (k0 + 64 <= N) {
 #pragma unroll
         for (int x = 0; x < Sh::DMA; ++x)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 16), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16,
                                                      kdma + x * RPC * D, k0 * D, 0, 0);
         return;
     }
@@ -406,8 +409,7 @@ __device__ __forceinline__ void load_k8(uint8_t *__restrict__ dst, __amdgpu_buff
         const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
         const int key = max(0, min(k0 + r, N - 1));
         const uint32_t o = (uint32_t)(key * D + ((ps ^ k8swz<D>(r)) * 16));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 16), 16, o, 0, 0,
-                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16, o, 0, 0, 0);
     }
 }
 
@@ -419,9 +421,11 @@ __device__ __forceinline__ void load_v8(uint8_t *__restrict__ dst, __amdgpu_buff
 {
     using Sh = F8Shape<BETA, D>;
     const int c0 = min(k0, NP - 64);
+    __attribute__((address_space(3))) char *lbase = (__attribute__((address_space(3))) char *)(lds_void *)(dst + wv * 64 * 16);
+    asm volatile("" : "+s"(lbase));
 #pragma unroll
     for (int x = 0; x < Sh::DMA; ++x)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (x * Sh::NW + wv) * 64 * 16), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16,
                                                  vdma + x * vstep, c0, 0, 0);
 }
 
