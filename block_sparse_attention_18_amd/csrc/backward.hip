@@ -13,13 +13,15 @@
 //    dP^T = V dO^T on bf16 MFMA with Q and dO in registers; dS^T, packed to
 //    bf16, is directly the B operand of dQ^T += K^T dS^T (K^T by
 //    transposing LDS reads).
-//  * bwd_dkdv_kernel: one workgroup per (key block, head), each wave owning
-//    32 keys, K and V in registers.  The workgroup first lists, by binary
-//    search in each block row (columns ascend), the query blocks that keep
-//    its key block; their Q and dO tiles stream through LDS.  S = Q K^T and
-//    dP = dO V^T with the query rows in the permuted order, so that P and
-//    dS packed to bf16 are the B operands of dV^T += dO^T P and
-//    dK^T += Q^T dS (dO^T, Q^T by transposing LDS reads).
+//  * bwd_dkdv_kernel: one workgroup per (key block, head) of 2 * block / 32
+//    waves, each wave owning 32 keys and one 32-query half of every 64-query
+//    sub-tile; the block's K and V sit in LDS.  The workgroup first lists,
+//    by binary search in each block row (columns ascend), the query blocks
+//    that keep its key block; their Q and dO sub-tiles stream through LDS.
+//    S = Q K^T and dP = dO V^T with the query rows in the permuted order, so
+//    that P and dS packed to bf16 are the B operands of dV^T += dO^T P and
+//    dK^T += Q^T dS (dO^T, Q^T by transposing LDS reads); the two query
+//    halves' partial sums are added through LDS at the end.
 // Tiles read both by rows and transposed use one XOR swizzle of the 16-byte
 // chunk index that keeps both read patterns on distinct bank slots.
 #include "common.h"
@@ -290,24 +292,129 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (key block, head)
 // ---------------------------------------------------------------------------
-template <int BETA, int D>
-__global__ __launch_bounds__(BETA / 32 * 64, 1) void bwd_dkdv_kernel(const BwdParams p)
+// P and dS of one 32-query half (rows 32 h + 8 hl + koff(r) of the
+// sub-tile) from its S and dP, in place (s <- P, dp <- dS), packed to bf16
+// as the B operands (two 16-query k-steps) of dV^T += dO^T P and
+// dK^T += Q^T dS.  Query rows past N carry -inf scores (masked before).
+__device__ __forceinline__ void bw_probs_half(f32x16 &s, f32x16 &dp, const float *stats, int h, float c, int hl,
+                                              bf16x8 (&pp)[2], bf16x8 (&ps)[2])
 {
-    using Sh = BwShape<BETA, D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * Sh::TILE];   // two (Q, dO) buffers
-    __shared__ int wcount[Sh::NW];
-    extern __shared__ int qlist[];                                          // query blocks keeping this key block
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int r0 = 32 * h + 8 * hl + koff(4 * g);
+        const float4 l2 = *reinterpret_cast<const float4 *>(stats + r0);
+        const float4 dl = *reinterpret_cast<const float4 *>(stats + 64 + r0);
+        const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+        const float dv4[4] = {dl.x, dl.y, dl.z, dl.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float pr = fast_exp2(__builtin_fmaf(s[r], c, -lv[e]));
+            s[r] = pr;
+            dp[r] = pr * (dp[r] - dv4[e]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        uint4 a, b;
+        a.x = pack_bf16x2(s[8 * u + 0], s[8 * u + 1]);
+        a.y = pack_bf16x2(s[8 * u + 2], s[8 * u + 3]);
+        a.z = pack_bf16x2(s[8 * u + 4], s[8 * u + 5]);
+        a.w = pack_bf16x2(s[8 * u + 6], s[8 * u + 7]);
+        b.x = pack_bf16x2(dp[8 * u + 0], dp[8 * u + 1]);
+        b.y = pack_bf16x2(dp[8 * u + 2], dp[8 * u + 3]);
+        b.z = pack_bf16x2(dp[8 * u + 4], dp[8 * u + 5]);
+        b.w = pack_bf16x2(dp[8 * u + 6], dp[8 * u + 7]);
+        pp[u] = as_bf16x8(a);
+        ps[u] = as_bf16x8(b);
+    }
+}
+
+// out[d] += X^T (32-column group d, rows 32 h .. 32 h + 31) * pf
+template <int D>
+__device__ __forceinline__ void bw_tr_half(const uint16_t *__restrict__ X, const BwOffsets<D> &off, int h,
+                                           const bf16x8 (&pf)[2], f32x16 (&out)[D / 32])
+{
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d) {
+            s16x4 h2[2];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const uint16_t *rowp = X + (h * 32 + 16 * u) * D;
+                h2[pp] = __builtin_bit_cast(
+                    s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                               (__attribute__((address_space(3))) bf16x4 *)lds_at<uint16_t>(rowp, off.tr[pp] ^ (VSTEP * d))));
+            }
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            out[d] = mfma32x32x16(a, pf[u], out[d]);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV with two waves per key group: one workgroup per (key block, head)
+// of 2 * BETA / 32 waves; wave w owns the 32 keys of group w % (BETA / 32)
+// and the 32-query half w / (BETA / 32) of every 64-query sub-tile.  The
+// key block's K and V stay in LDS (B operands read per MFMA), which keeps a
+// wave within 256 registers (two waves per SIMD).  The two halves' partial
+// dK, dV are added through LDS at the end.
+// ---------------------------------------------------------------------------
+template <int BETA, int D>
+struct DkShape {
+    static constexpr int NKG = BETA / 32;
+    static constexpr int NW = 2 * NKG;
+    static constexpr int NT = NW * 64;
+    static constexpr int QS = D / 16;
+    static constexpr int DT = D / 32;
+    static constexpr int KCH = D / 8;
+    static constexpr int KV = BETA * D;          // bf16 elements of the block's K (or V)
+    static constexpr int QT = 64 * D;            // bf16 elements of a 64-query tile
+    static constexpr int BUF = 2 * QT + 256;     // Q, dO, then 2 x 64 fp32 statistics
+    static constexpr int SMEM = 2 * KV + 2 * BUF;
+};
+
+// Copy of R rows (from r0; rows past N repeat row N-1) into LDS with the
+// backward's chunk swizzle; NT threads, 16 bytes each per copy.
+template <int R, int D, int NT>
+__device__ __forceinline__ void bw_load_rows(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t rs, int64_t sn,
+                                              int r0, int N, int tid)
+{
+    constexpr int KCH = D / 8, CP = R * KCH / NT;
+    static_assert(R * KCH % NT == 0, "tile split");
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    __attribute__((address_space(3))) char *lbase = (__attribute__((address_space(3))) char *)(lds_void *)(dst + wv * 64 * 8);
+    asm volatile("" : "+s"(lbase));
+#pragma unroll
+    for (int x = 0; x < CP; ++x) {
+        const int slot = (x * (NT / 64) + wv) * 64 + lane;
+        const int r = slot / KCH, ps = slot % KCH;
+        const int src = max(0, min(r0 + r, N - 1));
+        const uint32_t o = (uint32_t)(src * sn * 2 + ((ps ^ bswz<D>(r)) * 16));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * (NT / 64) * 64 * 16), 16, o, 0, 0, 0);
+    }
+}
+
+template <int BETA, int D>
+__global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const BwdParams p)
+{
+    using G = DkShape<BETA, D>;
+    __shared__ __attribute__((aligned(16))) uint16_t dsm[G::SMEM];
+    extern __shared__ int qlist[];                       // query blocks keeping this key block
+    uint16_t *const Kt = dsm, *const Vt = dsm + G::KV;
+    uint16_t *const Bf0 = dsm + 2 * G::KV;
+    __shared__ int wcount[G::NW];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wv % G::NKG, qh = wv / G::NKG;
     const int hl = lane >> 5, n = lane & 31;
     const int BH = p.B * p.H;
     const int j = blockIdx.x / BH, bh = blockIdx.x - j * BH;
     const int b = bh / p.H, hh = bh - b * p.H;
 
-    // the query blocks whose row lists j (binary search: columns ascend),
-    // in ascending order
+    // query blocks whose row lists j, ascending
     int count = 0;
-    for (int base = 0; base < p.nB; base += Sh::NT) {
+    for (int base = 0; base < p.nB; base += G::NT) {
         const int i = base + tid;
         bool f = false;
         if (i < p.nB) {
@@ -325,7 +432,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 1) void bwd_dkdv_kernel(const BwdPa
         if (lane == 0) wcount[wv] = __popcll(m);
         __syncthreads();
         int pre = count, tot = 0;
-        for (int w = 0; w < Sh::NW; ++w) {
+        for (int w = 0; w < G::NW; ++w) {
             if (w < wv) pre += wcount[w];
             tot += wcount[w];
         }
@@ -333,23 +440,36 @@ __global__ __launch_bounds__(BETA / 32 * 64, 1) void bwd_dkdv_kernel(const BwdPa
         __syncthreads();
         count += tot;
     }
-    const int T = count * Sh::SUB;
+    const int T = count * (BETA / 64);
 
-    const int krow = j * BETA + wv * 32 + n;   // the lane's key
-    const bool kok = krow < p.N;
-    bf16x8 kf[Sh::QS], vf[Sh::QS];
-    {
-        const uint16_t *kb = p.k.p + b * p.k.sb + hh * p.k.sh + (int64_t)krow * p.k.sn;
-        const uint16_t *vb = p.v.p + b * p.v.sb + hh * p.v.sh + (int64_t)krow * p.v.sn;
-#pragma unroll
-        for (int s = 0; s < Sh::QS; ++s) {
-            kf[s] = as_bf16x8(kok ? ld_g16(kb + 16 * s + 8 * hl) : zero_u4());
-            vf[s] = as_bf16x8(kok ? ld_g16(vb + 16 * s + 8 * hl) : zero_u4());
+    const uint16_t *kb = p.k.p + b * p.k.sb + hh * p.k.sh;
+    const uint16_t *vb = p.v.p + b * p.v.sb + hh * p.v.sh;
+    const uint16_t *qb = p.q.p + b * p.q.sb + hh * p.q.sh;
+    const uint16_t *gb = p.dO.p + b * p.dO.sb + hh * p.dO.sh;
+    const __amdgpu_buffer_rsrc_t krs = buffer_desc(kb, (uint32_t)(((int64_t)(p.N - 1) * p.k.sn + D) * 2));
+    const __amdgpu_buffer_rsrc_t vrs = buffer_desc(vb, (uint32_t)(((int64_t)(p.N - 1) * p.v.sn + D) * 2));
+    const __amdgpu_buffer_rsrc_t qrs = buffer_desc(qb, (uint32_t)(((int64_t)(p.N - 1) * p.q.sn + D) * 2));
+    const __amdgpu_buffer_rsrc_t grs = buffer_desc(gb, (uint32_t)(((int64_t)(p.N - 1) * p.dO.sn + D) * 2));
+    const __amdgpu_buffer_rsrc_t lrs = buffer_desc(p.lse2 + (int64_t)bh * p.N, (uint32_t)p.N * 4);
+    const __amdgpu_buffer_rsrc_t drs = buffer_desc(p.delta + (int64_t)bh * p.N, (uint32_t)p.N * 4);
+    auto qstart = [&](int t) { return qlist[t / (BETA / 64)] * BETA + 64 * (t % (BETA / 64)); };
+    auto buf = [&](int t) { return Bf0 + (t & 1) * G::BUF; };
+    auto load = [&](int t) {
+        const int q0 = qstart(t);
+        uint16_t *B0 = buf(t);
+        bw_load_rows<64, D, G::NT>(B0, qrs, p.q.sn, q0, p.N, tid);
+        bw_load_rows<64, D, G::NT>(B0 + G::QT, grs, p.dO.sn, q0, p.N, tid);
+        if (wv == 0) {
+            float *st = reinterpret_cast<float *>(B0 + 2 * G::QT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void *)st, 4, (uint32_t)lane * 4, (uint32_t)q0 * 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void *)(st + 64), 4, (uint32_t)lane * 4,
+                                                     (uint32_t)q0 * 4, 0, 0);
         }
-    }
-    f32x16 dk[Sh::DT], dv[Sh::DT];
+    };
+
+    f32x16 dk[G::DT], dv[G::DT];
 #pragma unroll
-    for (int d = 0; d < Sh::DT; ++d)
+    for (int d = 0; d < G::DT; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             dk[d][r] = 0.f;
@@ -357,97 +477,83 @@ __global__ __launch_bounds__(BETA / 32 * 64, 1) void bwd_dkdv_kernel(const BwdPa
         }
     const float c = p.scale_log2;
     const BwOffsets<D> off = bw_offsets<D>(lane);
-    const uint16_t *qb = p.q.p + b * p.q.sb + hh * p.q.sh;
-    const uint16_t *gb = p.dO.p + b * p.dO.sb + hh * p.dO.sh;
-    const __amdgpu_buffer_rsrc_t qrs = buffer_desc(qb, (uint32_t)(((int64_t)(p.N - 1) * p.q.sn + D) * 2));
-    const __amdgpu_buffer_rsrc_t grs = buffer_desc(gb, (uint32_t)(((int64_t)(p.N - 1) * p.dO.sn + D) * 2));
-    const float *lse2 = p.lse2 + (int64_t)bh * p.N;
-    const float *delta = p.delta + (int64_t)bh * p.N;
-    auto qstart = [&](int t) { return qlist[t / Sh::SUB] * BETA + 64 * (t % Sh::SUB); };
-    const bool vec_stats = ((int64_t)bh * p.N) % 4 == 0;   // 16-byte aligned rows of lse2, delta
+    // B operand rows of the wave's keys in Kt / Vt (natural order)
+    const int krow_l = kg * 32 + n;
+    const uint32_t brow = (uint32_t)(krow_l * D * 2 + 16 * (hl ^ bswz<D>(krow_l)));
 
     if (T > 0) {
-        int q0 = qstart(0);
-        bw_load_tile<BETA, D>(smem, qrs, p.q.sn, q0, p.N, wv, lane);
-        bw_load_tile<BETA, D>(smem + Sh::TILE, grs, p.dO.sn, q0, p.N, wv, lane);
+        bw_load_rows<BETA, D, G::NT>(Kt, krs, p.k.sn, j * BETA, p.N, tid);
+        bw_load_rows<BETA, D, G::NT>(Vt, vrs, p.v.sn, j * BETA, p.N, tid);
+        load(0);
         for (int t = 0; t < T; ++t) {
-            uint16_t *Qc = smem + (t & 1) * 2 * Sh::TILE, *Gc = Qc + Sh::TILE;
-            __syncthreads();
-            int qn = 0;
-            if (t + 1 < T) {
-                qn = qstart(t + 1);
-                uint16_t *Qn = smem + ((t + 1) & 1) * 2 * Sh::TILE;
-                bw_load_tile<BETA, D>(Qn, qrs, p.q.sn, qn, p.N, wv, lane);
-                bw_load_tile<BETA, D>(Qn + Sh::TILE, grs, p.dO.sn, qn, p.N, wv, lane);
+            __syncthreads();                  // sub-tile t in LDS; buffer (t+1)&1 free
+            if (t + 1 < T) load(t + 1);
+            const uint16_t *Qc = buf(t), *Gc = Qc + G::QT;
+            const float *stats = reinterpret_cast<const float *>(Qc + 2 * G::QT);
+            const int q0 = qstart(t) + 32 * qh;
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.f;
+                dp[r] = 0.f;
             }
-            // row statistics of the lane's 32 accumulator rows: query
-            // q0 + 32 kt + 8 hl + koff(r), in groups of 4 consecutive rows
-            // (16-byte loads when the head's rows are 16-byte aligned)
-            float4 l2[2][4], dl[2][4];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int k = 0; k < G::QS; ++k) {
+                const bf16x8 aq = *lds_at<bf16x8>(Qc + qh * 32 * D, off.rows ^ (KSTEP * k));
+                const bf16x8 bk = *lds_at<bf16x8>(Kt, brow ^ (KSTEP * k));
+                s = mfma32x32x16(aq, bk, s);
+                const bf16x8 ag = *lds_at<bf16x8>(Gc + qh * 32 * D, off.rows ^ (KSTEP * k));
+                const bf16x8 bv = *lds_at<bf16x8>(Vt, brow ^ (KSTEP * k));
+                dp = mfma32x32x16(ag, bv, dp);
+            }
+            if (q0 + 32 > p.N) {
+                const int lim = p.N - q0 - 8 * hl;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int r0 = q0 + 32 * kt + 8 * hl + koff(4 * g);
-                    if (vec_stats && r0 + 4 <= p.N) {
-                        l2[kt][g] = *reinterpret_cast<const float4 *>(lse2 + r0);
-                        dl[kt][g] = *reinterpret_cast<const float4 *>(delta + r0);
-                    } else {
-                        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), d4 = a;
-                        if (r0 + 0 < p.N) { a.x = lse2[r0 + 0]; d4.x = delta[r0 + 0]; }
-                        if (r0 + 1 < p.N) { a.y = lse2[r0 + 1]; d4.y = delta[r0 + 1]; }
-                        if (r0 + 2 < p.N) { a.z = lse2[r0 + 2]; d4.z = delta[r0 + 2]; }
-                        if (r0 + 3 < p.N) { a.w = lse2[r0 + 3]; d4.w = delta[r0 + 3]; }
-                        l2[kt][g] = a;
-                        dl[kt][g] = d4;
-                    }
-                }
-            f32x16 s[2], dp[2];
-            bw_rows_mfma<D>(Qc, off.rows, kf, s);
-            bw_rows_mfma<D>(Gc, off.rows, vf, dp);
-            if (q0 + 64 > p.N) mask_keys(s, p.N - q0 - 8 * hl);   // query rows past N
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float lv[4] = {l2[kt][g].x, l2[kt][g].y, l2[kt][g].z, l2[kt][g].w};
-                    const float dv4[4] = {dl[kt][g].x, dl[kt][g].y, dl[kt][g].z, dl[kt][g].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * g + e;
-                        const float pr = fast_exp2(__builtin_fmaf(s[kt][r], c, -lv[e]));
-                        s[kt][r] = pr;                              // P
-                        dp[kt][r] = pr * (dp[kt][r] - dv4[e]);      // dS
-                    }
-                }
-            bf16x8 pp[2][2], ps[2][2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    pp[kt][u] = pack8(s, kt, u);
-                    ps[kt][u] = pack8(dp, kt, u);
-                }
-            bw_tr_mfma<D>(Gc, off, pp, dv);
-            bw_tr_mfma<D>(Qc, off, ps, dk);
-            q0 = qn;
+                for (int r = 0; r < 16; ++r)
+                    if (koff(r) >= lim) s[r] = -INFINITY;
+            }
+            bf16x8 pp[2], ps[2];
+            bw_probs_half(s, dp, stats, qh, c, hl, pp, ps);
+            bw_tr_half<D>(Gc, off, qh, pp, dv);
+            bw_tr_half<D>(Qc, off, qh, ps, dk);
         }
     }
-    if (kok) {
-        const float sc = p.scale;
-        uint16_t *krow_k = p.dk + b * p.dk_sb + hh * p.dk_sh + (int64_t)krow * p.dk_sn;
-        uint16_t *krow_v = p.dv + b * p.dv_sb + hh * p.dv_sh + (int64_t)krow * p.dv_sn;
+
+    // add the two query halves' partial sums through LDS: the second half's
+    // waves park theirs, the first half's add them and store
+    __syncthreads();
+    float *park = reinterpret_cast<float *>(dsm);
+    const int slot0 = (kg * G::DT) * 64 + lane;
+    if (qh == 1) {
 #pragma unroll
-        for (int d = 0; d < Sh::DT; ++d)
+        for (int d = 0; d < G::DT; ++d)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
+                *reinterpret_cast<float4 *>(park + ((slot0 + d * 64) * 2 * 4 + g) * 4) =
+                    make_float4(dk[d][4 * g], dk[d][4 * g + 1], dk[d][4 * g + 2], dk[d][4 * g + 3]);
+                *reinterpret_cast<float4 *>(park + ((slot0 + d * 64) * 2 * 4 + 4 + g) * 4) =
+                    make_float4(dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]);
+            }
+    }
+    __syncthreads();
+    const int krow = j * BETA + kg * 32 + n;
+    if (qh == 0 && krow < p.N) {
+        const float sc = p.scale;
+        uint16_t *rk = p.dk + b * p.dk_sb + hh * p.dk_sh + (int64_t)krow * p.dk_sn;
+        uint16_t *rv = p.dv + b * p.dv_sb + hh * p.dv_sh + (int64_t)krow * p.dv_sn;
+#pragma unroll
+        for (int d = 0; d < G::DT; ++d)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 ok = *reinterpret_cast<const float4 *>(park + ((slot0 + d * 64) * 2 * 4 + g) * 4);
+                const float4 ov = *reinterpret_cast<const float4 *>(park + ((slot0 + d * 64) * 2 * 4 + 4 + g) * 4);
                 uint2 a, v2;
-                a.x = pack_bf16x2(dk[d][4 * g + 0] * sc, dk[d][4 * g + 1] * sc);
-                a.y = pack_bf16x2(dk[d][4 * g + 2] * sc, dk[d][4 * g + 3] * sc);
-                v2.x = pack_bf16x2(dv[d][4 * g + 0], dv[d][4 * g + 1]);
-                v2.y = pack_bf16x2(dv[d][4 * g + 2], dv[d][4 * g + 3]);
-                *reinterpret_cast<uint2 *>(krow_k + d * 32 + 8 * g + 4 * hl) = a;
-                *reinterpret_cast<uint2 *>(krow_v + d * 32 + 8 * g + 4 * hl) = v2;
+                a.x = pack_bf16x2((dk[d][4 * g + 0] + ok.x) * sc, (dk[d][4 * g + 1] + ok.y) * sc);
+                a.y = pack_bf16x2((dk[d][4 * g + 2] + ok.z) * sc, (dk[d][4 * g + 3] + ok.w) * sc);
+                v2.x = pack_bf16x2(dv[d][4 * g + 0] + ov.x, dv[d][4 * g + 1] + ov.y);
+                v2.y = pack_bf16x2(dv[d][4 * g + 2] + ov.z, dv[d][4 * g + 3] + ov.w);
+                *reinterpret_cast<uint2 *>(rk + d * 32 + 8 * g + 4 * hl) = a;
+                *reinterpret_cast<uint2 *>(rv + d * 32 + 8 * g + 4 * hl) = v2;
             }
     }
 }
@@ -459,8 +565,11 @@ static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t s)
     const int64_t grid = (int64_t)p.B * p.H * p.nB;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_dq_kernel<BETA, D>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BETA, D>), dim3((unsigned)grid), dim3(Sh::NT), (size_t)p.nB * sizeof(int), s,
-                       p);
+    using G = DkShape<BETA, D>;
+    static_assert(G::SMEM * 2 + G::NW * 4 + kBwdMaxBlocks * 4 <= 160 * 1024, "dK/dV LDS");
+    if (p.nB > kBwdMaxBlocks) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BETA, D>), dim3((unsigned)grid), dim3(G::NT), (size_t)p.nB * sizeof(int),
+                       s, p);
     return hipGetLastError();
 }
 

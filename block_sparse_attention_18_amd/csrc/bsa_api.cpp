@@ -686,7 +686,7 @@ bsa_status bsa_backward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tens
     if (!row_ptr || !col_idx || !lse) return fail(BSA_ERR_INVALID_ARG, "row_ptr / col_idx / lse null");
     if (std::isnan(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
     const int64_t nB = ceil_div(q->N, block);
-    if (nB > 8192) return fail(BSA_ERR_UNSUPPORTED, "more than 8192 blocks");
+    if (nB > bsa::kBwdMaxBlocks) return fail(BSA_ERR_UNSUPPORTED, "more than %d blocks", bsa::kBwdMaxBlocks);
     if (q->B * q->H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many blocks");
     const size_t need = bsa_backward_workspace_size(q->B, q->H, q->N);
     if (!workspace || !aligned16(workspace) || workspace_bytes < need)

@@ -88,7 +88,10 @@ struct FwdParams {
     NbGeom nb;
 };
 
-// Backward of the forward (see bsa_backward).
+// Backward of the forward (see bsa_backward).  The dK/dV kernel keeps the
+// list of query blocks of its key block in LDS beside the block's K and V
+// and two Q/dO sub-tiles, which bounds the number of blocks per head.
+constexpr int kBwdMaxBlocks = 7680;
 struct BwdParams {
     Tensor4 q, k, v, o, dO;
     const float *lse;           // [B][H][N], natural log

@@ -226,7 +226,7 @@ bsa_status bsa_forward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tenso
  * no kept block give zero gradients).  The workspace
  * (bsa_backward_workspace_size bytes, 16-byte aligned) holds two fp32
  * [B][H][N] arrays.  Results are deterministic.  Errors: INVALID_ARG,
- * UNSUPPORTED (D, block, more than 8192 blocks), WORKSPACE.
+ * UNSUPPORTED (D, block, more than 7680 blocks per head), WORKSPACE.
  * ---------------------------------------------------------------------- */
 size_t bsa_backward_workspace_size(int64_t B, int64_t H, int64_t N);
 bsa_status bsa_backward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_tensor *o,
