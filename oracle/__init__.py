@@ -11,6 +11,8 @@ library is compiled with gcc on first use (or by ``build()``).
 Every function follows the definitions stated in ``bsa_oracle.c``:
   pool_mean               mean of each block's rows
   scores_meanpool_proj    S_ij = (W^T qbar_i) . (W^T kbar_j)
+  score_grad              its vector-Jacobian product: dW, dqbar, dkbar for
+                          an upstream gradient dS
   scores_exact_avgpool    S_ij = block-average of softmax(scale * Q K^T)
   select_rows / select    text rows dense, text columns forced, top-k per
                           column group with lower-index tie-break
@@ -73,6 +75,8 @@ def _load():
         lib.oracle_pool_mean.restype = ctypes.c_int
         lib.oracle_scores_meanpool_proj.argtypes = [P, P, I, I, I, I, I, P, I, P]
         lib.oracle_scores_meanpool_proj.restype = ctypes.c_int
+        lib.oracle_score_grad.argtypes = [P, P, I, I, I, I, I, P, I, P, P, P, P]
+        lib.oracle_score_grad.restype = ctypes.c_int
         lib.oracle_scores_exact_avgpool.argtypes = [P, P, I, I, I, I, I, D, P, I, P]
         lib.oracle_scores_exact_avgpool.restype = ctypes.c_int
         lib.oracle_select_rows.argtypes = [P, P, I, I, I, P, I, P, P, I]
@@ -143,6 +147,26 @@ def scores_meanpool_proj(q: np.ndarray, k: np.ndarray, block: int, w: np.ndarray
     _check(_load().oracle_scores_meanpool_proj(_ptr(q), _ptr(k), B, H, N, D, block,
                                                _ptr(w), w.shape[1], _ptr(S)), "scores_meanpool_proj")
     return S
+
+
+def score_grad(q: np.ndarray, k: np.ndarray, block: int, w: np.ndarray,
+               dS: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradient of L with dL/dS = dS through S = scores_meanpool_proj(q, k,
+    block, w): returns fp64 (dW [D, r], dqbar [B,H,nB,D], dkbar [B,H,nB,D])."""
+    q, k = _u16(q), _u16(k)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    B, H, N, D = q.shape
+    r = w.shape[1]
+    nB = n_blocks(N, block)
+    assert k.shape == q.shape and w.shape[0] == D
+    dS = np.ascontiguousarray(dS, dtype=np.float64)
+    assert dS.shape == (B, H, nB, nB)
+    dW = np.empty((D, r), dtype=np.float64)
+    dq = np.empty((B, H, nB, D), dtype=np.float64)
+    dk = np.empty((B, H, nB, D), dtype=np.float64)
+    _check(_load().oracle_score_grad(_ptr(q), _ptr(k), B, H, N, D, block, _ptr(w), r, _ptr(dS),
+                                     _ptr(dW), _ptr(dq), _ptr(dk)), "score_grad")
+    return dW, dq, dk
 
 
 def scores_exact_avgpool(q: np.ndarray, k: np.ndarray, block: int, scale: Optional[float] = None,

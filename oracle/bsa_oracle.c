@@ -140,6 +140,91 @@ done:
 }
 
 /* ------------------------------------------------------------------------
+ * Gradient of the content-driven block score (block-sparse DiT write-up,
+ * 2.2, where the projection is trained jointly with the model).  The pages
+ * give no loss, so this is the vector-Jacobian product of the score map for
+ * a caller's upstream gradient dS = dL/dS [B][H][nB][nB]:
+ *   S_ij = p_i . p'_j,  p_i = W^T qbar_i,  p'_j = W^T kbar_j
+ *   dL/dp_i  = sum_j dS_ij p'_j          dL/dp'_j = sum_i dS_ij p_i
+ *   dL/dW    = sum_{b,h} ( sum_i qbar_i (dL/dp_i)^T + sum_j kbar_j (dL/dp'_j)^T )
+ *   dL/dqbar_i = W dL/dp_i,   dL/dkbar_j = W dL/dp'_j
+ * dW is [D][r] row-major; dqbar, dkbar are [B][H][nB][D] (either may be
+ * NULL).  The gradient of a token of block i is dL/dqbar_i / n_i.
+ * ---------------------------------------------------------------------- */
+int oracle_score_grad(const uint16_t *q, const uint16_t *k,
+                      int64_t B, int64_t H, int64_t N, int64_t D, int64_t beta,
+                      const float *w, int64_t r, const double *dS,
+                      double *dW, double *dqbar, double *dkbar)
+{
+    if (!q || !k || !w || !dS || !dW || r <= 0) return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta);
+    const int64_t total = B * H * nB;
+    double *qbar = malloc(sizeof(double) * total * D);
+    double *kbar = malloc(sizeof(double) * total * D);
+    double *pq = malloc(sizeof(double) * total * r);
+    double *pk = malloc(sizeof(double) * total * r);
+    double *gq = malloc(sizeof(double) * total * r);
+    double *gk = malloc(sizeof(double) * total * r);
+    int rc = OR_OK;
+    if (!qbar || !kbar || !pq || !pk || !gq || !gk) { rc = OR_ENOMEM; goto done; }
+    if ((rc = oracle_pool_mean(q, B, H, N, D, beta, qbar)) != OR_OK) goto done;
+    if ((rc = oracle_pool_mean(k, B, H, N, D, beta, kbar)) != OR_OK) goto done;
+
+    /* the projections, as in the score itself */
+#pragma omp parallel for schedule(static)
+    for (int64_t item = 0; item < total; ++item) {
+        for (int64_t m = 0; m < r; ++m) {
+            double a = 0.0, c = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                a += (double)w[d * r + m] * qbar[item * D + d];
+                c += (double)w[d * r + m] * kbar[item * D + d];
+            }
+            pq[item * r + m] = a;
+            pk[item * r + m] = c;
+        }
+    }
+    /* dL/dp_i over the row i of dS, dL/dp'_j over the column j */
+#pragma omp parallel for schedule(static)
+    for (int64_t item = 0; item < total; ++item) {
+        const int64_t bh = item / nB, x = item % nB;
+        for (int64_t m = 0; m < r; ++m) {
+            double a = 0.0, c = 0.0;
+            for (int64_t y = 0; y < nB; ++y) {
+                a += dS[(bh * nB + x) * nB + y] * pk[(bh * nB + y) * r + m];
+                c += dS[(bh * nB + y) * nB + x] * pq[(bh * nB + y) * r + m];
+            }
+            gq[item * r + m] = a;
+            gk[item * r + m] = c;
+        }
+    }
+    /* dW: the outer products summed over every block of every head */
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < D * r; ++e) {
+        const int64_t d = e / r, m = e % r;
+        double s = 0.0;
+        for (int64_t item = 0; item < total; ++item)
+            s += qbar[item * D + d] * gq[item * r + m] + kbar[item * D + d] * gk[item * r + m];
+        dW[e] = s;
+    }
+    /* the pooled blocks' gradients */
+#pragma omp parallel for schedule(static)
+    for (int64_t item = 0; item < total; ++item) {
+        for (int64_t d = 0; d < D; ++d) {
+            double a = 0.0, c = 0.0;
+            for (int64_t m = 0; m < r; ++m) {
+                a += (double)w[d * r + m] * gq[item * r + m];
+                c += (double)w[d * r + m] * gk[item * r + m];
+            }
+            if (dqbar) dqbar[item * D + d] = a;
+            if (dkbar) dkbar[item * D + d] = c;
+        }
+    }
+done:
+    free(qbar); free(kbar); free(pq); free(pk); free(gq); free(gk);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
  * Exact block score (SparseD notes, isolated selection):
  *   A_ts = softmax_s(scale * Q_t . K_s) over all N keys of the head;
  *   S_ij = (1 / (n_i n_j)) * sum_{t in block i} sum_{s in block j} A_ts.
