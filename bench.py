@@ -72,6 +72,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward (dQ, dK, dV) of the forward on the workload's "
                          "layout, for a synthetic output gradient")
+    ap.add_argument("--score-grad", action="store_true",
+                    help="also time the gradient of the mean-pool / projection block score "
+                         "(dW and the pooled dQ, dK) for a seeded upstream gradient")
     ap.add_argument("--fp8", action="store_true",
                     help="run the forward in the FP8 (E4M3) mode on inputs quantised once "
                          "before the timed region (quantisation timed separately)")
@@ -366,6 +369,10 @@ def main():
                                                        and np.any(fwd_kw["head_modes"] == bsa.HEAD_SKIP)):
             raise SystemExit("--backward: block layouts without SKIP heads, bf16 only")
         res["backward"] = backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx, kept_pairs)
+    if args.score_grad:
+        if wl.score_mode != bsa.SCORE_MEANPOOL_PROJ or wl.layout in ("arrow", "neighborhood"):
+            raise SystemExit("--score-grad: a workload scored by mean-pool / projection (C1, C3)")
+        res["score_grad"] = score_grad_bench(torch, bsa, dev, stream, wl, q, k, w)
     if args.cpu_seconds > 0 and not args.fp8:
         res["cpu_baseline"] = cpu_baseline(wl, x, row_ptr, col_idx, args.cpu_seconds,
                                            fwd_kw.get("head_modes"))
@@ -605,6 +612,37 @@ def backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx
             "executed_tflops": round(1.4 * alg / (med * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(alg / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "flop_per_pair": "10 * block^2 * D (dQ, dK, dV, dP, S); 14 executed"}
+
+
+def score_grad_bench(torch, bsa, dev, stream, wl, q, k, w, reps=50):
+    """Times bsa_score_grad (pooling, g = dS p' and dS^T p, W g, the per-head
+    partial dW and its reduction) for a seeded N(0, 1) upstream gradient.
+    Algorithmic bytes: Q and K read once (bf16), dS read once, dW and the
+    pooled gradients written once (fp32)."""
+    B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
+    nB, r = bsa.n_blocks(N, block), int(w.shape[1])
+    g = np.random.default_rng(wl.seed + 3000).standard_normal((B, H, nB, nB)).astype(np.float32)
+    dS = torch.from_numpy(g).to(dev)
+    dw = torch.empty((D, r), dtype=torch.float32, device=dev)
+    dqp = torch.empty((B, H, nB, D), dtype=torch.float32, device=dev)
+    dkp = torch.empty_like(dqp)
+    ws = torch.empty(bsa.score_grad_workspace_size(B, H, N, D, block, r), dtype=torch.uint8, device=dev)
+
+    def run():
+        bsa.score_grad(q, k, block, w, dS, dw=dw, dq_pool=dqp, dk_pool=dkp, workspace=ws)
+    for _ in range(5):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(reps):
+        ev[i].record(stream)
+        run()
+    ev[reps].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+    alg = 2 * B * H * N * D * 2 + B * H * nB * nB * 4 + D * r * 4 + 2 * B * H * nB * D * 4
+    return {"ms": round(ms, 4), "algorithmic_bytes": alg, "GB_per_s": round(alg / (ms * 1e-3) / 1e9, 1),
+            "kernels": "pool_proj, score_grad_p, score_grad_w, score_grad_reduce"}
 
 
 def cpu_baseline(wl, x, row_ptr, col_idx, seconds, modes):

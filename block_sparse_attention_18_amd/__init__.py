@@ -117,6 +117,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         sig = {
             "bsa_pool_scores_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32, I32]),
             "bsa_pool_scores": (I32, [TP, TP, I32, I32, V, I32, F, V, V, SZ, V]),
+            "bsa_score_grad_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32]),
+            "bsa_score_grad": (I32, [TP, TP, I32, V, I32, V, V, V, V, V, SZ, V]),
             "bsa_select_capacity": (I64, [I64, I64, I32, I32, GP, I32]),
             "bsa_select_workspace_size": (SZ, [I64, I64, I32]),
             "bsa_select_topk": (I32, [V, I64, I64, I32, I32, GP, I32, V, V, I64, V, SZ, V]),
@@ -221,6 +223,47 @@ def pool_scores(q: torch.Tensor, k: torch.Tensor, block: int, mode: int = SCORE_
                                float(scale or 0.0), _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(q.device)))
     return out
+
+
+def score_grad_workspace_size(B, H, N, D, block, r) -> int:
+    return int(load().bsa_score_grad_workspace_size(B, H, N, D, block, r))
+
+
+def score_grad(q: torch.Tensor, k: torch.Tensor, block: int, w: torch.Tensor, dscores: torch.Tensor,
+               dw: Optional[torch.Tensor] = None, dq_pool: Optional[torch.Tensor] = None,
+               dk_pool: Optional[torch.Tensor] = None, pooled: bool = True,
+               workspace: Optional[torch.Tensor] = None):
+    """Gradient of the MEANPOOL_PROJ score for the upstream gradient dscores
+    = dL/dS [B, H, nB, nB] (fp32): returns (dW [D, r], dL/dqbar, dL/dkbar
+    [B, H, nB, D]); the pooled gradients are None with pooled=False."""
+    lib = load()
+    B, H, N, D = q.shape
+    nB = n_blocks(N, block)
+    if w is None or w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 2:
+        raise ValueError("w must be a contiguous fp32 [D, r] device tensor")
+    r = int(w.shape[1])
+    if (dscores.dtype != torch.float32 or not dscores.is_contiguous()
+            or tuple(dscores.shape) != (B, H, nB, nB)):
+        raise ValueError("dscores must be a contiguous fp32 [B, H, nB, nB] device tensor")
+    if dw is None:
+        dw = torch.empty((D, r), dtype=torch.float32, device=q.device)
+    if pooled:
+        if dq_pool is None:
+            dq_pool = torch.empty((B, H, nB, D), dtype=torch.float32, device=q.device)
+        if dk_pool is None:
+            dk_pool = torch.empty((B, H, nB, D), dtype=torch.float32, device=q.device)
+    for name, t, shape in (("dw", dw, (D, r)), ("dq_pool", dq_pool, (B, H, nB, D)),
+                           ("dk_pool", dk_pool, (B, H, nB, D))):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape):
+            raise ValueError(f"{name} must be a contiguous fp32 {list(shape)} device tensor")
+    if workspace is None:
+        workspace = torch.empty(max(score_grad_workspace_size(B, H, N, D, block, r), 16), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk = _desc(q, "q"), _desc(k, "k")
+    _check(lib.bsa_score_grad(ctypes.byref(dq), ctypes.byref(dk), block, _ptr(w), r, _ptr(dscores), _ptr(dw),
+                              _ptr(dq_pool), _ptr(dk_pool), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return dw, dq_pool, dk_pool
 
 
 def select_capacity(B, H, nB, text_blocks, groups) -> int:

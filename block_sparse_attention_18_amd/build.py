@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["bsa_api.cpp", "forward.hip", "backward.hip", "fp8.hip", "diag.hip", "neighborhood.hip", "scores.hip", "select.hip", "arrow.hip"]
+SOURCES = ["bsa_api.cpp", "forward.hip", "backward.hip", "fp8.hip", "diag.hip", "neighborhood.hip", "scores.hip", "score_grad.hip", "select.hip", "arrow.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -229,6 +229,72 @@ bsa_status bsa_pool_scores(const bsa_tensor *q, const bsa_tensor *k, int32_t blo
     return BSA_OK;
 }
 
+static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t bsa_score_grad_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int32_t block, int32_t r)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || !block_ok(block) || r < 1 || r > 64) return 0;
+    const size_t rows = (size_t)(B * H * ceil_div(N, block));
+    const size_t f = sizeof(float);
+    const size_t parts = (size_t)(B * H) * (size_t)ceil_div(ceil_div(N, block), bsa::kGradChunk);
+    return up256(2 * rows * r * f) + up256(2 * rows * D * f) + up256(2 * rows * r * f) + up256(parts * D * r * f);
+}
+
+bsa_status bsa_score_grad(const bsa_tensor *q, const bsa_tensor *k, int32_t block, const float *w, int32_t r,
+                          const float *dscores, float *dw, float *dq_pool, float *dk_pool, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSA_OK) return st;
+    if (!same_shape(q, k)) return fail(BSA_ERR_INVALID_ARG, "q and k shapes differ");
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    if (!w || !dscores || !dw) return fail(BSA_ERR_INVALID_ARG, "w / dscores / dw null");
+    if (r < 1 || r > 64) return fail(BSA_ERR_INVALID_ARG, "projection width r=%d outside 1..64", r);
+    const int64_t nB = ceil_div(q->N, block);
+    if (q->B * q->H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many blocks");
+    const size_t need = bsa_score_grad_workspace_size(q->B, q->H, q->N, q->D, block, r);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        return fail(BSA_ERR_WORKSPACE, "score gradient workspace needs %zu bytes (16-byte aligned)", need);
+    const size_t rows = (size_t)(q->B * q->H * nB);
+    char *ws = static_cast<char *>(workspace);
+    float *proj = reinterpret_cast<float *>(ws);
+    ws += up256(2 * rows * r * sizeof(float));
+    float *mean = reinterpret_cast<float *>(ws);
+    ws += up256(2 * rows * q->D * sizeof(float));
+    float *g = reinterpret_cast<float *>(ws);
+    ws += up256(2 * rows * r * sizeof(float));
+    float *wpart = reinterpret_cast<float *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+
+    bsa::PoolParams pp{};
+    pp.x[0] = t4(q);
+    pp.x[1] = t4(k);
+    pp.w = w;
+    pp.proj = proj;
+    pp.mean = mean;
+    pp.B = (int32_t)q->B; pp.H = (int32_t)q->H; pp.N = (int32_t)q->N;
+    pp.nB = (int32_t)nB; pp.r = r;
+    if ((e = bsa::launch_pool_proj(pp, block, (int)q->D, s)) != hipSuccess) return hip_fail(e, "pool launch");
+    bsa::ScoreGradParams gp{};
+    gp.proj = proj;
+    gp.mean = mean;
+    gp.dS = dscores;
+    gp.w = w;
+    gp.g = g;
+    gp.dpool[0] = dq_pool;
+    gp.dpool[1] = dk_pool;
+    gp.wpart = wpart;
+    gp.dw = dw;
+    gp.BH = (int32_t)(q->B * q->H);
+    gp.nB = (int32_t)nB;
+    gp.D = (int32_t)q->D;
+    gp.r = r;
+    if ((e = bsa::launch_score_grad(gp, s)) != hipSuccess) return hip_fail(e, "score gradient launch");
+    return BSA_OK;
+}
+
 // ---------------------------------------------------------------------------
 int64_t bsa_select_capacity(int64_t B, int64_t H, int32_t n_blocks, int32_t text_blocks,
                             const bsa_group *groups, int32_t n_groups)

@@ -161,7 +161,23 @@ struct PoolParams {
     Tensor4 x[2];               // q, k
     const float *w;             // [D][r]
     float *proj;                // [2][B*H*nB][r]
+    float *mean;                // [2][B*H*nB][D] block means, or null
     int32_t B, H, N, nB, r;
+};
+
+// Gradient of the projected score (see bsa_score_grad); dW is summed from
+// partials over chunks of kGradChunk blocks of a head.
+constexpr int kGradChunk = 16;
+struct ScoreGradParams {
+    const float *proj;          // [2][BH*nB][r]   p_i, p'_j
+    const float *mean;          // [2][BH*nB][D]   qbar_i, kbar_j
+    const float *dS;            // [BH][nB][nB]
+    const float *w;             // [D][r]
+    float *g;                   // [2][BH*nB][r]   dL/dp_i, dL/dp'_j
+    float *dpool[2];            // [BH*nB][D] dL/dqbar, dL/dkbar, or null
+    float *wpart;               // [BH * chunks][D*r] partial dW per chunk of blocks
+    float *dw;                  // [D][r]
+    int32_t BH, nB, D, r;
 };
 
 struct ScoreParams {
@@ -259,6 +275,7 @@ hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s);
 __host__ __device__ inline int64_t partial_slot_floats(int block, int D) { return (int64_t)block * D + 2 * block; }
 hipError_t launch_pool_proj(const PoolParams &p, int block, int D, hipStream_t s);
 hipError_t launch_scores(const ScoreParams &p, hipStream_t s);
+hipError_t launch_score_grad(const ScoreGradParams &p, hipStream_t s);
 hipError_t launch_exact_scores(const ExactParams &p, int block, int D, int slots, hipStream_t s);
 hipError_t launch_select(const SelectParams &p, hipStream_t s);
 hipError_t launch_scan(int32_t *row_ptr, int64_t rows, hipStream_t s);

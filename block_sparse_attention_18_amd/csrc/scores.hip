@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256) void pool_proj_kernel(const PoolParams p, int 
         float s = 0.f;
         for (int r = 0; r < RS; ++r) s += red[r][tid];
         mean[tid] = s / (float)n_i;
+        if (p.mean) p.mean[((int64_t)which * p.B * p.H * p.nB + item) * D + tid] = mean[tid];
     }
     __syncthreads();
     if (tid < p.r) {

@@ -115,6 +115,36 @@ bsa_status bsa_pool_scores(const bsa_tensor *q, const bsa_tensor *k, int32_t blo
                            void *stream);
 
 /* ------------------------------------------------------------------------
+ * bsa_score_grad -- gradient of the BSA_SCORE_MEANPOOL_PROJ score ([W] 2.2:
+ * the projection is trained jointly with the model).  The pages state no
+ * loss, so this is the vector-Jacobian product of the score map for the
+ * caller's upstream gradient dscores = dL/dS:
+ *   p_i = W^T qbar_i,  p'_j = W^T kbar_j,  S_ij = p_i . p'_j
+ *   g_i = sum_j dS_ij p'_j,   g'_j = sum_i dS_ij p_i
+ *   dw      = sum over b, h and blocks of  qbar_i g_i^T + kbar_j g'_j^T
+ *   dq_pool = W g_i (dL/dqbar_i),  dk_pool = W g'_j (dL/dkbar_j)
+ *
+ * q, k, block, w [D][r], r: as for bsa_pool_scores (device; r in 1..64).
+ * dscores: fp32 [B][H][nB][nB], row-major, device.
+ * dw: fp32 [D][r], device, overwritten (summed over batch and heads).
+ * dq_pool, dk_pool: fp32 [B][H][nB][D], device, overwritten, or NULL when
+ *   not wanted.  A token t of block i has dL/dQ_t = dq_pool_i / n_i (n_i =
+ *   the tokens of block i), and likewise for K.
+ * workspace: at least bsa_score_grad_workspace_size() bytes of device
+ *   memory, 16-byte aligned (scratch; contents on return are unspecified).
+ * Deterministic: fixed summation orders, no atomics.
+ * Errors: INVALID_ARG (null pointers, q/k shapes differ, r outside 1..64,
+ * misaligned data or strides), UNSUPPORTED (D, block, more than 2^31 - 1
+ * blocks), WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t bsa_score_grad_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D,
+                                     int32_t block, int32_t r);
+bsa_status bsa_score_grad(const bsa_tensor *q, const bsa_tensor *k, int32_t block,
+                          const float *w, int32_t r, const float *dscores, float *dw,
+                          float *dq_pool, float *dk_pool, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * bsa_select_topk -- CSR block list from a score matrix ([W] 2.2, 2.3;
  * [S] isolated selection).  For row (b, h, i):
  *   - a text query block (i < text_blocks) keeps every key block;

@@ -159,6 +159,32 @@ def test_pool_scores_validation():
     assert need_exact == (1 * 2 * 4) * 4 * 64 * 4
 
 
+def test_score_grad_validation_and_workspace():
+    lib = bsa.load()
+    q, k = _t(), _t()
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    call = lambda w=FAKE, r=32, ds=FAKE, dw=FAKE, ws=FAKE, wsb=1 << 20, block=64, kk=k: lib.bsa_score_grad(
+        ctypes.byref(q), ctypes.byref(kk), block, P(w), r, P(ds), P(dw), None, None, P(ws), wsb, None)
+    assert call(w=0) == 1 and call(ds=0) == 1 and call(dw=0) == 1
+    assert call(r=0) == 1 and call(r=65) == 1
+    assert call(block=96) == 2
+    assert call(wsb=64) == 4 and "workspace" in _err()
+    assert call(ws=0) == 4 and call(ws=FAKE + 8) == 4
+    k2 = _t(N=128)
+    assert call(kk=k2) == 1 and "shapes differ" in _err()
+    # proj, means, g (per block and side) and a partial dW per chunk of 16
+    # blocks of a head, each 256-byte aligned
+    up = lambda x: (x + 255) // 256 * 256
+    rows = 1 * 2 * 4
+    assert lib.bsa_score_grad_workspace_size(1, 2, 256, 64, 64, 32) == \
+        up(2 * rows * 32 * 4) + up(2 * rows * 64 * 4) + up(2 * rows * 32 * 4) + up(2 * 1 * 64 * 32 * 4)
+    rows = 1 * 2 * 17                               # 17 blocks: two chunks per head
+    assert lib.bsa_score_grad_workspace_size(1, 2, 17 * 64, 128, 64, 8) == \
+        up(2 * rows * 8 * 4) + up(2 * rows * 128 * 4) + up(2 * rows * 8 * 4) + up(2 * 2 * 128 * 8 * 4)
+    assert lib.bsa_score_grad_workspace_size(1, 2, 256, 64, 64, 0) == 0
+    assert lib.bsa_score_grad_workspace_size(1, 2, 256, 64, 96, 32) == 0
+
+
 def test_select_validation_and_capacity():
     lib = bsa.load()
     G = bsa.BsaGroup
