@@ -359,8 +359,24 @@ bsa_status bsa_select_topk(const float *scores, int64_t B, int64_t H, int32_t n_
         sp.g_end[g] = groups[g].col_end;
         sp.g_k[g] = groups[g].k;
     }
+    // disjoint groups that leave the text columns alone fix every row's length
+    bool direct = true;
+    for (int32_t g = 0; g < n_groups && direct; ++g) {
+        const bsa_group &a = groups[g];
+        if (a.k == 0) continue;
+        if (a.col_begin < text_blocks) direct = false;
+        for (int32_t h = g + 1; h < n_groups && direct; ++h) {
+            const bsa_group &b = groups[h];
+            if (b.k > 0 && a.col_begin < b.col_end && b.col_begin < a.col_end) direct = false;
+        }
+    }
+    sp.direct = direct ? 1 : 0;
+    sp.row_len = (int32_t)select_row_bound(n_blocks, text_blocks, groups, n_groups);
+    sp.col_idx = col_idx;
+    sp.capacity = capacity;
     hipError_t e;
     if ((e = bsa::launch_select(sp, s)) != hipSuccess) return hip_fail(e, "select launch");
+    if (direct) return BSA_OK;
     if ((e = bsa::launch_scan(row_ptr, rows, s)) != hipSuccess) return hip_fail(e, "scan launch");
     bsa::ExpandParams xp{};
     xp.bits = sp.bits;

@@ -196,10 +196,13 @@ struct ExactParams {
 
 struct SelectParams {
     const float *S;             // [rows][nB]
-    int32_t *row_ptr;           // counts written to row_ptr[r + 1]
-    uint32_t *bits;             // [rows][words]
-    int64_t rows;
+    int32_t *row_ptr;           // counts written to row_ptr[r + 1] (direct: offsets)
+    uint32_t *bits;             // [rows][words] (two-pass path only)
+    int32_t *col_idx;           // direct path only
+    int64_t rows, capacity;
     int32_t nB, words, text_blocks, n_groups;
+    int32_t direct;             // row lengths known: write row_ptr and col_idx in place
+    int32_t row_len;            // length of a non-text row on the direct path
     int32_t g_begin[8], g_end[8], g_k[8];
 };
 

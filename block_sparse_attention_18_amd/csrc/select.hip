@@ -14,6 +14,10 @@
 //  2. scan: one workgroup turns the row lengths into row_ptr in place.
 //  3. expand: one wavefront per row writes the set bits as ascending
 //     column indices at row_ptr[row].
+// When the column groups are pairwise disjoint and leave the text columns
+// alone, every row's length is known beforehand (text rows nB, the others
+// text_blocks + sum of k), so select writes its row_ptr entry and its
+// column indices itself and the other two kernels are not launched.
 #include "common.h"
 #include "internal.h"
 
@@ -124,6 +128,32 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectParams p)
             else select_group<16>(srow, c0, c1, kk, wbits);
             __syncthreads();
         }
+    }
+    if (p.direct) {
+        // closed-form offsets: each head holds text_blocks rows of nB columns,
+        // then nB - text_blocks rows of row_len columns
+        const int64_t tb = p.text_blocks;
+        const int64_t head = tb * p.nB + (int64_t)(p.nB - tb) * p.row_len;
+        int64_t start = (row / p.nB) * head + (i < tb ? (int64_t)i * p.nB : tb * p.nB + (int64_t)(i - tb) * p.row_len);
+        if (lane == 0) {
+            p.row_ptr[row + 1] = (int32_t)(start + (i < tb ? p.nB : p.row_len));
+            if (row == 0) p.row_ptr[0] = 0;
+        }
+        for (int w0 = 0; w0 < p.words; w0 += 64) {
+            const int w = w0 + lane;
+            uint32_t v = w < p.words ? wbits[w] : 0u;
+            const int c = __popc(v);
+            const int incl = wave_incl_scan(c);
+            int64_t pos = start + incl - c;
+            while (v) {
+                const int bit = __ffs(v) - 1;
+                v &= v - 1u;
+                if (pos < p.capacity) p.col_idx[pos] = w * 32 + bit;
+                ++pos;
+            }
+            start += __shfl(incl, 63, 64);
+        }
+        return;
     }
     int cnt = 0;
     for (int w = lane; w < p.words; w += 64) {

@@ -242,6 +242,10 @@ SELECT_CASES = [
     (1, 1, 1024, 2, ((2, 1024, 300),), 5),
     (1, 2, 100, 0, ((0, 100, 100), (0, 1, 1)), 0),            # k = width; overlapping groups
     (1, 2, 70, 70, ((0, 70, 3),), 0),                         # every row is a text row
+    # disjoint groups clear of the text columns (row lengths in closed form,
+    # one kernel): a gap, a k = 0 group, k = width
+    (2, 2, 37, 3, ((3, 20, 5), (25, 37, 12), (20, 25, 0)), 2),
+    (1, 3, 9, 2, (), 0),                                      # no groups: text columns only
 ]
 
 
