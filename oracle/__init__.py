@@ -26,6 +26,8 @@ Every function follows the definitions stated in ``bsa_oracle.c``:
                           token order, block layout with full / partial flags
   forward_f64 / backward  the forward on fp64 inputs and its gradient
                           (dQ, dK, dV of the kept-block softmax)
+  forward_neighborhood_f64 / backward_neighborhood
+                          the same under the 2-D neighbourhood token mask
   output_rse              per-head relative squared error of an output
   mask_jaccard            per-head Jaccard similarity of two block masks
 """
@@ -75,6 +77,11 @@ def _load():
         lib.oracle_pool_mean.restype = ctypes.c_int
         lib.oracle_scores_meanpool_proj.argtypes = [P, P, I, I, I, I, I, P, I, P]
         lib.oracle_scores_meanpool_proj.restype = ctypes.c_int
+        D_ = ctypes.c_double
+        lib.oracle_forward_neighborhood_f64.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, D_, P, P]
+        lib.oracle_forward_neighborhood_f64.restype = ctypes.c_int
+        lib.oracle_backward_neighborhood_f64.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, D_, P, P, P]
+        lib.oracle_backward_neighborhood_f64.restype = ctypes.c_int
         lib.oracle_score_grad.argtypes = [P, P, I, I, I, I, I, P, I, P, P, P, P]
         lib.oracle_score_grad.restype = ctypes.c_int
         lib.oracle_scores_exact_avgpool.argtypes = [P, P, I, I, I, I, I, D, P, I, P]
@@ -484,4 +491,33 @@ def backward(q, k, v, dO, block: int, row_ptr, col_idx, scale: Optional[float] =
     dQ = np.empty_like(q); dK = np.empty_like(q); dV = np.empty_like(q)
     _check(_load().oracle_backward_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), B, H, N, D, block, _ptr(rp), _ptr(ci),
                                        scale, _ptr(dQ), _ptr(dK), _ptr(dV)), "backward")
+    return dQ, dK, dV
+
+
+def forward_neighborhood_f64(q, k, v, text_len: int, grid: Tuple[int, int], window: Tuple[int, int],
+                             stride: Tuple[int, int] = (1, 1), scale: Optional[float] = None):
+    """The neighbourhood forward on fp64 (or bf16-bit) inputs, natural token
+    order: (O, LSE) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    (R, C), (kh, kw), (sh, sw) = grid, window, stride
+    O = np.empty((B, H, N, D), np.float64); L = np.empty((B, H, N), np.float64)
+    _check(_load().oracle_forward_neighborhood_f64(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, text_len, R, C, kh, kw,
+                                                   sh, sw, scale, _ptr(O), _ptr(L)), "forward_neighborhood_f64")
+    return O, L
+
+
+def backward_neighborhood(q, k, v, dO, text_len: int, grid: Tuple[int, int], window: Tuple[int, int],
+                          stride: Tuple[int, int] = (1, 1), scale: Optional[float] = None):
+    """(dQ, dK, dV) in fp64 of the neighbourhood forward (natural token order)
+    for the output gradient dO (fp64 or bf16-bit inputs)."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    (R, C), (kh, kw), (sh, sw) = grid, window, stride
+    dQ = np.empty_like(q); dK = np.empty_like(q); dV = np.empty_like(q)
+    _check(_load().oracle_backward_neighborhood_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), B, H, N, D, text_len, R, C,
+                                                    kh, kw, sh, sw, scale, _ptr(dQ), _ptr(dK), _ptr(dV)),
+           "backward_neighborhood")
     return dQ, dK, dV

@@ -1001,3 +1001,117 @@ int oracle_backward_f64(const double *q, const double *k, const double *v, const
     }
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the 2-D neighbourhood attention (GNA notes, 1.1), natural
+ * token order, fp64 inputs: the gradient of the dense softmax under the
+ * token mask na_token_keep (the same formulas as oracle_backward_f64 with
+ * that mask in place of the kept blocks).  oracle_forward_neighborhood_f64
+ * is the forward on the same fp64 inputs (for finite-difference checks).
+ * Every query keeps at least the keys of its window, so no row is empty.
+ * ---------------------------------------------------------------------- */
+static void na_row_probs(const double *q, const double *k, int64_t N, int64_t D, int64_t bh, int64_t t,
+                         const na_geom *g, double scale, double *p, double *lse)
+{
+    double m = -INFINITY;
+    for (int64_t s = 0; s < N; ++s) {
+        if (!na_token_keep(t, s, g)) { p[s] = -INFINITY; continue; }
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc += q[(bh * N + t) * D + d] * k[(bh * N + s) * D + d];
+        p[s] = scale * acc;
+        if (p[s] > m) m = p[s];
+    }
+    double l = 0.0;
+    for (int64_t s = 0; s < N; ++s) {
+        p[s] = p[s] == -INFINITY ? 0.0 : exp(p[s] - m);
+        l += p[s];
+    }
+    for (int64_t s = 0; s < N; ++s) p[s] /= l;
+    if (lse) *lse = m + log(l);
+}
+
+int oracle_forward_neighborhood_f64(const double *q, const double *k, const double *v, int64_t B, int64_t H,
+                                    int64_t N, int64_t D, int64_t text_len, int64_t R, int64_t C, int64_t kh,
+                                    int64_t kw, int64_t sh, int64_t sw, double scale, double *O, double *LSE)
+{
+    if (!q || !k || !v || !O || !LSE || B <= 0 || H <= 0 || D <= 0 || !na_check(N, text_len, R, C, kh, kw, sh, sw))
+        return OR_EINVAL;
+    const na_geom g = {text_len, R, C, kh, kw, sh, sw};
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *p = malloc(sizeof(double) * N);
+        if (!p) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t row = 0; row < B * H * N; ++row) {
+                const int64_t bh = row / N, t = row % N;
+                na_row_probs(q, k, N, D, bh, t, &g, scale, p, &LSE[row]);
+                for (int64_t d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int64_t s = 0; s < N; ++s)
+                        if (p[s] != 0.0) acc += p[s] * v[(bh * N + s) * D + d];
+                    O[row * D + d] = acc;
+                }
+            }
+        }
+        free(p);
+    }
+    return rc;
+}
+
+int oracle_backward_neighborhood_f64(const double *q, const double *k, const double *v, const double *dO, int64_t B,
+                                     int64_t H, int64_t N, int64_t D, int64_t text_len, int64_t R, int64_t C,
+                                     int64_t kh, int64_t kw, int64_t sh, int64_t sw, double scale, double *dQ,
+                                     double *dK, double *dV)
+{
+    if (!q || !k || !v || !dO || !dQ || !dK || !dV || B <= 0 || H <= 0 || D <= 0 ||
+        !na_check(N, text_len, R, C, kh, kw, sh, sw))
+        return OR_EINVAL;
+    const na_geom g = {text_len, R, C, kh, kw, sh, sw};
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *p = malloc(sizeof(double) * N);
+        double *dp = malloc(sizeof(double) * N);
+        if (!p || !dp) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+            /* one (b, h) per iteration: dK, dV of a head are touched by its rows only */
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < B * H; ++bh) {
+                memset(dK + bh * N * D, 0, sizeof(double) * N * D);
+                memset(dV + bh * N * D, 0, sizeof(double) * N * D);
+                for (int64_t t = 0; t < N; ++t) {
+                    double *dq = dQ + (bh * N + t) * D;
+                    const double *go = dO + (bh * N + t) * D;
+                    na_row_probs(q, k, N, D, bh, t, &g, scale, p, NULL);
+                    double delta = 0.0;
+                    for (int64_t s = 0; s < N; ++s) {
+                        if (p[s] == 0.0) { dp[s] = 0.0; continue; }
+                        double acc = 0.0;
+                        for (int64_t d = 0; d < D; ++d) acc += go[d] * v[(bh * N + s) * D + d];
+                        dp[s] = acc;
+                        delta += p[s] * acc;
+                    }
+                    for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
+                    for (int64_t s = 0; s < N; ++s) {
+                        if (p[s] == 0.0) continue;
+                        const double ds = p[s] * (dp[s] - delta);
+                        for (int64_t d = 0; d < D; ++d) {
+                            dV[(bh * N + s) * D + d] += p[s] * go[d];
+                            dq[d] += scale * ds * k[(bh * N + s) * D + d];
+                            dK[(bh * N + s) * D + d] += scale * ds * q[(bh * N + t) * D + d];
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return rc;
+}
