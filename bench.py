@@ -365,10 +365,12 @@ def main():
     }
 
     if args.backward:
-        if wl.layout == "neighborhood" or args.fp8 or ("head_modes" in fwd_kw and fwd_kw["head_modes"] is not None
-                                                       and np.any(fwd_kw["head_modes"] == bsa.HEAD_SKIP)):
-            raise SystemExit("--backward: block layouts without SKIP heads, bf16 only")
-        res["backward"] = backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx, kept_pairs)
+        if args.fp8 or ("head_modes" in fwd_kw and fwd_kw["head_modes"] is not None
+                        and np.any(fwd_kw["head_modes"] == bsa.HEAD_SKIP)):
+            raise SystemExit("--backward: layouts without SKIP heads, bf16 only")
+        nbk = (nb, flags, token_pairs) if wl.layout == "neighborhood" else None
+        res["backward"] = backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx, kept_pairs,
+                                         nbk=nbk)
     if args.score_grad:
         if wl.score_mode != bsa.SCORE_MEANPOOL_PROJ or wl.layout in ("arrow", "neighborhood"):
             raise SystemExit("--score-grad: a workload scored by mean-pool / projection (C1, C3)")
@@ -580,21 +582,30 @@ def reuse_loop(torch, bsa, synth, dev, args):
     return res
 
 
-def backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx, kept_pairs, reps=20):
+def backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx, kept_pairs, reps=20, nbk=None):
     """Times bsa_backward (Delta/LSE prep, dQ kernel, dK/dV kernel) after one
     forward, for a seeded N(0, 1) output gradient.  Algorithmic work: the five
     products of the backward (S recomputed, dP, dV, dK, dQ), 10 * block^2 * D
     FLOP per kept block pair; the dQ and dK/dV kernels each recompute S and
-    dP, so 14 * block^2 * D are executed."""
+    dP, so 14 * block^2 * D are executed.  nbk = (geometry, entry flags,
+    token pairs) runs the neighbourhood backward on the tile-major tensors
+    and also reports the token-level rate (10 * D FLOP per kept token pair)."""
     B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
     g = synth.random_qkv(B, H, N, D, seed=wl.seed + 2000)[0]
     gd = torch.from_numpy(np.ascontiguousarray(g).view(np.int16)).view(torch.bfloat16).to(dev)
-    O, L = bsa.forward(q, k, v, block, row_ptr, col_idx)
+    if nbk is None:
+        O, L = bsa.forward(q, k, v, block, row_ptr, col_idx)
+    else:
+        O, L = bsa.forward_neighborhood(q, k, v, row_ptr, col_idx, nbk[1], nbk[0])
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(int(bsa.load().bsa_backward_workspace_size(B, H, N)), dtype=torch.uint8, device=dev)
 
     def run():
-        bsa.backward(q, k, v, O, gd, block, row_ptr, col_idx, L, dq=dq, dk=dk, dv=dv, workspace=ws)
+        if nbk is None:
+            bsa.backward(q, k, v, O, gd, block, row_ptr, col_idx, L, dq=dq, dk=dk, dv=dv, workspace=ws)
+        else:
+            bsa.backward_neighborhood(q, k, v, O, gd, row_ptr, col_idx, nbk[1], nbk[0], L, dq=dq, dk=dk, dv=dv,
+                                      workspace=ws)
     for _ in range(3):
         run()
     torch.cuda.synchronize()
@@ -611,6 +622,8 @@ def backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx
             "algorithmic_tflops": round(alg / (med * 1e-3) / 1e12, 2),
             "executed_tflops": round(1.4 * alg / (med * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(alg / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "token_level_tflops": (None if nbk is None else
+                                   round(10.0 * D * nbk[2] / (med * 1e-3) / 1e12, 2)),
             "flop_per_pair": "10 * block^2 * D (dQ, dK, dV, dP, S); 14 executed"}
 
 

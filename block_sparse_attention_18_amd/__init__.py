@@ -141,6 +141,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                ctypes.POINTER(BsaSplit), V]),
             "bsa_backward_workspace_size": (SZ, [I64, I64, I64]),
             "bsa_backward": (I32, [TP, TP, TP, TP, TP, I32, V, V, V, F, TP, TP, TP, V, SZ, V]),
+            "bsa_backward_neighborhood": (I32, [TP, TP, TP, TP, TP, I32, V, V, V, ctypes.POINTER(BsaNeighborhood), V, F,
+                                                TP, TP, TP, V, SZ, V]),
             "bsa_status_string": (ctypes.c_char_p, [I32]),
             "bsa_last_error": (ctypes.c_char_p, []),
             "bsa_version": (ctypes.c_char_p, []),
@@ -673,6 +675,36 @@ def forward_neighborhood(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_
                                         ctypes.byref(do), _ptr(lse), None if sp is None else ctypes.byref(sp),
                                         _stream(q.device)))
     return out, lse
+
+
+def backward_neighborhood(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dO: torch.Tensor,
+                          row_ptr: torch.Tensor, col_idx: torch.Tensor, entry_flags: torch.Tensor,
+                          nb: BsaNeighborhood, lse: torch.Tensor, scale: Optional[float] = None,
+                          dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                          dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """(dQ, dK, dV) bf16 in tile-major order of forward_neighborhood, given its
+    tile-major output O and LSE and the tile-major output gradient dO."""
+    lib = load()
+    B, H, N, D = q.shape
+    block = nb.tile_rows * nb.tile_cols
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx), ("entry_flags", entry_flags)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.bsa_backward_workspace_size(B, H, N)), 16), dtype=torch.uint8,
+                                device=q.device)
+    ds = [_desc(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"), (dq, "dq"), (dk, "dk"),
+                                   (dv, "dv"))]
+    _check(lib.bsa_backward_neighborhood(*[ctypes.byref(d) for d in ds[:5]], block, _ptr(row_ptr), _ptr(col_idx),
+                                         _ptr(entry_flags), ctypes.byref(nb), _ptr(lse), float(scale or 0.0),
+                                         *[ctypes.byref(d) for d in ds[5:]], _ptr(workspace),
+                                         workspace.numel(), _stream(q.device)))
+    return dq, dk, dv
 
 
 def output_rse(test: torch.Tensor, ref: torch.Tensor, out: Optional[torch.Tensor] = None,

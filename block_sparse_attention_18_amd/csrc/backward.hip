@@ -24,6 +24,12 @@
 //    halves' partial sums are added through LDS at the end.
 // Tiles read both by rows and transposed use one XOR swizzle of the 16-byte
 // chunk index that keeps both read patterns on distinct bank slots.
+// With a 2-D neighbourhood layout (NBM), the scores of partially covered
+// entries are masked per token as in the forward: dQ tests each key of a
+// sub-tile against its lane's query window; dK/dV, whose lanes own keys,
+// tests each query against the range of query rows and columns whose
+// windows hold the lane's key (window starts do not decrease along an axis,
+// so that range is an interval, found once by binary search).
 #include "common.h"
 #include "internal.h"
 
@@ -185,9 +191,43 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16 (&x)[2], int kt, int u)
 }
 
 // ---------------------------------------------------------------------------
+// 2-D neighbourhood helpers
+// ---------------------------------------------------------------------------
+// Grid row and column of the image token at tile-major position t >= T.
+template <int BETA>
+__device__ __forceinline__ void nb_pos(const NbGeom &g, int t, int &r, int &c)
+{
+    const int pt = t - g.T, tile = pt / BETA, o = pt - tile * BETA;
+    const int a = tile / g.tpr;
+    r = a * g.th + (o >> g.tw_log2);
+    c = (tile - a * g.tpr) * g.tw + (o & (g.tw - 1));
+}
+
+// The positions i in [0, L) whose window [start(i), start(i) + k) holds x:
+// start(i) does not decrease with i, so they form [lo, hi] (empty: lo > hi).
+__device__ __forceinline__ void nb_seen_by(int x, int L, int k, int s, int &lo, int &hi)
+{
+    int a = 0, b = L;
+    while (a < b) {
+        const int m = (a + b) >> 1;
+        if (nb_start(m, L, k, s) <= x) a = m + 1;
+        else b = m;
+    }
+    hi = a - 1;
+    a = 0;
+    b = L;
+    while (a < b) {
+        const int m = (a + b) >> 1;
+        if (nb_start(m, L, k, s) + k <= x) a = m + 1;
+        else b = m;
+    }
+    lo = a;
+}
+
+// ---------------------------------------------------------------------------
 // dQ: one workgroup per (query block, head)
 // ---------------------------------------------------------------------------
-template <int BETA, int D>
+template <int BETA, int D, bool NBM>
 __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdParams p)
 {
     using Sh = BwShape<BETA, D>;
@@ -214,6 +254,17 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
             dof[s] = as_bf16x8(qok ? ld_g16(gb + 16 * s + 8 * hl) : zero_u4());
         }
     }
+    // neighbourhood: the window of the lane's query (image queries only)
+    int wr0 = 0, wc0 = 0;
+    const bool qimg = NBM && qok && qrow >= p.nb.T;
+    if (qimg) {
+        int rq, cq;
+        nb_pos<BETA>(p.nb, qrow, rq, cq);
+        wr0 = nb_start(rq, p.nb.R, p.nb.kh, p.nb.sh);
+        wc0 = nb_start(cq, p.nb.C, p.nb.kw, p.nb.sw);
+    }
+    const __attribute__((address_space(4))) int32_t *cflag =
+        (const __attribute__((address_space(4))) int32_t *)(NBM ? p.flags + e0 : p.col_idx);
     const int64_t qtok = (int64_t)bh * p.N + (qok ? qrow : 0);
     const float lse2 = qok ? p.lse2[qtok] : 0.f;
     const float delta = qok ? p.delta[qtok] : 0.f;
@@ -257,6 +308,24 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
             bw_rows_mfma<D>(Kc, off.rows, qf, s);
             bw_rows_mfma<D>(Vc, off.rows, dof, dp);
             if (!vcur || kcur + 64 > p.N) mask_keys(s, (vcur ? p.N - kcur : 0) - 8 * hl);
+            if (NBM && vcur && cflag[t / Sh::SUB] != 0) {
+                // a partially covered entry: keys outside the lane's query window
+                const int jj = kcur / BETA;
+                if (qimg && jj >= p.nb.Tb) {
+                    const int tk = jj - p.nb.Tb, ak = tk / p.nb.tpr;
+                    const int kr0 = ak * p.nb.th - wr0, kc0 = (tk - ak * p.nb.tpr) * p.nb.tw - wc0;
+                    const int o0 = kcur - jj * BETA + 8 * hl;
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int o = o0 + kt * 32 + koff(r);
+                            const int dr = kr0 + (o >> p.nb.tw_log2), dc = kc0 + (o & (p.nb.tw - 1));
+                            if ((unsigned)dr >= (unsigned)p.nb.kh || (unsigned)dc >= (unsigned)p.nb.kw)
+                                s[kt][r] = -INFINITY;
+                        }
+                }
+            }
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -395,12 +464,12 @@ __device__ __forceinline__ void bw_load_rows(uint16_t *__restrict__ dst, __amdgp
     }
 }
 
-template <int BETA, int D>
+template <int BETA, int D, bool NBM>
 __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const BwdParams p)
 {
     using G = DkShape<BETA, D>;
     __shared__ __attribute__((aligned(16))) uint16_t dsm[G::SMEM];
-    extern __shared__ int qlist[];                       // query blocks keeping this key block
+    extern __shared__ int qlist[];   // query blocks keeping this key block (bit 30: partial entry)
     uint16_t *const Kt = dsm, *const Vt = dsm + G::KV;
     uint16_t *const Bf0 = dsm + 2 * G::KV;
     __shared__ int wcount[G::NW];
@@ -415,7 +484,7 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     // query blocks whose row lists j, ascending
     int count = 0;
     for (int base = 0; base < p.nB; base += G::NT) {
-        const int i = base + tid;
+        int i = base + tid;
         bool f = false;
         if (i < p.nB) {
             const int64_t r = (int64_t)bh * p.nB + i;
@@ -427,6 +496,7 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
                 else hi = mid;
             }
             f = lo < end && p.col_idx[lo] == j;
+            if (NBM && f && p.flags[lo] != 0) i |= 1 << 30;
         }
         const uint64_t m = __ballot(f);
         if (lane == 0) wcount[wv] = __popcll(m);
@@ -452,7 +522,8 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     const __amdgpu_buffer_rsrc_t grs = buffer_desc(gb, (uint32_t)(((int64_t)(p.N - 1) * p.dO.sn + D) * 2));
     const __amdgpu_buffer_rsrc_t lrs = buffer_desc(p.lse2 + (int64_t)bh * p.N, (uint32_t)p.N * 4);
     const __amdgpu_buffer_rsrc_t drs = buffer_desc(p.delta + (int64_t)bh * p.N, (uint32_t)p.N * 4);
-    auto qstart = [&](int t) { return qlist[t / (BETA / 64)] * BETA + 64 * (t % (BETA / 64)); };
+    auto qblock = [&](int t) { return qlist[t / (BETA / 64)] & ((1 << 30) - 1); };
+    auto qstart = [&](int t) { return qblock(t) * BETA + 64 * (t % (BETA / 64)); };
     auto buf = [&](int t) { return Bf0 + (t & 1) * G::BUF; };
     auto load = [&](int t) {
         const int q0 = qstart(t);
@@ -479,6 +550,16 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     const BwOffsets<D> off = bw_offsets<D>(lane);
     // B operand rows of the wave's keys in Kt / Vt (natural order)
     const int krow_l = kg * 32 + n;
+    // neighbourhood: the query rows [qr0, qr1] and columns [qc0, qc1] whose
+    // windows hold the lane's key (image keys only)
+    int qr0 = 0, qr1 = -1, qc0 = 0, qc1 = -1;
+    const bool kimg = NBM && j >= p.nb.Tb;
+    if (kimg) {
+        int kr, kc;
+        nb_pos<BETA>(p.nb, j * BETA + krow_l, kr, kc);
+        nb_seen_by(kr, p.nb.R, p.nb.kh, p.nb.sh, qr0, qr1);
+        nb_seen_by(kc, p.nb.C, p.nb.kw, p.nb.sw, qc0, qc1);
+    }
     const uint32_t brow = (uint32_t)(krow_l * D * 2 + 16 * (hl ^ bswz<D>(krow_l)));
 
     if (T > 0) {
@@ -513,6 +594,19 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
                     if (koff(r) >= lim) s[r] = -INFINITY;
             }
             bf16x8 pp[2], ps[2];
+            if (NBM && kimg && (qlist[t / (BETA / 64)] >> 30) != 0) {
+                // a partially covered entry (an image query block): queries
+                // whose window misses the lane's key
+                const int i = qblock(t), tq = i - p.nb.Tb, aq = tq / p.nb.tpr;
+                const int orow = aq * p.nb.th, ocol = (tq - aq * p.nb.tpr) * p.nb.tw;
+                const int o0 = q0 - i * BETA + 8 * hl;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int o = o0 + koff(r);
+                    const int rq = orow + (o >> p.nb.tw_log2), cq = ocol + (o & (p.nb.tw - 1));
+                    if (rq < qr0 || rq > qr1 || cq < qc0 || cq > qc1) s[r] = -INFINITY;
+                }
+            }
             bw_probs_half(s, dp, stats, qh, c, hl, pp, ps);
             bw_tr_half<D>(Gc, off, qh, pp, dv);
             bw_tr_half<D>(Qc, off, qh, ps, dk);
@@ -558,19 +652,25 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     }
 }
 
-template <int BETA, int D>
+template <int BETA, int D, bool NBM>
 static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t s)
 {
     using Sh = BwShape<BETA, D>;
     const int64_t grid = (int64_t)p.B * p.H * p.nB;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_kernel<BETA, D>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<BETA, D, NBM>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
     using G = DkShape<BETA, D>;
     static_assert(G::SMEM * 2 + G::NW * 4 + kBwdMaxBlocks * 4 <= 160 * 1024, "dK/dV LDS");
     if (p.nB > kBwdMaxBlocks) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BETA, D>), dim3((unsigned)grid), dim3(G::NT), (size_t)p.nB * sizeof(int),
-                       s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BETA, D, NBM>), dim3((unsigned)grid), dim3(G::NT),
+                       (size_t)p.nB * sizeof(int), s, p);
     return hipGetLastError();
+}
+
+template <int BETA, int D>
+static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t s)
+{
+    return p.flags ? launch_bwd_t<BETA, D, true>(p, s) : launch_bwd_t<BETA, D, false>(p, s);
 }
 
 hipError_t launch_backward(const BwdParams &p, int block, int D, hipStream_t s)

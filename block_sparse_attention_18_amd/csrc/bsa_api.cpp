@@ -752,10 +752,11 @@ size_t bsa_backward_workspace_size(int64_t B, int64_t H, int64_t N)
     return 2 * (((size_t)(B * H * N) * sizeof(float) + 255) & ~(size_t)255);
 }
 
-bsa_status bsa_backward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_tensor *o,
-                        const bsa_tensor *dO, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
-                        const float *lse, float scale, const bsa_tensor *dq, const bsa_tensor *dk,
-                        const bsa_tensor *dv, void *workspace, size_t workspace_bytes, void *stream)
+static bsa_status backward_impl(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_tensor *o,
+                                const bsa_tensor *dO, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                                const float *lse, float scale, const bsa_tensor *dq, const bsa_tensor *dk,
+                                const bsa_tensor *dv, void *workspace, size_t workspace_bytes, void *stream,
+                                const int32_t *entry_flags, const bsa::NbGeom *nb)
 {
     bsa_status st;
     const bsa_tensor *ts[] = {q, k, v, o, dO, dq, dk, dv};
@@ -797,9 +798,36 @@ bsa_status bsa_backward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tens
     p.nB = (int32_t)nB;
     p.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
     p.scale_log2 = p.scale * 1.4426950408889634f;
+    p.flags = entry_flags;
+    if (nb) p.nb = *nb;
     hipError_t e = bsa::launch_backward(p, block, (int)q->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return BSA_OK;
+}
+
+bsa_status bsa_backward(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_tensor *o,
+                        const bsa_tensor *dO, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                        const float *lse, float scale, const bsa_tensor *dq, const bsa_tensor *dk,
+                        const bsa_tensor *dv, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return backward_impl(q, k, v, o, dO, block, row_ptr, col_idx, lse, scale, dq, dk, dv, workspace,
+                         workspace_bytes, stream, nullptr, nullptr);
+}
+
+bsa_status bsa_backward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                     const bsa_tensor *o, const bsa_tensor *dO, int32_t block,
+                                     const int32_t *row_ptr, const int32_t *col_idx, const int32_t *entry_flags,
+                                     const bsa_neighborhood *nb, const float *lse, float scale,
+                                     const bsa_tensor *dq, const bsa_tensor *dk, const bsa_tensor *dv,
+                                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if (!entry_flags) return fail(BSA_ERR_INVALID_ARG, "entry_flags null");
+    bsa::NbGeom g;
+    if ((st = check_nb(nb, q->N, block, &g)) != BSA_OK) return st;
+    return backward_impl(q, k, v, o, dO, block, row_ptr, col_idx, lse, scale, dq, dk, dv, workspace,
+                         workspace_bytes, stream, entry_flags, &g);
 }
 
 // ---------------------------------------------------------------------------

@@ -97,6 +97,8 @@ struct BwdParams {
     const float *lse;           // [B][H][N], natural log
     float *lse2, *delta;        // workspace: LSE * log2(e), rowsum(dO * O)
     const int32_t *row_ptr, *col_idx;
+    const int32_t *flags;       // neighbourhood layouts: 1 = partially covered entry; else null
+    NbGeom nb;
     uint16_t *dq, *dk, *dv;
     int64_t dq_sb, dq_sh, dq_sn, dk_sb, dk_sh, dk_sn, dv_sb, dv_sh, dv_sn;
     int32_t B, H, N, D, nB;
@@ -266,7 +268,7 @@ struct JaccardParams {
 hipError_t launch_forward(const FwdParams &p, int block, int D, int64_t grid, hipStream_t s);
 hipError_t launch_output_rse(const RseParams &p, hipStream_t s);
 hipError_t launch_permute_tokens(const PermuteParams &p, hipStream_t s);
-hipError_t launch_backward(const BwdParams &p, int block, int D, hipStream_t s);
+hipError_t launch_backward(const BwdParams &p, int block, int D, hipStream_t s);   // masks when p.flags
 hipError_t launch_neighborhood_layout(const NbLayoutParams &p, hipStream_t s);
 hipError_t launch_mask_jaccard(const JaccardParams &p, hipStream_t s);
 hipError_t launch_quantize_fp8(const Fp8QuantParams &p, int D, hipStream_t s);

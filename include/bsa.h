@@ -321,6 +321,21 @@ bsa_status bsa_forward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, co
                                     const bsa_neighborhood *nb, float scale, const bsa_tensor *o, float *lse,
                                     const bsa_split *split, void *stream);
 
+/* bsa_backward_neighborhood -- bsa_backward for the 2-D neighbourhood
+ * layout (GNA notes, 1.1 and 2.1): tile-major Q, K, V, O, dO and LSE as
+ * bsa_forward_neighborhood produced them, its block list and entry flags
+ * and the same geometry; partially covered entries are masked per token as
+ * in the forward.  dQ, dK, dV come out in tile-major order (the caller
+ * permutes them back with bsa_permute_tokens, inverse = 1).  Same
+ * workspace, limits and errors as bsa_backward, plus the geometry checks of
+ * bsa_forward_neighborhood. */
+bsa_status bsa_backward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                     const bsa_tensor *o, const bsa_tensor *dO, int32_t block,
+                                     const int32_t *row_ptr, const int32_t *col_idx, const int32_t *entry_flags,
+                                     const bsa_neighborhood *nb, const float *lse, float scale,
+                                     const bsa_tensor *dq, const bsa_tensor *dk, const bsa_tensor *dv,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * FP8 forward (OCP E4M3 operands on the gfx950 FP8 matrix cores).
  *

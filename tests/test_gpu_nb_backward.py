@@ -1,0 +1,96 @@
+"""GPU parity of the backward of 2-D neighbourhood (GNA) attention against the
+fp64 oracle gradient under the token mask.
+
+Natural-order inputs are permuted to tile-major order on the GPU, the
+forward and the backward run there (the partially covered entries masked
+per token in both backward kernels), and dQ, dK, dV are permuted back.
+Tolerances as for the block-sparse backward (tests/test_gpu_backward.py):
+max 2e-2 of each gradient's largest element, mean 1e-2 of its mean
+magnitude (bf16 P, dS, O and gradients)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import block_sparse_attention_18_amd as bsa
+from helpers import bf16_bits, bf16_to_f64, dev, to_dev_bf16
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+MAX_REL = 2e-2
+MEAN_REL = 1e-2
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check_grad(g, want, name):
+    d = np.abs(g - want)
+    mx = float(d.max()) / max(float(np.abs(want).max()), 1e-30)
+    mean = float(d.mean()) / max(float(np.abs(want).mean()), 1e-30)
+    _log(f"  {name}: max {mx:.2e} of max|g|, mean {mean:.2e} of mean|g|")
+    assert mx <= MAX_REL and mean <= MEAN_REL, name
+
+
+def _backward_natural(q, k, v, g, nb):
+    B, H, N, D = q.shape
+    qd, kd, vd, gd = (bsa.permute_tokens(to_dev_bf16(a), nb) for a in (q, k, v, g))
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    Op, Lp = bsa.forward_neighborhood(qd, kd, vd, rp, ci, fl, nb)
+    dq, dk, dv = bsa.backward_neighborhood(qd, kd, vd, Op, gd, rp, ci, fl, nb, Lp)
+    out = [bsa.permute_tokens(x, nb, inverse=True) for x in (dq, dk, dv)]
+    torch.cuda.synchronize()
+    return out, fl
+
+
+GEOMS = [
+    # T, grid, tile, window, stride, D
+    (128, (16, 32), (8, 16), (5, 9), (1, 1), 64),          # sliding window, mostly partial tiles
+    (0, (32, 32), (8, 16), (16, 32), (16, 32), 128),       # stride = window: no partial tile
+    (64, (16, 24), (8, 8), (8, 12), (4, 4), 64),           # block 64, a stride between
+    (256, (32, 64), (8, 16), (12, 20), (2, 3), 128),       # uneven strides, window not a tile multiple
+    (128, (8, 16), (8, 16), (8, 16), (1, 1), 64),          # window = whole grid: dense
+    (64, (24, 16), (8, 8), (3, 16), (1, 1), 128),          # block 64 at D 128, window spanning whole rows
+]
+
+
+@pytest.mark.parametrize("T,grid,tile,window,stride,D", GEOMS)
+def test_backward_matches_oracle(T, grid, tile, window, stride, D):
+    _log(f"nb backward T={T} grid={grid} tile={tile} window={window} stride={stride} D={D}")
+    B, H = 1, 2
+    N = T + grid[0] * grid[1]
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    q, k, v = synth.random_qkv(B, H, N, D, seed=1201)
+    g = synth.random_qkv(B, H, N, D, seed=1202)[0]
+    (dq, dk, dv), fl = _backward_natural(q, k, v, g, nb)
+    wq, wk, wv = oracle.backward_neighborhood(q, k, v, g, T, grid, window, stride)
+    _check_grad(bf16_to_f64(dq), wq, "dQ")
+    _check_grad(bf16_to_f64(dk), wk, "dK")
+    _check_grad(bf16_to_f64(dv), wv, "dV")
+    if window == stride:
+        assert int(fl.sum().item()) == 0
+
+
+def test_backward_peaked_logits_and_determinism():
+    # logits of sigma 3 (sharper rows) and two calls agreeing bit for bit
+    T, grid, tile, window, stride, D = 128, (16, 32), (8, 16), (7, 11), (1, 2), 128
+    B, H = 1, 2
+    N = T + grid[0] * grid[1]
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    q, k, _ = synth.random_qkv(B, H, N, D, seed=1211, scale=3.0)
+    v = synth.random_qkv(B, H, N, D, seed=1212)[2]
+    g = synth.random_qkv(B, H, N, D, seed=1213)[0]
+    a, _ = _backward_natural(q, k, v, g, nb)
+    b, _ = _backward_natural(q, k, v, g, nb)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(bf16_bits(x), bf16_bits(y))
+    wq, wk, wv = oracle.backward_neighborhood(q, k, v, g, T, grid, window, stride)
+    _check_grad(bf16_to_f64(a[0]), wq, "dQ")
+    _check_grad(bf16_to_f64(a[1]), wk, "dK")
+    _check_grad(bf16_to_f64(a[2]), wv, "dV")

@@ -79,3 +79,24 @@ def test_fp64_forward_matches_bf16_input_forward():
     O2, L2 = oracle.forward_neighborhood_f64(_f64(q), _f64(k), _f64(v), T, grid, window, stride)
     np.testing.assert_allclose(O2, O1, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(L2, L1, rtol=1e-12, atol=1e-13)
+
+
+def test_token_mask_changes_the_gradient():
+    # the sliding-window case of the GPU parity tests: the block-sparse
+    # gradient over the same blocks without the token mask misses the masked
+    # gradient by far more than the GPU tolerance (2e-2 of the largest
+    # element), so that parity holds only if the kernels mask
+    T, grid, tile, window, stride, D = 128, (16, 32), (8, 16), (5, 9), (1, 1), 64
+    B, H = 1, 2
+    N = T + grid[0] * grid[1]
+    q, k, v = random_qkv(B, H, N, D, seed=1201)
+    g = random_qkv(B, H, N, D, seed=1202)[0]
+    want = oracle.backward_neighborhood(q, k, v, g, T, grid, window, stride)
+    perm = oracle.tile_permutation(T, grid, tile)
+    rp, ci, flags = oracle.neighborhood_layout(T, grid, tile, window, stride)
+    assert flags.mean() > 0.5
+    rp_all = np.concatenate([rp[:-1] + h * rp[-1] for h in range(B * H)] + [[B * H * rp[-1]]]).astype(np.int32)
+    got = oracle.backward(*(x[:, :, perm] for x in (q, k, v, g)), 128, rp_all, np.tile(ci, B * H))
+    inv = np.argsort(perm)
+    for a, b in zip(got, want):
+        assert np.abs(a[:, :, inv] - b).max() > 0.2 * np.abs(b).max()
