@@ -226,12 +226,18 @@ def main():
             print("the FP8 forward computes every head: pick a workload without SKIP heads",
                   file=sys.stderr)
             sys.exit(2)
+        if wl.layout == "neighborhood":
+            layout()                      # the tile-major Q, K, V that are quantised
         qkv8 = bsa.quantize_fp8(q, k, v)
         ws_q = torch.empty(max(bsa.quantize_fp8_workspace_size(B, H, N, D), 16), dtype=torch.uint8,
                            device=dev)
 
-        def forward():
-            bsa.forward_fp8(qkv8, block, row_ptr, col_idx, out=out, lse=lse)
+        if wl.layout == "neighborhood":
+            def forward():
+                bsa.forward_fp8_neighborhood(qkv8, row_ptr, col_idx, flags, nb, out=out_t, lse=lse_t)
+        else:
+            def forward():
+                bsa.forward_fp8(qkv8, block, row_ptr, col_idx, out=out, lse=lse)
 
         def quantize():
             bsa.quantize_fp8(q, k, v, out=qkv8, workspace=ws_q)

@@ -130,6 +130,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_quantize_fp8_workspace_size": (SZ, [I64, I64, I64, I64]),
             "bsa_quantize_fp8": (I32, [TP, TP, TP, ctypes.POINTER(BsaFp8Qkv), V, SZ, V]),
             "bsa_forward_fp8": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, F, TP, V, V]),
+            "bsa_forward_fp8_neighborhood": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, V,
+                                                   ctypes.POINTER(BsaNeighborhood), F, TP, V, V]),
             "bsa_output_rse_workspace_size": (SZ, [I64, I64, I64, I64]),
             "bsa_output_rse": (I32, [TP, TP, V, V, SZ, V]),
             "bsa_mask_jaccard": (I32, [I64, I64, I32, V, V, V, V, V, V]),
@@ -553,6 +555,32 @@ def forward_fp8(qkv: Fp8QKV, block: int, row_ptr: torch.Tensor, col_idx: torch.T
     d8, do = qkv.desc(), _desc(out, "out")
     _check(lib.bsa_forward_fp8(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx), float(scale or 0.0),
                                ctypes.byref(do), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def forward_fp8_neighborhood(qkv: Fp8QKV, row_ptr: torch.Tensor, col_idx: torch.Tensor,
+                             entry_flags: torch.Tensor, nb: "BsaNeighborhood", scale: Optional[float] = None,
+                             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                             return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """FP8 forward of 2-D neighbourhood attention on E4M3 operands quantised
+    from tile-major Q, K, V.  Returns (O bf16, LSE fp32) in tile-major order."""
+    lib = load()
+    B, H, N, D = qkv.shape
+    dev = qkv.q8.device
+    block = nb.tile_rows * nb.tile_cols
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx), ("entry_flags", entry_flags)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    d8, do = qkv.desc(), _desc(out, "out")
+    _check(lib.bsa_forward_fp8_neighborhood(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx),
+                                            _ptr(entry_flags), ctypes.byref(nb), float(scale or 0.0),
+                                            ctypes.byref(do), _ptr(lse), _stream(dev)))
     return out, lse
 
 

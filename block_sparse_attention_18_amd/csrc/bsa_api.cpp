@@ -880,8 +880,9 @@ bsa_status bsa_quantize_fp8(const bsa_tensor *q, const bsa_tensor *k, const bsa_
     return BSA_OK;
 }
 
-bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
-                           float scale, const bsa_tensor *o, float *lse, void *stream)
+static bsa_status forward_fp8_impl(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
+                                   const int32_t *col_idx, float scale, const bsa_tensor *o, float *lse, void *stream,
+                                   const int32_t *entry_flags, const bsa::NbGeom *nb)
 {
     bsa_status st;
     if ((st = check_fp8(in, "in")) != BSA_OK) return st;
@@ -916,9 +917,30 @@ bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *
     p.NP = 64 * p.NT;
     const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)in->D);
     p.scale_log2 = sc * 1.4426950408889634f;
+    p.flags = entry_flags;
+    if (nb) p.nb = *nb;
     hipError_t e = bsa::launch_forward_fp8(p, block, (int)in->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fp8 forward launch");
     return BSA_OK;
+}
+
+bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                           float scale, const bsa_tensor *o, float *lse, void *stream)
+{
+    return forward_fp8_impl(in, block, row_ptr, col_idx, scale, o, lse, stream, nullptr, nullptr);
+}
+
+bsa_status bsa_forward_fp8_neighborhood(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
+                                        const int32_t *col_idx, const int32_t *entry_flags,
+                                        const bsa_neighborhood *nb, float scale, const bsa_tensor *o, float *lse,
+                                        void *stream)
+{
+    bsa_status st;
+    if ((st = check_fp8(in, "in")) != BSA_OK) return st;
+    if (!entry_flags) return fail(BSA_ERR_INVALID_ARG, "entry_flags null");
+    bsa::NbGeom g;
+    if ((st = check_nb(nb, in->N, block, &g)) != BSA_OK) return st;
+    return forward_fp8_impl(in, block, row_ptr, col_idx, scale, o, lse, stream, entry_flags, &g);
 }
 
 // ---------------------------------------------------------------------------

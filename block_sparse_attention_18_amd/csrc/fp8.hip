@@ -287,6 +287,8 @@ struct F8State {
     uint32_t kread;              // K operand, k-step 0, first 16 bytes; (ks, x): ^ (64 ks + 16 x)
     uint32_t vread;              // V^T operand, d tile 0, first 16 bytes; x: ^ 16
     uint32_t kdma, vdma;         // source offset of the lane's first copy of a tile
+    int wr0, wc0;                // neighbourhood: window start (row, column) of the lane's query
+    bool qimg;                   // neighbourhood: the lane's query is an image token
 };
 
 __device__ __forceinline__ i32x8 lds_i32x8(const uint8_t *base, uint32_t o0, uint32_t o1)
@@ -333,6 +335,27 @@ __device__ __forceinline__ void mask8(f32x16 (&sacc)[2], int lim)
 __device__ __forceinline__ void mask_scores8(bool valid, int k0, int N, int lane, f32x16 (&sacc)[2])
 {
     if (!valid || k0 + 64 > N) mask8(sacc, (valid ? N - k0 : 0) - 4 * (lane >> 5));
+}
+
+// 2-D neighbourhood masking of a partially covered key tile (image keys
+// only): a score survives when the key's grid position lies in the window
+// (row start wr0, column start wc0) of the lane's image query.
+template <int BETA>
+__device__ __forceinline__ void mask_window8(const NbGeom &g, int k0, int wr0, int wc0, int lane, f32x16 (&sacc)[2])
+{
+    const int j = k0 / BETA;
+    if (j < g.Tb) return;
+    const int tk = j - g.Tb, ak = tk / g.tpr;
+    const int kr0 = ak * g.th - wr0, kc0 = (tk - ak * g.tpr) * g.tw - wc0;
+    const int o0 = (k0 - j * BETA) + 4 * (lane >> 5);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int o = o0 + 32 * a + 8 * (r >> 2) + (r & 3);
+            const int dr = kr0 + (o >> g.tw_log2), dc = kc0 + (o & (g.tw - 1));
+            if ((unsigned)dr >= (unsigned)g.kh || (unsigned)dc >= (unsigned)g.kw) sacc[a][r] = -INFINITY;
+        }
 }
 
 template <int BETA, int D>
@@ -433,6 +456,7 @@ struct F8Tile {
     int k0;        // first key of the sub-tile
     bool valid;    // block index in range
     float c;       // scale * log2(e) * q_scale * k_scale of the tile (> 0)
+    bool partial;  // neighbourhood layouts: a partially covered entry
 };
 
 // Steady-state step t, two scheduled regions of MFMAs with the vector work
@@ -444,7 +468,7 @@ struct F8Tile {
 // max of t is known; when the lazy rescale then moves the reference (rare:
 // the first sub-tile of a row, or a max that grows by more than 2^8) they
 // are recomputed.  Masking of t's scores sits between the two regions.
-template <int BETA, int D>
+template <int BETA, int D, bool NBM>
 __device__ __forceinline__ void step8(const uint8_t *__restrict__ Kc, const uint8_t *__restrict__ Vp,
                                       uint8_t *__restrict__ Kn, uint8_t *__restrict__ Vn, const F8Tile &cur,
                                       const F8Tile &prv, bool load_k, int k0_k, __amdgpu_buffer_rsrc_t krs,
@@ -464,6 +488,7 @@ __device__ __forceinline__ void step8(const uint8_t *__restrict__ Kc, const uint
     // this use the compiler sinks their computation past it, out of region A
     asm volatile("" ::"v"(pf_prev));
     mask_scores8(cur.valid, cur.k0, p.N, lane, s_cur);
+    if (NBM && cur.partial && st.qimg) mask_window8<BETA>(p.nb, cur.k0, st.wr0, st.wc0, lane, s_cur);
     pv8<BETA, D>(Vp, pf_prev, st);
     const bool has_keys = cur.valid && cur.k0 < p.N;
     const float mx = tile_max(s_cur, cur.c) + (has_keys ? 0.f : -INFINITY);
@@ -476,7 +501,7 @@ __device__ __forceinline__ void step8(const uint8_t *__restrict__ Kc, const uint
 
 // Occupancy target (waves per SIMD): two, so that a wave's accumulators,
 // scores of two sub-tiles and Q codes fit its registers without spilling.
-template <int BETA, int D>
+template <int BETA, int D, bool NBM>
 __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdParams p)
 {
     using Sh = F8Shape<BETA, D>;
@@ -516,6 +541,14 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
         qs = p.q_scale[qtok];
     }
     st.cq = p.scale_log2 * qs;
+    st.qimg = NBM && qrow < p.N && qrow >= p.nb.T;
+    st.wr0 = st.wc0 = 0;
+    if (NBM && st.qimg) {
+        const int pq = qrow - p.nb.T, tq = pq / BETA, oq = pq - tq * BETA, aq = tq / p.nb.tpr;
+        const int rq = aq * p.nb.th + (oq >> p.nb.tw_log2), cq = (tq - aq * p.nb.tpr) * p.nb.tw + (oq & (p.nb.tw - 1));
+        st.wr0 = nb_start(rq, p.nb.R, p.nb.kh, p.nb.sh);
+        st.wc0 = nb_start(cq, p.nb.C, p.nb.kw, p.nb.sw);
+    }
 #pragma unroll
     for (int d = 0; d < Sh::DT; ++d)
 #pragma unroll
@@ -546,6 +579,8 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
     // wave-uniform block indices and K tile scales through scalar loads
     const __attribute__((address_space(4))) int32_t *cidx =
         (const __attribute__((address_space(4))) int32_t *)(p.col_idx + e0);
+    const __attribute__((address_space(4))) int32_t *cflag =
+        (const __attribute__((address_space(4))) int32_t *)(NBM ? p.flags + e0 : p.col_idx);
     const __attribute__((address_space(4))) float *kscl =
         (const __attribute__((address_space(4))) float *)(p.k_scale + (int64_t)bh * p.NT);
     auto tile = [&](int t) {
@@ -557,9 +592,10 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
         // a zero scale means all-zero codes; any positive c gives the same
         // scores and keeps -inf * c a -inf for masked keys
         x.c = fmaxf(st.cq * ks, 1.17549435e-38f);
+        x.partial = NBM && cflag[t / Sh::SUB] != 0;
         return x;
     };
-    const F8Tile none = {0, false, 1.f};
+    const F8Tile none = {0, false, 1.f, false};
 
     f32x16 sa[2], sb[2];
     i32x8 pa, pb;
@@ -574,6 +610,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
         load_v8<BETA, D>(V0, vrs, st.vdma, vstep, p.NP, cur.k0, wv);
         qk8<BETA, D>(K0, st, sa);
         mask_scores8(cur.valid, cur.k0, p.N, lane, sa);
+        if (NBM && cur.partial && st.qimg) mask_window8<BETA>(p.nb, cur.k0, st.wr0, st.wc0, lane, sa);
         lazy_rescale8<BETA, D>((cur.valid && cur.k0 < p.N) ? tile_max(sa, cur.c) : -INFINITY, st);
         probs_half<0>(sa, cur.c, st.m_run, pa);
         __syncthreads();
@@ -582,7 +619,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
         for (int t = 1; t < T; t += 2) {
             nxt = none;
             if (t + 1 < T) nxt = tile(t + 1);
-            step8<BETA, D>(K1, V0, K0, V1, cur, prv, t + 1 < T, nxt.k0, krs, vrs, vstep, p, wv, lane, st, sb, sa,
+            step8<BETA, D, NBM>(K1, V0, K0, V1, cur, prv, t + 1 < T, nxt.k0, krs, vrs, vstep, p, wv, lane, st, sb, sa,
                            pa, pb);
             __syncthreads();
             prv = cur;
@@ -590,7 +627,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
             if (t + 1 >= T) break;
             nxt = none;
             if (t + 2 < T) nxt = tile(t + 2);
-            step8<BETA, D>(K0, V1, K1, V0, cur, prv, t + 2 < T, nxt.k0, krs, vrs, vstep, p, wv, lane, st, sa, sb,
+            step8<BETA, D, NBM>(K0, V1, K1, V0, cur, prv, t + 2 < T, nxt.k0, krs, vrs, vstep, p, wv, lane, st, sa, sb,
                            pb, pa);
             __syncthreads();
             prv = cur;
@@ -634,7 +671,10 @@ static hipError_t launch_fwd8_t(const Fp8FwdParams &p, hipStream_t s)
     using Sh = F8Shape<BETA, D>;
     const int64_t grid = (int64_t)p.B * p.H * p.nB;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd8_kernel<BETA, D>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
+    if (p.flags)
+        hipLaunchKernelGGL((fwd8_kernel<BETA, D, true>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd8_kernel<BETA, D, false>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
     return hipGetLastError();
 }
 

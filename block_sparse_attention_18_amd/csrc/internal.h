@@ -246,6 +246,8 @@ struct Fp8FwdParams {
     float *lse;
     const int32_t *row_ptr;
     const int32_t *col_idx;
+    const int32_t *flags;       // neighbourhood layouts: 1 = partially covered entry; else null
+    NbGeom nb;
     int32_t B, H, N, nB, NT, NP;
     float scale_log2;
 };

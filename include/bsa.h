@@ -387,6 +387,18 @@ bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *
                            const int32_t *col_idx, float scale, const bsa_tensor *o, float *lse,
                            void *stream);
 
+/* bsa_forward_fp8_neighborhood -- bsa_forward_fp8 for the 2-D neighbourhood
+ * layout (GNA notes, 2.1: its FP8 mode): `in` quantised from tile-major Q,
+ * K, V (bsa_permute_tokens, then bsa_quantize_fp8), the block list and
+ * entry flags of bsa_build_neighborhood_layout and the same geometry;
+ * partially covered entries are masked per token as in
+ * bsa_forward_neighborhood.  O and LSE come out in tile-major order.
+ * Errors as for bsa_forward_fp8 plus the geometry checks. */
+bsa_status bsa_forward_fp8_neighborhood(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
+                                        const int32_t *col_idx, const int32_t *entry_flags,
+                                        const bsa_neighborhood *nb, float scale, const bsa_tensor *o, float *lse,
+                                        void *stream);
+
 /* ------------------------------------------------------------------------
  * Diagnostics of sparse attention.
  *

@@ -1,0 +1,75 @@
+"""GPU parity of the FP8 (E4M3) forward of 2-D neighbourhood attention.
+
+The GPU permutes natural-order Q, K, V to tile-major order, quantises them
+and runs the FP8 forward with the neighbourhood layout (partial entries
+masked per token); O and LSE are permuted back.  The reference permutes on
+the host, quantises with the oracle, dequantises (code times scale) and
+runs the oracle's fp64 neighbourhood forward in natural order: the only
+difference left is the kernel's rounding of P to E4M3, bounded as in
+tests/test_gpu_fp8.py."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import block_sparse_attention_18_amd as bsa
+from helpers import bf16_to_f64, dev, to_dev_bf16
+from test_gpu_fp8 import FP8_LSE_MAX_ABS, FP8_O_MAX_ABS, FP8_O_MEAN_ABS
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dequantised_natural(q, k, v, T, grid, tile):
+    """Oracle E4M3 quantisation in tile-major order, dequantised to fp64 and
+    returned in natural order."""
+    perm = oracle.tile_permutation(T, grid, tile)
+    q8, qs, k8, ks, v8, vs = oracle.quantize_fp8(q[:, :, perm], k[:, :, perm], v[:, :, perm])
+    N = q.shape[2]
+    tiles = np.arange(N) // 64
+    qd = oracle.e4m3_decode(q8) * qs[..., None]
+    kd = oracle.e4m3_decode(k8) * ks[:, :, tiles][..., None]
+    vd = oracle.e4m3_decode(v8) * vs[:, :, None, :]
+    out = []
+    for x in (qd, kd, vd):
+        nat = np.empty_like(x)
+        nat[:, :, perm] = x
+        out.append(nat)
+    return out
+
+
+GEOMS = [
+    # T, grid, tile, window, stride, D
+    (128, (16, 32), (8, 16), (5, 9), (1, 1), 64),          # sliding window, mostly partial tiles
+    (0, (32, 32), (8, 16), (16, 32), (16, 32), 128),       # stride = window: no partial tile
+    (64, (16, 24), (8, 8), (8, 12), (4, 4), 64),           # block 64, a stride between
+    (256, (32, 64), (8, 16), (12, 20), (2, 3), 128),       # uneven strides
+]
+
+
+@pytest.mark.parametrize("T,grid,tile,window,stride,D", GEOMS)
+def test_fp8_neighborhood_matches_dequantised_oracle(T, grid, tile, window, stride, D):
+    _log(f"fp8 nb T={T} grid={grid} tile={tile} window={window} stride={stride} D={D}")
+    B, H = 1, 2
+    N = T + grid[0] * grid[1]
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    q, k, v = synth.random_qkv(B, H, N, D, seed=1301)
+    qd, kd, vd = (bsa.permute_tokens(to_dev_bf16(a), nb) for a in (q, k, v))
+    qkv = bsa.quantize_fp8(qd, kd, vd)
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    Op, Lp = bsa.forward_fp8_neighborhood(qkv, rp, ci, fl, nb)
+    O, L = bsa.permute_tokens(Op, nb, inverse=True, lse=Lp)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.forward_neighborhood_f64(*_dequantised_natural(q, k, v, T, grid, tile), T, grid, window, stride)
+    err = np.abs(bf16_to_f64(O) - Oo)
+    lerr = np.abs(L.cpu().numpy().astype(np.float64) - Lo)
+    _log(f"  O max {err.max():.2e} mean {err.mean():.2e}  LSE max {lerr.max():.2e}")
+    assert err.max() <= FP8_O_MAX_ABS and err.mean() <= FP8_O_MEAN_ABS and lerr.max() <= FP8_LSE_MAX_ABS
