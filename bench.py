@@ -86,6 +86,10 @@ def main():
     ap.add_argument("--reuse-skip", type=float, default=0.2)
     ap.add_argument("--reuse-diag-every", type=int, default=16,
                     help="diagnose every this many sparse steps (and the selection step)")
+    ap.add_argument("--sweep-select", default=None, metavar="WORKLOAD",
+                    help="only run the forward-time sweep over the top-k budget on a content-driven "
+                         "workload (C3: k of the 64 image key blocks; C5: the fraction rho of each "
+                         "column group) with a least-squares fit")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the kept-pairs sweep of the forward at the C4 shape "
                          "(arrow windows 0..127 and all-FULL) with a least-squares fit")
@@ -119,6 +123,9 @@ def main():
     bsa.load()
     if args.sweep:
         print(json.dumps(sweep(torch, bsa, synth, dev)), flush=True)
+        return
+    if args.sweep_select:
+        print(json.dumps(select_sweep(torch, bsa, synth, dev, args.sweep_select)), flush=True)
         return
     if args.reuse:
         print(json.dumps(reuse_loop(torch, bsa, synth, dev, args)), flush=True)
@@ -348,6 +355,8 @@ def main():
         "forward_ms": round(fwd_avg, 4),
         "forward_ms_p10_p50_p90": [round(float(np.percentile(fwd_ms, q_)), 4) for q_ in (10, 50, 90)],
         "layout_ms": {k2: round(v2, 4) for k2, v2 in part_ms.items()},
+        "scoring_ratio": (round((part_ms["pool_scores"] + part_ms["select"]) / fwd_avg, 4)
+                          if "pool_scores" in part_ms else None),
         "permute_out_ms": None if post_ms is None else round(post_ms, 4),
         "token_pairs": token_pairs,
         "token_level_tflops": (None if token_pairs is None else
@@ -464,6 +473,64 @@ def sweep(torch, bsa, synth, dev, windows=(0, 1, 2, 4, 8, 18, 32, 64, 127), reps
         theoretical = full["kept_pairs"] / p_["kept_pairs"]
         p_["speedup_realised_over_theoretical"] = round(realised / theoretical, 3)
     return {"sweep": "forward time vs kept pairs, C4 shape (B1 H24 N16896 D128 block 128)",
+            "fit_ms": {"intercept": round(float(a), 4), "us_per_kept_pair": round(float(b) * 1e3, 6),
+                       "r2": round(r2, 5)},
+            "points": pts}
+
+
+def select_sweep(torch, bsa, synth, dev, name, reps=None):
+    """Forward time against kept pairs over the top-k budget of a
+    content-driven workload: the scores are computed once, then each budget
+    (every group's k scaled to the fraction rho of its width, up to all
+    columns) is selected and its forward timed; least-squares fit
+    t = a + b * pairs and realised over theoretical speedup against the
+    all-columns point."""
+    wl = synth.WORKLOADS[name]
+    if wl.layout != "select":
+        raise SystemExit("--sweep-select needs a content-driven (select) workload")
+    x = synth.make_inputs(wl)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = d(x["q"]), d(x["k"]), d(x["v"])
+    w = torch.from_numpy(x["w"]).to(dev) if "w" in x else None
+    B, H, N, D, block, nB = wl.B, wl.H, wl.N, wl.D, wl.block, wl.n_blocks
+    S = bsa.pool_scores(q, k, block, wl.score_mode, w=w)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    reps = reps or (30 if N <= 8192 else 5)
+    pts = []
+    for rho in (0.0625, 0.125, 0.25, 0.5, 0.75, 1.0):
+        groups = tuple((c0, c1, max(1, int(round(rho * (c1 - c0))))) for c0, c1, _ in wl.groups)
+        rp, ci = bsa.select_topk(S, wl.text_blocks, groups)
+        split = bsa.select_split_policy(B, H, nB, wl.text_blocks, groups, block=block)
+        kw = {"split": split} if split is not None else {}
+        for _ in range(3):
+            bsa.forward(q, k, v, block, rp, ci, out=out, lse=lse, **kw)
+        torch.cuda.synchronize()
+        pairs = int(rp[-1].item())
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            bsa.forward(q, k, v, block, rp, ci, out=out, lse=lse, **kw)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        t = float(np.median(ts))
+        pts.append({"rho": rho, "groups": [list(g) for g in groups], "kept_pairs": pairs, "forward_ms": round(t, 4),
+                    "tflops": round(4.0 * block * block * D * pairs / (t * 1e-3) / 1e12, 1)})
+    xs = np.array([p_["kept_pairs"] for p_ in pts], dtype=np.float64)
+    ys = np.array([p_["forward_ms"] for p_ in pts], dtype=np.float64)
+    A = np.stack([np.ones_like(xs), xs], axis=1)
+    (a, b), *_ = np.linalg.lstsq(A, ys, rcond=None)
+    r2 = 1.0 - float(((ys - (a + b * xs)) ** 2).sum() / ((ys - ys.mean()) ** 2).sum())
+    full = pts[-1]
+    for p_ in pts:
+        p_["speedup_realised_over_theoretical"] = round(
+            (full["forward_ms"] / p_["forward_ms"]) / (full["kept_pairs"] / p_["kept_pairs"]), 3)
+    return {"sweep": f"forward time vs top-k budget, {wl.name} shape (B{B} H{H} N{N} D{D} block {block})",
             "fit_ms": {"intercept": round(float(a), 4), "us_per_kept_pair": round(float(b) * 1e3, 6),
                        "r2": round(r2, 5)},
             "points": pts}
