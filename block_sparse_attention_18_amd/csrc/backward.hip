@@ -594,7 +594,7 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
                     if (koff(r) >= lim) s[r] = -INFINITY;
             }
             bf16x8 pp[2], ps[2];
-            if (NBM && kimg && (qlist[t / (BETA / 64)] >> 30) != 0) {
+            if (NBM && kimg && (qlist[t / (BETA / 64)] >> 30) != 0 && qblock(t) >= p.nb.Tb) {
                 // a partially covered entry (an image query block): queries
                 // whose window misses the lane's key
                 const int i = qblock(t), tq = i - p.nb.Tb, aq = tq / p.nb.tpr;
