@@ -60,6 +60,7 @@ CASES = [
     (2, 2, 3 * 128 + 40, 128, 128, 702),
     (1, 3, 5 * 64, 128, 64, 703),
     (2, 1, 4 * 128, 64, 128, 704),
+    (1, 3, 33, 128, 128, 706),          # one partial block, its second sub-tile empty
 ]
 
 
@@ -75,6 +76,32 @@ def test_backward_random_block_lists(B, H, N, D, block, seed):
     _check_grad(bf16_to_f64(dq), wq, "dQ")
     _check_grad(bf16_to_f64(dk), wk, "dK")
     _check_grad(bf16_to_f64(dv), wv, "dV")
+
+
+def test_backward_one_token():
+    # N = 1: a non-empty row keeps only the token itself, so P = 1, O = V,
+    # Delta = dO . V = dP and dS = 0 exactly: dQ = dK = 0 and dV = dO (to
+    # fp32 rounding of the two equal dot products).  An empty row gives zeros.
+    B, H, N, D, block = 1, 3, 1, 64, 64
+    q, k, v = synth.random_qkv(B, H, N, D, seed=705)
+    g = synth.random_qkv(B, H, N, D, seed=755)[0]
+    rp = np.array([0, 1, 1, 2], np.int32)                  # heads 0 and 2 keep the block, head 1 is empty
+    ci = np.array([0, 0], np.int32)
+    dq, dk, dv = _run(q, k, v, g, block, rp, ci)
+    gq, gk, gv = (bf16_to_f64(t) for t in (dq, dk, dv))
+    qf, kf, vf, gf = (bf16_to_f64(to_dev_bf16(a)) for a in (q, k, v, g))
+    scale = 1.0 / np.sqrt(D)
+    for h in (0, 2):
+        np.testing.assert_allclose(gv[0, h], gf[0, h], rtol=2 ** -8, atol=0)
+        # dP and Delta are the same D products (exact in fp32) summed in two
+        # orders: |dS| <= 2 D 2^-24 sum |dO V| (4x margin below); dQ = scale dS K,
+        # dK = scale dS Q
+        ds = 4 * 2 * D * 2.0 ** -24 * float(np.abs(gf[0, h, 0] * vf[0, h, 0]).sum())
+        assert np.abs(gq[0, h]).max() <= scale * ds * np.abs(kf[0, h]).max()
+        assert np.abs(gk[0, h]).max() <= scale * ds * np.abs(qf[0, h]).max()
+    assert np.all(gq[0, 1] == 0) and np.all(gk[0, 1] == 0) and np.all(gv[0, 1] == 0)
+    wq, wk, wv = oracle.backward(q, k, v, g, block, rp, ci)
+    np.testing.assert_allclose(gv, wv, rtol=2 ** -8, atol=1e-12)
 
 
 def test_backward_scale_large_logits_and_determinism():

@@ -47,6 +47,7 @@ FWD_CASES = [
     (2, 2, 3 * 128, 64, 128, 103),
     (1, 3, 6 * 64, 128, 64, 104),
     (1, 1, 40, 128, 128, 105),          # a single partial block
+    (1, 3, 1, 64, 64, 106),             # one token: rows empty or holding the token itself
 ]
 
 
