@@ -86,6 +86,9 @@ def main():
     ap.add_argument("--reuse-skip", type=float, default=0.2)
     ap.add_argument("--reuse-diag-every", type=int, default=16,
                     help="diagnose every this many sparse steps (and the selection step)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step (layout + forward [+ permutation back]) in a HIP graph, "
+                         "check three replays against the eager step bit for bit, and time replays")
     ap.add_argument("--sweep-select", default=None, metavar="WORKLOAD",
                     help="only run the forward-time sweep over the top-k budget on a content-driven "
                          "workload (C3: k of the 64 image key blocks; C5: the fraction rho of each "
@@ -298,6 +301,8 @@ def main():
     fwd_avg = float(np.mean(fwd_ms))
     part_ms = {name: float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev]))
                for j, name in enumerate(layout_parts)}
+    graph = graph_step(torch, stream, layout, forward, post, [out, lse, row_ptr, col_idx], args.steps) \
+        if args.graph else None
     if args.fp8:
         # quantisation of Q, K, V: reads them (V twice: channel maxima, then
         # codes) and writes the codes; the scales are negligible
@@ -365,6 +370,7 @@ def main():
         "forward_dense_equiv_tflops": round(dense_flop / (fwd_avg * 1e-3) / 1e12, 2),
         "step_wall_ms": round(wall * 1e3 / args.steps, 4),
         "fp8_quantize": quant,
+        "graph": graph,
         "roofline": {
             "bound": "mfma",
             "kernel": ("bsa::fwd8_kernel" if args.fp8 else
@@ -476,6 +482,43 @@ def sweep(torch, bsa, synth, dev, windows=(0, 1, 2, 4, 8, 18, 32, 64, 127), reps
             "fit_ms": {"intercept": round(float(a), 4), "us_per_kept_pair": round(float(b) * 1e3, 6),
                        "r2": round(r2, 5)},
             "points": pts}
+
+
+def graph_step(torch, stream, layout, forward, post, outs, steps):
+    """One step captured in a HIP graph (torch.cuda.graph: the library's
+    launches go to the capturing stream).  Three replays, each after an eager
+    step, must reproduce the eager outputs bit for bit; then `steps` replays
+    are timed with events."""
+    def step():
+        layout()
+        forward()
+        if post is not None:
+            post()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        step()
+        torch.cuda.synchronize()
+        eager = [t.clone() for t in outs]
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(outs, eager)):
+            raise SystemExit("a graph replay differs from the eager step")
+    for _ in range(3):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"ms_per_step": round(e0.elapsed_time(e1) / steps, 4), "replays_checked_bitwise": 3}
 
 
 def select_sweep(torch, bsa, synth, dev, name, reps=None):
