@@ -363,11 +363,14 @@ def _makespan(costs, slots: int) -> float:
 # the predicted gain a split must reach (the list-schedule model ignores that
 # the last workgroups run faster on an emptier chip, so it is optimistic).
 _ITEM_OVERHEAD = 0.5
-_SPLIT_OVERHEAD = 8.0
-_SPLIT_GAIN = 0.8
+# the plan and combine kernels cost ~15-25 us; in block steps of one
+# workgroup that is ~4 at block 128 and ~20 at block 64 (measured on the
+# FLUX 1024^2 mix, the 2K MMDiT arrow layout and the content-driven DiT)
+_SPLIT_OVERHEAD = {128: 4.0, 64: 20.0}
+_SPLIT_GAIN = 0.95
 
 
-def _split_from_rows(nB: int, lens, typical: int, target_chunks: int, slots: int):
+def _split_from_rows(nB: int, lens, typical: int, target_chunks: int, slots: int, overhead: float):
     """Split plan from per-row block counts given in dispatch order.  Rows longer
     than L = max(typical, ceil(nB / target_chunks)) would be cut into at most
     ceil(nB / L) chunks; the plan is returned only when the list-schedule
@@ -383,7 +386,7 @@ def _split_from_rows(nB: int, lens, typical: int, target_chunks: int, slots: int
     for x in lens:
         c = min(S, -(-x // L)) if x > L else 1
         cut += [x / c + _ITEM_OVERHEAD] * c
-    if _makespan(cut, slots) + _SPLIT_OVERHEAD >= _SPLIT_GAIN * _makespan(whole, slots):
+    if _makespan(cut, slots) + overhead >= _SPLIT_GAIN * _makespan(whole, slots):
         return None
     return {"chunk_blocks": L, "max_chunks": S, "max_split_rows": long_rows}
 
@@ -419,7 +422,7 @@ def arrow_split_policy(B: int, H: int, N: int, block: int, text_len: int, head_m
         typical = -(-nB // target_chunks)
     # dispatch order of the forward: query-block-major, then batch and head
     lens = [per_head[h][i] for i in range(nB) for _ in range(B) for h in range(H)]
-    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block))
+    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block), _SPLIT_OVERHEAD[block])
 
 
 def select_split_policy(B: int, H: int, nB: int, text_blocks: int, groups, target_chunks: int = 4,
@@ -428,7 +431,7 @@ def select_split_policy(B: int, H: int, nB: int, text_blocks: int, groups, targe
     text + k blocks), or None when splitting would not pay."""
     typical = min(nB, text_blocks + sum(int(g[2]) for g in groups))
     lens = [nB if i < text_blocks else typical for i in range(nB) for _ in range(B * H)]
-    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block))
+    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block), _SPLIT_OVERHEAD[block])
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,

@@ -124,10 +124,15 @@ def test_split_policies():
     # w = 0: the text rows dominate; they are cut into 4 chunks of <= 33 blocks
     plan = bsa.arrow_split_policy(1, 24, 16896, 128, 512, modes, [0] * 24)
     assert plan == {"chunk_blocks": 33, "max_chunks": 4, "max_split_rows": 96}
-    # FLUX 1024^2 mix (12 arrow w=1 / 8 full / 4 skip): the predicted gain is
-    # marginal, so the policy keeps rows whole
+    # FLUX 1024^2 mix (12 arrow w=1 / 8 full / 4 skip): the full heads' and the
+    # text rows (36 blocks) against 7-block arrow rows leave a tail; they are
+    # cut into 4 chunks of <= 9 blocks
     modes2 = [1] * 12 + [0] * 8 + [2] * 4
-    assert bsa.arrow_split_policy(1, 24, 4608, 128, 512, modes2, [1] * 24) is None
+    plan2 = bsa.arrow_split_policy(1, 24, 4608, 128, 512, modes2, [1] * 24)
+    assert plan2 == {"chunk_blocks": 9, "max_chunks": 4, "max_split_rows": 8 * 36 + 12 * 4}
+    # the content-driven DiT (block 64): the plan and combine cost more than
+    # the tail of its text rows
+    assert bsa.select_split_policy(2, 16, 68, 4, ((4, 68, 16),), block=64) is None
     # with a single long head among many windowed ones the split pays
     modes3 = [0] + [1] * 63
     plan3 = bsa.arrow_split_policy(1, 64, 4608, 128, 512, modes3, [0] * 64)
