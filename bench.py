@@ -178,8 +178,9 @@ def main():
                 mark()
             bsa.build_neighborhood_layout(B, H, nb, row_ptr=row_ptr, col_idx=col_idx, flags=flags)
         layout_parts = ("permute_in", "layout")
-        split = bsa.arrow_split_policy(B, H, N, block, wl.text_len, [bsa.HEAD_ARROW] * H,
-                                       [max(wl.nb_window) // max(wl.nb_tile)] * H)
+        # the split policy reads the row lengths of the built layout
+        layout()
+        split = bsa.row_split_policy(row_ptr[:B * H * nB + 1].cpu().tolist(), B, H, nB, block)
         fwd_kw = {}
 
         def post():

@@ -425,6 +425,18 @@ def arrow_split_policy(B: int, H: int, N: int, block: int, text_len: int, head_m
     return _split_from_rows(nB, lens, typical, target_chunks, _slots(block), _SPLIT_OVERHEAD[block])
 
 
+def row_split_policy(row_ptr, B: int, H: int, nB: int, block: int, target_chunks: int = 4):
+    """Long-row split for any built block list, from its row lengths (a host
+    copy of row_ptr, [B*H*nB + 1], as a sequence of ints) in the forward's
+    dispatch order (query-block-major); the typical row is the longest one
+    short of nB."""
+    rp = [int(x) for x in row_ptr]
+    lens = [rp[bh * nB + i + 1] - rp[bh * nB + i] for i in range(nB) for bh in range(B * H)]
+    short = [x for x in lens if x < nB]
+    typical = max(short) if short else 1
+    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block), _SPLIT_OVERHEAD[block])
+
+
 def select_split_policy(B: int, H: int, nB: int, text_blocks: int, groups, target_chunks: int = 4,
                         block: int = 128):
     """Long-row split for a top-k selection (dense text rows next to rows of

@@ -363,3 +363,20 @@ def test_binding_refuses_host_tensors():
         bsa._desc(q, "q")
     with pytest.raises(ValueError):
         bsa._desc(torch.zeros(1, 1, 64, 64), "q")
+
+
+def test_row_split_policy_reads_row_lengths():
+    # the policy from a built block list: 8 heads of 64 blocks whose first row
+    # is dense (64 blocks) and the others hold 2; the dense rows set the
+    # makespan and are cut into 4 chunks of 16
+    nB, BH = 64, 8
+    lens = [64] + [2] * 63
+    rp = [0]
+    for _ in range(BH):
+        for x in lens:
+            rp.append(rp[-1] + x)
+    plan = bsa.row_split_policy(rp, 1, BH, nB, 128)
+    assert plan == {"chunk_blocks": 16, "max_chunks": 4, "max_split_rows": BH}
+    # uniform rows: nothing to split
+    rp_u = [3 * r for r in range(BH * nB + 1)]
+    assert bsa.row_split_policy(rp_u, 1, BH, nB, 128) is None
