@@ -813,15 +813,17 @@ def cpu_baseline(wl, x, row_ptr, col_idx, seconds, modes):
         kept = (rp[r + 1] - rp[r]).astype(np.float64)
         return float((4.0 * block * D * kept).sum())
 
-    probe = rows_of(64)
-    t = time.perf_counter()
-    run(probe)
-    dt = max(time.perf_counter() - t, 1e-3)
-    n = int(min(max(64 * seconds / dt, 64), 1000000))
-    rows = rows_of(n)
-    t = time.perf_counter()
-    run(rows)
-    dt = time.perf_counter() - t
+    # grow the sample until it takes at least half the target time (a small
+    # probe overestimates the per-row cost: thread start-up dominates it)
+    n = 64
+    while True:
+        rows = rows_of(n)
+        t = time.perf_counter()
+        run(rows)
+        dt = time.perf_counter() - t
+        if dt >= 0.5 * seconds or n >= 1000000:
+            break
+        n = int(min(max(n * seconds / max(dt, 1e-3), 2 * n), 1000000))
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
