@@ -26,6 +26,7 @@ Every function follows the definitions stated in ``bsa_oracle.c``:
                           token order, block layout with full / partial flags
   forward_f64 / backward  the forward on fp64 inputs and its gradient
                           (dQ, dK, dV of the kept-block softmax)
+  backward_dq_rows        dQ of selected query rows (full-size checks)
   forward_neighborhood_f64 / backward_neighborhood
                           the same under the 2-D neighbourhood token mask
   output_rse              per-head relative squared error of an output
@@ -82,6 +83,8 @@ def _load():
         lib.oracle_forward_neighborhood_f64.restype = ctypes.c_int
         lib.oracle_backward_neighborhood_f64.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, D_, P, P, P]
         lib.oracle_backward_neighborhood_f64.restype = ctypes.c_int
+        lib.oracle_backward_dq_rows.argtypes = [P, P, P, P, I, I, I, I, I, P, P, D_, P, I, P]
+        lib.oracle_backward_dq_rows.restype = ctypes.c_int
         lib.oracle_score_grad.argtypes = [P, P, I, I, I, I, I, P, I, P, P, P, P]
         lib.oracle_score_grad.restype = ctypes.c_int
         lib.oracle_scores_exact_avgpool.argtypes = [P, P, I, I, I, I, I, D, P, I, P]
@@ -492,6 +495,20 @@ def backward(q, k, v, dO, block: int, row_ptr, col_idx, scale: Optional[float] =
     _check(_load().oracle_backward_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), B, H, N, D, block, _ptr(rp), _ptr(ci),
                                        scale, _ptr(dQ), _ptr(dK), _ptr(dV)), "backward")
     return dQ, dK, dV
+
+
+def backward_dq_rows(q, k, v, dO, block: int, row_ptr, col_idx, rows, scale: Optional[float] = None):
+    """dQ (fp64, [len(rows), D]) of the flat query rows `rows` (indices into
+    [B*H*N]) of the block-sparse forward's gradient."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rp, ci = _csr(row_ptr, col_idx)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((len(r), D), np.float64)
+    _check(_load().oracle_backward_dq_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), B, H, N, D, block, _ptr(rp),
+                                           _ptr(ci), scale, _ptr(r), len(r), _ptr(out)), "backward_dq_rows")
+    return out
 
 
 def forward_neighborhood_f64(q, k, v, text_len: int, grid: Tuple[int, int], window: Tuple[int, int],

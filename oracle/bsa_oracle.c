@@ -1002,6 +1002,58 @@ int oracle_backward_f64(const double *q, const double *k, const double *v, const
     return rc;
 }
 
+/* dQ of selected query rows only (flat row indices into [B*H*N]): row t's
+ * gradient needs only row t of P and dP, so rows of a full-size problem can
+ * be checked one by one.  Same formulas as oracle_backward_f64. */
+int oracle_backward_dq_rows(const double *q, const double *k, const double *v, const double *dO, int64_t B,
+                            int64_t H, int64_t N, int64_t D, int64_t beta, const int32_t *row_ptr,
+                            const int32_t *col_idx, double scale, const int64_t *rows, int64_t n_rows, double *dQ)
+{
+    if (!q || !k || !v || !dO || !rows || !dQ || B <= 0 || H <= 0 || N <= 0 || D <= 0 || beta <= 0)
+        return OR_EINVAL;
+    const int64_t nB = nblocks(N, beta);
+    if (!bw_check_csr(B * H * nB, nB, row_ptr, col_idx)) return OR_EINVAL;
+    for (int64_t x = 0; x < n_rows; ++x)
+        if (rows[x] < 0 || rows[x] >= B * H * N) return OR_EINVAL;
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *p = malloc(sizeof(double) * N);
+        double *dp = malloc(sizeof(double) * N);
+        unsigned char *kept = malloc((size_t)nB);
+        if (!p || !dp || !kept) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t x = 0; x < n_rows; ++x) {
+                const int64_t bh = rows[x] / N, t = rows[x] % N;
+                double *dq = dQ + x * D;
+                for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
+                if (!bw_row_probs(q, k, N, D, beta, nB, bh, t, row_ptr, col_idx, scale, kept, p, NULL)) continue;
+                const double *go = dO + (bh * N + t) * D;
+                double delta = 0.0;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (p[s] == 0.0) { dp[s] = 0.0; continue; }
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d) acc += go[d] * v[(bh * N + s) * D + d];
+                    dp[s] = acc;
+                    delta += p[s] * acc;
+                }
+                for (int64_t s = 0; s < N; ++s) {
+                    if (p[s] == 0.0) continue;
+                    const double ds = p[s] * (dp[s] - delta);
+                    for (int64_t d = 0; d < D; ++d) dq[d] += scale * ds * k[(bh * N + s) * D + d];
+                }
+            }
+        }
+        free(p);
+        free(dp);
+        free(kept);
+    }
+    return rc;
+}
+
 /* ------------------------------------------------------------------------
  * Backward of the 2-D neighbourhood attention (GNA notes, 1.1), natural
  * token order, fp64 inputs: the gradient of the dense softmax under the

@@ -131,3 +131,32 @@ def test_backward_arrow_2k_shape_two_heads():
     _check_grad(bf16_to_f64(dq), wq, "dQ")
     _check_grad(bf16_to_f64(dk), wk, "dK")
     _check_grad(bf16_to_f64(dv), wv, "dV")
+
+
+def test_backward_full_2k_workload_sampled_rows_and_sums():
+    """The full 2K MMDiT workload (24 heads, arrow w = 8) as bench.py times it:
+    sampled dQ rows against the oracle row by row, and two identities that
+    hold at any size.  Every row of P sums to one, so the keys' dV add up to
+    the sum of dO over the (non-empty) query rows; every row of dS sums to
+    zero, so the keys' dK add up to zero.  Both sums keep rounding that is
+    random in sign (Delta from the bf16 O, P and dS rounded to bf16), summed
+    over 16896 tokens: bounded by 2e-3 of the sum of magnitudes (measured
+    1.6e-4 for dK, 9.4e-5 for dV)."""
+    wl = synth.WORKLOADS["C4"]
+    x = synth.make_inputs(wl)
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    g = synth.random_qkv(B, H, N, D, seed=730)[0]
+    rp, ci = oracle.arrow(B, H, wl.n_blocks, wl.text_blocks, x["head_modes"], x["head_windows"])
+    _log("backward full C4")
+    dq, dk, dv = _run(x["q"], x["k"], x["v"], g, wl.block, rp, ci)
+    rng = np.random.default_rng(731)
+    rows = np.concatenate([[0, 511, 512, N - 1, (H - 1) * N + 600],
+                           (rng.integers(0, H, 59) * N + rng.integers(0, N, 59))]).astype(np.int64)
+    want = oracle.backward_dq_rows(x["q"], x["k"], x["v"], g, wl.block, rp, ci, rows)
+    _check_grad(bf16_to_f64(dq).reshape(-1, D)[rows], want, "dQ rows")
+    gk, gv = bf16_to_f64(dk), bf16_to_f64(dv)
+    go = synth.bf16_to_f32(g).astype(np.float64)
+    dk_sum = np.abs(gk.sum(axis=2)) / np.abs(gk).sum(axis=2)          # [B, H, D]
+    dv_err = np.abs(gv.sum(axis=2) - go.sum(axis=2)) / np.abs(gv).sum(axis=2)
+    _log(f"  sum dK / sum |dK|: max {dk_sum.max():.2e}; |sum dV - sum dO| / sum |dV|: max {dv_err.max():.2e}")
+    assert dk_sum.max() <= 2e-3 and dv_err.max() <= 2e-3

@@ -86,3 +86,15 @@ def test_forward_f64_matches_the_bf16_oracle():
     O2, L2 = oracle.forward_f64(q, k, v, block, rp, ci)
     np.testing.assert_allclose(O2, O, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(L2[np.isfinite(L)], L[np.isfinite(L)], rtol=1e-12)
+
+
+def test_dq_rows_are_the_full_gradient_rows():
+    # the per-row dQ (for full-size checks) is the full backward's dQ,
+    # including an empty row and the ragged last block
+    q, k, v = synth.random_qkv(2, 2, 200, 16, seed=3)
+    g = synth.random_qkv(2, 2, 200, 16, seed=4)[0]
+    rp, ci = synth.random_block_lists(2, 2, 4, seed=5, density=0.5, empty_rows=1)
+    dq, _, _ = oracle.backward(q, k, v, g, 64, rp, ci)
+    rows = np.array([0, 5, 63, 64, 199, 200, 401, 799])
+    got = oracle.backward_dq_rows(q, k, v, g, 64, rp, ci, rows)
+    np.testing.assert_array_equal(got, dq.reshape(-1, 16)[rows])
