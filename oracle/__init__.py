@@ -85,6 +85,9 @@ def _load():
         lib.oracle_backward_neighborhood_f64.restype = ctypes.c_int
         lib.oracle_backward_dq_rows.argtypes = [P, P, P, P, I, I, I, I, I, P, P, D_, P, I, P]
         lib.oracle_backward_dq_rows.restype = ctypes.c_int
+        lib.oracle_backward_neighborhood_dq_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, D_, P, I,
+                                                             P]
+        lib.oracle_backward_neighborhood_dq_rows.restype = ctypes.c_int
         lib.oracle_score_grad.argtypes = [P, P, I, I, I, I, I, P, I, P, P, P, P]
         lib.oracle_score_grad.restype = ctypes.c_int
         lib.oracle_scores_exact_avgpool.argtypes = [P, P, I, I, I, I, I, D, P, I, P]
@@ -538,3 +541,19 @@ def backward_neighborhood(q, k, v, dO, text_len: int, grid: Tuple[int, int], win
                                                     kh, kw, sh, sw, scale, _ptr(dQ), _ptr(dK), _ptr(dV)),
            "backward_neighborhood")
     return dQ, dK, dV
+
+
+def backward_neighborhood_dq_rows(q, k, v, dO, text_len: int, grid: Tuple[int, int], window: Tuple[int, int],
+                                  stride: Tuple[int, int], rows, scale: Optional[float] = None):
+    """dQ (fp64, [len(rows), D]) of the flat natural-order query rows `rows`
+    of the neighbourhood backward."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    (R, C), (kh, kw), (sh, sw) = grid, window, stride
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((len(r), D), np.float64)
+    _check(_load().oracle_backward_neighborhood_dq_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), B, H, N, D, text_len,
+                                                        R, C, kh, kw, sh, sw, scale, _ptr(r), len(r), _ptr(out)),
+           "backward_neighborhood_dq_rows")
+    return out

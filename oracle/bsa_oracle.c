@@ -1167,3 +1167,54 @@ int oracle_backward_neighborhood_f64(const double *q, const double *k, const dou
     }
     return rc;
 }
+
+/* dQ of selected query rows (flat indices into [B*H*N], natural order) of
+ * the neighbourhood backward: the same arithmetic as
+ * oracle_backward_neighborhood_f64 restricted to those rows. */
+int oracle_backward_neighborhood_dq_rows(const double *q, const double *k, const double *v, const double *dO,
+                                         int64_t B, int64_t H, int64_t N, int64_t D, int64_t text_len, int64_t R,
+                                         int64_t C, int64_t kh, int64_t kw, int64_t sh, int64_t sw, double scale,
+                                         const int64_t *rows, int64_t n_rows, double *dQ)
+{
+    if (!q || !k || !v || !dO || !rows || !dQ || B <= 0 || H <= 0 || D <= 0 ||
+        !na_check(N, text_len, R, C, kh, kw, sh, sw))
+        return OR_EINVAL;
+    for (int64_t x = 0; x < n_rows; ++x)
+        if (rows[x] < 0 || rows[x] >= B * H * N) return OR_EINVAL;
+    const na_geom g = {text_len, R, C, kh, kw, sh, sw};
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *p = malloc(sizeof(double) * N);
+        double *dp = malloc(sizeof(double) * N);
+        if (!p || !dp) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t x = 0; x < n_rows; ++x) {
+                const int64_t bh = rows[x] / N, t = rows[x] % N;
+                double *dq = dQ + x * D;
+                const double *go = dO + (bh * N + t) * D;
+                na_row_probs(q, k, N, D, bh, t, &g, scale, p, NULL);
+                double delta = 0.0;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (p[s] == 0.0) { dp[s] = 0.0; continue; }
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d) acc += go[d] * v[(bh * N + s) * D + d];
+                    dp[s] = acc;
+                    delta += p[s] * acc;
+                }
+                for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
+                for (int64_t s = 0; s < N; ++s) {
+                    if (p[s] == 0.0) continue;
+                    const double ds = p[s] * (dp[s] - delta);
+                    for (int64_t d = 0; d < D; ++d) dq[d] += scale * ds * k[(bh * N + s) * D + d];
+                }
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return rc;
+}

@@ -94,3 +94,32 @@ def test_backward_peaked_logits_and_determinism():
     _check_grad(bf16_to_f64(a[0]), wq, "dQ")
     _check_grad(bf16_to_f64(a[1]), wk, "dK")
     _check_grad(bf16_to_f64(a[2]), wv, "dV")
+
+
+@pytest.mark.parametrize("stride", [(1, 1), (32, 32)])
+def test_backward_full_g1_workload_sampled_rows_and_sums(stride):
+    """The full 2-D neighbourhood workload G1 (FLUX 2048², 24 heads, window
+    32 x 32, tiles 8 x 16) as bench.py runs it: sampled dQ rows against the
+    oracle row by row, and the column-sum identities of dK (zero) and dV (the
+    sum of dO), bounded as for the 2K arrow workload (2e-3 of the sum of
+    magnitudes)."""
+    wl = synth.WORKLOADS["G1"]
+    x = synth.make_inputs(wl)
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    T = wl.text_len
+    nb = bsa.neighborhood(T, wl.nb_grid, wl.nb_tile, wl.nb_window, stride)
+    g = synth.random_qkv(B, H, N, D, seed=1220)[0]
+    _log(f"nb backward full G1 stride {stride}")
+    (dq, dk, dv), _ = _backward_natural(x["q"], x["k"], x["v"], g, nb)
+    rng = np.random.default_rng(1221)
+    rows = np.concatenate([[0, T - 1, T, T + 127, N - 1, (H - 1) * N + T + 5000],
+                           rng.integers(0, H, 42) * N + rng.integers(0, N, 42)]).astype(np.int64)
+    want = oracle.backward_neighborhood_dq_rows(x["q"], x["k"], x["v"], g, T, wl.nb_grid, wl.nb_window, stride,
+                                                rows)
+    _check_grad(bf16_to_f64(dq).reshape(-1, D)[rows], want, "dQ rows")
+    gk, gv = bf16_to_f64(dk), bf16_to_f64(dv)
+    go = synth.bf16_to_f32(g).astype(np.float64)
+    dk_sum = np.abs(gk.sum(axis=2)) / np.abs(gk).sum(axis=2)
+    dv_err = np.abs(gv.sum(axis=2) - go.sum(axis=2)) / np.abs(gv).sum(axis=2)
+    _log(f"  sum dK / sum |dK|: max {dk_sum.max():.2e}; |sum dV - sum dO| / sum |dV|: max {dv_err.max():.2e}")
+    assert dk_sum.max() <= 2e-3 and dv_err.max() <= 2e-3

@@ -100,3 +100,14 @@ def test_token_mask_changes_the_gradient():
     inv = np.argsort(perm)
     for a, b in zip(got, want):
         assert np.abs(a[:, :, inv] - b).max() > 0.2 * np.abs(b).max()
+
+
+def test_dq_rows_are_the_full_gradient_rows():
+    T, grid, window, stride = 4, (6, 8), (3, 5), (1, 2)
+    N = T + grid[0] * grid[1]
+    q, k, v = random_qkv(1, 2, N, 8, seed=1401)
+    g = random_qkv(1, 2, N, 8, seed=1402)[0]
+    dq, _, _ = oracle.backward_neighborhood(q, k, v, g, T, grid, window, stride)
+    rows = np.array([0, 3, 4, 30, N - 1, N, 2 * N - 1])
+    got = oracle.backward_neighborhood_dq_rows(q, k, v, g, T, grid, window, stride, rows)
+    np.testing.assert_array_equal(got, dq.reshape(-1, 8)[rows])
