@@ -65,6 +65,10 @@ def main():
     ap.add_argument("--no-split", action="store_true", help="run every row in one workgroup")
     ap.add_argument("--stride", default=None, help="neighbourhood workloads: stride 'rows,cols'")
     ap.add_argument("--nb-window", default=None, help="neighbourhood workloads: window 'rows,cols'")
+    ap.add_argument("--nb-permuted", action="store_true",
+                    help="neighbourhood workloads: permute Q, K, V to tile-major order and O, LSE back in "
+                         "separate passes (the FP8 and backward runs always do) instead of the forward's "
+                         "natural-order gather")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -151,9 +155,13 @@ def main():
 
     post = None
     token_pairs = None
+    nb_natural = False
     if wl.layout == "neighborhood":
-        # inputs arrive in natural order: the step permutes Q, K, V to tile-major
-        # order, builds the layout, runs the forward and permutes O, LSE back
+        # inputs arrive in natural order: the step builds the layout and runs the
+        # forward, which gathers the tile-major tiles from natural order and
+        # scatters O, LSE back; with --nb-permuted (and for the FP8 and backward
+        # runs) it permutes Q, K, V to tile-major order and O, LSE back in
+        # separate passes
         stride = tuple(int(v2) for v2 in args.stride.split(",")) if args.stride else wl.nb_stride
         window = tuple(int(v2) for v2 in args.nb_window.split(",")) if args.nb_window else wl.nb_window
         wl = wl.replace(nb_stride=stride, nb_window=window)
@@ -164,27 +172,36 @@ def main():
         flags = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
         kept_pairs = cap
         computed_heads = B * H
-        qn, kn, vn = q, k, v
-        q, k, v = torch.empty_like(qn), torch.empty_like(kn), torch.empty_like(vn)
-        out_t = torch.empty_like(q)
-        lse_t = torch.empty_like(lse)
         R_, C_ = wl.nb_grid
         token_pairs = B * H * (wl.text_len * N + R_ * C_ * (wl.text_len + wl.nb_window[0] * wl.nb_window[1]))
+        nb_natural = not (args.fp8 or args.backward or args.nb_permuted)
+        if nb_natural:
+            out_t, lse_t = out, lse
 
-        def layout(mark=None):
-            for src, dst in ((qn, q), (kn, k), (vn, v)):
-                bsa.permute_tokens(src, nb, out=dst)
-            if mark is not None:
-                mark()
-            bsa.build_neighborhood_layout(B, H, nb, row_ptr=row_ptr, col_idx=col_idx, flags=flags)
-        layout_parts = ("permute_in", "layout")
+            def layout(mark=None):
+                bsa.build_neighborhood_layout(B, H, nb, row_ptr=row_ptr, col_idx=col_idx, flags=flags)
+            layout_parts = ("layout",)
+        else:
+            qn, kn, vn = q, k, v
+            q, k, v = torch.empty_like(qn), torch.empty_like(kn), torch.empty_like(vn)
+            out_t = torch.empty_like(q)
+            lse_t = torch.empty_like(lse)
+
+            def layout(mark=None):
+                for src, dst in ((qn, q), (kn, k), (vn, v)):
+                    bsa.permute_tokens(src, nb, out=dst)
+                if mark is not None:
+                    mark()
+                bsa.build_neighborhood_layout(B, H, nb, row_ptr=row_ptr, col_idx=col_idx, flags=flags)
+            layout_parts = ("permute_in", "layout")
         # the split policy reads the row lengths of the built layout
         layout()
         split = bsa.row_split_policy(row_ptr[:B * H * nB + 1].cpu().tolist(), B, H, nB, block)
         fwd_kw = {}
 
-        def post():
-            bsa.permute_tokens(out_t, nb, inverse=True, lse=lse_t, out=out, lse_out=lse)
+        if not nb_natural:
+            def post():
+                bsa.permute_tokens(out_t, nb, inverse=True, lse=lse_t, out=out, lse_out=lse)
     elif wl.layout == "arrow":
         modes, wins = x["head_modes"], x["head_windows"]
         cap = bsa.arrow_capacity(B, H, N, block, wl.text_len, modes, wins)
@@ -254,7 +271,7 @@ def main():
             bsa.quantize_fp8(q, k, v, out=qkv8, workspace=ws_q)
     elif wl.layout == "neighborhood":
         def forward():
-            bsa.forward_neighborhood(q, k, v, row_ptr, col_idx, flags, nb, out=out_t, lse=lse_t,
+            bsa.forward_neighborhood(q, k, v, row_ptr, col_idx, flags, nb, out=out_t, lse=lse_t, natural=nb_natural,
                                      **({"split": fwd_kw["split"]} if "split" in fwd_kw else {}))
     else:
         def forward():
@@ -320,7 +337,7 @@ def main():
         quant = {"ms": round(q_ms, 4), "hbm_bytes": 4 * 2 * elems + 3 * elems,
                  "GBps": round((4 * 2 * elems + 3 * elems) / (q_ms * 1e-3) / 1e9, 1)}
     cold = None
-    if wl.layout != "arrow":
+    if wl.layout == "select":
         cold = cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr,
                                  wl.score_mode == synth.SCORE_EXACT_AVGPOOL)
 

@@ -141,6 +141,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                     V]),
             "bsa_forward_neighborhood": (I32, [TP, TP, TP, I32, V, V, V, ctypes.POINTER(BsaNeighborhood), F, TP, V,
                                                ctypes.POINTER(BsaSplit), V]),
+            "bsa_forward_neighborhood_natural": (I32, [TP, TP, TP, I32, V, V, V, ctypes.POINTER(BsaNeighborhood), F, TP, V,
+                                               ctypes.POINTER(BsaSplit), V]),
             "bsa_backward_workspace_size": (SZ, [I64, I64, I64]),
             "bsa_backward": (I32, [TP, TP, TP, TP, TP, I32, V, V, V, F, TP, TP, TP, V, SZ, V]),
             "bsa_backward_neighborhood": (I32, [TP, TP, TP, TP, TP, I32, V, V, V, ctypes.POINTER(BsaNeighborhood), V, F,
@@ -690,9 +692,11 @@ def forward_neighborhood(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_
                          col_idx: torch.Tensor, entry_flags: torch.Tensor, nb: BsaNeighborhood,
                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                          lse: Optional[torch.Tensor] = None, return_lse: bool = True,
-                         split: Optional[dict] = None):
+                         split: Optional[dict] = None, natural: bool = False):
     """Block-sparse forward on tile-major Q, K, V, masking the partially
-    covered key tiles per token.  Returns (O, LSE) in tile-major order."""
+    covered key tiles per token.  Returns (O, LSE) in tile-major order; with
+    natural=True, Q, K, V and the returned O, LSE are in natural order (the
+    kernel gathers the tiles itself)."""
     lib = load()
     B, H, N, D = q.shape
     block = nb.tile_rows * nb.tile_cols
@@ -713,7 +717,8 @@ def forward_neighborhood(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_
         sp = BsaSplit(int(split["chunk_blocks"]), int(split["max_chunks"]), int(split["max_split_rows"]),
                       ws.data_ptr(), ws.numel() * ws.element_size())
     dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
-    _check(lib.bsa_forward_neighborhood(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), block, _ptr(row_ptr),
+    fn = lib.bsa_forward_neighborhood_natural if natural else lib.bsa_forward_neighborhood
+    _check(fn(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), block, _ptr(row_ptr),
                                         _ptr(col_idx), _ptr(entry_flags), ctypes.byref(nb), float(scale or 0.0),
                                         ctypes.byref(do), _ptr(lse), None if sp is None else ctypes.byref(sp),
                                         _stream(q.device)))

@@ -471,7 +471,7 @@ static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const b
                                const int32_t *row_ptr, const int32_t *col_idx, const int8_t *head_modes,
                                const bsa_tensor *o_cache, const float *lse_cache, float scale,
                                const bsa_tensor *o, float *lse, const bsa_split *split, void *stream,
-                               const int32_t *entry_flags, const bsa::NbGeom *nb)
+                               const int32_t *entry_flags, const bsa::NbGeom *nb, int natural = 0)
 {
     bsa_status st;
     if ((st = check_tensor(q, "q")) != BSA_OK) return st;
@@ -511,6 +511,7 @@ static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const b
     fp.v = t4(v);
     fp.flags = entry_flags;
     if (nb) fp.nb = *nb;
+    fp.natural = natural;
     fp.o = static_cast<uint16_t *>(o->data);
     fp.o_sb = o->stride_b;
     fp.o_sh = o->stride_h;
@@ -581,6 +582,8 @@ static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const b
         cp.D = (int32_t)q->D;
         cp.block = block;
         cp.max_chunks = split->max_chunks;
+        cp.natural = natural;
+        if (nb) cp.nb = *nb;
         if ((e = bsa::launch_combine(cp, split_rows, s)) != hipSuccess) return hip_fail(e, "combine launch");
     }
     if (any_skip) {
@@ -743,6 +746,21 @@ bsa_status bsa_forward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, co
     if ((st = check_nb(nb, q->N, block, &g)) != BSA_OK) return st;
     return forward_impl(q, k, v, block, row_ptr, col_idx, nullptr, nullptr, nullptr, scale, o, lse, split, stream,
                         entry_flags, &g);
+}
+
+bsa_status bsa_forward_neighborhood_natural(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                            int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                                            const int32_t *entry_flags, const bsa_neighborhood *nb, float scale,
+                                            const bsa_tensor *o, float *lse, const bsa_split *split,
+                                            void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if (!entry_flags) return fail(BSA_ERR_INVALID_ARG, "entry_flags null");
+    bsa::NbGeom g;
+    if ((st = check_nb(nb, q->N, block, &g)) != BSA_OK) return st;
+    return forward_impl(q, k, v, block, row_ptr, col_idx, nullptr, nullptr, nullptr, scale, o, lse, split, stream,
+                        entry_flags, &g, 1);
 }
 
 // ---------------------------------------------------------------------------

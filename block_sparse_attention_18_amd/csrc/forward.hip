@@ -69,6 +69,7 @@ struct WaveState {
     uint32_t kread;              // K operand of k-step 0 (bytes in a tile); k-step s: ^ KSTEP * s
     uint32_t vread;              // V^T operand of d tile 0, keys 0..3; d tile d: ^ VSTEP * d
     uint32_t kdma, vdma;         // source offset of the lane's first 16-byte copy of a tile
+    uint32_t knat, vnat;         // the same in natural token order (neighbourhood image tiles)
 };
 
 template <int BETA, int D>
@@ -90,6 +91,9 @@ __device__ __forceinline__ void init_offsets(WaveState<BETA, D> &st, const FwdPa
     const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
     st.kdma = (uint32_t)(r * p.k.sn * 2 + ((ps ^ kswz<D>(r)) * 16));
     st.vdma = (uint32_t)(r * p.v.sn * 2 + ((ps ^ vswz<D>(r)) * 16));
+    const int rn = nb_rowoff(p.nb, r);
+    st.knat = (uint32_t)(rn * p.k.sn * 2 + ((ps ^ kswz<D>(r)) * 16));
+    st.vnat = (uint32_t)(rn * p.v.sn * 2 + ((ps ^ vswz<D>(r)) * 16));
 }
 
 
@@ -196,11 +200,15 @@ __device__ __forceinline__ void pv_mfma(const uint16_t *__restrict__ Vc, const b
 // Issue the copy of one 64-key tile (K or V rows from key k0) into LDS.
 // Lane l of copy x writes the 16-byte slot (x*NW + wave)*64 + l; slot s holds
 // tile row s / KCH, chunk (s % KCH) XOR the row's swizzle.  A partial tile
-// repeats its last key (those scores are masked).
-template <int BETA, int D>
+// repeats its last key (those scores are masked).  NAT: with natural-order
+// inputs an image tile is gathered from its grid rows (tile row o sits
+// nb_rowoff(o) tokens after the tile's first token; a copy step adds the
+// same to every lane, so the source stays a per-lane offset offn plus a
+// scalar one).
+template <int BETA, int D, bool NAT = false>
 __device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t rs, int64_t sn,
-                                          uint32_t off0, bool is_v, const FwdParams &p, int k0, int wv,
-                                          int lane)
+                                          uint32_t off0, uint32_t offn, bool is_v, const FwdParams &p, int k0,
+                                          int wv, int lane)
 {
     using Sh = FwdShape<BETA, D>;
     const int rows = p.N - k0;
@@ -210,6 +218,28 @@ __device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_b
     // add), rather than a loop-invariant value of its own kept in a register
     __attribute__((address_space(3))) char *lbase = (__attribute__((address_space(3))) char *)(lds_void *)(dst + wv * 64 * 8);
     asm volatile("" : "+s"(lbase));
+    if (NAT && p.natural && k0 >= p.nb.T) {
+        // whole tiles only (text and grid are whole numbers of blocks)
+        const uint32_t sn0 = (uint32_t)((int64_t)nb_natural(p.nb, BETA, k0) * sn * 2);
+        if (Sh::UNIFORM_COPY) {
+#pragma unroll
+            for (int x = 0; x < Sh::DMA; ++x)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16, offn,
+                    sn0 + (uint32_t)((int64_t)nb_rowoff(p.nb, x * Sh::ROWS_PER_COPY) * sn * 2), 0, 0);
+        } else {
+#pragma unroll
+            for (int x = 0; x < Sh::DMA; ++x) {
+                const int slot = (x * Sh::NW + wv) * 64 + lane;
+                const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
+                const uint32_t o = (uint32_t)(nb_rowoff(p.nb, r) * sn * 2 +
+                                              ((ps ^ (is_v ? vswz<D>(r) : kswz<D>(r))) * 16));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16, o, sn0,
+                                                         0, 0);
+            }
+        }
+        return;
+    }
     if (Sh::UNIFORM_COPY && rows >= 64) {
         // full tile: copy x is copy 0 moved by x * ROWS_PER_COPY rows
         const uint32_t step = (uint32_t)((int64_t)Sh::ROWS_PER_COPY * sn * 2);
@@ -284,8 +314,8 @@ __device__ __forceinline__ void fused_step(
     // scheduled regions, and t's scores are not live yet
     mask_scores<BETA, D>(valid_p, k0_p, p.N, lane, s_prev);
     if (NBM && partial_p) mask_window<BETA, D>(p, k0_p, qrow, lane, s_prev);
-    if (load_k) load_tile<BETA, D>(Kn, krs, p.k.sn, st.kdma, false, p, k0_k, wv, lane);
-    load_tile<BETA, D>(Vn, vrs, p.v.sn, st.vdma, true, p, k0, wv, lane);
+    if (load_k) load_tile<BETA, D, NBM>(Kn, krs, p.k.sn, st.kdma, st.knat, false, p, k0_k, wv, lane);
+    load_tile<BETA, D, NBM>(Vn, vrs, p.v.sn, st.vdma, st.vnat, true, p, k0, wv, lane);
     const float c = p.scale_log2;
     bf16x8 pf[2][2];
     constexpr int PV_HALF = 2 * Sh::DT;        // MFMAs of PV over 32 keys
@@ -311,14 +341,14 @@ __device__ __forceinline__ void fused_step(
 }
 
 // First step: S^T of sub-tile 0 and its row max; copies K(1) and V(0).
-template <int BETA, int D>
+template <int BETA, int D, bool NBM>
 __device__ __forceinline__ void first_step(
     const uint16_t *__restrict__ Kc, uint16_t *__restrict__ Kn, uint16_t *__restrict__ Vn, bool valid,
     int k0, bool load_k, int k0_k, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
     const FwdParams &p, int wv, int lane, WaveState<BETA, D> &st, f32x16 (&s_cur)[2])
 {
-    if (load_k) load_tile<BETA, D>(Kn, krs, p.k.sn, st.kdma, false, p, k0_k, wv, lane);
-    load_tile<BETA, D>(Vn, vrs, p.v.sn, st.vdma, true, p, k0, wv, lane);
+    if (load_k) load_tile<BETA, D, NBM>(Kn, krs, p.k.sn, st.kdma, st.knat, false, p, k0_k, wv, lane);
+    load_tile<BETA, D, NBM>(Vn, vrs, p.v.sn, st.vdma, st.vnat, true, p, k0, wv, lane);
     qk_mfma<BETA, D>(Kc, st, s_cur);
     lazy_rescale<BETA, D>((valid && k0 < p.N) ? tile_max(s_cur, p.scale_log2) : -INFINITY, st);
 }
@@ -394,9 +424,11 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
     WaveState<BETA, D> st;
     // Q^T fragments: lane (hl, n) holds query row n, d = 16 s + 8 hl .. +7.
     const int qrow = i * BETA + wv * 32 + n;
+    // natural-order neighbourhood inputs: the query's natural position
+    const int qpos = (NBM && p.natural && qrow < p.N) ? nb_natural(p.nb, BETA, qrow) : qrow;
 #pragma unroll
     for (int s = 0; s < Sh::QS; ++s) {
-        uint4 u = qrow < p.N ? ld_g16(qb + (int64_t)qrow * p.q.sn + 16 * s + 8 * hl) : zero_u4();
+        uint4 u = qrow < p.N ? ld_g16(qb + (int64_t)qpos * p.q.sn + 16 * s + 8 * hl) : zero_u4();
         st.qf[s] = as_bf16x8(u);
     }
 #pragma unroll
@@ -441,9 +473,9 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
         int k_cur = tile_key0(0, v_cur), k_nxt = 0, k_prv;
         if (T > 1) k_nxt = tile_key0(1, v_nxt);
         bool f_cur = tile_partial(0, v_cur), f_nxt = T > 1 && tile_partial(1, v_nxt), f_prv;
-        load_tile<BETA, D>(K0, krs, p.k.sn, st.kdma, false, p, k_cur, wv, lane);
+        load_tile<BETA, D, NBM>(K0, krs, p.k.sn, st.kdma, st.knat, false, p, k_cur, wv, lane);
         __syncthreads();   // Q in registers; K(0) in LDS
-        first_step<BETA, D>(K0, K1, V0, v_cur, k_cur, T > 1, k_nxt, krs, vrs, p, wv, lane, st, sa);
+        first_step<BETA, D, NBM>(K0, K1, V0, v_cur, k_cur, T > 1, k_nxt, krs, vrs, p, wv, lane, st, sa);
         __syncthreads();
         v_prv = v_cur; k_prv = k_cur; f_prv = f_cur;
         v_cur = v_nxt; k_cur = k_nxt; f_cur = f_nxt;
@@ -499,7 +531,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
     // epilogue: normalise and store O (bf16) and LSE (natural log)
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < p.N) {
-        uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)qrow * p.o_sn;
+        uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)qpos * p.o_sn;
 #pragma unroll
         for (int d = 0; d < Sh::DT; ++d)
 #pragma unroll
@@ -511,7 +543,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
             }
         if (p.lse && hl == 0) {
             const float lse = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-            p.lse[(int64_t)bh * p.N + qrow] = lse;
+            p.lse[(int64_t)bh * p.N + qpos] = lse;
         }
     }
 }
@@ -625,6 +657,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p)
         const int tq = x >> 1, d0 = (x & 1) * HALF;
         const int t = i * p.block + tq;
         if (t >= p.N) continue;
+        const int tpos = p.natural ? nb_natural(p.nb, p.block, t) : t;
         float M = -INFINITY;
         for (int c = 0; c < chunks; ++c) M = fmaxf(M, base[c * slot_floats + p.block * D + tq]);
         float L = 0.f;
@@ -647,7 +680,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p)
             }
         }
         const float inv = L > 0.f ? 1.f / L : 0.f;
-        uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)t * p.o_sn + d0;
+        uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)tpos * p.o_sn + d0;
 #pragma unroll
         for (int d = 0; d < HALF; d += 8) {
             uint4 st;
@@ -658,7 +691,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p)
             *reinterpret_cast<uint4 *>(orow + d) = st;
         }
         if (p.lse && (x & 1) == 0)
-            p.lse[(int64_t)bh * p.N + t] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+            p.lse[(int64_t)bh * p.N + tpos] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
 }
 

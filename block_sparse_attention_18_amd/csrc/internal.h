@@ -35,6 +35,21 @@ __host__ __device__ inline int32_t nb_start(int32_t i, int32_t L, int32_t k, int
     return a < 0 ? 0 : (a > L - k ? L - k : a);
 }
 
+// Natural position of the token at tile-major position t (text tokens keep
+// theirs), and the natural offset of tile-major row o inside a tile (o <
+// block): the tile's rows are tw-token runs of the grid, C apart.
+__host__ __device__ inline int32_t nb_rowoff(const NbGeom &g, int32_t o)
+{
+    return (o >> g.tw_log2) * g.C + (o & (g.tw - 1));
+}
+
+__host__ __device__ inline int32_t nb_natural(const NbGeom &g, int32_t block, int32_t t)
+{
+    if (t < g.T) return t;
+    const int32_t pt = t - g.T, tile = pt / block, a = tile / g.tpr;
+    return g.T + a * g.th * g.C + (tile - a * g.tpr) * g.tw + nb_rowoff(g, pt - tile * block);
+}
+
 // Image query tile i (i >= Tb): the key tile ranges its queries' windows
 // touch ([r0, r1) x [c0, c1) in tiles) and the token ranges every one of
 // its queries sees ([ir0, ir1) x [ic0, ic1), possibly empty).
@@ -86,6 +101,7 @@ struct FwdParams {
     // (query, key) pair of the block pair kept, 1 = masked per token
     const int32_t *flags;
     NbGeom nb;
+    int32_t natural;            // neighbourhood: Q, K, V, O, LSE in natural token order
 };
 
 // Backward of the forward (see bsa_backward).  The dK/dV kernel keeps the
@@ -146,6 +162,8 @@ struct CombineParams {
     float *lse;
     int32_t H, N, nB, D, block;
     int32_t max_chunks;
+    int32_t natural;            // neighbourhood: write O, LSE at natural token positions
+    NbGeom nb;
 };
 
 struct SkipCopyParams {

@@ -321,6 +321,18 @@ bsa_status bsa_forward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, co
                                     const bsa_neighborhood *nb, float scale, const bsa_tensor *o, float *lse,
                                     const bsa_split *split, void *stream);
 
+/* bsa_forward_neighborhood_natural -- bsa_forward_neighborhood on Q, K, V
+ * in natural order (text, then the grid row-major), with O and LSE written
+ * in natural order: the kernel gathers each tile-major tile from its grid
+ * rows and scatters its outputs, so no permutation pass is needed.  The
+ * block list and flags are those of bsa_build_neighborhood_layout
+ * (tile-major block indices).  Same errors as bsa_forward_neighborhood. */
+bsa_status bsa_forward_neighborhood_natural(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                            int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
+                                            const int32_t *entry_flags, const bsa_neighborhood *nb, float scale,
+                                            const bsa_tensor *o, float *lse, const bsa_split *split,
+                                            void *stream);
+
 /* bsa_backward_neighborhood -- bsa_backward for the 2-D neighbourhood
  * layout (GNA notes, 1.1 and 2.1): tile-major Q, K, V, O, dO and LSE as
  * bsa_forward_neighborhood produced them, its block list and entry flags

@@ -115,3 +115,27 @@ def test_workload_g1(stride):
     Lg = L.cpu().numpy().reshape(-1)[rows].astype(np.float64)
     mx, mean = check_forward(Og, Lg, Oo, Lo, f"G1 stride {stride}")
     _log(f"G1 stride {stride}: {len(rows)} rows, max|dO|={mx:.2e} mean|dO|={mean:.2e}")
+
+
+@pytest.mark.parametrize("T,grid,tile,window,stride,D", GEOMS)
+@pytest.mark.parametrize("split", [False, True])
+def test_natural_order_forward_equals_the_permuted_path(T, grid, tile, window, stride, D, split):
+    """bsa_forward_neighborhood_natural gathers the tiles from natural-order
+    Q, K, V and scatters O, LSE itself: the same arithmetic on the same tiles
+    as permute -> forward -> permute back, so the results agree bit for bit
+    (with long rows split as well)."""
+    _log(f"natural T={T} grid={grid} tile={tile} window={window} stride={stride} D={D} split={split}")
+    B, H = 1, 2
+    N = T + grid[0] * grid[1]
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    q, k, v = synth.random_qkv(B, H, N, D, seed=541)
+    sp = {"chunk_blocks": 2, "max_chunks": 4, "max_split_rows": 64} if split else None
+    O1, L1 = _forward_natural(q, k, v, nb, split=dict(sp) if sp else None)
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    O2, L2 = bsa.forward_neighborhood(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), rp, ci, fl, nb,
+                                      split=dict(sp) if sp else None, natural=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(O2), bf16_bits(O1))
+    np.testing.assert_array_equal(L2.cpu().numpy(), L1.cpu().numpy())
+    Oo, Lo = oracle.forward_neighborhood(q, k, v, T, grid, window, stride)
+    check_forward(bf16_to_f64(O2), L2.cpu().numpy().astype(np.float64), Oo, Lo, "natural")
