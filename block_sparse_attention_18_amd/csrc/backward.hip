@@ -311,19 +311,17 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
             if (NBM && vcur && cflag[t / Sh::SUB] != 0) {
                 // a partially covered entry: keys outside the lane's query window
                 const int jj = kcur / BETA;
-                if (qimg && jj >= p.nb.Tb) {
+                if (jj >= p.nb.Tb) {
                     const int tk = jj - p.nb.Tb, ak = tk / p.nb.tpr;
-                    const int kr0 = ak * p.nb.th - wr0, kc0 = (tk - ak * p.nb.tpr) * p.nb.tw - wc0;
-                    const int o0 = kcur - jj * BETA + 8 * hl;
+                    uint64_t bits = nb_window_bits(p.nb, kcur - jj * BETA, ak * p.nb.th - wr0,
+                                                   (tk - ak * p.nb.tpr) * p.nb.tw - wc0, p.nb.kh, p.nb.kw);
+                    bits = qimg ? bits >> (8 * hl) : ~0ull;   // bit kt*32 + koff(r): register r of chain kt
 #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
+                    for (int kt = 0; kt < 2; ++kt) {
+                        const uint32_t w = (uint32_t)(bits >> (32 * kt));
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int o = o0 + kt * 32 + koff(r);
-                            const int dr = kr0 + (o >> p.nb.tw_log2), dc = kc0 + (o & (p.nb.tw - 1));
-                            if ((unsigned)dr >= (unsigned)p.nb.kh || (unsigned)dc >= (unsigned)p.nb.kw)
-                                s[kt][r] = -INFINITY;
-                        }
+                        for (int r = 0; r < 16; ++r) s[kt][r] = keep_if_bit(s[kt][r], w, koff(r));
+                    }
                 }
             }
 #pragma unroll
@@ -596,16 +594,15 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
             bf16x8 pp[2], ps[2];
             if (NBM && kimg && (qlist[t / (BETA / 64)] >> 30) != 0 && qblock(t) >= p.nb.Tb) {
                 // a partially covered entry (an image query block): queries
-                // whose window misses the lane's key
+                // whose window misses the lane's key are masked.  The queries
+                // that see it, [qr0, qr1] x [qc0, qc1], act as a window over
+                // the query tile; register r holds query 8 hl + koff(r).
                 const int i = qblock(t), tq = i - p.nb.Tb, aq = tq / p.nb.tpr;
-                const int orow = aq * p.nb.th, ocol = (tq - aq * p.nb.tpr) * p.nb.tw;
-                const int o0 = q0 - i * BETA + 8 * hl;
+                const uint32_t w = (uint32_t)(nb_window_bits(p.nb, q0 - i * BETA, aq * p.nb.th - qr0,
+                                                             (tq - aq * p.nb.tpr) * p.nb.tw - qc0, qr1 - qr0 + 1,
+                                                             qc1 - qc0 + 1) >> (8 * hl));
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int o = o0 + koff(r);
-                    const int rq = orow + (o >> p.nb.tw_log2), cq = ocol + (o & (p.nb.tw - 1));
-                    if (rq < qr0 || rq > qr1 || cq < qc0 || cq > qc1) s[r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r) s[r] = keep_if_bit(s[r], w, koff(r));
             }
             bw_probs_half(s, dp, stats, qh, c, hl, pp, ps);
             bw_tr_half<D>(Gc, off, qh, pp, dv);

@@ -650,6 +650,8 @@ static bsa_status check_nb(const bsa_neighborhood *g, int64_t N, int32_t block, 
     x.kw = g->window_cols;
     x.sh = g->stride_rows;
     x.sw = g->stride_cols;
+    x.rep = 1;
+    for (int b = x.tw; x.tw < 64 && b < 64; b += x.tw) x.rep |= 1ull << b;
     *out = x;
     return BSA_OK;
 }

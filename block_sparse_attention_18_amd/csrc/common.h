@@ -106,6 +106,14 @@ constexpr uint32_t KSTEP = 32, VSTEP = 64;
 // perm_row order) holds key 8 hl + koff(r) of its 32 keys.
 __device__ __forceinline__ constexpr int koff(int r) { return (r & 3) + 4 * ((r >> 2) & 1) + 16 * ((r >> 3) & 1); }
 
+// x if bit c of w is set, else -inf, without a branch: the sign-extended
+// bit selects between the two bit patterns.
+__device__ __forceinline__ float keep_if_bit(float x, uint32_t w, int c)
+{
+    const int m = (int)(w << (31 - c)) >> 31;
+    return __int_as_float((__float_as_int(x) & m) | ((int)0xff800000 & ~m));
+}
+
 // Scores of keys at offset >= lim (per lane: key offset within the 64-key
 // sub-tile minus 8 hl) become -inf.
 __device__ __forceinline__ void mask_keys(f32x16 (&sacc)[2], int lim)

@@ -261,28 +261,24 @@ __device__ __forceinline__ void load_tile(uint16_t *__restrict__ dst, __amdgpu_b
 
 // 2-D neighbourhood masking of a partially covered key tile: the score of
 // (query, key) survives when the key's grid position lies in the query's
-// window.  Text queries and text keys are never masked.
+// window, whose first grid row and column are wr0, wc0 (wr0 < 0: a text
+// query, never masked; text keys are never masked either).  The window test
+// of the sub-tile's 64 keys is one bitmap per lane, read bit by bit.
 template <int BETA, int D>
-__device__ __forceinline__ void mask_window(const FwdParams &p, int k0, int qrow, int lane, f32x16 (&sacc)[2])
+__device__ __forceinline__ void mask_window(const FwdParams &p, int k0, int wr0, int wc0, int lane, f32x16 (&sacc)[2])
 {
     const NbGeom &g = p.nb;
     const int j = k0 / BETA;
-    if (j < g.Tb || qrow < g.T || qrow >= p.N) return;
-    const int pq = qrow - g.T, tq = pq / BETA, oq = pq - tq * BETA;
-    const int aq = tq / g.tpr;
-    const int rq = aq * g.th + (oq >> g.tw_log2), cq = (tq - aq * g.tpr) * g.tw + (oq & (g.tw - 1));
-    const int rs = nb_start(rq, g.R, g.kh, g.sh), cs = nb_start(cq, g.C, g.kw, g.sw);
+    if (j < g.Tb) return;
     const int tk = j - g.Tb, ak = tk / g.tpr;
-    const int kr0 = ak * g.th - rs, kc0 = (tk - ak * g.tpr) * g.tw - cs;
-    const int o0 = (k0 - j * BETA) + 8 * (lane >> 5);   // key offset in the tile of register 0
+    uint64_t bits = nb_window_bits(g, k0 - j * BETA, ak * g.th - wr0, (tk - ak * g.tpr) * g.tw - wc0, g.kh, g.kw);
+    bits = wr0 < 0 ? ~0ull : bits >> (8 * (lane >> 5));   // bit kt*32 + koff(r): register r of chain kt
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+        const uint32_t w = (uint32_t)(bits >> (32 * kt));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int o = o0 + kt * 32 + koff(r);
-            const int dr = kr0 + (o >> g.tw_log2), dc = kc0 + (o & (g.tw - 1));
-            if ((unsigned)dr >= (unsigned)g.kh || (unsigned)dc >= (unsigned)g.kw) sacc[kt][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) sacc[kt][r] = keep_if_bit(sacc[kt][r], w, koff(r));
+    }
 }
 
 // Scores of a sub-tile whose block index is invalid, or of keys past N in
@@ -307,13 +303,13 @@ __device__ __forceinline__ void fused_step(
     const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vp, uint16_t *__restrict__ Kn,
     uint16_t *__restrict__ Vn, bool valid, int k0, bool valid_p, int k0_p, bool load_k, int k0_k,
     __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const FwdParams &p, int wv, int lane,
-    WaveState<BETA, D> &st, f32x16 (&s_cur)[2], f32x16 (&s_prev)[2], bool partial_p, int qrow)
+    WaveState<BETA, D> &st, f32x16 (&s_cur)[2], f32x16 (&s_prev)[2], bool partial_p, int wr0, int wc0)
 {
     using Sh = FwdShape<BETA, D>;
     // masking of t-1's scores first: a branch here does not split the
     // scheduled regions, and t's scores are not live yet
     mask_scores<BETA, D>(valid_p, k0_p, p.N, lane, s_prev);
-    if (NBM && partial_p) mask_window<BETA, D>(p, k0_p, qrow, lane, s_prev);
+    if (NBM && partial_p) mask_window<BETA, D>(p, k0_p, wr0, wc0, lane, s_prev);
     if (load_k) load_tile<BETA, D, NBM>(Kn, krs, p.k.sn, st.kdma, st.knat, false, p, k0_k, wv, lane);
     load_tile<BETA, D, NBM>(Vn, vrs, p.v.sn, st.vdma, st.vnat, true, p, k0, wv, lane);
     const float c = p.scale_log2;
@@ -357,10 +353,10 @@ __device__ __forceinline__ void first_step(
 template <int BETA, int D, bool NBM>
 __device__ __forceinline__ void last_step(const uint16_t *__restrict__ Vp, bool valid_p, int k0_p,
                                           const FwdParams &p, int lane, WaveState<BETA, D> &st,
-                                          f32x16 (&s_prev)[2], bool partial_p, int qrow)
+                                          f32x16 (&s_prev)[2], bool partial_p, int wr0, int wc0)
 {
     mask_scores<BETA, D>(valid_p, k0_p, p.N, lane, s_prev);
-    if (NBM && partial_p) mask_window<BETA, D>(p, k0_p, qrow, lane, s_prev);
+    if (NBM && partial_p) mask_window<BETA, D>(p, k0_p, wr0, wc0, lane, s_prev);
     bf16x8 pf[2][2];
     softmax_probs<BETA, D>(s_prev, p.scale_log2, st, pf);
     pv_mfma<BETA, D>(Vp, pf, st);
@@ -426,6 +422,14 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
     const int qrow = i * BETA + wv * 32 + n;
     // natural-order neighbourhood inputs: the query's natural position
     const int qpos = (NBM && p.natural && qrow < p.N) ? nb_natural(p.nb, BETA, qrow) : qrow;
+    // neighbourhood layouts: the window origin of an image query (-1: none)
+    int wr0 = -1, wc0 = 0;
+    if (NBM && qrow >= p.nb.T && qrow < p.N) {
+        const NbGeom &g = p.nb;
+        const int pq = qrow - g.T, tq = pq / BETA, oq = pq - tq * BETA, aq = tq / g.tpr;
+        wr0 = nb_start(aq * g.th + (oq >> g.tw_log2), g.R, g.kh, g.sh);
+        wc0 = nb_start((tq - aq * g.tpr) * g.tw + (oq & (g.tw - 1)), g.C, g.kw, g.sw);
+    }
 #pragma unroll
     for (int s = 0; s < Sh::QS; ++s) {
         uint4 u = qrow < p.N ? ld_g16(qb + (int64_t)qpos * p.q.sn + 16 * s + 8 * hl) : zero_u4();
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
                 f_nxt = tile_partial(t + 1, v_nxt);
             }
             fused_step<BETA, D, NBM>(K1, V0, K0, V1, v_cur, k_cur, v_prv, k_prv, t + 1 < T, k_nxt, krs, vrs, p, wv,
-                                lane, st, sb, sa, f_prv, qrow);
+                                lane, st, sb, sa, f_prv, wr0, wc0);
             __syncthreads();
             v_prv = v_cur; k_prv = k_cur; f_prv = f_cur;
             v_cur = v_nxt; k_cur = k_nxt; f_cur = f_nxt;
@@ -499,14 +503,14 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void f
                 f_nxt = tile_partial(t + 2, v_nxt);
             }
             fused_step<BETA, D, NBM>(K0, V1, K1, V0, v_cur, k_cur, v_prv, k_prv, t + 2 < T, k_nxt, krs, vrs, p, wv,
-                                lane, st, sa, sb, f_prv, qrow);
+                                lane, st, sa, sb, f_prv, wr0, wc0);
             __syncthreads();
             v_prv = v_cur; k_prv = k_cur; f_prv = f_cur;
             v_cur = v_nxt; k_cur = k_nxt; f_cur = f_nxt;
         }
         // finish sub-tile T-1 (V(T-1) in V[(T-1)&1])
-        if (T & 1) last_step<BETA, D, NBM>(V0, v_prv, k_prv, p, lane, st, sa, f_prv, qrow);
-        else last_step<BETA, D, NBM>(V1, v_prv, k_prv, p, lane, st, sb, f_prv, qrow);
+        if (T & 1) last_step<BETA, D, NBM>(V0, v_prv, k_prv, p, lane, st, sa, f_prv, wr0, wc0);
+        else last_step<BETA, D, NBM>(V1, v_prv, k_prv, p, lane, st, sb, f_prv, wr0, wc0);
     }
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);

@@ -339,23 +339,23 @@ __device__ __forceinline__ void mask_scores8(bool valid, int k0, int N, int lane
 
 // 2-D neighbourhood masking of a partially covered key tile (image keys
 // only): a score survives when the key's grid position lies in the window
-// (row start wr0, column start wc0) of the lane's image query.
+// (row start wr0, column start wc0) of the lane's image query.  The window
+// test of the sub-tile's 64 keys is one bitmap per lane, read bit by bit.
 template <int BETA>
 __device__ __forceinline__ void mask_window8(const NbGeom &g, int k0, int wr0, int wc0, int lane, f32x16 (&sacc)[2])
 {
     const int j = k0 / BETA;
     if (j < g.Tb) return;
     const int tk = j - g.Tb, ak = tk / g.tpr;
-    const int kr0 = ak * g.th - wr0, kc0 = (tk - ak * g.tpr) * g.tw - wc0;
-    const int o0 = (k0 - j * BETA) + 4 * (lane >> 5);
+    // register r of chain a holds key 32 a + 8 (r >> 2) + 4 hl + (r & 3)
+    const uint64_t bits =
+        nb_window_bits(g, k0 - j * BETA, ak * g.th - wr0, (tk - ak * g.tpr) * g.tw - wc0, g.kh, g.kw) >> (4 * (lane >> 5));
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a) {
+        const uint32_t w = (uint32_t)(bits >> (32 * a));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int o = o0 + 32 * a + 8 * (r >> 2) + (r & 3);
-            const int dr = kr0 + (o >> g.tw_log2), dc = kc0 + (o & (g.tw - 1));
-            if ((unsigned)dr >= (unsigned)g.kh || (unsigned)dc >= (unsigned)g.kw) sacc[a][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) sacc[a][r] = keep_if_bit(sacc[a][r], w, 8 * (r >> 2) + (r & 3));
+    }
 }
 
 template <int BETA, int D>

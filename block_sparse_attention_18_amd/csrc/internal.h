@@ -21,9 +21,12 @@ struct Tensor4 {
 // Geometry of 2-D neighbourhood attention in tile-major token order: T text
 // tokens (Tb blocks), then an R x C image grid cut into th x tw tiles (one
 // block each, tw a power of two, tpr tiles per tile row), window kh x kw,
-// stride sh x sw.
+// stride sh x sw.  rep has bit x tw set for every x < 64 / tw (tw < 64),
+// else only bit 0: multiplying a tw-bit pattern by it repeats the pattern
+// across 64 bits.
 struct NbGeom {
     int32_t T, Tb, R, C, th, tw, tw_log2, tpr, kh, kw, sh, sw;
+    uint64_t rep;
 };
 
 // First position of the window of position i on an axis of length L
@@ -49,6 +52,34 @@ __host__ __device__ inline int32_t nb_natural(const NbGeom &g, int32_t block, in
     const int32_t pt = t - g.T, tile = pt / block, a = tile / g.tpr;
     return g.T + a * g.th * g.C + (tile - a * g.tpr) * g.tw + nb_rowoff(g, pt - tile * block);
 }
+
+#ifdef __HIPCC__
+// Bits a .. b-1 of a 64-bit word (a, b clamped to 0..64; empty if b <= a).
+__device__ __forceinline__ uint64_t bit_range64(int a, int b)
+{
+    a = min(max(a, 0), 64);
+    b = min(max(b, 0), 64);
+    const uint64_t hi = b >= 64 ? ~0ull : (1ull << b) - 1;
+    const uint64_t lo = a >= 64 ? ~0ull : (1ull << a) - 1;
+    return hi & ~lo;
+}
+
+// Which of 64 consecutive tokens of an image tile lie in a window of kh x kw
+// grid positions: bit b stands for the token at offset s0 + b in the tile,
+// kr / kc are the tile's first grid row / column minus the window's.  Tile
+// row x holds offsets x tw .. x tw + tw - 1, so the window's rows form one
+// run of bits and its columns a run repeated every tw bits.  s0 is a
+// multiple of 64, or of 32 when only bits 0..31 are read.
+__device__ __forceinline__ uint64_t nb_window_bits(const NbGeom &g, int s0, int kr, int kc, int kh, int kw)
+{
+    const int rlo = max(0, -kr), rhi = min(g.th, kh - kr);
+    const uint64_t rows = rhi > rlo ? bit_range64(rlo * g.tw - s0, rhi * g.tw - s0) : 0ull;
+    const int cs0 = s0 & (g.tw - 1);
+    const int clo = max(0, -kc), chi = min(g.tw, kw - kc);
+    const uint64_t cols = bit_range64(clo - cs0, chi - cs0) * g.rep;
+    return rows & cols;
+}
+#endif
 
 // Image query tile i (i >= Tb): the key tile ranges its queries' windows
 // touch ([r0, r1) x [c0, c1) in tiles) and the token ranges every one of

@@ -52,6 +52,10 @@ GEOMS = [
     (0, (32, 32), (8, 16), (16, 32), (16, 32), 128),       # stride = window: no partial tile
     (64, (16, 24), (8, 8), (8, 12), (4, 4), 64),           # block 64, a stride between
     (256, (32, 64), (8, 16), (12, 20), (2, 3), 128),       # uneven strides
+    (0, (8, 256), (1, 128), (3, 40), (1, 1), 128),         # one-row tiles 128 wide
+    (128, (16, 128), (2, 64), (5, 70), (1, 2), 64),        # tiles 64 wide, window wider than a tile
+    (64, (8, 128), (1, 64), (3, 20), (2, 1), 128),         # block 64, one-row tiles 64 wide
+    (128, (16, 64), (4, 32), (6, 20), (1, 1), 128),        # tiles 32 wide
 ]
 
 
