@@ -67,7 +67,7 @@ def main():
     ap.add_argument("--nb-window", default=None, help="neighbourhood workloads: window 'rows,cols'")
     ap.add_argument("--nb-permuted", action="store_true",
                     help="neighbourhood workloads: permute Q, K, V to tile-major order and O, LSE back in "
-                         "separate passes (the FP8 and backward runs always do) instead of the forward's "
+                         "separate passes (the backward runs always do) instead of the forward's "
                          "natural-order gather")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
@@ -159,7 +159,8 @@ def main():
     if wl.layout == "neighborhood":
         # inputs arrive in natural order: the step builds the layout and runs the
         # forward, which gathers the tile-major tiles from natural order and
-        # scatters O, LSE back; with --nb-permuted (and for the FP8 and backward
+        # scatters O, LSE back (FP8: the quantisation writes tile-major codes
+        # from natural-order inputs); with --nb-permuted (and for the backward
         # runs) it permutes Q, K, V to tile-major order and O, LSE back in
         # separate passes
         stride = tuple(int(v2) for v2 in args.stride.split(",")) if args.stride else wl.nb_stride
@@ -174,7 +175,7 @@ def main():
         computed_heads = B * H
         R_, C_ = wl.nb_grid
         token_pairs = B * H * (wl.text_len * N + R_ * C_ * (wl.text_len + wl.nb_window[0] * wl.nb_window[1]))
-        nb_natural = not (args.fp8 or args.backward or args.nb_permuted)
+        nb_natural = not (args.backward or args.nb_permuted)
         if nb_natural:
             out_t, lse_t = out, lse
 
@@ -255,20 +256,22 @@ def main():
                   file=sys.stderr)
             sys.exit(2)
         if wl.layout == "neighborhood":
-            layout()                      # the tile-major Q, K, V that are quantised
-        qkv8 = bsa.quantize_fp8(q, k, v)
+            layout()                      # (permuted runs: the tile-major Q, K, V that are quantised)
+        qnb = nb if nb_natural else None  # natural-order inputs, tile-major codes
+        qkv8 = bsa.quantize_fp8(q, k, v, nb=qnb)
         ws_q = torch.empty(max(bsa.quantize_fp8_workspace_size(B, H, N, D), 16), dtype=torch.uint8,
                            device=dev)
 
         if wl.layout == "neighborhood":
             def forward():
-                bsa.forward_fp8_neighborhood(qkv8, row_ptr, col_idx, flags, nb, out=out_t, lse=lse_t)
+                bsa.forward_fp8_neighborhood(qkv8, row_ptr, col_idx, flags, nb, out=out_t, lse=lse_t,
+                                             natural=nb_natural)
         else:
             def forward():
                 bsa.forward_fp8(qkv8, block, row_ptr, col_idx, out=out, lse=lse)
 
         def quantize():
-            bsa.quantize_fp8(q, k, v, out=qkv8, workspace=ws_q)
+            bsa.quantize_fp8(q, k, v, out=qkv8, workspace=ws_q, nb=qnb)
     elif wl.layout == "neighborhood":
         def forward():
             bsa.forward_neighborhood(q, k, v, row_ptr, col_idx, flags, nb, out=out_t, lse=lse_t, natural=nb_natural,

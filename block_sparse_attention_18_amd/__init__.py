@@ -132,6 +132,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_forward_fp8": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, F, TP, V, V]),
             "bsa_forward_fp8_neighborhood": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, V,
                                                    ctypes.POINTER(BsaNeighborhood), F, TP, V, V]),
+            "bsa_forward_fp8_neighborhood_natural": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, V,
+                                                           ctypes.POINTER(BsaNeighborhood), F, TP, V, V]),
+            "bsa_quantize_fp8_neighborhood": (I32, [TP, TP, TP, I32, ctypes.POINTER(BsaNeighborhood),
+                                                    ctypes.POINTER(BsaFp8Qkv), V, SZ, V]),
             "bsa_output_rse_workspace_size": (SZ, [I64, I64, I64, I64]),
             "bsa_output_rse": (I32, [TP, TP, V, V, SZ, V]),
             "bsa_mask_jaccard": (I32, [I64, I64, I32, V, V, V, V, V, V]),
@@ -533,9 +537,11 @@ def quantize_fp8_workspace_size(B, H, N, D) -> int:
 
 
 def quantize_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optional[Fp8QKV] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Fp8QKV:
+                 workspace: Optional[torch.Tensor] = None, nb: Optional["BsaNeighborhood"] = None) -> Fp8QKV:
     """E4M3 codes with max-abs scales: per token for Q, per 64-key tile for K,
-    per channel for V."""
+    per channel for V.  With a neighbourhood geometry `nb`, Q, K, V are in
+    natural order and the codes come out in its tile-major order
+    (bsa_quantize_fp8_neighborhood)."""
     lib = load()
     B, H, N, D = q.shape
     if out is None:
@@ -545,8 +551,13 @@ def quantize_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optiona
                                 device=q.device)
     dq, dk, dv = _desc(q, "q"), _desc(k, "k"), _desc(v, "v")
     d8 = out.desc()
-    _check(lib.bsa_quantize_fp8(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(d8),
-                                _ptr(workspace), workspace.numel(), _stream(q.device)))
+    if nb is None:
+        _check(lib.bsa_quantize_fp8(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(d8),
+                                    _ptr(workspace), workspace.numel(), _stream(q.device)))
+    else:
+        _check(lib.bsa_quantize_fp8_neighborhood(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                                                 nb.tile_rows * nb.tile_cols, ctypes.byref(nb), ctypes.byref(d8),
+                                                 _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out
 
 
@@ -578,9 +589,11 @@ def forward_fp8(qkv: Fp8QKV, block: int, row_ptr: torch.Tensor, col_idx: torch.T
 def forward_fp8_neighborhood(qkv: Fp8QKV, row_ptr: torch.Tensor, col_idx: torch.Tensor,
                              entry_flags: torch.Tensor, nb: "BsaNeighborhood", scale: Optional[float] = None,
                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                             return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """FP8 forward of 2-D neighbourhood attention on E4M3 operands quantised
-    from tile-major Q, K, V.  Returns (O bf16, LSE fp32) in tile-major order."""
+                             return_lse: bool = True, natural: bool = False
+                             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """FP8 forward of 2-D neighbourhood attention on E4M3 operands in
+    tile-major order.  Returns (O bf16, LSE fp32), in tile-major order, or in
+    natural order with natural=True (bsa_forward_fp8_neighborhood_natural)."""
     lib = load()
     B, H, N, D = qkv.shape
     dev = qkv.q8.device
@@ -595,9 +608,9 @@ def forward_fp8_neighborhood(qkv: Fp8QKV, row_ptr: torch.Tensor, col_idx: torch.
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 device tensor")
     d8, do = qkv.desc(), _desc(out, "out")
-    _check(lib.bsa_forward_fp8_neighborhood(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx),
-                                            _ptr(entry_flags), ctypes.byref(nb), float(scale or 0.0),
-                                            ctypes.byref(do), _ptr(lse), _stream(dev)))
+    fn = lib.bsa_forward_fp8_neighborhood_natural if natural else lib.bsa_forward_fp8_neighborhood
+    _check(fn(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx), _ptr(entry_flags), ctypes.byref(nb),
+              float(scale or 0.0), ctypes.byref(do), _ptr(lse), _stream(dev)))
     return out, lse
 
 

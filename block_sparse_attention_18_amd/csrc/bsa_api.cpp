@@ -858,8 +858,9 @@ size_t bsa_quantize_fp8_workspace_size(int64_t B, int64_t H, int64_t N, int64_t 
     return fp8_ws_inv_bytes(BH, D) + (size_t)(BH * ceil_div(N, 256) * D) * sizeof(float);
 }
 
-bsa_status bsa_quantize_fp8(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_fp8_qkv *out,
-                            void *workspace, size_t workspace_bytes, void *stream)
+static bsa_status quantize_fp8_impl(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                    const bsa_fp8_qkv *out, void *workspace, size_t workspace_bytes, void *stream,
+                                    const bsa::NbGeom *nb, int32_t nb_block)
 {
     bsa_status st;
     if ((st = check_tensor(q, "q")) != BSA_OK) return st;
@@ -895,14 +896,35 @@ bsa_status bsa_quantize_fp8(const bsa_tensor *q, const bsa_tensor *k, const bsa_
     p.NT = (int32_t)ceil_div(q->N, 64);
     p.NP = 64 * p.NT;
     p.S = (int32_t)ceil_div(q->N, 256);
+    if (nb) {
+        p.nb = *nb;
+        p.nb_block = nb_block;
+    }
     hipError_t e = bsa::launch_quantize_fp8(p, (int)q->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fp8 quantisation launch");
     return BSA_OK;
 }
 
+bsa_status bsa_quantize_fp8(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, const bsa_fp8_qkv *out,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    return quantize_fp8_impl(q, k, v, out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+bsa_status bsa_quantize_fp8_neighborhood(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                         int32_t block, const bsa_neighborhood *nb, const bsa_fp8_qkv *out,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    bsa::NbGeom g;
+    if ((st = check_nb(nb, q->N, block, &g)) != BSA_OK) return st;
+    return quantize_fp8_impl(q, k, v, out, workspace, workspace_bytes, stream, &g, block);
+}
+
 static bsa_status forward_fp8_impl(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
                                    const int32_t *col_idx, float scale, const bsa_tensor *o, float *lse, void *stream,
-                                   const int32_t *entry_flags, const bsa::NbGeom *nb)
+                                   const int32_t *entry_flags, const bsa::NbGeom *nb, int natural = 0)
 {
     bsa_status st;
     if ((st = check_fp8(in, "in")) != BSA_OK) return st;
@@ -939,6 +961,7 @@ static bsa_status forward_fp8_impl(const bsa_fp8_qkv *in, int32_t block, const i
     p.scale_log2 = sc * 1.4426950408889634f;
     p.flags = entry_flags;
     if (nb) p.nb = *nb;
+    p.natural = nb ? natural : 0;
     hipError_t e = bsa::launch_forward_fp8(p, block, (int)in->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fp8 forward launch");
     return BSA_OK;
@@ -961,6 +984,19 @@ bsa_status bsa_forward_fp8_neighborhood(const bsa_fp8_qkv *in, int32_t block, co
     bsa::NbGeom g;
     if ((st = check_nb(nb, in->N, block, &g)) != BSA_OK) return st;
     return forward_fp8_impl(in, block, row_ptr, col_idx, scale, o, lse, stream, entry_flags, &g);
+}
+
+bsa_status bsa_forward_fp8_neighborhood_natural(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
+                                                const int32_t *col_idx, const int32_t *entry_flags,
+                                                const bsa_neighborhood *nb, float scale, const bsa_tensor *o,
+                                                float *lse, void *stream)
+{
+    bsa_status st;
+    if ((st = check_fp8(in, "in")) != BSA_OK) return st;
+    if (!entry_flags) return fail(BSA_ERR_INVALID_ARG, "entry_flags null");
+    bsa::NbGeom g;
+    if ((st = check_nb(nb, in->N, block, &g)) != BSA_OK) return st;
+    return forward_fp8_impl(in, block, row_ptr, col_idx, scale, o, lse, stream, entry_flags, &g, 1);
 }
 
 // ---------------------------------------------------------------------------

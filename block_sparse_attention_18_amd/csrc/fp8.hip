@@ -68,6 +68,13 @@ __device__ __forceinline__ int fp8_vcol(int k)
 // ---------------------------------------------------------------------------
 // quantisation
 // ---------------------------------------------------------------------------
+// Input row of the token at position t of the codes: t itself, or with a
+// neighbourhood geometry the natural position of tile-major position t.
+__device__ __forceinline__ int64_t quant_src(const Fp8QuantParams &p, int t)
+{
+    return p.nb_block ? nb_natural(p.nb, p.nb_block, t) : t;
+}
+
 // Q: one scale per token; D/8 lanes per token, 16 bytes of bf16 each.
 template <int D>
 __global__ __launch_bounds__(256) void quant_q_kernel(const Fp8QuantParams p)
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(256) void quant_q_kernel(const Fp8QuantParams p)
     if (ok) {
         const int64_t bh = tok / p.N, t = tok - bh * p.N;
         const int b = (int)(bh / p.H), h = (int)(bh - (int64_t)b * p.H);
-        unpack_bf16x8(ld_g16(p.q.p + b * p.q.sb + h * p.q.sh + t * p.q.sn + 8 * c), x);
+        unpack_bf16x8(ld_g16(p.q.p + b * p.q.sb + h * p.q.sh + quant_src(p, (int)t) * p.q.sn + 8 * c), x);
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
     }
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(256) void quant_k_kernel(const Fp8QuantParams p)
         const int t = T * 64 + row;
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
-        if (t < p.N) unpack_bf16x8(ld_g16(p.k.p + b * p.k.sb + h * p.k.sh + (int64_t)t * p.k.sn + 8 * c), x[i]);
+        if (t < p.N) unpack_bf16x8(ld_g16(p.k.p + b * p.k.sb + h * p.k.sh + quant_src(p, t) * p.k.sn + 8 * c), x[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
     }
@@ -141,7 +148,9 @@ __global__ __launch_bounds__(256) void quant_k_kernel(const Fp8QuantParams p)
     if (tid == 0) p.k_scale[bh * p.NT + T] = sc;
 }
 
-// V, pass 1: channel maxima of 256-key chunks.  Grid (B*H, S).
+// V, pass 1: channel maxima of 256-key chunks.  Grid (B*H, S).  The
+// maxima over all keys do not depend on their order, so the chunks are
+// read in input order also when the codes are reordered.
 template <int D>
 __global__ __launch_bounds__(256) void vmax_kernel(const Fp8QuantParams p)
 {
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const Fp8QuantParams p)
         const int slot = i * 256 + tid, row = slot / CH, c = slot % CH;
         const int t = T * 64 + row;
         float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (t < p.N) unpack_bf16x8(ld_g16(p.v.p + b * p.v.sb + h * p.v.sh + (int64_t)t * p.v.sn + 8 * c), x);
+        if (t < p.N) unpack_bf16x8(ld_g16(p.v.p + b * p.v.sb + h * p.v.sh + quant_src(p, t) * p.v.sn + 8 * c), x);
         const float4 i0 = *reinterpret_cast<const float4 *>(p.v_inv + bh * D + 8 * c);
         const float4 i1 = *reinterpret_cast<const float4 *>(p.v_inv + bh * D + 8 * c + 4);
         const uint32_t w0 = pack_fp8x4(x[0] * i0.x, x[1] * i0.y, x[2] * i0.z, x[3] * i0.w);
@@ -647,7 +656,9 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
     const float l_tot = st.lacc[0];
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < p.N) {
-        uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)qrow * p.o_sn;
+        // natural-order outputs of a neighbourhood layout: the query's grid position
+        const int qpos = (NBM && p.natural) ? nb_natural(p.nb, BETA, qrow) : qrow;
+        uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)qpos * p.o_sn;
         const float *vs = p.v_scale + (int64_t)bh * D;
 #pragma unroll
         for (int d = 0; d < Sh::DT; ++d)
@@ -661,7 +672,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
                 *reinterpret_cast<uint2 *>(orow + c0) = sv;
             }
         if (p.lse && hl == 0)
-            p.lse[qtok] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+            p.lse[(int64_t)bh * p.N + qpos] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 

@@ -284,6 +284,10 @@ struct Fp8QuantParams {
     float *v_inv;               // [B*H][D] 448 / amax
     int64_t BHN;
     int32_t B, H, N, NT, NP, S;
+    // neighbourhood layouts: codes in tile-major order read from natural-order
+    // inputs (nb_block = the block of the geometry nb; 0: no reordering)
+    NbGeom nb;
+    int32_t nb_block;
 };
 
 // FP8 forward (see bsa_forward_fp8).
@@ -299,6 +303,7 @@ struct Fp8FwdParams {
     NbGeom nb;
     int32_t B, H, N, nB, NT, NP;
     float scale_log2;
+    int32_t natural;            // neighbourhood layouts: O and LSE written in natural token order
 };
 
 // Per-head RSE of an output against a reference (see bsa_output_rse).

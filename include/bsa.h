@@ -411,6 +411,25 @@ bsa_status bsa_forward_fp8_neighborhood(const bsa_fp8_qkv *in, int32_t block, co
                                         const bsa_neighborhood *nb, float scale, const bsa_tensor *o, float *lse,
                                         void *stream);
 
+/* bsa_quantize_fp8_neighborhood -- bsa_quantize_fp8 of natural-order Q, K,
+ * V (text, then the grid row-major) whose codes come out in the tile-major
+ * order of the geometry (block = tile_rows * tile_cols): the result equals,
+ * bit for bit, bsa_permute_tokens of each tensor followed by
+ * bsa_quantize_fp8 (GNA notes, 2.2: the permutation folded into a pass that
+ * reads the tensors anyway).  Errors as for bsa_quantize_fp8 plus the
+ * geometry checks.
+ *
+ * bsa_forward_fp8_neighborhood_natural -- bsa_forward_fp8_neighborhood
+ * with O and LSE written in natural order (the kernel scatters each query
+ * row to its grid position); `in` in tile-major order as above. */
+bsa_status bsa_quantize_fp8_neighborhood(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                         int32_t block, const bsa_neighborhood *nb, const bsa_fp8_qkv *out,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+bsa_status bsa_forward_fp8_neighborhood_natural(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
+                                                const int32_t *col_idx, const int32_t *entry_flags,
+                                                const bsa_neighborhood *nb, float scale, const bsa_tensor *o,
+                                                float *lse, void *stream);
+
 /* ------------------------------------------------------------------------
  * Diagnostics of sparse attention.
  *

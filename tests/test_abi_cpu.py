@@ -354,6 +354,19 @@ def test_neighborhood_validation():
                                                              capacity, None)
     need = lib.bsa_neighborhood_capacity(1, 2, 128, ctypes.byref(nb))
     assert lay(need - 1) == 3
+    # FP8 with natural-order inputs and outputs: the geometry is checked
+    # against the tensors before anything else runs
+    ws = lib.bsa_quantize_fp8_workspace_size(1, 2, 16896, 128)
+    quant = lambda N=16896, block=128: lib.bsa_quantize_fp8_neighborhood(
+        ctypes.byref(t(N)), ctypes.byref(t(N)), ctypes.byref(t(N)), block, ctypes.byref(nb),
+        ctypes.byref(_fp8(B=1, H=2, N=N, D=128)), ctypes.c_void_p(FAKE), ws, None)
+    assert quant(N=16895) == 1 and "N" in _err()
+    assert quant(block=64) == 1 and "tile_rows" in _err()
+    fwd8 = lambda N=16896, fl=FAKE: lib.bsa_forward_fp8_neighborhood_natural(
+        ctypes.byref(_fp8(B=1, H=2, N=N, D=128)), 128, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(fl) if fl else None, ctypes.byref(nb), 0.0, ctypes.byref(t(N)), None, None)
+    assert fwd8(N=16895) == 1 and "N" in _err()
+    assert fwd8(fl=0) == 1 and "entry_flags" in _err()
 
 
 def test_binding_refuses_host_tensors():

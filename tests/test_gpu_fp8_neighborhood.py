@@ -77,3 +77,30 @@ def test_fp8_neighborhood_matches_dequantised_oracle(T, grid, tile, window, stri
     lerr = np.abs(L.cpu().numpy().astype(np.float64) - Lo)
     _log(f"  O max {err.max():.2e} mean {err.mean():.2e}  LSE max {lerr.max():.2e}")
     assert err.max() <= FP8_O_MAX_ABS and err.mean() <= FP8_O_MEAN_ABS and lerr.max() <= FP8_LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("T,grid,tile,window,stride,D", GEOMS)
+def test_natural_order_quantisation_and_forward_equal_the_permuted_path(T, grid, tile, window, stride, D):
+    """bsa_quantize_fp8_neighborhood reads natural-order Q, K, V and writes the
+    codes in tile-major order: the same codes and scales, bit for bit, as
+    permuting first.  bsa_forward_fp8_neighborhood_natural writes O and LSE
+    at the natural positions: bit for bit the permuted path's outputs moved
+    back."""
+    _log(f"fp8 nb natural T={T} grid={grid} tile={tile} window={window} stride={stride} D={D}")
+    B, H = 1, 2
+    N = T + grid[0] * grid[1]
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    q, k, v = synth.random_qkv(B, H, N, D, seed=1311)
+    qd, kd, vd = (to_dev_bf16(a) for a in (q, k, v))
+    a = bsa.quantize_fp8(*(bsa.permute_tokens(x, nb) for x in (qd, kd, vd)))
+    b = bsa.quantize_fp8(qd, kd, vd, nb=nb)
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    Op, Lp = bsa.forward_fp8_neighborhood(a, rp, ci, fl, nb)
+    O1, L1 = bsa.permute_tokens(Op, nb, inverse=True, lse=Lp)
+    O2, L2 = bsa.forward_fp8_neighborhood(b, rp, ci, fl, nb, natural=True)
+    torch.cuda.synchronize()
+    for name in ("q8", "q_scale", "k8", "k_scale", "v8t", "v_scale"):
+        x, y = getattr(a, name), getattr(b, name)
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), name
+    np.testing.assert_array_equal(O2.view(torch.int16).cpu().numpy(), O1.view(torch.int16).cpu().numpy())
+    np.testing.assert_array_equal(L2.cpu().numpy(), L1.cpu().numpy())
