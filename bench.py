@@ -67,7 +67,7 @@ def main():
     ap.add_argument("--nb-window", default=None, help="neighbourhood workloads: window 'rows,cols'")
     ap.add_argument("--nb-permuted", action="store_true",
                     help="neighbourhood workloads: permute Q, K, V to tile-major order and O, LSE back in "
-                         "separate passes (the backward runs always do) instead of the forward's "
+                         "separate passes instead of the kernels' "
                          "natural-order gather")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
@@ -160,9 +160,9 @@ def main():
         # inputs arrive in natural order: the step builds the layout and runs the
         # forward, which gathers the tile-major tiles from natural order and
         # scatters O, LSE back (FP8: the quantisation writes tile-major codes
-        # from natural-order inputs); with --nb-permuted (and for the backward
-        # runs) it permutes Q, K, V to tile-major order and O, LSE back in
-        # separate passes
+        # from natural-order inputs; the backward gathers and scatters too);
+        # with --nb-permuted it permutes Q, K, V to tile-major order and O, LSE
+        # back in separate passes
         stride = tuple(int(v2) for v2 in args.stride.split(",")) if args.stride else wl.nb_stride
         window = tuple(int(v2) for v2 in args.nb_window.split(",")) if args.nb_window else wl.nb_window
         wl = wl.replace(nb_stride=stride, nb_window=window)
@@ -175,7 +175,7 @@ def main():
         computed_heads = B * H
         R_, C_ = wl.nb_grid
         token_pairs = B * H * (wl.text_len * N + R_ * C_ * (wl.text_len + wl.nb_window[0] * wl.nb_window[1]))
-        nb_natural = not (args.backward or args.nb_permuted)
+        nb_natural = not args.nb_permuted
         if nb_natural:
             out_t, lse_t = out, lse
 
@@ -410,7 +410,7 @@ def main():
         if args.fp8 or ("head_modes" in fwd_kw and fwd_kw["head_modes"] is not None
                         and np.any(fwd_kw["head_modes"] == bsa.HEAD_SKIP)):
             raise SystemExit("--backward: layouts without SKIP heads, bf16 only")
-        nbk = (nb, flags, token_pairs) if wl.layout == "neighborhood" else None
+        nbk = (nb, flags, token_pairs, nb_natural) if wl.layout == "neighborhood" else None
         res["backward"] = backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx, kept_pairs,
                                          nbk=nbk)
     if args.score_grad:
@@ -725,15 +725,16 @@ def backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx
     products of the backward (S recomputed, dP, dV, dK, dQ), 10 * block^2 * D
     FLOP per kept block pair; the dQ and dK/dV kernels each recompute S and
     dP, so 14 * block^2 * D are executed.  nbk = (geometry, entry flags,
-    token pairs) runs the neighbourhood backward on the tile-major tensors
-    and also reports the token-level rate (10 * D FLOP per kept token pair)."""
+    token pairs, natural) runs the neighbourhood backward (on natural-order
+    tensors if natural, else tile-major ones) and also reports the
+    token-level rate (10 * D FLOP per kept token pair)."""
     B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
     g = synth.random_qkv(B, H, N, D, seed=wl.seed + 2000)[0]
     gd = torch.from_numpy(np.ascontiguousarray(g).view(np.int16)).view(torch.bfloat16).to(dev)
     if nbk is None:
         O, L = bsa.forward(q, k, v, block, row_ptr, col_idx)
     else:
-        O, L = bsa.forward_neighborhood(q, k, v, row_ptr, col_idx, nbk[1], nbk[0])
+        O, L = bsa.forward_neighborhood(q, k, v, row_ptr, col_idx, nbk[1], nbk[0], natural=nbk[3])
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(int(bsa.load().bsa_backward_workspace_size(B, H, N)), dtype=torch.uint8, device=dev)
 
@@ -742,7 +743,7 @@ def backward_bench(torch, bsa, synth, dev, stream, wl, q, k, v, row_ptr, col_idx
             bsa.backward(q, k, v, O, gd, block, row_ptr, col_idx, L, dq=dq, dk=dk, dv=dv, workspace=ws)
         else:
             bsa.backward_neighborhood(q, k, v, O, gd, row_ptr, col_idx, nbk[1], nbk[0], L, dq=dq, dk=dk, dv=dv,
-                                      workspace=ws)
+                                      workspace=ws, natural=nbk[3])
     for _ in range(3):
         run()
     torch.cuda.synchronize()

@@ -151,6 +151,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_backward": (I32, [TP, TP, TP, TP, TP, I32, V, V, V, F, TP, TP, TP, V, SZ, V]),
             "bsa_backward_neighborhood": (I32, [TP, TP, TP, TP, TP, I32, V, V, V, ctypes.POINTER(BsaNeighborhood), V, F,
                                                 TP, TP, TP, V, SZ, V]),
+            "bsa_backward_neighborhood_natural": (I32, [TP, TP, TP, TP, TP, I32, V, V, V,
+                                                        ctypes.POINTER(BsaNeighborhood), V, F, TP, TP, TP, V, SZ, V]),
             "bsa_status_string": (ctypes.c_char_p, [I32]),
             "bsa_last_error": (ctypes.c_char_p, []),
             "bsa_version": (ctypes.c_char_p, []),
@@ -742,9 +744,12 @@ def backward_neighborhood(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
                           row_ptr: torch.Tensor, col_idx: torch.Tensor, entry_flags: torch.Tensor,
                           nb: BsaNeighborhood, lse: torch.Tensor, scale: Optional[float] = None,
                           dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                          dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                          dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          natural: bool = False):
     """(dQ, dK, dV) bf16 in tile-major order of forward_neighborhood, given its
-    tile-major output O and LSE and the tile-major output gradient dO."""
+    tile-major output O and LSE and the tile-major output gradient dO; with
+    natural=True every tensor is in natural token order
+    (bsa_backward_neighborhood_natural)."""
     lib = load()
     B, H, N, D = q.shape
     block = nb.tile_rows * nb.tile_cols
@@ -761,10 +766,10 @@ def backward_neighborhood(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
                                 device=q.device)
     ds = [_desc(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"), (dq, "dq"), (dk, "dk"),
                                    (dv, "dv"))]
-    _check(lib.bsa_backward_neighborhood(*[ctypes.byref(d) for d in ds[:5]], block, _ptr(row_ptr), _ptr(col_idx),
-                                         _ptr(entry_flags), ctypes.byref(nb), _ptr(lse), float(scale or 0.0),
-                                         *[ctypes.byref(d) for d in ds[5:]], _ptr(workspace),
-                                         workspace.numel(), _stream(q.device)))
+    fn = lib.bsa_backward_neighborhood_natural if natural else lib.bsa_backward_neighborhood
+    _check(fn(*[ctypes.byref(d) for d in ds[:5]], block, _ptr(row_ptr), _ptr(col_idx), _ptr(entry_flags),
+              ctypes.byref(nb), _ptr(lse), float(scale or 0.0), *[ctypes.byref(d) for d in ds[5:]],
+              _ptr(workspace), workspace.numel(), _stream(q.device)))
     return dq, dk, dv
 
 

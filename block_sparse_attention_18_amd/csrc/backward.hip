@@ -68,8 +68,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
     if (ok) {
         const int64_t bh = tok / p.N, t = tok - bh * p.N;
         const int b = (int)(bh / p.H), h = (int)(bh - (int64_t)b * p.H);
-        const uint4 a = ld_g16(p.dO.p + b * p.dO.sb + h * p.dO.sh + t * p.dO.sn + 8 * c);
-        const uint4 o = ld_g16(p.o.p + b * p.o.sb + h * p.o.sh + t * p.o.sn + 8 * c);
+        // natural-order tensors: the row of tile-major token t
+        const int64_t tn = p.natural ? nb_natural(p.nb, p.natural, (int)t) : t;
+        const uint4 a = ld_g16(p.dO.p + b * p.dO.sb + h * p.dO.sh + tn * p.dO.sn + 8 * c);
+        const uint4 o = ld_g16(p.o.p + b * p.o.sb + h * p.o.sh + tn * p.o.sn + 8 * c);
         const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, ow[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -79,8 +81,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
     }
     for (int d = 1; d < lpt; d <<= 1) acc += __shfl_xor(acc, d, 64);
     if (ok && c == 0) {
-        p.delta[tok] = acc;
-        p.lse2[tok] = p.lse[tok] * kLog2e;
+        const int64_t bh = tok / p.N, t = tok - bh * p.N;
+        const int64_t tn = p.natural ? nb_natural(p.nb, p.natural, (int)t) : t;
+        p.delta[tok] = acc;                              // workspace: tile-major order
+        p.lse2[tok] = p.lse[bh * p.N + tn] * kLog2e;
     }
 }
 
@@ -89,15 +93,34 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p)
 // ---------------------------------------------------------------------------
 // Copy of a 64-row tile (rows from r0 of a [N][D] bf16 matrix with row
 // stride sn) into LDS, slot s = (x*NW + wave)*64 + lane holding row s / KCH,
-// chunk (s % KCH) ^ bswz(row); rows past N repeat row N-1.
+// chunk (s % KCH) ^ bswz(row); rows past N repeat row N-1.  nat: the matrix
+// is in natural token order and tile-major row r0 + r is gathered from its
+// natural position.
 template <int BETA, int D>
 __device__ __forceinline__ void bw_load_tile(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t rs, int64_t sn,
-                                             int r0, int N, int wv, int lane)
+                                             int r0, int N, int wv, int lane, bool nat = false,
+                                             const NbGeom &g = NbGeom{})
 {
     using Sh = BwShape<BETA, D>;
     // one opaque LDS base per call: each copy's destination is a scalar add
     __attribute__((address_space(3))) char *lbase = (__attribute__((address_space(3))) char *)(lds_void *)(dst + wv * 64 * 8);
     asm volatile("" : "+s"(lbase));
+    if (nat && r0 >= g.T) {
+        // the tile's 64 rows gathered from natural order: a scalar base (the
+        // first row's position) plus a per-lane offset that is the same for
+        // every tile (the row offsets add over the disjoint bits of r0 mod
+        // BETA, a multiple of 64, and r < 64)
+        const int b0 = r0 & ~(BETA - 1);
+        const uint32_t so = (uint32_t)((nb_natural(g, BETA, b0) + nb_rowoff(g, r0 - b0)) * sn * 2);
+#pragma unroll
+        for (int x = 0; x < Sh::DMA; ++x) {
+            const int slot = (x * Sh::NW + wv) * 64 + lane;
+            const int r = slot / Sh::KCH, ps = slot % Sh::KCH;
+            const uint32_t o = (uint32_t)(nb_rowoff(g, r) * sn * 2 + ((ps ^ bswz<D>(r)) * 16));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * Sh::NW * 64 * 16), 16, o, so, 0, 0);
+        }
+        return;
+    }
 #pragma unroll
     for (int x = 0; x < Sh::DMA; ++x) {
         const int slot = (x * Sh::NW + wv) * 64 + lane;
@@ -244,10 +267,14 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
 
     const int qrow = i * BETA + wv * 32 + n;
     const bool qok = qrow < p.N;
+    // natural-order tensors: rows are gathered from (and dQ scattered to)
+    // the natural positions of the tile-major tokens
+    const bool nat = NBM && p.natural;
+    const int qpos = (nat && qok) ? nb_natural(p.nb, BETA, qrow) : qrow;
     bf16x8 qf[Sh::QS], dof[Sh::QS];
     {
-        const uint16_t *qb = p.q.p + b * p.q.sb + hh * p.q.sh + (int64_t)qrow * p.q.sn;
-        const uint16_t *gb = p.dO.p + b * p.dO.sb + hh * p.dO.sh + (int64_t)qrow * p.dO.sn;
+        const uint16_t *qb = p.q.p + b * p.q.sb + hh * p.q.sh + (int64_t)qpos * p.q.sn;
+        const uint16_t *gb = p.dO.p + b * p.dO.sb + hh * p.dO.sh + (int64_t)qpos * p.dO.sn;
 #pragma unroll
         for (int s = 0; s < Sh::QS; ++s) {
             qf[s] = as_bf16x8(qok ? ld_g16(qb + 16 * s + 8 * hl) : zero_u4());
@@ -291,8 +318,8 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
     if (T > 0) {
         bool vcur;
         int kcur = key0(0, vcur);
-        bw_load_tile<BETA, D>(smem, krs, p.k.sn, kcur, p.N, wv, lane);
-        bw_load_tile<BETA, D>(smem + Sh::TILE, vrs, p.v.sn, kcur, p.N, wv, lane);
+        bw_load_tile<BETA, D>(smem, krs, p.k.sn, kcur, p.N, wv, lane, nat, p.nb);
+        bw_load_tile<BETA, D>(smem + Sh::TILE, vrs, p.v.sn, kcur, p.N, wv, lane, nat, p.nb);
         for (int t = 0; t < T; ++t) {
             uint16_t *Kc = smem + (t & 1) * 2 * Sh::TILE, *Vc = Kc + Sh::TILE;
             bool vnxt = false;
@@ -301,8 +328,8 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
             if (t + 1 < T) {
                 knxt = key0(t + 1, vnxt);
                 uint16_t *Kn = smem + ((t + 1) & 1) * 2 * Sh::TILE;
-                bw_load_tile<BETA, D>(Kn, krs, p.k.sn, knxt, p.N, wv, lane);
-                bw_load_tile<BETA, D>(Kn + Sh::TILE, vrs, p.v.sn, knxt, p.N, wv, lane);
+                bw_load_tile<BETA, D>(Kn, krs, p.k.sn, knxt, p.N, wv, lane, nat, p.nb);
+                bw_load_tile<BETA, D>(Kn + Sh::TILE, vrs, p.v.sn, knxt, p.N, wv, lane, nat, p.nb);
             }
             f32x16 s[2], dp[2];
             bw_rows_mfma<D>(Kc, off.rows, qf, s);
@@ -343,7 +370,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
     }
     if (qok) {
         const float sc = p.scale;
-        uint16_t *orow = p.dq + b * p.dq_sb + hh * p.dq_sh + (int64_t)qrow * p.dq_sn;
+        uint16_t *orow = p.dq + b * p.dq_sb + hh * p.dq_sh + (int64_t)qpos * p.dq_sn;
 #pragma unroll
         for (int d = 0; d < Sh::DT; ++d)
 #pragma unroll
@@ -442,16 +469,33 @@ struct DkShape {
 };
 
 // Copy of R rows (from r0; rows past N repeat row N-1) into LDS with the
-// backward's chunk swizzle; NT threads, 16 bytes each per copy.
-template <int R, int D, int NT>
+// backward's chunk swizzle; NT threads, 16 bytes each per copy.  nat: the
+// matrix is in natural token order (rows gathered as in bw_load_tile;
+// blocks of BETA tokens).
+template <int R, int D, int NT, int BETA>
 __device__ __forceinline__ void bw_load_rows(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t rs, int64_t sn,
-                                              int r0, int N, int tid)
+                                              int r0, int N, int tid, bool nat = false, const NbGeom &g = NbGeom{})
 {
     constexpr int KCH = D / 8, CP = R * KCH / NT;
     static_assert(R * KCH % NT == 0, "tile split");
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     __attribute__((address_space(3))) char *lbase = (__attribute__((address_space(3))) char *)(lds_void *)(dst + wv * 64 * 8);
     asm volatile("" : "+s"(lbase));
+    if (nat && r0 >= g.T) {
+        // natural order: scalar base plus a per-lane offset, as in bw_load_tile
+        // (r0 mod BETA is a multiple of R, and r < R)
+        const int b0 = r0 & ~(BETA - 1);
+        const uint32_t so = (uint32_t)((nb_natural(g, BETA, b0) + nb_rowoff(g, r0 - b0)) * sn * 2);
+#pragma unroll
+        for (int x = 0; x < CP; ++x) {
+            const int slot = (x * (NT / 64) + wv) * 64 + lane;
+            const int r = slot / KCH, ps = slot % KCH;
+            const uint32_t o = (uint32_t)(nb_rowoff(g, r) * sn * 2 + ((ps ^ bswz<D>(r)) * 16));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbase + x * (NT / 64) * 64 * 16), 16, o, so, 0,
+                                                     0);
+        }
+        return;
+    }
 #pragma unroll
     for (int x = 0; x < CP; ++x) {
         const int slot = (x * (NT / 64) + wv) * 64 + lane;
@@ -478,6 +522,9 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     const int BH = p.B * p.H;
     const int j = blockIdx.x / BH, bh = blockIdx.x - j * BH;
     const int b = bh / p.H, hh = bh - b * p.H;
+    // natural-order tensors: rows gathered from (and dK, dV scattered to)
+    // the natural positions of the tile-major tokens
+    const bool nat = NBM && p.natural;
 
     // query blocks whose row lists j, ascending
     int count = 0;
@@ -526,8 +573,8 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     auto load = [&](int t) {
         const int q0 = qstart(t);
         uint16_t *B0 = buf(t);
-        bw_load_rows<64, D, G::NT>(B0, qrs, p.q.sn, q0, p.N, tid);
-        bw_load_rows<64, D, G::NT>(B0 + G::QT, grs, p.dO.sn, q0, p.N, tid);
+        bw_load_rows<64, D, G::NT, BETA>(B0, qrs, p.q.sn, q0, p.N, tid, nat, p.nb);
+        bw_load_rows<64, D, G::NT, BETA>(B0 + G::QT, grs, p.dO.sn, q0, p.N, tid, nat, p.nb);
         if (wv == 0) {
             float *st = reinterpret_cast<float *>(B0 + 2 * G::QT);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void *)st, 4, (uint32_t)lane * 4, (uint32_t)q0 * 4, 0, 0);
@@ -561,8 +608,8 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     const uint32_t brow = (uint32_t)(krow_l * D * 2 + 16 * (hl ^ bswz<D>(krow_l)));
 
     if (T > 0) {
-        bw_load_rows<BETA, D, G::NT>(Kt, krs, p.k.sn, j * BETA, p.N, tid);
-        bw_load_rows<BETA, D, G::NT>(Vt, vrs, p.v.sn, j * BETA, p.N, tid);
+        bw_load_rows<BETA, D, G::NT, BETA>(Kt, krs, p.k.sn, j * BETA, p.N, tid, nat, p.nb);
+        bw_load_rows<BETA, D, G::NT, BETA>(Vt, vrs, p.v.sn, j * BETA, p.N, tid, nat, p.nb);
         load(0);
         for (int t = 0; t < T; ++t) {
             __syncthreads();                  // sub-tile t in LDS; buffer (t+1)&1 free
@@ -629,9 +676,10 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     __syncthreads();
     const int krow = j * BETA + kg * 32 + n;
     if (qh == 0 && krow < p.N) {
+        const int kpos = nat ? nb_natural(p.nb, BETA, krow) : krow;
         const float sc = p.scale;
-        uint16_t *rk = p.dk + b * p.dk_sb + hh * p.dk_sh + (int64_t)krow * p.dk_sn;
-        uint16_t *rv = p.dv + b * p.dv_sb + hh * p.dv_sh + (int64_t)krow * p.dv_sn;
+        uint16_t *rk = p.dk + b * p.dk_sb + hh * p.dk_sh + (int64_t)kpos * p.dk_sn;
+        uint16_t *rv = p.dv + b * p.dv_sb + hh * p.dv_sh + (int64_t)kpos * p.dv_sn;
 #pragma unroll
         for (int d = 0; d < G::DT; ++d)
 #pragma unroll

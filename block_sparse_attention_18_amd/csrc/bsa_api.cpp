@@ -776,7 +776,7 @@ static bsa_status backward_impl(const bsa_tensor *q, const bsa_tensor *k, const 
                                 const bsa_tensor *dO, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
                                 const float *lse, float scale, const bsa_tensor *dq, const bsa_tensor *dk,
                                 const bsa_tensor *dv, void *workspace, size_t workspace_bytes, void *stream,
-                                const int32_t *entry_flags, const bsa::NbGeom *nb)
+                                const int32_t *entry_flags, const bsa::NbGeom *nb, int natural = 0)
 {
     bsa_status st;
     const bsa_tensor *ts[] = {q, k, v, o, dO, dq, dk, dv};
@@ -820,6 +820,7 @@ static bsa_status backward_impl(const bsa_tensor *q, const bsa_tensor *k, const 
     p.scale_log2 = p.scale * 1.4426950408889634f;
     p.flags = entry_flags;
     if (nb) p.nb = *nb;
+    p.natural = (nb && natural) ? block : 0;
     hipError_t e = bsa::launch_backward(p, block, (int)q->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return BSA_OK;
@@ -848,6 +849,23 @@ bsa_status bsa_backward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, c
     if ((st = check_nb(nb, q->N, block, &g)) != BSA_OK) return st;
     return backward_impl(q, k, v, o, dO, block, row_ptr, col_idx, lse, scale, dq, dk, dv, workspace,
                          workspace_bytes, stream, entry_flags, &g);
+}
+
+bsa_status bsa_backward_neighborhood_natural(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                             const bsa_tensor *o, const bsa_tensor *dO, int32_t block,
+                                             const int32_t *row_ptr, const int32_t *col_idx,
+                                             const int32_t *entry_flags, const bsa_neighborhood *nb,
+                                             const float *lse, float scale, const bsa_tensor *dq,
+                                             const bsa_tensor *dk, const bsa_tensor *dv, void *workspace,
+                                             size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if (!entry_flags) return fail(BSA_ERR_INVALID_ARG, "entry_flags null");
+    bsa::NbGeom g;
+    if ((st = check_nb(nb, q->N, block, &g)) != BSA_OK) return st;
+    return backward_impl(q, k, v, o, dO, block, row_ptr, col_idx, lse, scale, dq, dk, dv, workspace,
+                         workspace_bytes, stream, entry_flags, &g, 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -150,6 +150,9 @@ struct BwdParams {
     int64_t dq_sb, dq_sh, dq_sn, dk_sb, dk_sh, dk_sn, dv_sb, dv_sh, dv_sn;
     int32_t B, H, N, D, nB;
     float scale, scale_log2;
+    // neighbourhood layouts: 0, or the block when every [B][H][N] tensor is in
+    // natural token order (the kernels gather and scatter tile-major rows)
+    int32_t natural;
 };
 
 // Tile-major token permutation (see bsa_permute_tokens).

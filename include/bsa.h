@@ -348,6 +348,20 @@ bsa_status bsa_backward_neighborhood(const bsa_tensor *q, const bsa_tensor *k, c
                                      const bsa_tensor *dq, const bsa_tensor *dk, const bsa_tensor *dv,
                                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* bsa_backward_neighborhood_natural -- bsa_backward_neighborhood with Q, K,
+ * V, O, dO and LSE in natural order (as bsa_forward_neighborhood_natural
+ * produced O and LSE) and dQ, dK, dV written in natural order: the kernels
+ * gather the tile-major tiles from the grid rows and scatter the gradient
+ * rows, so no permutation pass is needed.  Block list and flags as for
+ * bsa_backward_neighborhood; same workspace, limits and errors. */
+bsa_status bsa_backward_neighborhood_natural(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                                             const bsa_tensor *o, const bsa_tensor *dO, int32_t block,
+                                             const int32_t *row_ptr, const int32_t *col_idx,
+                                             const int32_t *entry_flags, const bsa_neighborhood *nb,
+                                             const float *lse, float scale, const bsa_tensor *dq,
+                                             const bsa_tensor *dk, const bsa_tensor *dv, void *workspace,
+                                             size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * FP8 forward (OCP E4M3 operands on the gfx950 FP8 matrix cores).
  *

@@ -367,6 +367,12 @@ def test_neighborhood_validation():
         ctypes.c_void_p(fl) if fl else None, ctypes.byref(nb), 0.0, ctypes.byref(t(N)), None, None)
     assert fwd8(N=16895) == 1 and "N" in _err()
     assert fwd8(fl=0) == 1 and "entry_flags" in _err()
+    bwd = lambda N=16896, fl=FAKE: lib.bsa_backward_neighborhood_natural(
+        *[ctypes.byref(t(N)) for _ in range(5)], 128, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(fl) if fl else None, ctypes.byref(nb), ctypes.c_void_p(FAKE), 0.0,
+        *[ctypes.byref(t(N)) for _ in range(3)], ctypes.c_void_p(FAKE), 1 << 30, None)
+    assert bwd(N=16895) == 1 and "N" in _err()
+    assert bwd(fl=0) == 1 and "entry_flags" in _err()
 
 
 def test_binding_refuses_host_tensors():

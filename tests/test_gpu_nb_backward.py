@@ -127,3 +127,25 @@ def test_backward_full_g1_workload_sampled_rows_and_sums(stride):
     dv_err = np.abs(gv.sum(axis=2) - go.sum(axis=2)) / np.abs(gv).sum(axis=2)
     _log(f"  sum dK / sum |dK|: max {dk_sum.max():.2e}; |sum dV - sum dO| / sum |dV|: max {dv_err.max():.2e}")
     assert dk_sum.max() <= 2e-3 and dv_err.max() <= 2e-3
+
+
+@pytest.mark.parametrize("T,grid,tile,window,stride,D", GEOMS)
+def test_natural_order_backward_equals_the_permuted_path(T, grid, tile, window, stride, D):
+    """bsa_backward_neighborhood_natural takes natural-order Q, K, V, O, dO and
+    LSE (those of the natural-order forward) and writes natural-order dQ, dK,
+    dV: the same arithmetic on the same tiles as the tile-major backward, so
+    the gradients equal its permuted-back ones bit for bit."""
+    _log(f"nb backward natural T={T} grid={grid} tile={tile} window={window} stride={stride} D={D}")
+    B, H = 1, 2
+    N = T + grid[0] * grid[1]
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    q, k, v = synth.random_qkv(B, H, N, D, seed=1231)
+    g = synth.random_qkv(B, H, N, D, seed=1232)[0]
+    want, _ = _backward_natural(q, k, v, g, nb)
+    qd, kd, vd, gd = (to_dev_bf16(a) for a in (q, k, v, g))
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    O, L = bsa.forward_neighborhood(qd, kd, vd, rp, ci, fl, nb, natural=True)
+    got = bsa.backward_neighborhood(qd, kd, vd, O, gd, rp, ci, fl, nb, L, natural=True)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dQ", "dK", "dV"), got, want):
+        np.testing.assert_array_equal(bf16_bits(x), bf16_bits(y), err_msg=name)
