@@ -81,6 +81,8 @@ def _load():
         D_ = ctypes.c_double
         lib.oracle_forward_neighborhood_f64.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, D_, P, P]
         lib.oracle_forward_neighborhood_f64.restype = ctypes.c_int
+        lib.oracle_forward_neighborhood_f64_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, D_, P, I, P, P]
+        lib.oracle_forward_neighborhood_f64_rows.restype = ctypes.c_int
         lib.oracle_backward_neighborhood_f64.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, D_, P, P, P]
         lib.oracle_backward_neighborhood_f64.restype = ctypes.c_int
         lib.oracle_backward_dq_rows.argtypes = [P, P, P, P, I, I, I, I, I, P, P, D_, P, I, P]
@@ -515,13 +517,22 @@ def backward_dq_rows(q, k, v, dO, block: int, row_ptr, col_idx, rows, scale: Opt
 
 
 def forward_neighborhood_f64(q, k, v, text_len: int, grid: Tuple[int, int], window: Tuple[int, int],
-                             stride: Tuple[int, int] = (1, 1), scale: Optional[float] = None):
+                             stride: Tuple[int, int] = (1, 1), scale: Optional[float] = None,
+                             rows: Optional[Sequence[int]] = None):
     """The neighbourhood forward on fp64 (or bf16-bit) inputs, natural token
-    order: (O, LSE) in fp64."""
+    order: (O, LSE) in fp64; with `rows`, only those flat query rows
+    ((b*H + h)*N + t): O [len(rows), D], LSE [len(rows)]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     (R, C), (kh, kw), (sh, sw) = grid, window, stride
+    if rows is not None:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        O = np.empty((len(r), D), np.float64); L = np.empty((len(r),), np.float64)
+        _check(_load().oracle_forward_neighborhood_f64_rows(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, text_len, R, C,
+                                                            kh, kw, sh, sw, scale, _ptr(r), len(r), _ptr(O),
+                                                            _ptr(L)), "forward_neighborhood_f64 rows")
+        return O, L
     O = np.empty((B, H, N, D), np.float64); L = np.empty((B, H, N), np.float64)
     _check(_load().oracle_forward_neighborhood_f64(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, text_len, R, C, kh, kw,
                                                    sh, sw, scale, _ptr(O), _ptr(L)), "forward_neighborhood_f64")

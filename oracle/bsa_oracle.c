@@ -1114,6 +1114,44 @@ int oracle_forward_neighborhood_f64(const double *q, const double *k, const doub
     return rc;
 }
 
+/* The same forward for the flat query rows rows[0..nrows) ((b*H + h)*N + t)
+ * only: O [nrows][D], LSE [nrows]. */
+int oracle_forward_neighborhood_f64_rows(const double *q, const double *k, const double *v, int64_t B, int64_t H,
+                                         int64_t N, int64_t D, int64_t text_len, int64_t R, int64_t C, int64_t kh,
+                                         int64_t kw, int64_t sh, int64_t sw, double scale, const int64_t *rows,
+                                         int64_t nrows, double *O, double *LSE)
+{
+    if (!q || !k || !v || !O || !LSE || !rows || nrows < 0 || B <= 0 || H <= 0 || D <= 0 ||
+        !na_check(N, text_len, R, C, kh, kw, sh, sw))
+        return OR_EINVAL;
+    for (int64_t i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= B * H * N) return OR_EINVAL;
+    const na_geom g = {text_len, R, C, kh, kw, sh, sw};
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        double *p = malloc(sizeof(double) * N);
+        if (!p) {
+#pragma omp atomic write
+            rc = OR_ENOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < nrows; ++i) {
+                const int64_t bh = rows[i] / N, t = rows[i] % N;
+                na_row_probs(q, k, N, D, bh, t, &g, scale, p, &LSE[i]);
+                for (int64_t d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int64_t s = 0; s < N; ++s)
+                        if (p[s] != 0.0) acc += p[s] * v[(bh * N + s) * D + d];
+                    O[i * D + d] = acc;
+                }
+            }
+        }
+        free(p);
+    }
+    return rc;
+}
+
 int oracle_backward_neighborhood_f64(const double *q, const double *k, const double *v, const double *dO, int64_t B,
                                      int64_t H, int64_t N, int64_t D, int64_t text_len, int64_t R, int64_t C,
                                      int64_t kh, int64_t kw, int64_t sh, int64_t sw, double scale, double *dQ,

@@ -16,8 +16,8 @@ import torch
 import oracle
 import synth
 import block_sparse_attention_18_amd as bsa
-from helpers import bf16_to_f64, dev, to_dev_bf16
-from test_gpu_fp8 import FP8_LSE_MAX_ABS, FP8_O_MAX_ABS, FP8_O_MEAN_ABS
+from helpers import bf16_to_f64, dev, sample_rows, to_dev_bf16
+from test_gpu_fp8 import FP8_LSE_MAX_ABS, FP8_O_MAX_ABS, FP8_O_MEAN_ABS, _check_quant
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -104,3 +104,33 @@ def test_natural_order_quantisation_and_forward_equal_the_permuted_path(T, grid,
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), name
     np.testing.assert_array_equal(O2.view(torch.int16).cpu().numpy(), O1.view(torch.int16).cpu().numpy())
     np.testing.assert_array_equal(L2.cpu().numpy(), L1.cpu().numpy())
+
+
+@pytest.mark.slow
+def test_workload_g1_fp8_natural_sampled_rows():
+    """The full G1 workload (FLUX 2048², 24 heads, window 32 x 32, tiles
+    8 x 16, stride 1) in the launch configuration bench.py --fp8 times:
+    natural-order quantisation to tile-major codes, the layout, and the FP8
+    forward writing natural-order O and LSE.  The codes and scales are
+    checked bit for bit against the oracle's quantisation of the host-permuted
+    tensors, and sampled rows against the oracle's fp64 forward on the
+    dequantised natural-order tensors, with the FP8 tolerances."""
+    wl = synth.WORKLOADS["G1"]
+    x = synth.make_inputs(wl)
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    T, grid, tile, window, stride = wl.text_len, wl.nb_grid, wl.nb_tile, wl.nb_window, wl.nb_stride
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    qkv = bsa.quantize_fp8(*(to_dev_bf16(a) for a in (x["q"], x["k"], x["v"])), nb=nb)
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    O, L = bsa.forward_fp8_neighborhood(qkv, rp, ci, fl, nb, natural=True)
+    torch.cuda.synchronize()
+    perm = oracle.tile_permutation(T, grid, tile)
+    _check_quant(qkv, oracle.quantize_fp8(*(a[:, :, perm] for a in (x["q"], x["k"], x["v"]))))
+    must = [((0 * H + h) * N + t) for h in (0, H - 1) for t in (0, T - 1, T, T + 200, N // 2, N - 1)]
+    rows = sample_rows(B, H, N, 192, 1321, must)
+    qn, kn, vn = _dequantised_natural(x["q"], x["k"], x["v"], T, grid, tile)
+    Oo, Lo = oracle.forward_neighborhood_f64(qn, kn, vn, T, grid, window, stride, rows=rows)
+    err = np.abs(bf16_to_f64(O).reshape(-1, D)[rows] - Oo)
+    lerr = np.abs(L.cpu().numpy().reshape(-1)[rows].astype(np.float64) - Lo)
+    _log(f"G1 fp8 natural: {len(rows)} rows, O max {err.max():.2e} mean {err.mean():.2e}  LSE max {lerr.max():.2e}")
+    assert err.max() <= FP8_O_MAX_ABS and err.mean() <= FP8_O_MEAN_ABS and lerr.max() <= FP8_LSE_MAX_ABS

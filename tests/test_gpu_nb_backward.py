@@ -103,7 +103,7 @@ def test_backward_peaked_logits_and_determinism():
 @pytest.mark.parametrize("stride", [(1, 1), (32, 32)])
 def test_backward_full_g1_workload_sampled_rows_and_sums(stride):
     """The full 2-D neighbourhood workload G1 (FLUX 2048², 24 heads, window
-    32 x 32, tiles 8 x 16) as bench.py runs it: sampled dQ rows against the
+    32 x 32, tiles 8 x 16) as bench.py runs it (natural-order tensors): sampled dQ rows against the
     oracle row by row, and the column-sum identities of dK (zero) and dV (the
     sum of dO), bounded as for the 2K arrow workload (2e-3 of the sum of
     magnitudes)."""
@@ -114,7 +114,12 @@ def test_backward_full_g1_workload_sampled_rows_and_sums(stride):
     nb = bsa.neighborhood(T, wl.nb_grid, wl.nb_tile, wl.nb_window, stride)
     g = synth.random_qkv(B, H, N, D, seed=1220)[0]
     _log(f"nb backward full G1 stride {stride}")
-    (dq, dk, dv), _ = _backward_natural(x["q"], x["k"], x["v"], g, nb)
+    # natural-order forward and backward, as bench.py --backward runs them
+    qd, kd, vd, gd = (to_dev_bf16(a) for a in (x["q"], x["k"], x["v"], g))
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    O, L = bsa.forward_neighborhood(qd, kd, vd, rp, ci, fl, nb, natural=True)
+    dq, dk, dv = bsa.backward_neighborhood(qd, kd, vd, O, gd, rp, ci, fl, nb, L, natural=True)
+    torch.cuda.synchronize()
     rng = np.random.default_rng(1221)
     rows = np.concatenate([[0, T - 1, T, T + 127, N - 1, (H - 1) * N + T + 5000],
                            rng.integers(0, H, 42) * N + rng.integers(0, N, 42)]).astype(np.int64)

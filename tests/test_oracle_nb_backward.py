@@ -111,3 +111,15 @@ def test_dq_rows_are_the_full_gradient_rows():
     rows = np.array([0, 3, 4, 30, N - 1, N, 2 * N - 1])
     got = oracle.backward_neighborhood_dq_rows(q, k, v, g, T, grid, window, stride, rows)
     np.testing.assert_array_equal(got, dq.reshape(-1, 8)[rows])
+
+
+def test_fp64_forward_rows_are_the_full_forward_rows():
+    T, grid, window, stride = 4, (6, 8), (3, 5), (2, 1)
+    N = T + grid[0] * grid[1]
+    rng = np.random.default_rng(1501)
+    q, k, v = (rng.standard_normal((1, 2, N, 8)) for _ in range(3))
+    O, L = oracle.forward_neighborhood_f64(q, k, v, T, grid, window, stride)
+    rows = np.array([0, 3, 4, 30, N - 1, N, 2 * N - 1])
+    Or, Lr = oracle.forward_neighborhood_f64(q, k, v, T, grid, window, stride, rows=rows)
+    np.testing.assert_array_equal(Or, O.reshape(-1, 8)[rows])
+    np.testing.assert_array_equal(Lr, L.reshape(-1)[rows])
