@@ -363,13 +363,14 @@ __device__ __forceinline__ void last_step(const uint16_t *__restrict__ Vp, bool 
 }
 
 // Occupancy: two waves per SIMD (β=128: two 4-wave workgroups per CU; β=64,
-// D=64: four 2-wave workgroups, whose 32 KB of tiles fit the LDS four times).
+// D=64: four 2-wave workgroups, whose 32 KB of tiles fit the LDS four
+// times).  The launch bound's second argument is waves per SIMD.
 template <int BETA, int D>
-constexpr int fwd_min_blocks() { return BETA == 128 ? 2 : (D == 64 ? 4 : 2); }
+constexpr int fwd_waves_per_simd() { return 2; }
 
 // NBM: neighbourhood masking of the tiles the layout flags as partial.
 template <int BETA, int D, bool NBM>
-__global__ __launch_bounds__(BETA / 32 * 64, (fwd_min_blocks<BETA, D>())) void fwd_kernel(const FwdParams p)
+__global__ __launch_bounds__(BETA / 32 * 64, (fwd_waves_per_simd<BETA, D>())) void fwd_kernel(const FwdParams p)
 {
     using Sh = FwdShape<BETA, D>;
     // two buffers, each a 64-key K tile and a 64-key V tile
