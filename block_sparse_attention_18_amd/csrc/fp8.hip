@@ -186,8 +186,19 @@ __global__ __launch_bounds__(D) void vscale_kernel(const Fp8QuantParams p)
 {
     const int64_t bh = blockIdx.x;
     const int d = threadIdx.x;
-    float a = 0.f;
-    for (int s = 0; s < p.S; ++s) a = fmaxf(a, p.vmax_part[(bh * p.S + s) * D + d]);
+    // four independent maxima keep four loads in flight (the chunks' maxima
+    // are non-negative, and max is exact in any order)
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    const float *mp = p.vmax_part + bh * p.S * D + d;
+    int s = 0;
+    for (; s + 4 <= p.S; s += 4) {
+        a0 = fmaxf(a0, mp[(int64_t)(s + 0) * D]);
+        a1 = fmaxf(a1, mp[(int64_t)(s + 1) * D]);
+        a2 = fmaxf(a2, mp[(int64_t)(s + 2) * D]);
+        a3 = fmaxf(a3, mp[(int64_t)(s + 3) * D]);
+    }
+    for (; s < p.S; ++s) a0 = fmaxf(a0, mp[(int64_t)s * D]);
+    const float a = fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
     float sc, inv;
     fp8_group_scale(a, sc, inv);
     p.v_scale[bh * D + d] = sc;
