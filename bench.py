@@ -69,6 +69,8 @@ def main():
                     help="neighbourhood workloads: permute Q, K, V to tile-major order and O, LSE back in "
                          "separate passes instead of the kernels' "
                          "natural-order gather")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time a large dense bf16 GEMM (torch.mm, hipBLASLt) as the practical MFMA ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -126,6 +128,27 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": max(args.steps, 1)}))
+        return
+    if args.gemm_ceiling:
+        # the practical bf16 MFMA rate on this machine: a large dense GEMM of
+        # contiguous operands through the vendor library
+        n = 8192
+        a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        for _ in range(3):
+            torch.mm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(args.steps, 1)
+        e0.record()
+        for _ in range(reps):
+            torch.mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm_ceiling": {"m": n, "n": n, "k": n, "dtype": "bf16", "ms": round(ms, 4),
+                                           "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}}))
         return
     bsa.load()
     if args.sweep:
