@@ -307,6 +307,8 @@ int oracle_scores_exact_avgpool(const uint16_t *q, const uint16_t *k,
  *   - otherwise keep F = {j < text_blocks} united with, for each group g
  *     (column range [c_g, e_g), budget k_g), the first k_g columns of that
  *     range ordered by descending score, lower column first on equal scores.
+ * A NaN score carries no evidence for its block: it ranks after every
+ * number (-inf included), NaNs among themselves by lower column.
  * Output: CSR over the listed rows, columns ascending.  Returns nnz >= 0 or
  * a negative error.
  * ---------------------------------------------------------------------- */
@@ -315,8 +317,12 @@ typedef struct { double s; int32_t j; } scored_col;
 static int cmp_scored(const void *a, const void *b)
 {
     const scored_col *x = a, *y = b;
-    if (x->s > y->s) return -1;
-    if (x->s < y->s) return 1;
+    const int xn = isnan(x->s), yn = isnan(y->s);
+    if (xn != yn) return xn ? 1 : -1;
+    if (!xn) {
+        if (x->s > y->s) return -1;
+        if (x->s < y->s) return 1;
+    }
     return (x->j < y->j) ? -1 : (x->j > y->j);
 }
 

@@ -218,6 +218,21 @@ def test_select_ties_lower_index_and_signed_zero():
     assert ci.tolist() == [1, 3]
 
 
+def test_select_nan_scores_rank_last():
+    """A NaN score ranks after every number, -inf included; NaNs among
+    themselves by lower column (the selection's defined order for scores
+    that carry no evidence)."""
+    nan, inf = float("nan"), float("inf")
+    row = np.array([nan, 2.0, -inf, nan, 0.5, -1.0, nan, 3.0], np.float32)
+    order = [7, 1, 4, 5, 2, 0, 3, 6]          # numbers by value, then NaNs by column
+    for kk in range(len(row) + 1):
+        rp, ci = oracle.select_rows(row[None, :], [0], 0, ((0, 8, kk),))
+        assert ci.tolist() == sorted(order[:kk])
+    # a row of NaNs only: the lowest columns
+    rp, ci = oracle.select_rows(np.full((1, 6), nan, np.float32), [0], 0, ((0, 6, 2),))
+    assert ci.tolist() == [0, 1]
+
+
 def test_select_forced_text_and_counts():
     nB, tb, kk = 10, 3, 4
     S = random_scores(1, 2, nB, seed=18)
