@@ -464,13 +464,21 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
 
     split: None, or {"chunk_blocks", "max_chunks", "max_split_rows"[, "workspace"]}
     to cut long rows over several workgroups (see arrow_split_policy /
-    select_split_policy).  A missing workspace is allocated here."""
+    select_split_policy).  A missing workspace is allocated here.
+
+    The LSE of a SKIP head is copied from lse_cache; without lse_cache the C
+    ABI leaves it untouched, so an LSE tensor allocated here holds NaN for
+    those heads (a caller-given lse keeps its contents there)."""
     lib = load()
     B, H, N, D = q.shape
     if out is None:
         out = torch.empty_like(q)
+    modes = None if head_modes is None else _host_i8(head_modes, H)
     if lse is None and return_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        if modes is not None and lse_cache is None and any(m == HEAD_SKIP for m in modes):
+            lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=q.device)
+        else:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
     if lse_cache is not None and (lse_cache.dtype != torch.float32 or not lse_cache.is_contiguous()):
@@ -482,7 +490,6 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
         # a block list with no entries: the kernels never read col_idx, but the
         # C ABI wants a valid pointer
         col_idx = torch.zeros(1, dtype=torch.int32, device=row_ptr.device)
-    modes = None if head_modes is None else _host_i8(head_modes, H)
     dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
     dc = _desc(o_cache, "o_cache")
     sp = None

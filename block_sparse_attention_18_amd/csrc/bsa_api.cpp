@@ -52,6 +52,11 @@ bsa_status check_tensor(const bsa_tensor *t, const char *name)
         t->stride_h < 0 || t->stride_n < t->D)
         return fail(BSA_ERR_INVALID_ARG,
                     "%s: strides must be non-negative multiples of 8 with stride_n >= D", name);
+    // The kernels address one head's rows through a 32-bit buffer range from
+    // the head's base, (N - 1) * stride_n + D elements of 2 bytes.
+    if (((t->N - 1) * t->stride_n + t->D) * 2 >= (1ll << 32))
+        return fail(BSA_ERR_UNSUPPORTED,
+                    "%s: one head spans 4 GiB or more ((N - 1) * stride_n + D elements of 2 bytes)", name);
     return BSA_OK;
 }
 
@@ -67,6 +72,7 @@ bsa::Tensor4 t4(const bsa_tensor *t)
 }
 
 bool block_ok(int32_t block) { return block == 64 || block == 128; }
+
 
 size_t exact_slot_bytes(int64_t nB, int32_t block) { return (size_t)nB * block * sizeof(float); }
 

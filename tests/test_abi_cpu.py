@@ -78,6 +78,9 @@ def _err():
     (dict(v=_t(sn=60)), 1, "strides"),
     (dict(o=_t(sh=-64)), 1, "strides"),
     (dict(block=32), 2, "block size"),
+    # one head's rows span 4 GiB: beyond the kernels' 32-bit buffer range
+    (dict(q=_t(N=1 << 24, D=128)), 2, "4 GiB"),
+    (dict(k=_t(N=(1 << 19) + 8, D=128, sn=128 * 32)), 2, "4 GiB"),
     (dict(rp=0), 1, "row_ptr"),
     (dict(scale=float("nan")), 1, "NaN"),
 ])

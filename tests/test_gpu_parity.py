@@ -82,6 +82,93 @@ def test_forward_scale_and_large_logits():
     check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "scale 0.2")
 
 
+@pytest.mark.parametrize("N", [3 * 128 + 40, 4 * 128])
+def test_forward_large_logits_and_large_v(N):
+    """Large logits (Q, K of standard deviation 3, scale 0.2) with V of
+    standard deviation 3: the O bounds scale with V (relative tolerance).
+    Whole blocks and a ragged last block."""
+    B, H, D, block = 1, 2, 128, 128
+    q, k, _ = synth.random_qkv(B, H, N, D, seed=113, scale=3.0)
+    _, _, v = synth.random_qkv(B, H, N, D, seed=114, scale=3.0)
+    nB = -(-N // block)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=116, density=0.7)
+    O, L = _run_forward(q, k, v, block, rp, ci, scale=0.2)
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci, scale=0.2)
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "large V", v_scale=3.0)
+
+
+# Whole blocks at block 128, D 128 (the shape of the arrow and long-context
+# workloads): odd and single-block grids, sparse and mostly empty lists.
+WHOLE_CASES = [
+    # B, H, nB, density, empty rows, full rows, seed
+    (1, 2, 5, 0.5, 1, 2, 300),      # odd number of blocks
+    (2, 3, 8, 0.3, 2, 1, 301),      # sparse rows
+    (1, 1, 1, 1.0, 0, 1, 302),      # a single block
+    (1, 4, 12, 0.8, 3, 3, 303),
+    (1, 2, 6, 0.05, 4, 0, 304),     # mostly empty rows
+]
+
+
+@pytest.mark.parametrize("B,H,nB,dens,er,fr,seed", WHOLE_CASES)
+def test_forward_whole_blocks(B, H, nB, dens, er, fr, seed):
+    N, D, block = nB * 128, 128, 128
+    _log(f"whole blocks B={B} H={H} nB={nB} density={dens}")
+    q, k, v = synth.random_qkv(B, H, N, D, seed=seed)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=seed + 1, density=dens, empty_rows=er, full_rows=fr)
+    O, L = _run_forward(q, k, v, block, rp, ci)
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci)
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "whole blocks")
+    for x in [x for x in range(B * H * nB) if rp[x] == rp[x + 1]]:
+        bh, i = divmod(x, nB)
+        b, h = divmod(bh, H)
+        assert torch.all(O[b, h, i * block:(i + 1) * block] == 0)
+        assert torch.all(torch.isneginf(L[b, h, i * block:(i + 1) * block]))
+
+
+def test_forward_ignores_out_of_range_columns():
+    """Column indices outside [0, nB) are ignored (the ABI's rule): the
+    result equals the forward on the list without them."""
+    B, H, nB, D, block = 1, 2, 6, 128, 128
+    N = nB * block
+    q, k, v = synth.random_qkv(B, H, N, D, seed=310)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=311, density=0.5, empty_rows=1, full_rows=1)
+    rows = csr_rows(rp, ci)
+    bad = []
+    for x, r in enumerate(rows):     # an invalid index before and after the valid ones
+        bad.append(([-3] if x % 2 else []) + r + ([nB + 7] if x % 3 == 0 else []))
+    rpb = np.zeros(len(bad) + 1, np.int32)
+    rpb[1:] = np.cumsum([len(r) for r in bad])
+    cib = np.array([c for r in bad for c in r] or [0], np.int32)
+    O, L = _run_forward(q, k, v, block, rpb, cib)
+    O1, L1 = _run_forward(q, k, v, block, rp, ci)
+    assert torch.equal(O.view(torch.int16), O1.view(torch.int16))
+    assert torch.equal(L, L1)
+
+
+def test_forward_whole_blocks_strided_and_skip():
+    B, H, nB, D, block = 2, 4, 7, 128, 128
+    N = nB * block
+    q, k, v = synth.random_qkv(B, H, N, D, seed=320)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=321, density=0.6, empty_rows=1, full_rows=2)
+    modes = np.array([bsa.HEAD_SKIP, bsa.HEAD_FULL, bsa.HEAD_SKIP, bsa.HEAD_ARROW], np.int8)
+    cache = synth.random_qkv(B, H, N, D, seed=322)[0]
+
+    def strided(a):
+        t = to_dev_bf16(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+        return t.permute(0, 2, 1, 3)
+    out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev()).permute(0, 2, 1, 3)
+    O, L = bsa.forward(strided(q), strided(k), strided(v), block, _i32(rp), _i32(ci), head_modes=modes,
+                       o_cache=to_dev_bf16(cache), out=out)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci)
+    comp = modes != bsa.HEAD_SKIP
+    check_forward(bf16_to_f64(O)[:, comp], L.cpu().numpy()[:, comp].astype(np.float64), Oo[:, comp],
+                  Lo[:, comp], "strided whole blocks")
+    np.testing.assert_array_equal(bf16_bits(O)[:, ~comp], cache[:, ~comp])
+    # no LSE cache: the binding's own LSE tensor marks SKIP heads NaN
+    assert torch.isnan(L[:, torch.from_numpy(~comp)]).all()
+
+
 def test_forward_very_negative_logits_and_empty_last_subtile():
     """Every logit far below zero (about -260 in log2 units) with a last block
     of 40 keys, whose second 64-key sub-tile holds no key: that sub-tile must
@@ -315,6 +402,9 @@ def test_exact_scores_small(B, H, N, D, block):
 # the five workloads at full size
 # ---------------------------------------------------------------------------
 def _workload_forward_check(wl, x, rp, ci, n_sample, seed, must_blocks=(), modes=None, split=None):
+    """The forward on the workload against the oracle: on every computed row
+    when n_sample is None, else on a seeded sample plus the rows of
+    must_blocks."""
     B, H, N, D, block = wl.B, wl.H, wl.N, wl.D, wl.block
     kw = {} if split is None else {"split": split}
     if modes is not None:
@@ -325,14 +415,17 @@ def _workload_forward_check(wl, x, rp, ci, n_sample, seed, must_blocks=(), modes
     for (b, h, i) in must_blocks:
         t0 = i * block
         must += [((b * H + h) * N + t) for t in range(t0, min(N, t0 + block))]
-    rows = sample_rows(B, H, N, n_sample, seed, must)
+    if n_sample is None:
+        rows = np.arange(B * H * N, dtype=np.int64)
+    else:
+        rows = sample_rows(B, H, N, n_sample, seed, must)
     if modes is not None:
         rows = rows[modes[(rows // N) % H] != bsa.HEAD_SKIP]
     Oo, Lo = oracle.forward(x["q"], x["k"], x["v"], block, rp, ci, rows=rows)
     Og = bf16_to_f64(O).reshape(-1, D)[rows]
     Lg = L.cpu().numpy().reshape(-1)[rows].astype(np.float64)
     mx, mean = check_forward(Og, Lg, Oo, Lo, wl.name)
-    _log(f"{wl.name}: {len(rows)} sampled rows, max|dO|={mx:.2e} mean|dO|={mean:.2e}")
+    _log(f"{wl.name}: {len(rows)} rows, max|dO|={mx:.2e} mean|dO|={mean:.2e}")
     return O, L
 
 
@@ -347,7 +440,9 @@ def test_workload_c1_full_chain():
     torch.cuda.synchronize()
     So = oracle.scores_meanpool_proj(x["q"], x["k"], wl.block, x["w"])
     rpo, cio = oracle.select(So, tb, wl.groups)
-    g_rows = csr_rows(rp.cpu().numpy(), ci.cpu().numpy())
+    rpg, cig = rp.cpu().numpy(), ci.cpu().numpy()
+    check_csr_valid(rpg, cig[:rpg[-1]], nB)
+    g_rows = csr_rows(rpg, cig)
     qb = np.tile(np.arange(nB), wl.B * wl.H)
     differ = check_selection(g_rows, csr_rows(rpo, cio), So.reshape(-1, nB), qb, tb, wl.groups)
     counts = np.diff(rpo)
@@ -376,7 +471,7 @@ def test_workload_arrow(name):
     np.testing.assert_array_equal(ci.cpu().numpy(), cio)
     comp_heads = [h for h in range(wl.H) if modes[h] != bsa.HEAD_SKIP]
     must = [(0, comp_heads[0], 0), (0, comp_heads[-1], nB - 1), (0, comp_heads[len(comp_heads) // 2], nB // 2)]
-    O, L = _workload_forward_check(wl, x, rpo, cio, 384, seed=170, must_blocks=must, modes=modes)
+    O, L = _workload_forward_check(wl, x, rpo, cio, None, seed=170, modes=modes)
     # the same forward with long rows split over several workgroups
     # the same forward with long rows split over several workgroups (forced:
     # the policy may judge a split not worth it for this workload)
@@ -404,13 +499,14 @@ def test_workload_c3_content_driven():
     Sg = S.cpu().numpy().astype(np.float64)
     assert np.all(np.abs(Sg - So) <= 1e-5 * np.abs(So).max(axis=-1, keepdims=True) + 1e-7)
     rpo, cio = oracle.select(So, tb, wl.groups)
-    rpg = rp.cpu().numpy()
-    g_rows = csr_rows(rpg, ci.cpu().numpy())
+    rpg, cig = rp.cpu().numpy(), ci.cpu().numpy()
+    check_csr_valid(rpg, cig[:rpg[-1]], nB)
+    g_rows = csr_rows(rpg, cig)
     qb = np.tile(np.arange(nB), wl.B * wl.H)
     differ = check_selection(g_rows, csr_rows(rpo, cio), So.reshape(-1, nB), qb, tb, wl.groups)
     _log(f"C3: {differ} of {len(qb)} rows differ only by near-ties")
     assert rpo[-1] == wl.B * wl.H * (tb * nB + (nB - tb) * (tb + 16))
-    _workload_forward_check(wl, x, rpo, cio, 512, seed=171, must_blocks=[(1, 15, 0), (0, 3, nB - 1)])
+    _workload_forward_check(wl, x, rpo, cio, None, seed=171)
     plan = {"chunk_blocks": 20, "max_chunks": 4, "max_split_rows": 128}
     _workload_forward_check(wl, x, rpo, cio, 512, seed=172, must_blocks=[(1, 15, 0), (0, 3, 1)], split=plan)
 
@@ -429,22 +525,33 @@ def test_workload_c5_exact_selection_and_forward():
     rpg, cig = rp.cpu().numpy(), ci.cpu().numpy()
     check_csr_valid(rpg, cig[:rpg[-1]], nB)
     assert np.all(np.diff(rpg) == 154)
-    # the oracle scores a sample of query-block rows exactly
+    # selection, every row, bit-exact: the oracle's top-k on the GPU's own fp32 scores
+    Sg_all = S.cpu().numpy()
+    rps, cis = oracle.select(Sg_all, tb, wl.groups)
+    np.testing.assert_array_equal(rpg, rps)
+    np.testing.assert_array_equal(cig[:rpg[-1]], cis)
+    # the exact scores of 256 query-block rows, 8 per head (the first, the
+    # last two and five seeded others), computed by the oracle in fp64
     r = np.random.default_rng(180)
-    rows = sorted(set(r.choice(wl.B * wl.H * nB, size=10, replace=False).tolist()) | {0, nB - 1, 31 * nB + 479})
+    rows = []
+    for bh in range(wl.B * wl.H):
+        own = {0, nB - 2, nB - 1} | set(r.choice(np.arange(1, nB - 2), size=5, replace=False).tolist())
+        rows += [bh * nB + i for i in sorted(own)]
+    assert len(rows) >= 256
     _log(f"C5: oracle exact scores for {len(rows)} query blocks")
     So = oracle.scores_exact_avgpool(x["q"], x["k"], wl.block, rows=rows)
-    Sg = S.cpu().numpy().reshape(-1, nB)[rows].astype(np.float64)
+    Sg = Sg_all.reshape(-1, nB)[rows].astype(np.float64)
     rel = np.abs(Sg - So) / np.abs(So).max(axis=-1, keepdims=True)
     assert rel.max() <= 2e-5, f"C5 exact score rel err {rel.max():.2e}"
     np.testing.assert_allclose(So.sum(-1) * wl.block, 1.0, rtol=1e-9)
+    # the GPU selection of those rows against the oracle's on its own fp64 scores
     qb = [row % nB for row in rows]
     rpo, cio = oracle.select_rows(So, qb, tb, wl.groups)
     g_rows = [cig[rpg[row]:rpg[row + 1]].tolist() for row in rows]
-    differ = check_selection(g_rows, csr_rows(rpo, cio), So, qb, tb, wl.groups)
-    _log(f"C5: {differ} of {len(rows)} sampled rows differ only by near-ties")
+    differ = check_selection(g_rows, csr_rows(rpo, cio), So, qb, tb, wl.groups, nB=nB)
+    _log(f"C5: {differ} of {len(rows)} scored rows differ only by near-ties")
     del S, qd, kd
     torch.cuda.empty_cache()
-    # forward on a generator-built block list of the same shape
-    rps, cis = synth.block_lists_with_counts(wl.B, wl.H, nB, wl.groups, tb, seed=181)
-    _workload_forward_check(wl, x, rps, cis, 256, seed=182, must_blocks=[(0, 7, 0), (0, 31, nB - 1)])
+    # the end-to-end chain: the forward on the GPU's own block list
+    _workload_forward_check(wl, x, rpg, cig[:rpg[-1]], 8192, seed=182,
+                            must_blocks=[(0, 7, 0), (0, 31, nB - 1), (0, 0, nB - 2)])
