@@ -4,13 +4,16 @@
 // Three small kernels:
 //  1. select: one wavefront per query-block row.  Text rows keep every
 //     column; other rows keep the text columns plus, per column group, the
-//     k best columns.  Each group is ranked by a bitonic sort inside the
-//     wavefront: up to 1024 64-bit keys, 16 per lane in registers, exchanged
-//     across lanes with shuffles for strides below 64 and within a lane
-//     above.  A key is (order-preserving bits of the score) << 32 | ~column,
-//     so a descending sort ranks larger scores first and, on equal scores,
-//     the lower column first; -0.0 is folded onto +0.0 before encoding.  The
-//     kept set is a per-row bitmask; its population count is the row length.
+//     k best columns.  Only the k-th best score of a group is needed, not a
+//     sorted order: each score becomes an order-preserving 32-bit key
+//     (-0.0 folded onto +0.0, NaN mapped below -inf), the group's keys sit in
+//     registers (lane l holds columns c + 64 e + l), and a bitwise search
+//     from the top bit finds the largest key T with at least k keys >= T --
+//     32 rounds of one compare and one ballot per register.  The row keeps
+//     every key above T and, of the keys equal to T, the lowest columns up
+//     to k (lane prefix counts of the equality ballots, taken in column
+//     order).  The kept set is a per-row bitmask in LDS; its population
+//     count is the row length.
 //  2. scan: one workgroup turns the row lengths into row_ptr in place.
 //  3. expand: one wavefront per row writes the set bits as ascending
 //     column indices at row_ptr[row].
@@ -23,80 +26,67 @@
 
 namespace bsa {
 
-__device__ __forceinline__ uint64_t score_key(float s, int col)
+// Order-preserving key of a score: larger score, larger key; -0.0 ranks
+// equal to +0.0; NaN ranks below every number (key 0, like padding).
+__device__ __forceinline__ uint32_t score_key(float s)
 {
-    if (s == 0.f) s = 0.f;   // -0.0 ranks equal to +0.0
+    if (s == 0.f) s = 0.f;
     uint32_t u = __float_as_uint(s);
     u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(col));
+    return (s != s) ? 0u : u;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
-{
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
+__device__ __forceinline__ int ballot_count(bool x) { return __popcll(__ballot(x)); }
 
-// Sort E*64 keys descending; element x = e*64 + lane lives in k[e] of that lane.
+// Keep the kk best columns of [c0, c1) (kk < c1 - c0): set their bits in the
+// row bitmask wbits.  Columns past c1 are padding with key 0 and the highest
+// columns, so they never reach the kept set.
 template <int E>
-__device__ __forceinline__ void wave_bitonic_desc(uint64_t (&k)[E])
+__device__ void select_group(const float *srow, int c0, int c1, int kk, uint32_t *wbits, int words)
 {
     const int lane = threadIdx.x & 63;
-    constexpr int P = E * 64;
-#pragma unroll
-    for (int size = 2; size <= P; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (stride >= 64) {
-                const int es = stride / 64;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int pe = e ^ es;
-                    if (pe > e) {
-                        const int x = e * 64 + lane;          // the lower index of the pair
-                        const bool desc = (x & size) == 0;
-                        const uint64_t a = k[e], bb = k[pe];
-                        const bool sw = desc ? (a < bb) : (a > bb);
-                        k[e] = sw ? bb : a;
-                        k[pe] = sw ? a : bb;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int x = e * 64 + lane;
-                    const uint64_t other = shfl_xor_u64(k[e], stride);
-                    const bool lower = (lane & stride) == 0;
-                    const bool desc = (x & size) == 0;
-                    const uint64_t mx = k[e] > other ? k[e] : other;
-                    const uint64_t mn = k[e] > other ? other : k[e];
-                    k[e] = (lower == desc) ? mx : mn;
-                }
-            }
-        }
-    }
-}
-
-template <int E>
-__device__ void select_group(const float *srow, int c0, int c1, int kk, uint32_t *wbits)
-{
-    const int lane = threadIdx.x & 63;
-    uint64_t key[E];
+    uint32_t key[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int col = c0 + e * 64 + lane;
-        key[e] = col < c1 ? score_key(srow[col], col) : 0ull;   // padding ranks last
+        key[e] = col < c1 ? score_key(srow[col]) : 0u;
     }
-    wave_bitonic_desc<E>(key);
+    // T = the kk-th largest key: the largest value with >= kk keys at or above it
+    uint32_t T = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) cnt += ballot_count(key[e] >= cand);
+        if (cnt >= kk) T = cand;
+    }
+    int need = kk;
+#pragma unroll
+    for (int e = 0; e < E; ++e) need -= ballot_count(key[e] > T);
+    // keys above T, then keys equal to T in column order until kk are kept
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const int x = e * 64 + lane;
-        if (x < kk) {
-            const int col = (int)(~static_cast<uint32_t>(key[e]));
-            atomicOr(&wbits[col >> 5], 1u << (col & 31));
+        const uint64_t eq = __ballot(key[e] == T);
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0));
+        const bool keep = key[e] > T || (key[e] == T && rank < need);
+        need -= __popcll(eq);
+        const uint64_t K = __ballot(keep);
+        // bits 0..63 of K stand for columns c0 + 64 e .. +63: or them into
+        // the (up to three) bitmask words they straddle
+        const int pos = c0 + e * 64, w0 = pos >> 5, sh = pos & 31;
+        const uint64_t lo = K << sh;
+        const uint32_t hi = sh ? (uint32_t)(K >> (64 - sh)) : 0u;
+        if (K != 0ull && lane < 3) {
+            const uint32_t v = lane == 0 ? (uint32_t)lo : lane == 1 ? (uint32_t)(lo >> 32) : hi;
+            if (v && w0 + lane < words) atomicOr(&wbits[w0 + lane], v);
         }
     }
+}
+
+// Keep every column of [c0, c1).
+__device__ void select_all(int c0, int c1, uint32_t *wbits)
+{
+    for (int col = c0 + (int)(threadIdx.x & 63); col < c1; col += 64) atomicOr(&wbits[col >> 5], 1u << (col & 31));
 }
 
 __global__ __launch_bounds__(64) void select_kernel(const SelectParams p)
@@ -121,13 +111,14 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectParams p)
             const int c0 = p.g_begin[g], c1 = p.g_end[g], kk = p.g_k[g];
             const int width = c1 - c0;
             if (kk <= 0) continue;
-            if (width <= 64) select_group<1>(srow, c0, c1, kk, wbits);
-            else if (width <= 128) select_group<2>(srow, c0, c1, kk, wbits);
-            else if (width <= 256) select_group<4>(srow, c0, c1, kk, wbits);
-            else if (width <= 512) select_group<8>(srow, c0, c1, kk, wbits);
-            else select_group<16>(srow, c0, c1, kk, wbits);
-            __syncthreads();
+            if (kk >= width) select_all(c0, c1, wbits);
+            else if (width <= 64) select_group<1>(srow, c0, c1, kk, wbits, p.words);
+            else if (width <= 128) select_group<2>(srow, c0, c1, kk, wbits, p.words);
+            else if (width <= 256) select_group<4>(srow, c0, c1, kk, wbits, p.words);
+            else if (width <= 512) select_group<8>(srow, c0, c1, kk, wbits, p.words);
+            else select_group<16>(srow, c0, c1, kk, wbits, p.words);
         }
+        __syncthreads();
     }
     if (p.direct) {
         // closed-form offsets: each head holds text_blocks rows of nB columns,

@@ -150,8 +150,9 @@ bsa_status bsa_score_grad(const bsa_tensor *q, const bsa_tensor *k, int32_t bloc
  *   - a text query block (i < text_blocks) keeps every key block;
  *   - otherwise it keeps the text key blocks {j < text_blocks} united with,
  *     for every group g, the k_g columns of [col_begin, col_end) with the
- *     largest scores; equal scores keep the lower column (-0.0 equals +0.0).
- * Columns are written ascending.  Scores must be finite.
+ *     largest scores; equal scores keep the lower column (-0.0 equals +0.0),
+ * and a NaN score ranks below every number (NaNs by lower column).
+ * Columns are written ascending.
  *
  * scores  : fp32 [B][H][nB][nB] device.   groups: host [n_groups].
  * row_ptr : int32 [B*H*nB + 1] device (written).

@@ -351,6 +351,29 @@ def test_select_matches_oracle(B, H, nB, tb, groups, ties):
     np.testing.assert_array_equal(ci.cpu().numpy()[:rp[-1]], cio)
 
 
+@pytest.mark.parametrize("B,H,nB,tb,groups", [
+    (1, 2, 68, 4, ((4, 68, 16),)),
+    (1, 2, 512, 0, ((0, 480, 144), (480, 512, 10))),
+    (1, 1, 300, 3, ((5, 300, 290), (0, 40, 7))),             # overlapping groups
+])
+def test_select_nan_and_infinite_scores(B, H, nB, tb, groups):
+    """NaN ranks below every number (-inf included), NaNs by lower column;
+    +-inf and NaN runs longer than a group's budget."""
+    S = synth.random_scores(B, H, nB, seed=145 + nB, tie_levels=2)
+    r = np.random.default_rng(146)
+    m = r.random(S.shape)
+    S[m < 0.15] = np.nan
+    S[(m >= 0.15) & (m < 0.2)] = -np.inf
+    S[(m >= 0.2) & (m < 0.22)] = np.inf
+    S[..., -1, :] = np.nan                    # a row of NaNs only
+    rp, ci = bsa.select_topk(torch.from_numpy(S).to(dev()), tb, groups)
+    torch.cuda.synchronize()
+    rpo, cio = oracle.select(S, tb, groups)
+    rp = rp.cpu().numpy()
+    np.testing.assert_array_equal(rp, rpo)
+    np.testing.assert_array_equal(ci.cpu().numpy()[:rp[-1]], cio)
+
+
 # ---------------------------------------------------------------------------
 # block scores
 # ---------------------------------------------------------------------------
