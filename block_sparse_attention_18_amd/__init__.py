@@ -117,6 +117,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         sig = {
             "bsa_pool_scores_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32, I32]),
             "bsa_pool_scores": (I32, [TP, TP, I32, I32, V, I32, F, V, V, SZ, V]),
+            "bsa_pool_scores_noalloc": (I32, [TP, TP, I32, I32, V, I32, F, V, V]),
             "bsa_score_grad_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32]),
             "bsa_score_grad": (I32, [TP, TP, I32, V, I32, V, V, V, V, V, SZ, V]),
             "bsa_select_capacity": (I64, [I64, I64, I32, I32, GP, I32]),
@@ -234,6 +235,28 @@ def pool_scores(q: torch.Tensor, k: torch.Tensor, block: int, mode: int = SCORE_
     _check(lib.bsa_pool_scores(ctypes.byref(dq), ctypes.byref(dk), block, mode, _ptr(w), r,
                                float(scale or 0.0), _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return out
+
+
+def pool_scores_noalloc(q: torch.Tensor, k: torch.Tensor, block: int, mode: int = SCORE_MEANPOOL_PROJ,
+                        w: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pool_scores through bsa_pool_scores_noalloc: the library's static
+    per-device scratch replaces the workspace (for callers that cannot
+    allocate; pass `out` to allocate nothing here either)."""
+    lib = load()
+    B, H, N, D = q.shape
+    nB = n_blocks(N, block)
+    r = 0
+    if mode == SCORE_MEANPOOL_PROJ:
+        if w is None or w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 2:
+            raise ValueError("w must be a contiguous fp32 [D, r] device tensor")
+        r = int(w.shape[1])
+    if out is None:
+        out = torch.empty((B, H, nB, nB), dtype=torch.float32, device=q.device)
+    dq, dk = _desc(q, "q"), _desc(k, "k")
+    _check(lib.bsa_pool_scores_noalloc(ctypes.byref(dq), ctypes.byref(dk), block, mode, _ptr(w), r,
+                                       float(scale or 0.0), _ptr(out), _stream(q.device)))
     return out
 
 

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "bsa.h"
 #include "internal.h"
@@ -233,6 +234,73 @@ bsa_status bsa_pool_scores(const bsa_tensor *q, const bsa_tensor *k, int32_t blo
     if ((e = bsa::launch_exact_scores(ep, block, (int)q->D, (int)slots, s)) != hipSuccess)
         return hip_fail(e, "exact score launch");
     return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Block scores without a caller workspace, for callers that cannot allocate.
+// The workspace is a file-scope device array; host code only ever uses the
+// address hipGetSymbolAddress returns for it on each device (the array's
+// name is a host-side stand-in, not a device address).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[BSA_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices];   // per device, resolved on its first call
+
+// The current device's copy of the scratch array (resolved once per device,
+// with that device current).
+bsa_status device_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(BSA_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev, kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(BSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return BSA_OK;
+}
+}  // namespace
+
+bsa_status bsa_pool_scores_noalloc(const bsa_tensor *q, const bsa_tensor *k, int32_t block, int32_t mode,
+                                   const float *w, int32_t r, float scale, float *scores, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    size_t bytes = 0;
+    if (mode == BSA_SCORE_MEANPOOL_PROJ) {
+        if (r < 1 || r > 64) return fail(BSA_ERR_INVALID_ARG, "projection width r=%d outside 1..64", r);
+        bytes = bsa_pool_scores_workspace_size(q->B, q->H, q->N, q->D, block, mode, r);
+        if (bytes > BSA_SCRATCH_BYTES)
+            return fail(BSA_ERR_WORKSPACE,
+                        "needs %zu bytes of scratch, above the %u this entry point holds per device "
+                        "(use bsa_pool_scores with a workspace)", bytes, (unsigned)BSA_SCRATCH_BYTES);
+    } else if (mode == BSA_SCORE_EXACT_AVGPOOL) {
+        const size_t slot = exact_slot_bytes(ceil_div(q->N, block), block);
+        if (slot > BSA_SCRATCH_BYTES)
+            return fail(BSA_ERR_WORKSPACE,
+                        "one exact-score slot needs %zu bytes, above the %u of scratch this entry point "
+                        "holds per device (use bsa_pool_scores with a workspace)", slot,
+                        (unsigned)BSA_SCRATCH_BYTES);
+        // as many slots as the scratch holds, up to what bsa_pool_scores would use
+        const size_t full = bsa_pool_scores_workspace_size(q->B, q->H, q->N, q->D, block, mode, r);
+        bytes = std::min<size_t>(full, (BSA_SCRATCH_BYTES / slot) * slot);
+    } else {
+        return fail(BSA_ERR_UNSUPPORTED, "unknown scoring mode %d", mode);
+    }
+    void *ws = nullptr;
+    if ((st = device_scratch(&ws)) != BSA_OK) return st;
+    return bsa_pool_scores(q, k, block, mode, w, r, scale, scores, ws, bytes, stream);
 }
 
 static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }

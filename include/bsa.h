@@ -15,7 +15,8 @@
  * "host" (head modes, windows, groups) are read during the call only.  The
  * library allocates and frees nothing and keeps no mutable global state, so
  * calls are reentrant; calls that share output buffers must be ordered by
- * the caller.
+ * the caller.  The one exception is bsa_pool_scores_noalloc, whose
+ * workspace is a static per-device scratch array shared by its calls.
  *
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Every
  * call only enqueues work on it and never synchronises.  Device-side faults
@@ -113,6 +114,28 @@ bsa_status bsa_pool_scores(const bsa_tensor *q, const bsa_tensor *k, int32_t blo
                            int32_t mode, const float *w, int32_t r, float scale,
                            float *scores, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_pool_scores_noalloc -- bsa_pool_scores for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments and results as
+ * bsa_pool_scores, without the workspace: the library's own static scratch
+ * array of BSA_SCRATCH_BYTES (32 MiB) per device serves instead.  It is
+ * resolved once per device, on that device's first call, and held until
+ * the process ends; nothing is allocated or freed.  MEANPOOL_PROJ needs
+ * 8*B*H*nB*r bytes of it; EXACT_AVGPOOL needs one slot of 4*nB*block bytes
+ * and runs with as many slots as fit (the same scores, possibly fewer
+ * persistent workgroups than bsa_pool_scores with a large workspace).
+ * Larger requests fail with BSA_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one device shares that device's scratch and leaves it
+ * holding its own intermediate values: calls that overlap in time on one
+ * device (different streams or host threads) race and must be ordered by
+ * the caller.  No part of the scratch needs to start at zero: every byte a
+ * call reads it has written first.
+ * ---------------------------------------------------------------------- */
+#define BSA_SCRATCH_BYTES (32u << 20)
+bsa_status bsa_pool_scores_noalloc(const bsa_tensor *q, const bsa_tensor *k, int32_t block, int32_t mode,
+                                   const float *w, int32_t r, float scale, float *scores, void *stream);
 
 /* ------------------------------------------------------------------------
  * bsa_score_grad -- gradient of the BSA_SCORE_MEANPOOL_PROJ score ([W] 2.2:

@@ -402,3 +402,20 @@ def test_row_split_policy_reads_row_lengths():
     # uniform rows: nothing to split
     rp_u = [3 * r for r in range(BH * nB + 1)]
     assert bsa.row_split_policy(rp_u, 1, BH, nB, 128) is None
+
+
+@pytest.mark.parametrize("mode,N,D,block,r", [
+    (0, 65536, 128, 64, 64),         # projections: 2 * 4 * 32 * 1024 * 64 * 4 bytes > 32 MiB
+    (1, 1 << 24, 64, 128, 0),        # one exact-score slot: 131072 * 128 * 4 bytes > 32 MiB
+])
+def test_pool_scores_noalloc_rejects_requests_beyond_its_scratch(mode, N, D, block, r):
+    """Checked before the scratch is resolved or anything is enqueued, so no
+    GPU is needed."""
+    lib = bsa.load()
+    q = _t(B=4, H=32, N=N, D=D)
+    k = _t(B=4, H=32, N=N, D=D)
+    st = lib.bsa_pool_scores_noalloc(ctypes.byref(q), ctypes.byref(k), block, mode,
+                                     ctypes.c_void_p(FAKE) if r else None, r, 0.0,
+                                     ctypes.c_void_p(FAKE), None)
+    assert st == 4
+    assert "scratch" in _err()
