@@ -6,7 +6,9 @@ synthetic input already resident in HBM: the arrow block layout
 (bsa_build_arrow_layout) followed by the block-sparse forward (bsa_forward)
 for the 2K MMDiT shape (B=1, H=24, N=16896 = 512 text + 128x128 image
 tokens, D=128, block 128, arrow window 8 on every head).  Content-driven
-workloads (--workload C1/C3/C5) run pool_scores + select_topk + forward.
+workloads (--workload C1/C3/C5) run the block selection (mean-pool scoring
+fused with top-k in one call where it applies, else pool_scores +
+select_topk) + forward.
 
 Prints ONE JSON line.  `value` is the actual (kept-block) TFLOP/s of the
 step; the dense-equivalent rate, the fraction of the bf16 MFMA peak, the
@@ -99,6 +101,9 @@ def main():
                     help="only run the forward-time sweep over the top-k budget on a content-driven "
                          "workload (C3: k of the 64 image key blocks; C5: the fraction rho of each "
                          "column group) with a least-squares fit")
+    ap.add_argument("--unfused", action="store_true",
+                    help="content-driven mean-pool workloads: score (bsa_pool_scores) and select "
+                         "(bsa_select_topk) in two calls instead of the fused bsa_select_meanpool")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the kept-pairs sweep of the forward at the C4 shape "
                          "(arrow windows 0..127 and all-FULL) with a least-squares fit")
@@ -254,17 +259,27 @@ def main():
         ws_sel = torch.empty(max(int(bsa.load().bsa_select_workspace_size(B, H, nB)), 16),
                              dtype=torch.uint8, device=dev)
 
-        def layout(mark=None):
-            bsa.pool_scores(q, k, block, wl.score_mode, w=w, out=scores, workspace=ws_s)
-            if mark is not None:
-                mark()
-            bsa.select_topk(scores, wl.text_blocks, wl.groups, row_ptr=row_ptr, col_idx=col_idx,
-                            workspace=ws_sel)
-        layout_parts = ("pool_scores", "select")
+        fused = (wl.score_mode == synth.SCORE_MEANPOOL_PROJ and not args.unfused and
+                 bsa.select_meanpool_applies(nB, wl.r, wl.text_blocks, wl.groups))
+        if fused:
+            ws_f = bsa.select_meanpool_workspace(B, H, N, block, wl.r, dev)
+
+            def layout(mark=None):
+                bsa.select_meanpool(q, k, block, w, wl.text_blocks, wl.groups, row_ptr=row_ptr,
+                                    col_idx=col_idx, workspace=ws_f)
+            layout_parts = ("select_meanpool",)
+        else:
+            def layout(mark=None):
+                bsa.pool_scores(q, k, block, wl.score_mode, w=w, out=scores, workspace=ws_s)
+                if mark is not None:
+                    mark()
+                bsa.select_topk(scores, wl.text_blocks, wl.groups, row_ptr=row_ptr, col_idx=col_idx,
+                                workspace=ws_sel)
+            layout_parts = ("pool_scores", "select")
         fwd_kw = {}
         computed_heads = B * H
         split = bsa.select_split_policy(B, H, nB, wl.text_blocks, wl.groups, block=block)
-    if args.no_split or args.fp8:
+    if args.no_split or (args.fp8 and wl.layout == "neighborhood"):
         split = None
     if split is not None:   # workspace allocated once, outside the timed region
         split["workspace"] = torch.empty(
@@ -274,10 +289,6 @@ def main():
 
     quant = None
     if args.fp8:
-        if "head_modes" in fwd_kw and np.any(fwd_kw["head_modes"] == bsa.HEAD_SKIP):
-            print("the FP8 forward computes every head: pick a workload without SKIP heads",
-                  file=sys.stderr)
-            sys.exit(2)
         if wl.layout == "neighborhood":
             layout()                      # (permuted runs: the tile-major Q, K, V that are quantised)
         qnb = nb if nb_natural else None  # natural-order inputs, tile-major codes
@@ -291,7 +302,7 @@ def main():
                                              natural=nb_natural)
         else:
             def forward():
-                bsa.forward_fp8(qkv8, block, row_ptr, col_idx, out=out, lse=lse)
+                bsa.forward_fp8(qkv8, block, row_ptr, col_idx, out=out, lse=lse, **fwd_kw)
 
         def quantize():
             bsa.quantize_fp8(q, k, v, out=qkv8, workspace=ws_q, nb=qnb)
@@ -365,7 +376,7 @@ def main():
     cold = None
     if wl.layout == "select":
         cold = cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr,
-                                 wl.score_mode == synth.SCORE_EXACT_AVGPOOL)
+                                 wl.score_mode == synth.SCORE_EXACT_AVGPOOL, fused=len(layout_parts) == 1)
 
     value = actual_flop / (ms_step * 1e-3) / 1e12
     achieved = actual_flop / (fwd_avg * 1e-3) / 1e12
@@ -404,8 +415,7 @@ def main():
         "forward_ms": round(fwd_avg, 4),
         "forward_ms_p10_p50_p90": [round(float(np.percentile(fwd_ms, q_)), 4) for q_ in (10, 50, 90)],
         "layout_ms": {k2: round(v2, 4) for k2, v2 in part_ms.items()},
-        "scoring_ratio": (round((part_ms["pool_scores"] + part_ms["select"]) / fwd_avg, 4)
-                          if "pool_scores" in part_ms else None),
+        "scoring_ratio": (round(sum(part_ms.values()) / fwd_avg, 4) if wl.layout == "select" else None),
         "permute_out_ms": None if post_ms is None else round(post_ms, 4),
         "token_pairs": token_pairs,
         "token_level_tflops": (None if token_pairs is None else
@@ -446,14 +456,30 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr, exact: bool, iters: int = 10):
+def cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr, exact: bool, iters: int = 10,
+                      fused: bool = False):
     """pool_scores and select timed with a 512 MB scratch write before every
     call, so the 256 MB last-level cache does not serve their inputs.  Rates
     against the algorithmic work: mean-pool scores are HBM-bound (Q and K
     read once); exact scores are MFMA-bound (one Q K^T over all pairs, plus
     one exp per pair); select reads the score matrix once and writes the
-    CSR once."""
+    CSR once.  The fused mean-pool selection is one call: its rate counts Q
+    and K read once."""
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    if fused:
+        t = []
+        for _ in range(iters):
+            scratch.fill_(1)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            layout()
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            t.append(e[0].elapsed_time(e[1]))
+        ms = float(np.median(t))
+        return {"select_meanpool_ms": round(ms, 4),
+                "qk_read_GBps": round(2.0 * B * H * N * D * 2 / (ms * 1e-3) / 1e9, 1),
+                "hbm_peak_GBps": PEAK_HBM_GBS}
     pool, sel = [], []
     for _ in range(iters):
         scratch.fill_(1)

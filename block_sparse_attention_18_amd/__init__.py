@@ -118,6 +118,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_pool_scores_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32, I32]),
             "bsa_pool_scores": (I32, [TP, TP, I32, I32, V, I32, F, V, V, SZ, V]),
             "bsa_pool_scores_noalloc": (I32, [TP, TP, I32, I32, V, I32, F, V, V]),
+            "bsa_select_meanpool_workspace_size": (SZ, [I64, I64, I64, I32, I32]),
+            "bsa_select_meanpool": (I32, [TP, TP, I32, V, I32, I32, GP, I32, V, V, V, I64, V, SZ, V]),
             "bsa_score_grad_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32]),
             "bsa_score_grad": (I32, [TP, TP, I32, V, I32, V, V, V, V, V, SZ, V]),
             "bsa_select_capacity": (I64, [I64, I64, I32, I32, GP, I32]),
@@ -130,7 +132,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_forward_split_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32, I64]),
             "bsa_quantize_fp8_workspace_size": (SZ, [I64, I64, I64, I64]),
             "bsa_quantize_fp8": (I32, [TP, TP, TP, ctypes.POINTER(BsaFp8Qkv), V, SZ, V]),
-            "bsa_forward_fp8": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, F, TP, V, V]),
+            "bsa_forward_fp8": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, V, TP, V, F, TP, V,
+                                      ctypes.POINTER(BsaSplit), V]),
             "bsa_forward_fp8_neighborhood": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, V,
                                                    ctypes.POINTER(BsaNeighborhood), F, TP, V, V]),
             "bsa_forward_fp8_neighborhood_natural": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, V,
@@ -328,6 +331,58 @@ def select_topk(scores: torch.Tensor, text_blocks: int, groups: Sequence[Tuple[i
     _check(lib.bsa_select_topk(_ptr(scores), B, H, nB, text_blocks, arr, ng, _ptr(row_ptr),
                                _ptr(col_idx), col_idx.numel(), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(dev)))
+    return row_ptr, col_idx
+
+
+MPS_MAX_BLOCKS, MPS_MAX_PROJ = 256, 4096
+
+
+def select_meanpool_applies(nB: int, r: int, text_blocks: int, groups) -> bool:
+    """Whether bsa_select_meanpool takes this shape: nB <= 256, nB * r <= 4096,
+    the groups with k > 0 pairwise disjoint and clear of the text columns."""
+    if nB > MPS_MAX_BLOCKS or nB * r > MPS_MAX_PROJ or not 1 <= r <= 64:
+        return False
+    live = sorted((int(g[0]), int(g[1])) for g in groups if int(g[2]) > 0)
+    if any(c0 < text_blocks for (c0, _) in live):
+        return False
+    return all(b0 >= a1 for (_, a1), (b0, _) in zip(live, live[1:]))
+
+
+def select_meanpool_workspace(B: int, H: int, N: int, block: int, r: int, device) -> torch.Tensor:
+    """A workspace for select_meanpool (the projected blocks)."""
+    n = int(load().bsa_select_meanpool_workspace_size(B, H, N, block, r))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def select_meanpool(q: torch.Tensor, k: torch.Tensor, block: int, w: torch.Tensor, text_blocks: int,
+                    groups: Sequence[Tuple[int, int, int]], scores: Optional[torch.Tensor] = None,
+                    row_ptr: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Mean-pool scores and top-k selection in one call (bsa_select_meanpool):
+    returns the CSR (row_ptr, col_idx); the scores go to `scores` when given
+    (fp32 [B, H, nB, nB]).  A missing workspace is allocated here."""
+    lib = load()
+    B, H, N, D = q.shape
+    nB = n_blocks(N, block)
+    if w is None or w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 2:
+        raise ValueError("w must be a contiguous fp32 [D, r] device tensor")
+    r = int(w.shape[1])
+    if scores is not None and (scores.dtype != torch.float32 or not scores.is_contiguous()
+                               or tuple(scores.shape) != (B, H, nB, nB)):
+        raise ValueError("scores must be a contiguous fp32 [B, H, nB, nB] device tensor")
+    arr, ng = _groups(groups)
+    cap = int(lib.bsa_select_capacity(B, H, nB, text_blocks, arr, ng))
+    dev = q.device
+    if row_ptr is None:
+        row_ptr = torch.empty(B * H * nB + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = select_meanpool_workspace(B, H, N, block, r, dev)
+    dq, dk = _desc(q, "q"), _desc(k, "k")
+    _check(lib.bsa_select_meanpool(ctypes.byref(dq), ctypes.byref(dk), block, _ptr(w), r, text_blocks, arr, ng,
+                                   _ptr(scores), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(dev)))
     return row_ptr, col_idx
 
 
@@ -595,26 +650,44 @@ def quantize_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: Optiona
 
 def forward_fp8(qkv: Fp8QKV, block: int, row_ptr: torch.Tensor, col_idx: torch.Tensor,
                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None,
-                return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Block-sparse attention forward on E4M3 operands.  Returns (O bf16, LSE fp32)."""
+                lse: Optional[torch.Tensor] = None, return_lse: bool = True, head_modes=None,
+                o_cache: Optional[torch.Tensor] = None, lse_cache: Optional[torch.Tensor] = None,
+                split: Optional[dict] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Block-sparse attention forward on E4M3 operands.  Returns (O bf16, LSE fp32).
+    head_modes / o_cache / lse_cache / split as for forward()."""
     lib = load()
     B, H, N, D = qkv.shape
     dev = qkv.q8.device
     if out is None:
         out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    modes = None if head_modes is None else _host_i8(head_modes, H)
     if lse is None and return_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        if modes is not None and lse_cache is None and any(m == HEAD_SKIP for m in modes):
+            lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
+        else:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    if lse_cache is not None and (lse_cache.dtype != torch.float32 or not lse_cache.is_contiguous()):
+        raise ValueError("lse_cache must be a contiguous fp32 [B, H, N] tensor")
     for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 device tensor")
     if col_idx.numel() == 0:
         col_idx = torch.zeros(1, dtype=torch.int32, device=row_ptr.device)
-    d8, do = qkv.desc(), _desc(out, "out")
-    _check(lib.bsa_forward_fp8(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx), float(scale or 0.0),
-                               ctypes.byref(do), _ptr(lse), _stream(dev)))
+    d8, do, dc = qkv.desc(), _desc(out, "out"), _desc(o_cache, "o_cache")
+    sp = None
+    if split is not None:
+        ws = split.get("workspace")
+        if ws is None:
+            need = split_workspace_size(B, H, N, D, block, split["max_chunks"], split["max_split_rows"])
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            split["workspace"] = ws
+        sp = BsaSplit(int(split["chunk_blocks"]), int(split["max_chunks"]), int(split["max_split_rows"]),
+                      ws.data_ptr(), ws.numel() * ws.element_size())
+    _check(lib.bsa_forward_fp8(ctypes.byref(d8), block, _ptr(row_ptr), _ptr(col_idx), modes, _ref(dc),
+                               _ptr(lse_cache), float(scale or 0.0), ctypes.byref(do), _ptr(lse),
+                               None if sp is None else ctypes.byref(sp), _stream(dev)))
     return out, lse
 
 

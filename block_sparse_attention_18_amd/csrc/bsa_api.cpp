@@ -370,6 +370,89 @@ bsa_status bsa_score_grad(const bsa_tensor *q, const bsa_tensor *k, int32_t bloc
 }
 
 // ---------------------------------------------------------------------------
+// Fused content-driven selection (mean-pool, projection, scores, top-k)
+// ---------------------------------------------------------------------------
+size_t bsa_select_meanpool_workspace_size(int64_t B, int64_t H, int64_t N, int32_t block, int32_t r)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || !block_ok(block) || r < 1 || r > 64) return 0;
+    const size_t bh = (size_t)(B * H), nB = (size_t)ceil_div(N, block);
+    return up256(bh * nB * (size_t)r * sizeof(float)) + bh * nB * (size_t)r * sizeof(float);
+}
+
+bsa_status bsa_select_meanpool(const bsa_tensor *q, const bsa_tensor *k, int32_t block, const float *w, int32_t r,
+                               int32_t text_blocks, const bsa_group *groups, int32_t n_groups, float *scores,
+                               int32_t *row_ptr, int32_t *col_idx, int64_t capacity, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    bsa_status st;
+    if ((st = check_tensor(q, "q")) != BSA_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSA_OK) return st;
+    if (!same_shape(q, k)) return fail(BSA_ERR_INVALID_ARG, "q and k shapes differ");
+    if (!block_ok(block)) return fail(BSA_ERR_UNSUPPORTED, "block size %d not supported", block);
+    if (!w || !row_ptr || !col_idx) return fail(BSA_ERR_INVALID_ARG, "w, row_ptr or col_idx null");
+    if (r < 1 || r > 64) return fail(BSA_ERR_INVALID_ARG, "projection width r=%d outside 1..64", r);
+    const int64_t nB = ceil_div(q->N, block);
+    if (nB > bsa::kMpsMaxBlocks || nB * r > bsa::kMpsMaxProj)
+        return fail(BSA_ERR_UNSUPPORTED,
+                    "fused selection holds at most %d blocks and %d projection values per head (nB=%lld, r=%d); "
+                    "use bsa_pool_scores and bsa_select_topk", bsa::kMpsMaxBlocks, bsa::kMpsMaxProj,
+                    (long long)nB, r);
+    if (q->B * q->H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many blocks");
+    if (text_blocks < 0 || text_blocks > nB)
+        return fail(BSA_ERR_INVALID_ARG, "text_blocks %d outside [0, %lld]", text_blocks, (long long)nB);
+    if (n_groups < 0 || n_groups > 8) return fail(BSA_ERR_UNSUPPORTED, "at most 8 groups");
+    if (n_groups > 0 && !groups) return fail(BSA_ERR_INVALID_ARG, "groups is null");
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const bsa_group &x = groups[g];
+        if (x.col_begin < 0 || x.col_end > nB || x.col_begin >= x.col_end || x.k < 0 || x.k > x.col_end - x.col_begin)
+            return fail(BSA_ERR_INVALID_ARG, "group %d = [%d, %d) k=%d invalid for %lld blocks", g, x.col_begin,
+                        x.col_end, x.k, (long long)nB);
+        if (x.k == 0) continue;
+        if (x.col_begin < text_blocks)
+            return fail(BSA_ERR_UNSUPPORTED, "fused selection needs groups clear of the text columns; "
+                                             "use bsa_pool_scores and bsa_select_topk");
+        for (int32_t h = g + 1; h < n_groups; ++h) {
+            const bsa_group &y = groups[h];
+            if (y.k > 0 && x.col_begin < y.col_end && y.col_begin < x.col_end)
+                return fail(BSA_ERR_UNSUPPORTED, "fused selection needs disjoint groups; "
+                                                 "use bsa_pool_scores and bsa_select_topk");
+        }
+    }
+    const int64_t need = bsa_select_capacity(q->B, q->H, (int32_t)nB, text_blocks, groups, n_groups);
+    if (need >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "nnz bound exceeds int32");
+    if (capacity < need)
+        return fail(BSA_ERR_CAPACITY, "capacity %lld below bound %lld", (long long)capacity, (long long)need);
+    const size_t ws = bsa_select_meanpool_workspace_size(q->B, q->H, q->N, block, r);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < ws)
+        return fail(BSA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned)", ws);
+
+    const size_t bh = (size_t)(q->B * q->H);
+    char *wsp = static_cast<char *>(workspace);
+    bsa::MeanpoolSelectParams mp{};
+    mp.q = t4(q);
+    mp.k = t4(k);
+    mp.w = w;
+    mp.proj_q = reinterpret_cast<float *>(wsp);
+    mp.proj_kt = reinterpret_cast<float *>(wsp + up256(bh * nB * r * sizeof(float)));
+    mp.scores = scores;
+    mp.row_ptr = row_ptr;
+    mp.col_idx = col_idx;
+    mp.capacity = capacity;
+    mp.B = (int32_t)q->B; mp.H = (int32_t)q->H; mp.N = (int32_t)q->N; mp.nB = (int32_t)nB; mp.r = r;
+    mp.text_blocks = text_blocks;
+    mp.n_groups = n_groups;
+    mp.row_len = (int32_t)select_row_bound(nB, text_blocks, groups, n_groups);
+    for (int32_t g = 0; g < n_groups; ++g) {
+        mp.g_begin[g] = groups[g].col_begin;
+        mp.g_end[g] = groups[g].col_end;
+        mp.g_k[g] = groups[g].k;
+    }
+    hipError_t e = bsa::launch_meanpool_select(mp, block, (int)q->D, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "mean-pool selection launch");
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
 int64_t bsa_select_capacity(int64_t B, int64_t H, int32_t n_blocks, int32_t text_blocks,
                             const bsa_group *groups, int32_t n_groups)
 {
@@ -541,6 +624,142 @@ size_t bsa_forward_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t
     return split_layout(rows, block, D, max_chunks, std::min(max_split_rows, rows)).total;
 }
 
+// Head modes of a forward call: the SKIP bitmask (o_cache then required,
+// with the output's shape).
+static bsa_status parse_head_modes(const int8_t *head_modes, int64_t H, const bsa_tensor *o_cache,
+                                   const bsa_tensor *o, uint32_t *skip_bits, bool *any_skip)
+{
+    *any_skip = false;
+    if (H > bsa::kMaxSkipHeads) return fail(BSA_ERR_UNSUPPORTED, "H above %d", bsa::kMaxSkipHeads);
+    if (head_modes) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int8_t m = head_modes[h];
+            if (m != BSA_HEAD_FULL && m != BSA_HEAD_ARROW && m != BSA_HEAD_SKIP)
+                return fail(BSA_ERR_INVALID_ARG, "head %lld: unknown mode %d", (long long)h, m);
+            if (m == BSA_HEAD_SKIP) {
+                skip_bits[h >> 5] |= 1u << (h & 31);
+                *any_skip = true;
+            }
+        }
+    }
+    if (*any_skip) {
+        bsa_status st;
+        if ((st = check_tensor(o_cache, "o_cache")) != BSA_OK) return st;
+        if (!same_shape(o, o_cache)) return fail(BSA_ERR_INVALID_ARG, "o_cache shape differs");
+    }
+    return BSA_OK;
+}
+
+// Long-row splitting of a forward call: validates the request, launches the
+// plan kernel and returns the work list and partial-result slots for the
+// forward kernel, and the launch size.
+struct SplitRun {
+    const int4 *items = nullptr;
+    const int32_t *counts = nullptr;
+    float *partials = nullptr;
+    const int2 *split_rows = nullptr;
+    int32_t max_chunks = 0;
+    int64_t n_split_rows = 0;
+    int64_t grid = 0;
+};
+
+static bsa_status split_begin(const bsa_split *split, int64_t BH, int64_t nB, int32_t block, int64_t D,
+                              SplitRun *run)
+{
+    const int64_t rows = BH * nB;
+    run->grid = rows;
+    if (!split) return BSA_OK;
+    if (split->chunk_blocks < 1 || split->max_chunks < 2 || split->max_chunks > 64 || split->max_split_rows < 1)
+        return fail(BSA_ERR_INVALID_ARG,
+                    "split: chunk_blocks >= 1, max_chunks in 2..64 and max_split_rows >= 1 required");
+    const int64_t split_rows = std::min<int64_t>(split->max_split_rows, rows);
+    const SplitLayout sl = split_layout(rows, block, D, split->max_chunks, split_rows);
+    if (!split->workspace || !aligned16(split->workspace) || split->workspace_bytes < sl.total)
+        return fail(BSA_ERR_WORKSPACE, "split workspace needs %zu bytes (16-byte aligned)", sl.total);
+    const int64_t grid = rows + split_rows * (split->max_chunks - 1);
+    if (grid >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "split work list too long");
+    char *ws = static_cast<char *>(split->workspace);
+    run->items = reinterpret_cast<const int4 *>(ws + sl.items);
+    run->counts = reinterpret_cast<const int32_t *>(ws);
+    run->partials = reinterpret_cast<float *>(ws + sl.partials);
+    run->split_rows = reinterpret_cast<const int2 *>(ws + sl.split_rows);
+    run->max_chunks = split->max_chunks;
+    run->n_split_rows = split_rows;
+    run->grid = grid;
+    return BSA_OK;
+}
+
+static bsa_status split_plan(const SplitRun &run, const int32_t *row_ptr, int64_t BH, int64_t H, int64_t nB,
+                             const bsa_split *split, const uint32_t *skip_bits, hipStream_t s)
+{
+    bsa::PlanParams pp{};
+    pp.row_ptr = row_ptr;
+    pp.items = const_cast<int4 *>(run.items);
+    pp.counts = const_cast<int32_t *>(run.counts);
+    pp.split_rows = const_cast<int2 *>(run.split_rows);
+    pp.BH = (int32_t)BH;
+    pp.H = (int32_t)H;
+    pp.nB = (int32_t)nB;
+    std::memcpy(pp.skip_bits, skip_bits, sizeof pp.skip_bits);
+    pp.chunk_blocks = split->chunk_blocks;
+    pp.max_chunks = split->max_chunks;
+    pp.max_split_rows = run.n_split_rows;
+    hipError_t e = bsa::launch_plan(pp, s);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    return BSA_OK;
+}
+
+static bsa_status split_combine(const SplitRun &run, const bsa_tensor *o, float *lse, int64_t H, int64_t N, int64_t nB,
+                                int64_t D, int32_t block, int natural, const bsa::NbGeom *nb, hipStream_t s)
+{
+    bsa::CombineParams cp{};
+    cp.partials = run.partials;
+    cp.counts = run.counts;
+    cp.split_rows = run.split_rows;
+    cp.o = static_cast<uint16_t *>(o->data);
+    cp.o_sb = o->stride_b;
+    cp.o_sh = o->stride_h;
+    cp.o_sn = o->stride_n;
+    cp.lse = lse;
+    cp.H = (int32_t)H;
+    cp.N = (int32_t)N;
+    cp.nB = (int32_t)nB;
+    cp.D = (int32_t)D;
+    cp.block = block;
+    cp.max_chunks = run.max_chunks;
+    cp.natural = natural;
+    if (nb) cp.nb = *nb;
+    hipError_t e = bsa::launch_combine(cp, run.n_split_rows, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return BSA_OK;
+}
+
+// SKIP heads: O (and LSE when a cache is given) copied from the caches.
+static bsa_status skip_heads_copy(const bsa_tensor *o_cache, const float *lse_cache, const bsa_tensor *o, float *lse,
+                                  const uint32_t *skip_bits, hipStream_t s)
+{
+    bsa::SkipCopyParams cp{};
+    cp.src = t4(o_cache);
+    cp.dst = static_cast<uint16_t *>(o->data);
+    cp.d_sb = o->stride_b;
+    cp.d_sh = o->stride_h;
+    cp.d_sn = o->stride_n;
+    cp.lse_src = lse_cache;
+    cp.lse_dst = lse;
+    cp.B = (int32_t)o->B;
+    cp.H = (int32_t)o->H;
+    cp.N = (int32_t)o->N;
+    cp.D = (int32_t)o->D;
+    cp.copy_o = !(o_cache->data == o->data && o_cache->stride_b == o->stride_b &&
+                  o_cache->stride_h == o->stride_h && o_cache->stride_n == o->stride_n);
+    std::memcpy(cp.skip_bits, skip_bits, sizeof cp.skip_bits);
+    if (cp.copy_o || (lse_cache && lse && lse_cache != lse)) {
+        hipError_t e = bsa::launch_skip_copy(cp, s);
+        if (e != hipSuccess) return hip_fail(e, "skip copy launch");
+    }
+    return BSA_OK;
+}
+
 static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,
                                const int32_t *row_ptr, const int32_t *col_idx, const int8_t *head_modes,
                                const bsa_tensor *o_cache, const float *lse_cache, float scale,
@@ -558,27 +777,15 @@ static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const b
     if (!row_ptr || !col_idx) return fail(BSA_ERR_INVALID_ARG, "row_ptr / col_idx null");
     if (std::isnan(scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
     const int64_t H = q->H;
-    if (H > bsa::kMaxSkipHeads) return fail(BSA_ERR_UNSUPPORTED, "H above %d", bsa::kMaxSkipHeads);
     const int64_t nB = ceil_div(q->N, block);
     if (q->B * H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many query blocks");
 
     bsa::FwdParams fp{};
     bool any_skip = false;
-    if (head_modes) {
-        for (int64_t h = 0; h < H; ++h) {
-            const int8_t m = head_modes[h];
-            if (m != BSA_HEAD_FULL && m != BSA_HEAD_ARROW && m != BSA_HEAD_SKIP)
-                return fail(BSA_ERR_INVALID_ARG, "head %lld: unknown mode %d", (long long)h, m);
-            if (m == BSA_HEAD_SKIP) {
-                fp.skip_bits[h >> 5] |= 1u << (h & 31);
-                any_skip = true;
-            }
-        }
-    }
-    if (any_skip) {
-        if ((st = check_tensor(o_cache, "o_cache")) != BSA_OK) return st;
-        if (!same_shape(q, o_cache)) return fail(BSA_ERR_INVALID_ARG, "o_cache shape differs");
-    }
+    if ((st = parse_head_modes(head_modes, H, o_cache, o, fp.skip_bits, &any_skip)) != BSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SplitRun run;
+    if ((st = split_begin(split, q->B * H, nB, block, q->D, &run)) != BSA_OK) return st;
 
     fp.q = t4(q);
     fp.k = t4(k);
@@ -599,86 +806,17 @@ static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const b
     fp.nB = (int32_t)nB;
     const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)q->D);
     fp.scale_log2 = sc * 1.4426950408889634f;
+    fp.items = run.items;
+    fp.counts = run.counts;
+    fp.partials = run.partials;
+    fp.max_chunks = run.max_chunks;
 
-    const int64_t rows = q->B * H * nB;
-    int64_t grid = rows, split_rows = 0;
-    SplitLayout sl{};
-    if (split) {
-        if (split->chunk_blocks < 1 || split->max_chunks < 2 || split->max_chunks > 64 ||
-            split->max_split_rows < 1)
-            return fail(BSA_ERR_INVALID_ARG,
-                        "split: chunk_blocks >= 1, max_chunks in 2..64 and max_split_rows >= 1 required");
-        split_rows = std::min<int64_t>(split->max_split_rows, rows);
-        sl = split_layout(rows, block, q->D, split->max_chunks, split_rows);
-        if (!split->workspace || !aligned16(split->workspace) || split->workspace_bytes < sl.total)
-            return fail(BSA_ERR_WORKSPACE, "split workspace needs %zu bytes (16-byte aligned)", sl.total);
-        grid = rows + split_rows * (split->max_chunks - 1);
-        if (grid >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "split work list too long");
-    }
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (split && (st = split_plan(run, row_ptr, q->B * H, H, nB, split, fp.skip_bits, s)) != BSA_OK) return st;
     hipError_t e;
-    if (split) {
-        char *ws = static_cast<char *>(split->workspace);
-        bsa::PlanParams pp{};
-        pp.row_ptr = row_ptr;
-        pp.items = reinterpret_cast<int4 *>(ws + sl.items);
-        pp.counts = reinterpret_cast<int32_t *>(ws);
-        pp.split_rows = reinterpret_cast<int2 *>(ws + sl.split_rows);
-        pp.BH = (int32_t)(q->B * H);
-        pp.H = (int32_t)H;
-        pp.nB = (int32_t)nB;
-        std::memcpy(pp.skip_bits, fp.skip_bits, sizeof pp.skip_bits);
-        pp.chunk_blocks = split->chunk_blocks;
-        pp.max_chunks = split->max_chunks;
-        pp.max_split_rows = split_rows;
-        if ((e = bsa::launch_plan(pp, s)) != hipSuccess) return hip_fail(e, "plan launch");
-        fp.items = pp.items;
-        fp.counts = pp.counts;
-        fp.partials = reinterpret_cast<float *>(ws + sl.partials);
-        fp.max_chunks = split->max_chunks;
-    }
-    if ((e = bsa::launch_forward(fp, block, (int)q->D, grid, s)) != hipSuccess)
+    if ((e = bsa::launch_forward(fp, block, (int)q->D, run.grid, s)) != hipSuccess)
         return hip_fail(e, "forward launch");
-    if (split) {
-        bsa::CombineParams cp{};
-        cp.partials = fp.partials;
-        cp.counts = fp.counts;
-        cp.split_rows = reinterpret_cast<const int2 *>(static_cast<char *>(split->workspace) + sl.split_rows);
-        cp.o = fp.o;
-        cp.o_sb = fp.o_sb;
-        cp.o_sh = fp.o_sh;
-        cp.o_sn = fp.o_sn;
-        cp.lse = lse;
-        cp.H = (int32_t)H;
-        cp.N = (int32_t)q->N;
-        cp.nB = (int32_t)nB;
-        cp.D = (int32_t)q->D;
-        cp.block = block;
-        cp.max_chunks = split->max_chunks;
-        cp.natural = natural;
-        if (nb) cp.nb = *nb;
-        if ((e = bsa::launch_combine(cp, split_rows, s)) != hipSuccess) return hip_fail(e, "combine launch");
-    }
-    if (any_skip) {
-        bsa::SkipCopyParams cp{};
-        cp.src = t4(o_cache);
-        cp.dst = static_cast<uint16_t *>(o->data);
-        cp.d_sb = o->stride_b;
-        cp.d_sh = o->stride_h;
-        cp.d_sn = o->stride_n;
-        cp.lse_src = lse_cache;
-        cp.lse_dst = lse;
-        cp.B = (int32_t)q->B;
-        cp.H = (int32_t)H;
-        cp.N = (int32_t)q->N;
-        cp.D = (int32_t)q->D;
-        cp.copy_o = !(o_cache->data == o->data && o_cache->stride_b == o->stride_b &&
-                      o_cache->stride_h == o->stride_h && o_cache->stride_n == o->stride_n);
-        std::memcpy(cp.skip_bits, fp.skip_bits, sizeof cp.skip_bits);
-        if (cp.copy_o || (lse_cache && lse && lse_cache != lse))
-            if ((e = bsa::launch_skip_copy(cp, s)) != hipSuccess) return hip_fail(e, "skip copy launch");
-    }
+    if (split && (st = split_combine(run, o, lse, H, q->N, nB, q->D, block, natural, nb, s)) != BSA_OK) return st;
+    if (any_skip && (st = skip_heads_copy(o_cache, lse_cache, o, lse, fp.skip_bits, s)) != BSA_OK) return st;
     return BSA_OK;
 }
 
@@ -1015,8 +1153,10 @@ bsa_status bsa_quantize_fp8_neighborhood(const bsa_tensor *q, const bsa_tensor *
 }
 
 static bsa_status forward_fp8_impl(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
-                                   const int32_t *col_idx, float scale, const bsa_tensor *o, float *lse, void *stream,
-                                   const int32_t *entry_flags, const bsa::NbGeom *nb, int natural = 0)
+                                   const int32_t *col_idx, const int8_t *head_modes, const bsa_tensor *o_cache,
+                                   const float *lse_cache, float scale, const bsa_tensor *o, float *lse,
+                                   const bsa_split *split, void *stream, const int32_t *entry_flags,
+                                   const bsa::NbGeom *nb, int natural = 0)
 {
     bsa_status st;
     if ((st = check_fp8(in, "in")) != BSA_OK) return st;
@@ -1030,6 +1170,11 @@ static bsa_status forward_fp8_impl(const bsa_fp8_qkv *in, int32_t block, const i
     if (in->B * in->H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many query blocks");
 
     bsa::Fp8FwdParams p{};
+    bool any_skip = false;
+    if ((st = parse_head_modes(head_modes, in->H, o_cache, o, p.skip_bits, &any_skip)) != BSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SplitRun run;
+    if ((st = split_begin(split, in->B * in->H, nB, block, in->D, &run)) != BSA_OK) return st;
     p.q8 = static_cast<const uint8_t *>(in->q8);
     p.k8 = static_cast<const uint8_t *>(in->k8);
     p.v8t = static_cast<const uint8_t *>(in->v8t);
@@ -1054,15 +1199,26 @@ static bsa_status forward_fp8_impl(const bsa_fp8_qkv *in, int32_t block, const i
     p.flags = entry_flags;
     if (nb) p.nb = *nb;
     p.natural = nb ? natural : 0;
-    hipError_t e = bsa::launch_forward_fp8(p, block, (int)in->D, static_cast<hipStream_t>(stream));
+    p.items = run.items;
+    p.counts = run.counts;
+    p.partials = run.partials;
+    p.max_chunks = run.max_chunks;
+    if (split && (st = split_plan(run, row_ptr, in->B * in->H, in->H, nB, split, p.skip_bits, s)) != BSA_OK)
+        return st;
+    hipError_t e = bsa::launch_forward_fp8(p, block, (int)in->D, run.grid, s);
     if (e != hipSuccess) return hip_fail(e, "fp8 forward launch");
+    if (split && (st = split_combine(run, o, lse, in->H, in->N, nB, in->D, block, p.natural, nb, s)) != BSA_OK)
+        return st;
+    if (any_skip && (st = skip_heads_copy(o_cache, lse_cache, o, lse, p.skip_bits, s)) != BSA_OK) return st;
     return BSA_OK;
 }
 
 bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr, const int32_t *col_idx,
-                           float scale, const bsa_tensor *o, float *lse, void *stream)
+                           const int8_t *head_modes, const bsa_tensor *o_cache, const float *lse_cache, float scale,
+                           const bsa_tensor *o, float *lse, const bsa_split *split, void *stream)
 {
-    return forward_fp8_impl(in, block, row_ptr, col_idx, scale, o, lse, stream, nullptr, nullptr);
+    return forward_fp8_impl(in, block, row_ptr, col_idx, head_modes, o_cache, lse_cache, scale, o, lse, split,
+                            stream, nullptr, nullptr);
 }
 
 bsa_status bsa_forward_fp8_neighborhood(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
@@ -1075,7 +1231,8 @@ bsa_status bsa_forward_fp8_neighborhood(const bsa_fp8_qkv *in, int32_t block, co
     if (!entry_flags) return fail(BSA_ERR_INVALID_ARG, "entry_flags null");
     bsa::NbGeom g;
     if ((st = check_nb(nb, in->N, block, &g)) != BSA_OK) return st;
-    return forward_fp8_impl(in, block, row_ptr, col_idx, scale, o, lse, stream, entry_flags, &g);
+    return forward_fp8_impl(in, block, row_ptr, col_idx, nullptr, nullptr, nullptr, scale, o, lse, nullptr, stream,
+                            entry_flags, &g);
 }
 
 bsa_status bsa_forward_fp8_neighborhood_natural(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
@@ -1088,7 +1245,8 @@ bsa_status bsa_forward_fp8_neighborhood_natural(const bsa_fp8_qkv *in, int32_t b
     if (!entry_flags) return fail(BSA_ERR_INVALID_ARG, "entry_flags null");
     bsa::NbGeom g;
     if ((st = check_nb(nb, in->N, block, &g)) != BSA_OK) return st;
-    return forward_fp8_impl(in, block, row_ptr, col_idx, scale, o, lse, stream, entry_flags, &g, 1);
+    return forward_fp8_impl(in, block, row_ptr, col_idx, nullptr, nullptr, nullptr, scale, o, lse, nullptr, stream,
+                            entry_flags, &g, 1);
 }
 
 // ---------------------------------------------------------------------------

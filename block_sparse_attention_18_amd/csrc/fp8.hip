@@ -536,13 +536,32 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
     const int n = lane & 31;
 
     const int BH = p.B * p.H;
-    const int i = blockIdx.x / BH;            // query-block-major
-    const int bh = blockIdx.x - i * BH;
+    int i, bh, chunk = 0, chunks = 1, rank = -1;
+    if (p.items) {   // one item of the long-row splitting work list
+        if ((int)blockIdx.x >= p.counts[0]) return;
+        const int4 it = p.items[blockIdx.x];
+        bh = it.x / p.nB;
+        i = it.x - bh * p.nB;
+        chunk = it.y;
+        chunks = it.z;
+        rank = it.w;
+    } else {         // query-block-major: every head's text rows first
+        i = blockIdx.x / BH;
+        bh = blockIdx.x - i * BH;
+    }
     const int b = bh / p.H, hh = bh - b * p.H;
+    if ((p.skip_bits[hh >> 5] >> (hh & 31)) & 1u) return;
 
     const int64_t row = (int64_t)bh * p.nB + i;
-    const int e0 = p.row_ptr[row];
-    const int e1 = p.row_ptr[row + 1];
+    int e0 = p.row_ptr[row];
+    int e1 = p.row_ptr[row + 1];
+    if (chunks > 1) {   // this workgroup takes one contiguous chunk of the row
+        const int len = e1 > e0 ? e1 - e0 : 0;
+        const int cs = (len + chunks - 1) / chunks;
+        const int lo = e0 + min(len, chunk * cs);
+        e1 = e0 + min(len, (chunk + 1) * cs);
+        e0 = lo;
+    }
     const int T = (e1 > e0 ? e1 - e0 : 0) * Sh::SUB;
 
     F8State<BETA, D> st;
@@ -665,6 +684,28 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
     }
 
     const float l_tot = st.lacc[0];
+    if (rank >= 0) {
+        // a chunk of a split row: park the output (channel scales applied,
+        // not normalised) and the (reference max, sum) of every query
+        float *slot = p.partials + ((int64_t)rank * p.max_chunks + chunk) * partial_slot_floats(BETA, D);
+        const int tq = wv * 32 + n;
+        const float *vs = p.v_scale + (int64_t)bh * D;
+#pragma unroll
+        for (int d = 0; d < Sh::DT; ++d)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = d * 32 + 8 * g + 4 * hl;
+                const float4 s4 = *reinterpret_cast<const float4 *>(vs + c0);
+                *reinterpret_cast<float4 *>(slot + tq * D + c0) =
+                    make_float4(st.oacc[d][4 * g + 0] * s4.x, st.oacc[d][4 * g + 1] * s4.y,
+                                st.oacc[d][4 * g + 2] * s4.z, st.oacc[d][4 * g + 3] * s4.w);
+            }
+        if (hl == 0) {
+            slot[BETA * D + tq] = st.m_run;
+            slot[BETA * D + BETA + tq] = l_tot;
+        }
+        return;
+    }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < p.N) {
         // natural-order outputs of a neighbourhood layout: the query's grid position
@@ -688,10 +729,9 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
 }
 
 template <int BETA, int D>
-static hipError_t launch_fwd8_t(const Fp8FwdParams &p, hipStream_t s)
+static hipError_t launch_fwd8_t(const Fp8FwdParams &p, int64_t grid, hipStream_t s)
 {
     using Sh = F8Shape<BETA, D>;
-    const int64_t grid = (int64_t)p.B * p.H * p.nB;
     if (grid == 0) return hipSuccess;
     if (p.flags)
         hipLaunchKernelGGL((fwd8_kernel<BETA, D, true>), dim3((unsigned)grid), dim3(Sh::NT), 0, s, p);
@@ -700,12 +740,12 @@ static hipError_t launch_fwd8_t(const Fp8FwdParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, hipStream_t s)
+hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, int64_t grid, hipStream_t s)
 {
-    if (block == 128 && D == 128) return launch_fwd8_t<128, 128>(p, s);
-    if (block == 128 && D == 64) return launch_fwd8_t<128, 64>(p, s);
-    if (block == 64 && D == 128) return launch_fwd8_t<64, 128>(p, s);
-    if (block == 64 && D == 64) return launch_fwd8_t<64, 64>(p, s);
+    if (block == 128 && D == 128) return launch_fwd8_t<128, 128>(p, grid, s);
+    if (block == 128 && D == 64) return launch_fwd8_t<128, 64>(p, grid, s);
+    if (block == 64 && D == 128) return launch_fwd8_t<64, 128>(p, grid, s);
+    if (block == 64 && D == 64) return launch_fwd8_t<64, 64>(p, grid, s);
     return hipErrorInvalidValue;
 }
 

@@ -260,6 +260,22 @@ struct SelectParams {
     int32_t g_begin[8], g_end[8], g_k[8];
 };
 
+// Fused mean-pool / projection / score / top-k selection (see
+// bsa_select_meanpool): the head's projections sit in LDS in phase 2.
+constexpr int kMpsMaxBlocks = 256;     // blocks per head
+constexpr int kMpsMaxProj = 4096;      // nB * r floats of one side's projections
+struct MeanpoolSelectParams {
+    Tensor4 q, k;
+    const float *w;             // [D][r]
+    float *proj_q;              // workspace [B*H*nB][r]
+    float *proj_kt;             // workspace [B*H][r][nB]
+    float *scores;              // [B*H][nB][nB] or null
+    int32_t *row_ptr, *col_idx;
+    int64_t capacity;
+    int32_t B, H, N, nB, r, text_blocks, n_groups, row_len;
+    int32_t g_begin[8], g_end[8], g_k[8];
+};
+
 struct ExpandParams {
     const uint32_t *bits;
     const int32_t *row_ptr;
@@ -307,6 +323,12 @@ struct Fp8FwdParams {
     int32_t B, H, N, nB, NT, NP;
     float scale_log2;
     int32_t natural;            // neighbourhood layouts: O and LSE written in natural token order
+    uint32_t skip_bits[kMaxSkipHeads / 32];   // SKIP heads: nothing computed
+    // long-row splitting (items == null: one workgroup per row), as in FwdParams
+    const int4 *items;
+    const int32_t *counts;
+    float *partials;
+    int32_t max_chunks;
 };
 
 // Per-head RSE of an output against a reference (see bsa_output_rse).
@@ -331,7 +353,7 @@ hipError_t launch_backward(const BwdParams &p, int block, int D, hipStream_t s);
 hipError_t launch_neighborhood_layout(const NbLayoutParams &p, hipStream_t s);
 hipError_t launch_mask_jaccard(const JaccardParams &p, hipStream_t s);
 hipError_t launch_quantize_fp8(const Fp8QuantParams &p, int D, hipStream_t s);
-hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, hipStream_t s);
+hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, int64_t grid, hipStream_t s);
 hipError_t launch_skip_copy(const SkipCopyParams &p, hipStream_t s);
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s);
@@ -342,6 +364,7 @@ hipError_t launch_scores(const ScoreParams &p, hipStream_t s);
 hipError_t launch_score_grad(const ScoreGradParams &p, hipStream_t s);
 hipError_t launch_exact_scores(const ExactParams &p, int block, int D, int slots, hipStream_t s);
 hipError_t launch_select(const SelectParams &p, hipStream_t s);
+hipError_t launch_meanpool_select(const MeanpoolSelectParams &p, int block, int D, hipStream_t s);
 hipError_t launch_scan(int32_t *row_ptr, int64_t rows, hipStream_t s);
 hipError_t launch_expand(const ExpandParams &p, hipStream_t s);
 hipError_t launch_arrow(const ArrowParams &p, hipStream_t s);

@@ -6,6 +6,7 @@
  *   bsa_pool_scores         block scores for content-driven selection
  *   bsa_select_topk         per query block, keep the top-k key blocks
  *   bsa_build_arrow_layout  arrow / full / skip block layout per head
+ *   (bsa_select_meanpool    the first two fused for mean-pool scoring)
  *   bsa_forward             online-softmax attention over the kept blocks
  *
  * Conventions shared by every call
@@ -193,6 +194,34 @@ bsa_status bsa_select_topk(const float *scores, int64_t B, int64_t H, int32_t n_
                            int32_t text_blocks, const bsa_group *groups, int32_t n_groups,
                            int32_t *row_ptr, int32_t *col_idx, int64_t capacity,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * bsa_select_meanpool -- content-driven selection in one call ([W] 2.2:
+ * mean-pool, one small projection, dot-product score, top-k; [W] 2.3: text
+ * rows and columns dense).  Computes the MEANPOOL_PROJ scores of
+ * bsa_pool_scores and the selection of bsa_select_topk in two short
+ * kernels: every block of Q and K is pooled and projected once, then one
+ * workgroup per head scores and selects that head's rows without the score
+ * matrix leaving the chip.  The scores agree with bsa_pool_scores to fp32
+ * rounding (the summation order differs); the CSR is the one
+ * bsa_select_topk gives for the scores written to `scores`.
+ *
+ * q, k, block, w [D][r] and r as in bsa_pool_scores; text_blocks, groups,
+ * row_ptr, col_idx and capacity as in bsa_select_topk.  scores: device fp32
+ * [B][H][nB][nB] or NULL (not written).
+ * Limits: nB <= 256 and nB * r <= 4096; the groups with k > 0 pairwise
+ * disjoint and clear of the text columns (every row's length is then known
+ * in advance).  Outside them the call fails with BSA_ERR_UNSUPPORTED; use
+ * bsa_pool_scores and bsa_select_topk.
+ * workspace: bsa_select_meanpool_workspace_size() bytes, 16-byte aligned
+ * (the projected blocks; contents on return are unspecified).
+ * Errors: INVALID_ARG, UNSUPPORTED, CAPACITY, WORKSPACE, HIP.
+ * ---------------------------------------------------------------------- */
+size_t bsa_select_meanpool_workspace_size(int64_t B, int64_t H, int64_t N, int32_t block, int32_t r);
+bsa_status bsa_select_meanpool(const bsa_tensor *q, const bsa_tensor *k, int32_t block, const float *w,
+                               int32_t r, int32_t text_blocks, const bsa_group *groups, int32_t n_groups,
+                               float *scores, int32_t *row_ptr, int32_t *col_idx, int64_t capacity,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * bsa_build_arrow_layout -- CSR block list of the arrow layout ([D] head-
@@ -414,10 +443,12 @@ bsa_status bsa_backward_neighborhood_natural(const bsa_tensor *q, const bsa_tens
  *
  * bsa_forward_fp8 computes O (bf16, any strides as in bsa_forward) and LSE
  * (natural log, fp32 [B][H][N] or NULL) from a bsa_fp8_qkv with the CSR of
- * bsa_forward; scale <= 0 means 1/sqrt(D).  Every head is computed (no
- * head modes, no long-row splitting).  The row sum that normalises O and
- * gives LSE is the sum of the E4M3-rounded probabilities.  Errors:
- * INVALID_ARG, UNSUPPORTED (D not in {64, 128}, block not in {64, 128}).
+ * bsa_forward; scale <= 0 means 1/sqrt(D).  head_modes, o_cache, lse_cache
+ * and split mean what they mean for bsa_forward: a SKIP head is copied from
+ * the caches bit for bit ([D] head-wise caching), long rows may be cut into
+ * chunks merged afterwards.  The row sum that normalises O and gives LSE is
+ * the sum of the E4M3-rounded probabilities.  Errors: INVALID_ARG,
+ * UNSUPPORTED (D not in {64, 128}, block not in {64, 128}), WORKSPACE.
  * ---------------------------------------------------------------------- */
 typedef struct bsa_fp8_qkv {
     void *q8;
@@ -434,8 +465,9 @@ bsa_status bsa_quantize_fp8(const bsa_tensor *q, const bsa_tensor *k, const bsa_
                             const bsa_fp8_qkv *out, void *workspace, size_t workspace_bytes,
                             void *stream);
 bsa_status bsa_forward_fp8(const bsa_fp8_qkv *in, int32_t block, const int32_t *row_ptr,
-                           const int32_t *col_idx, float scale, const bsa_tensor *o, float *lse,
-                           void *stream);
+                           const int32_t *col_idx, const int8_t *head_modes, const bsa_tensor *o_cache,
+                           const float *lse_cache, float scale, const bsa_tensor *o, float *lse,
+                           const bsa_split *split, void *stream);
 
 /* bsa_forward_fp8_neighborhood -- bsa_forward_fp8 for the 2-D neighbourhood
  * layout (GNA notes, 2.1: its FP8 mode): `in` quantised from tile-major Q,

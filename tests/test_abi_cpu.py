@@ -278,15 +278,23 @@ def test_fp8_workspace_and_quantize_validation():
 
 def test_fp8_forward_validation():
     lib = bsa.load()
-    call = lambda inp=None, block=64, rp=FAKE, ci=FAKE, scale=0.0, o=None: lib.bsa_forward_fp8(
-        ctypes.byref(inp or _fp8()), block, ctypes.c_void_p(rp) if rp else None,
-        ctypes.c_void_p(ci) if ci else None, scale, ctypes.byref(o or _t()), None, None)
+    call = lambda inp=None, block=64, rp=FAKE, ci=FAKE, scale=0.0, o=None, modes=None, oc=None, split=None: \
+        lib.bsa_forward_fp8(ctypes.byref(inp or _fp8()), block, ctypes.c_void_p(rp) if rp else None,
+                            ctypes.c_void_p(ci) if ci else None, modes, None if oc is None else ctypes.byref(oc),
+                            None, scale, ctypes.byref(o or _t()), None,
+                            None if split is None else ctypes.byref(split), None)
     assert call(block=32) == 2 and "block size" in _err()
     assert call(inp=_fp8(D=96), o=_t(D=96)) == 2
     assert call(o=_t(N=128)) == 1 and "shape" in _err()
     assert call(rp=0) == 1 and "row_ptr" in _err()
     assert call(scale=float("nan")) == 1 and "NaN" in _err()
     assert call(inp=_fp8(N=(1 << 24) + 1), o=_t(N=(1 << 24) + 1)) == 2 and "2^24" in _err()
+    skip = (ctypes.c_int8 * 2)(bsa.HEAD_FULL, bsa.HEAD_SKIP)
+    assert call(modes=skip) == 1 and "o_cache" in _err()             # a SKIP head needs the cache
+    bad = (ctypes.c_int8 * 2)(bsa.HEAD_FULL, 7)
+    assert call(modes=bad, oc=_t()) == 1 and "mode" in _err()
+    assert call(split=bsa.BsaSplit(0, 4, 8, FAKE, 1 << 30)) == 1 and "split" in _err()
+    assert call(split=bsa.BsaSplit(2, 4, 8, FAKE, 16)) == 4 and "workspace" in _err()
 
 
 def test_diagnostics_validation_and_workspace():
@@ -419,3 +427,30 @@ def test_pool_scores_noalloc_rejects_requests_beyond_its_scratch(mode, N, D, blo
                                      ctypes.c_void_p(FAKE), None)
     assert st == 4
     assert "scratch" in _err()
+
+
+@pytest.mark.parametrize("N,block,r,tb,groups,code,msg", [
+    (512, 64, 32, 1, [(0, 8, 4)], 2, "text columns"),            # a group over the text column
+    (4352, 64, 32, 4, [(4, 60, 8), (50, 68, 2)], 2, "disjoint"),   # overlapping groups
+    (300 * 64, 64, 8, 0, [(0, 300, 10)], 2, "at most 256"),        # more blocks than the fused kernel holds
+    (4352, 64, 64, 4, [(4, 68, 16)], 2, "at most"),                # nB * r above 4096
+    (4352, 64, 32, 4, [(4, 68, 70)], 1, "invalid"),                # k above the group's width
+])
+def test_select_meanpool_validation(N, block, r, tb, groups, code, msg):
+    lib = bsa.load()
+    q, k = _t(N=N, D=64), _t(N=N, D=64)
+    arr = (bsa.BsaGroup * len(groups))(*[bsa.BsaGroup(*g) for g in groups])
+    st = lib.bsa_select_meanpool(ctypes.byref(q), ctypes.byref(k), block, ctypes.c_void_p(FAKE), r, tb, arr,
+                                 len(groups), None, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 1 << 30,
+                                 ctypes.c_void_p(FAKE), 1 << 30, None)
+    assert st == code
+    assert msg in _err()
+
+
+def test_select_meanpool_applies_mirrors_the_abi_limits():
+    assert bsa.select_meanpool_applies(68, 32, 4, [(4, 68, 16)])
+    assert bsa.select_meanpool_applies(70, 32, 4, [(4, 60, 14), (60, 70, 3), (0, 70, 0)])
+    assert not bsa.select_meanpool_applies(8, 32, 1, [(0, 8, 4)])
+    assert not bsa.select_meanpool_applies(68, 32, 4, [(4, 60, 8), (50, 68, 2)])
+    assert not bsa.select_meanpool_applies(257, 8, 0, [(0, 257, 10)])
+    assert not bsa.select_meanpool_applies(68, 64, 4, [(4, 68, 16)])

@@ -166,6 +166,48 @@ def test_forward_fp8_exact_weights(B, H, N, D, block, q_exp, k_exps, nch, seed):
     np.testing.assert_allclose(Lg[fin], Lo[fin], rtol=0, atol=3e-5)
 
 
+@pytest.mark.parametrize("B,H,N,D,block,cb,mc,msr,seed", [
+    (1, 4, 6 * 128 + 40, 128, 128, 1, 4, 100, 316),      # every multi-block row split
+    (2, 3, 9 * 64, 64, 64, 2, 3, 4, 317),                # fewer split slots than long rows
+])
+def test_forward_fp8_split_and_skip_heads_exact(B, H, N, D, block, cb, mc, msr, seed):
+    """SKIP heads copied bit for bit from the caches, and long rows cut into
+    chunks and merged, on the exact-weight inputs: the computed heads must
+    match the FP8 oracle as tightly as the unsplit forward."""
+    _log(f"fp8 split+skip B={B} H={H} N={N} D={D} block={block} chunk={cb}")
+    q, k, v, scale = _pow2_inputs(B, H, N, D, seed, 0, (0, 1), 2)
+    nB = -(-N // block)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=seed + 1, density=0.7, empty_rows=1, full_rows=3)
+    modes = np.array([bsa.HEAD_FULL, bsa.HEAD_SKIP] + [bsa.HEAD_ARROW] * (H - 2), np.int8)
+    cache = synth.random_qkv(B, H, N, D, seed=seed + 2)[0]
+    lse_c = np.random.default_rng(seed + 3).standard_normal((B, H, N)).astype(np.float32)
+    qkv = _quantize(q, k, v)
+    ref = oracle.quantize_fp8(q, k, v)
+    split = {"chunk_blocks": cb, "max_chunks": mc, "max_split_rows": msr}
+    O, L = bsa.forward_fp8(qkv, block, _i32(rp), _i32(ci), scale=scale, head_modes=modes,
+                           o_cache=to_dev_bf16(cache), lse_cache=torch.from_numpy(lse_c).to(dev()), split=split)
+    torch.cuda.synchronize()
+    comp = modes != bsa.HEAD_SKIP
+    Oo, Lo = oracle.forward_fp8(*ref, block, rp, ci, scale=scale)
+    Og, Lg = bf16_to_f64(O), L.cpu().numpy().astype(np.float64)
+    vmax = np.abs(synth.bf16_to_f32(v)).max(axis=2, keepdims=True)
+    tol = 2.0 ** -8 * np.abs(Oo) + 1e-4 * vmax
+    bad = (np.abs(Og - Oo) > tol)[:, comp]
+    assert not bad.any(), f"{bad.sum()} outputs off; worst {np.abs(Og - Oo)[:, comp].max():.3e}"
+    fin = np.isfinite(Lo[:, comp])
+    np.testing.assert_array_equal(np.isfinite(Lg[:, comp]), fin)
+    np.testing.assert_allclose(Lg[:, comp][fin], Lo[:, comp][fin], rtol=0, atol=3e-5)
+    Ob = O.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(Ob[:, ~comp], cache[:, ~comp])
+    np.testing.assert_array_equal(L.cpu().numpy()[:, ~comp], lse_c[:, ~comp])
+    # the same without splitting: bit-identical SKIP heads, computed heads within rounding
+    O1, L1 = bsa.forward_fp8(qkv, block, _i32(rp), _i32(ci), scale=scale, head_modes=modes,
+                             o_cache=to_dev_bf16(cache))
+    torch.cuda.synchronize()
+    assert float((O1.float() - O.float()).abs().max()) <= 2e-2
+    assert torch.isnan(L1[:, torch.from_numpy(~comp)]).all()   # no LSE cache: NaN for SKIP heads
+
+
 # ---------------------------------------------------------------------------
 # forward, random inputs
 # ---------------------------------------------------------------------------
@@ -243,3 +285,35 @@ def test_workload_c4_fp8():
     mx, mean, dl = _stats(Og, Lg, *oracle.forward(x["q"], x["k"], x["v"], block, rpo, cio, rows=rows))
     _log(f"C4 fp8 vs bf16 oracle: max {mx:.2e} mean {mean:.2e} lse {dl:.2e}")
     assert mx <= E2E_O_MAX_ABS and mean <= E2E_O_MEAN_ABS and dl <= E2E_LSE_MAX_ABS
+
+
+@pytest.mark.slow
+def test_workload_c2_fp8_heads_and_split():
+    """The FLUX 1024^2 mix in FP8: 12 arrow, 8 full and 4 SKIP heads, long
+    rows split as the bf16 forward splits them."""
+    wl = synth.WORKLOADS["C2"]
+    x = synth.make_inputs(wl)
+    B, H, N, D, block, nB = wl.B, wl.H, wl.N, wl.D, wl.block, wl.n_blocks
+    modes, wins = x["head_modes"], x["head_windows"]
+    assert (modes == bsa.HEAD_SKIP).sum() == 4
+    rp, ci = bsa.build_arrow_layout(B, H, N, block, wl.text_len, modes, wins, device=dev())
+    qkv = _quantize(x["q"], x["k"], x["v"])
+    split = bsa.arrow_split_policy(B, H, N, block, wl.text_len, modes, wins) or \
+        {"chunk_blocks": 9, "max_chunks": 4, "max_split_rows": 1000}
+    O, L = bsa.forward_fp8(qkv, block, rp, ci, head_modes=modes, o_cache=to_dev_bf16(x["o_cache"]),
+                           lse_cache=torch.from_numpy(x["lse_cache"]).to(dev()), split=split)
+    torch.cuda.synchronize()
+    rpo, cio = oracle.arrow(B, H, nB, wl.text_blocks, modes, wins)
+    np.testing.assert_array_equal(rp.cpu().numpy(), rpo)
+    ref = oracle.quantize_fp8(x["q"], x["k"], x["v"])
+    skip = modes == bsa.HEAD_SKIP
+    Ob = O.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(Ob[:, skip], x["o_cache"][:, skip])
+    np.testing.assert_array_equal(L.cpu().numpy()[:, skip], x["lse_cache"][:, skip])
+    rows = sample_rows(B, H, N, 4096, 341)
+    rows = rows[~skip[(rows // N) % H]]
+    Og = bf16_to_f64(O).reshape(-1, D)[rows]
+    Lg = L.cpu().numpy().reshape(-1)[rows].astype(np.float64)
+    mx, mean, dl = _stats(Og, Lg, *oracle.forward_fp8(*ref, block, rpo, cio, rows=rows))
+    _log(f"C2 fp8 vs fp8 oracle ({len(rows)} rows): max {mx:.2e} mean {mean:.2e} lse {dl:.2e}")
+    assert mx <= FP8_O_MAX_ABS and mean <= FP8_O_MEAN_ABS and dl <= FP8_LSE_MAX_ABS

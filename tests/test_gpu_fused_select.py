@@ -1,0 +1,95 @@
+"""The fused content-driven selection (bsa_select_meanpool: mean-pool,
+projection, scores and top-k in one call) against the oracle: scores to
+fp32 rounding of the fp64 definition, and the CSR bit-exact with the
+oracle's selection on the kernel's own fp32 scores (the same rule the
+C5 test applies), plus the near-tie rule against the oracle's fp64 scores."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import block_sparse_attention_18_amd as bsa
+from helpers import check_csr_valid, check_selection, csr_rows, dev, to_dev_bf16
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _w(D, r, seed):
+    return (np.random.default_rng(seed).standard_normal((D, r)) / math.sqrt(D)).astype(np.float32)
+
+
+def _check_fused(q, k, w, block, tb, groups, ws=None):
+    B, H, N, D = q.shape
+    nB = -(-N // block)
+    S = torch.full((B, H, nB, nB), float("nan"), dtype=torch.float32, device=dev())
+    rp, ci = bsa.select_meanpool(to_dev_bf16(q), to_dev_bf16(k), block, torch.from_numpy(w).to(dev()), tb, groups,
+                                 scores=S, workspace=ws)
+    torch.cuda.synchronize()
+    So = oracle.scores_meanpool_proj(q, k, block, w)
+    Sg = S.cpu().numpy()
+    assert np.all(np.abs(Sg.astype(np.float64) - So) <= 1e-5 * np.abs(So).max(axis=-1, keepdims=True) + 1e-7)
+    rpg, cig = rp.cpu().numpy(), ci.cpu().numpy()
+    check_csr_valid(rpg, cig[:rpg[-1]], nB)
+    # bit-exact: the oracle's selection on the kernel's own scores
+    rps, cis = oracle.select(Sg, tb, groups)
+    np.testing.assert_array_equal(rpg, rps)
+    np.testing.assert_array_equal(cig[:rpg[-1]], cis)
+    # and the near-tie rule against the fp64 scores
+    rpo, cio = oracle.select(So, tb, groups)
+    qb = np.tile(np.arange(nB), B * H)
+    differ = check_selection(csr_rows(rpg, cig), csr_rows(rpo, cio), So.reshape(-1, nB), qb, tb, groups, nB=nB)
+    return rpg, cig, differ
+
+
+FUSED_CASES = [
+    # B, H, N, D, block, r, text_blocks, groups, seed
+    (1, 2, 512, 64, 64, 32, 1, ((0, 8, 4),), 500),                     # C1's shape (the group spans text: unsupported)
+    (2, 3, 5 * 64 + 9, 64, 64, 32, 1, ((1, 6, 2),), 501),              # ragged last block
+    (1, 2, 4 * 128, 128, 128, 17, 0, ((0, 4, 2),), 502),
+    (2, 2, 70 * 64, 64, 64, 32, 4, ((4, 60, 14), (60, 70, 3)), 503),   # two groups, nB > 64
+    (1, 2, 200 * 64 + 5, 64, 64, 16, 3, ((3, 120, 30), (130, 201, 71), (120, 130, 0)), 504),  # k = width, k = 0, nB > 128
+    (1, 1, 3 * 128 + 40, 128, 128, 64, 2, (), 505),                    # text columns only
+    (1, 3, 40 * 64, 64, 64, 8, 40, ((0, 40, 3),), 506),                # every row a text row
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,block,r,tb,groups,seed", FUSED_CASES)
+def test_fused_selection_matches_oracle(B, H, N, D, block, r, tb, groups, seed):
+    _log(f"fused B={B} H={H} N={N} D={D} block={block} r={r} tb={tb} groups={groups}")
+    q, k, _ = synth.random_qkv(B, H, N, D, seed=seed)
+    w = _w(D, r, seed + 1)
+    if any(kk > 0 and c0 < tb for (c0, _, kk) in groups):
+        with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+            bsa.select_meanpool(to_dev_bf16(q), to_dev_bf16(k), block, torch.from_numpy(w).to(dev()), tb, groups)
+        return
+    _check_fused(q, k, w, block, tb, groups)
+
+
+def test_fused_selection_reuses_its_workspace():
+    """Three calls on one workspace, the middle one on fewer heads and blocks,
+    each exact."""
+    ws = bsa.select_meanpool_workspace(2, 16, 4352, 64, 32, dev())
+    for call, (B, H, N) in enumerate([(2, 16, 4352), (1, 3, 20 * 64), (2, 16, 4352)]):
+        q, k, _ = synth.random_qkv(B, H, N, 64, seed=510 + call)
+        nB = N // 64
+        _check_fused(q, k, _w(64, 32, 511), 64, 4, ((4, nB, nB // 4),), ws=ws)
+
+
+@pytest.mark.slow
+def test_workload_c3_fused_chain():
+    wl = synth.WORKLOADS["C3"]
+    x = synth.make_inputs(wl)
+    rpg, cig, differ = _check_fused(x["q"], x["k"], x["w"], wl.block, wl.text_blocks, wl.groups)
+    _log(f"C3 fused: {differ} rows differ from the fp64 selection only by near-ties")
+    nB = wl.n_blocks
+    assert rpg[-1] == wl.B * wl.H * (wl.text_blocks * nB + (nB - wl.text_blocks) * (wl.text_blocks + 16))
