@@ -223,9 +223,8 @@ def main():
                     mark()
                 bsa.build_neighborhood_layout(B, H, nb, row_ptr=row_ptr, col_idx=col_idx, flags=flags)
             layout_parts = ("permute_in", "layout")
-        # the split policy reads the row lengths of the built layout
-        layout()
-        split = bsa.row_split_policy(row_ptr[:B * H * nB + 1].cpu().tolist(), B, H, nB, block)
+        # the split policy from the geometry's closed-form row lengths
+        split = bsa.neighborhood_split_policy(B, H, nb, block)
         fwd_kw = {}
 
         if not nb_natural:

@@ -38,7 +38,6 @@ mask that is selected once and reused:
 from __future__ import annotations
 
 import ctypes
-import heapq
 import math
 import os
 import threading
@@ -130,6 +129,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             "bsa_forward": (I32, [TP, TP, TP, I32, V, V, V, TP, V, F, TP, V,
                                   ctypes.POINTER(BsaSplit), V]),
             "bsa_forward_split_workspace_size": (SZ, [I64, I64, I64, I64, I32, I32, I64]),
+            "bsa_split_policy_arrow": (I32, [I64, I64, I64, I32, I64, V, V, ctypes.POINTER(BsaSplit)]),
+            "bsa_split_policy_select": (I32, [I64, I64, I32, I32, GP, I32, I32, ctypes.POINTER(BsaSplit)]),
+            "bsa_split_policy_neighborhood": (I32, [I64, I64, I32, ctypes.POINTER(BsaNeighborhood),
+                                                    ctypes.POINTER(BsaSplit)]),
             "bsa_quantize_fp8_workspace_size": (SZ, [I64, I64, I64, I64]),
             "bsa_quantize_fp8": (I32, [TP, TP, TP, ctypes.POINTER(BsaFp8Qkv), V, SZ, V]),
             "bsa_forward_fp8": (I32, [ctypes.POINTER(BsaFp8Qkv), I32, V, V, V, TP, V, F, TP, V,
@@ -430,106 +433,37 @@ def split_workspace_size(B, H, N, D, block, max_chunks, max_split_rows) -> int:
     return int(load().bsa_forward_split_workspace_size(B, H, N, D, block, max_chunks, max_split_rows))
 
 
-def _makespan(costs, slots: int) -> float:
-    """Greedy list schedule of work items (in dispatch order) onto `slots`
-    concurrent workgroups; returns the finishing time of the last one."""
-    if not costs:
-        return 0.0
-    if len(costs) <= slots:
-        return float(max(costs))
-    heap = [0.0] * slots
-    for c in costs:
-        t = heapq.heappop(heap)
-        heapq.heappush(heap, t + c)
-    return max(heap)
-
-
-# Cost model of the split decision, in units of one kept block's compute:
-# a workgroup's prologue / epilogue, the extra plan and combine launches, and
-# the predicted gain a split must reach (the list-schedule model ignores that
-# the last workgroups run faster on an emptier chip, so it is optimistic).
-_ITEM_OVERHEAD = 0.5
-# the plan and combine kernels cost ~15-25 us; in block steps of one
-# workgroup that is ~4 at block 128 and ~20 at block 64 (measured on the
-# FLUX 1024^2 mix, the 2K MMDiT arrow layout and the content-driven DiT)
-_SPLIT_OVERHEAD = {128: 4.0, 64: 20.0}
-_SPLIT_GAIN = 0.95
-
-
-def _split_from_rows(nB: int, lens, typical: int, target_chunks: int, slots: int, overhead: float):
-    """Split plan from per-row block counts given in dispatch order.  Rows longer
-    than L = max(typical, ceil(nB / target_chunks)) would be cut into at most
-    ceil(nB / L) chunks; the plan is returned only when the list-schedule
-    makespan with splitting (plus the plan / combine cost) beats the makespan
-    without it by a clear margin."""
-    L = max(1, typical, -(-nB // target_chunks))
-    S = min(64, max(2, -(-nB // L)))
-    long_rows = sum(1 for x in lens if x > L)
-    if long_rows == 0:
+def _split_dict(status: int, sp: "BsaSplit") -> Optional[dict]:
+    if status < 0:
+        raise ValueError("invalid arguments to the split policy")
+    if status == 0:
         return None
-    whole = [x + _ITEM_OVERHEAD for x in lens]
-    cut = []
-    for x in lens:
-        c = min(S, -(-x // L)) if x > L else 1
-        cut += [x / c + _ITEM_OVERHEAD] * c
-    if _makespan(cut, slots) + overhead >= _SPLIT_GAIN * _makespan(whole, slots):
-        return None
-    return {"chunk_blocks": L, "max_chunks": S, "max_split_rows": long_rows}
+    return {"chunk_blocks": int(sp.chunk_blocks), "max_chunks": int(sp.max_chunks),
+            "max_split_rows": int(sp.max_split_rows)}
 
 
-def _slots(block: int) -> int:
-    # concurrent forward workgroups on the 256 CUs: two per CU at block 128,
-    # about four at block 64 (smaller LDS tiles, two waves each)
-    return 512 if block == 128 else 1024
+def arrow_split_policy(B: int, H: int, N: int, block: int, text_len: int, head_modes, head_windows):
+    """Long-row split for an arrow layout (bsa_split_policy_arrow), or None when
+    every row should run whole."""
+    sp = BsaSplit()
+    st = load().bsa_split_policy_arrow(B, H, N, block, text_len, _host_i8(head_modes, H),
+                                       _host_i32(head_windows, H), ctypes.byref(sp))
+    return _split_dict(st, sp)
 
 
-def arrow_split_policy(B: int, H: int, N: int, block: int, text_len: int, head_modes, head_windows,
-                       target_chunks: int = 4):
-    """Long-row split for an arrow layout (text rows and full heads next to
-    short windowed rows), or None when splitting would not pay."""
-    nB = n_blocks(N, block)
-    tb = -(-text_len // block)
-    per_head, typical = [], 1
-    for h in range(H):
-        m, w = int(head_modes[h]), int(head_windows[h])
-        row = []
-        for i in range(nB):
-            if m == HEAD_SKIP:
-                ln = 0
-            elif m == HEAD_FULL or i < tb:
-                ln = nB
-            else:
-                lo, hi = max(tb, i - w), min(nB - 1, i + w)
-                ln = tb + max(0, hi - lo + 1)
-                typical = max(typical, ln)
-            row.append(ln)
-        per_head.append(row)
-    if all(int(m) == HEAD_FULL for m in head_modes):
-        typical = -(-nB // target_chunks)
-    # dispatch order of the forward: query-block-major, then batch and head
-    lens = [per_head[h][i] for i in range(nB) for _ in range(B) for h in range(H)]
-    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block), _SPLIT_OVERHEAD[block])
+def select_split_policy(B: int, H: int, nB: int, text_blocks: int, groups, block: int = 128):
+    """Long-row split for a top-k selection (bsa_split_policy_select), or None."""
+    arr, ng = _groups(groups)
+    sp = BsaSplit()
+    st = load().bsa_split_policy_select(B, H, nB, text_blocks, arr, ng, block, ctypes.byref(sp))
+    return _split_dict(st, sp)
 
 
-def row_split_policy(row_ptr, B: int, H: int, nB: int, block: int, target_chunks: int = 4):
-    """Long-row split for any built block list, from its row lengths (a host
-    copy of row_ptr, [B*H*nB + 1], as a sequence of ints) in the forward's
-    dispatch order (query-block-major); the typical row is the longest one
-    short of nB."""
-    rp = [int(x) for x in row_ptr]
-    lens = [rp[bh * nB + i + 1] - rp[bh * nB + i] for i in range(nB) for bh in range(B * H)]
-    short = [x for x in lens if x < nB]
-    typical = max(short) if short else 1
-    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block), _SPLIT_OVERHEAD[block])
-
-
-def select_split_policy(B: int, H: int, nB: int, text_blocks: int, groups, target_chunks: int = 4,
-                        block: int = 128):
-    """Long-row split for a top-k selection (dense text rows next to rows of
-    text + k blocks), or None when splitting would not pay."""
-    typical = min(nB, text_blocks + sum(int(g[2]) for g in groups))
-    lens = [nB if i < text_blocks else typical for i in range(nB) for _ in range(B * H)]
-    return _split_from_rows(nB, lens, typical, target_chunks, _slots(block), _SPLIT_OVERHEAD[block])
+def neighborhood_split_policy(B: int, H: int, nb: "BsaNeighborhood", block: int):
+    """Long-row split for a neighbourhood layout (bsa_split_policy_neighborhood), or None."""
+    sp = BsaSplit()
+    st = load().bsa_split_policy_neighborhood(B, H, block, ctypes.byref(nb), ctypes.byref(sp))
+    return _split_dict(st, sp)
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,

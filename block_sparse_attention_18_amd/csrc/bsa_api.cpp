@@ -8,7 +8,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <mutex>
+#include <queue>
+#include <vector>
 
 #include "bsa.h"
 #include "internal.h"
@@ -758,6 +761,151 @@ static bsa_status skip_heads_copy(const bsa_tensor *o_cache, const float *lse_ca
         if (e != hipSuccess) return hip_fail(e, "skip copy launch");
     }
     return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Long-row split policy (host computation from the layout's closed-form row
+// lengths; no device data).  Rows are dispatched query-block-major, then
+// batch and head; a row of L blocks costs L + kItemOverhead block steps of
+// one workgroup, and `slots` workgroups run at once (two per CU at block
+// 128, about four at block 64).  Rows longer than L0 = max(typical,
+// ceil(nB / 4)) would be cut into at most ceil(nB / L0) chunks; the split is
+// recommended only when the greedy list-schedule makespan with the cut rows,
+// plus the plan and combine cost, beats the makespan of whole rows by 5 %.
+// The costs were calibrated by forcing splits on the FLUX 1024^2 mix, the
+// 2K MMDiT arrow layout and the content-driven DiT.
+// ---------------------------------------------------------------------------
+static bsa_status check_nb(const bsa_neighborhood *g, int64_t N, int32_t block, bsa::NbGeom *out);
+
+namespace {
+constexpr double kItemOverhead = 0.5;
+constexpr double kSplitGain = 0.95;
+constexpr int kTargetChunks = 4;
+
+int policy_slots(int32_t block) { return block == 128 ? 512 : 1024; }
+double policy_overhead(int32_t block) { return block == 128 ? 4.0 : 20.0; }
+
+// Greedy list schedule of costs (in order) on `slots` workgroups: the
+// finishing time of the last one.
+double makespan(const std::vector<double> &costs, int slots)
+{
+    if (costs.empty()) return 0.0;
+    if ((int64_t)costs.size() <= slots) return *std::max_element(costs.begin(), costs.end());
+    std::priority_queue<double, std::vector<double>, std::greater<double>> heap;
+    for (int x = 0; x < slots; ++x) heap.push(0.0);
+    double end = 0.0;
+    for (double c : costs) {
+        const double t = heap.top() + c;
+        heap.pop();
+        heap.push(t);
+        end = std::max(end, t);
+    }
+    return end;
+}
+
+// 1 and *out filled when splitting pays, else 0.
+int32_t split_from_rows(int64_t nB, const std::vector<int64_t> &lens, int64_t typical, int32_t block,
+                        bsa_split *out)
+{
+    const int64_t L = std::max<int64_t>({1, typical, ceil_div(nB, kTargetChunks)});
+    const int64_t S = std::min<int64_t>(64, std::max<int64_t>(2, ceil_div(nB, L)));
+    int64_t long_rows = 0;
+    std::vector<double> whole, cut;
+    whole.reserve(lens.size());
+    for (int64_t x : lens) {
+        whole.push_back((double)x + kItemOverhead);
+        if (x > L) {
+            ++long_rows;
+            const int64_t c = std::min<int64_t>(S, ceil_div(x, L));
+            for (int64_t y = 0; y < c; ++y) cut.push_back((double)x / (double)c + kItemOverhead);
+        } else {
+            cut.push_back((double)x + kItemOverhead);
+        }
+    }
+    if (long_rows == 0) return 0;
+    const int slots = policy_slots(block);
+    if (makespan(cut, slots) + policy_overhead(block) >= kSplitGain * makespan(whole, slots)) return 0;
+    std::memset(out, 0, sizeof *out);
+    out->chunk_blocks = (int32_t)L;
+    out->max_chunks = (int32_t)S;
+    out->max_split_rows = long_rows;
+    return 1;
+}
+}  // namespace
+
+int32_t bsa_split_policy_arrow(int64_t B, int64_t H, int64_t N, int32_t block, int64_t text_len,
+                               const int8_t *head_modes, const int32_t *head_windows, bsa_split *out)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || !block_ok(block) || text_len < 0 || text_len > N || !head_modes ||
+        !head_windows || !out)
+        return -1;
+    const int64_t nB = ceil_div(N, block), tb = ceil_div(text_len, block);
+    if (B * H * nB > (1ll << 26)) return -1;
+    std::vector<int64_t> per(H * nB);
+    int64_t typical = 1;
+    bool all_full = true;
+    for (int64_t h = 0; h < H; ++h) {
+        const int8_t m = head_modes[h];
+        if (m != BSA_HEAD_FULL && m != BSA_HEAD_ARROW && m != BSA_HEAD_SKIP) return -1;
+        if (m == BSA_HEAD_ARROW && head_windows[h] < 0) return -1;
+        all_full = all_full && m == BSA_HEAD_FULL;
+        for (int64_t i = 0; i < nB; ++i) {
+            int64_t len;
+            if (m == BSA_HEAD_SKIP) len = 0;
+            else if (m == BSA_HEAD_FULL || i < tb) len = nB;
+            else {
+                const int64_t w = head_windows[h];
+                const int64_t lo = std::max(tb, i - w), hi = std::min(nB - 1, i + w);
+                len = tb + std::max<int64_t>(0, hi - lo + 1);
+                typical = std::max(typical, len);
+            }
+            per[h * nB + i] = len;
+        }
+    }
+    if (all_full) typical = ceil_div(nB, kTargetChunks);
+    std::vector<int64_t> lens;
+    lens.reserve(B * H * nB);
+    for (int64_t i = 0; i < nB; ++i)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t h = 0; h < H; ++h) lens.push_back(per[h * nB + i]);
+    return split_from_rows(nB, lens, typical, block, out);
+}
+
+int32_t bsa_split_policy_select(int64_t B, int64_t H, int32_t n_blocks, int32_t text_blocks,
+                                const bsa_group *groups, int32_t n_groups, int32_t block, bsa_split *out)
+{
+    if (B <= 0 || H <= 0 || n_blocks <= 0 || text_blocks < 0 || text_blocks > n_blocks || n_groups < 0 ||
+        (n_groups > 0 && !groups) || !block_ok(block) || !out || B * H * n_blocks > (1ll << 26))
+        return -1;
+    const int64_t nB = n_blocks;
+    const int64_t typical = select_row_bound(nB, text_blocks, groups, n_groups);
+    std::vector<int64_t> lens;
+    lens.reserve(B * H * nB);
+    for (int64_t i = 0; i < nB; ++i)
+        for (int64_t x = 0; x < B * H; ++x) lens.push_back(i < text_blocks ? nB : typical);
+    return split_from_rows(nB, lens, typical, block, out);
+}
+
+int32_t bsa_split_policy_neighborhood(int64_t B, int64_t H, int32_t block, const bsa_neighborhood *nb,
+                                      bsa_split *out)
+{
+    if (B <= 0 || H <= 0 || !nb || !out) return -1;
+    bsa::NbGeom g;
+    const int64_t N = (int64_t)nb->text_len + (int64_t)nb->rows * nb->cols;
+    if (check_nb(nb, N, block, &g) != BSA_OK) return -1;
+    const int64_t nB = ceil_div(N, block);
+    if (B * H * nB > (1ll << 26)) return -1;
+    std::vector<int64_t> per(nB);
+    int64_t typical = 1;
+    for (int64_t i = 0; i < nB; ++i) {
+        per[i] = bsa::nb_row_len(g, (int32_t)nB, (int32_t)i);
+        if (per[i] < nB) typical = std::max(typical, per[i]);
+    }
+    std::vector<int64_t> lens;
+    lens.reserve(B * H * nB);
+    for (int64_t i = 0; i < nB; ++i)
+        for (int64_t x = 0; x < B * H; ++x) lens.push_back(per[i]);
+    return split_from_rows(nB, lens, typical, block, out);
 }
 
 static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v, int32_t block,

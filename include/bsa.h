@@ -265,6 +265,23 @@ typedef struct bsa_split {
 size_t bsa_forward_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t D, int32_t block,
                                         int32_t max_chunks, int64_t max_split_rows);
 
+/* Split recommendation for the layouts whose row lengths are known in
+ * closed form (computed on the host from the layout's parameters; no device
+ * data is read and nothing is enqueued).  Each returns 1 and fills
+ * chunk_blocks, max_chunks and max_split_rows of *out (workspace set to
+ * NULL, workspace_bytes to 0) when cutting the long rows is predicted to
+ * shorten the forward, 0 when every row should run whole, and -1 on invalid
+ * arguments.  The prediction is a greedy list schedule of the rows, in the
+ * forward's dispatch order, over the workgroups that run at once, with the
+ * plan and combine cost added; rows longer than max(typical row,
+ * ceil(nB / 4)) are the candidates.  Arguments as for the matching layout
+ * builder (bsa_build_arrow_layout, bsa_select_topk, and
+ * bsa_build_neighborhood_layout with its block). */
+int32_t bsa_split_policy_arrow(int64_t B, int64_t H, int64_t N, int32_t block, int64_t text_len,
+                               const int8_t *head_modes, const int32_t *head_windows, bsa_split *out);
+int32_t bsa_split_policy_select(int64_t B, int64_t H, int32_t n_blocks, int32_t text_blocks,
+                                const bsa_group *groups, int32_t n_groups, int32_t block, bsa_split *out);
+
 /* ------------------------------------------------------------------------
  * bsa_forward -- block-sparse attention forward ([W] 3.1, [D] fused
  * kernel, [S] sparse attention with a precomputed mask).  For every token
@@ -365,6 +382,9 @@ typedef struct bsa_neighborhood {
 
 bsa_status bsa_permute_tokens(const bsa_tensor *in, const bsa_tensor *out, const float *lse_in, float *lse_out,
                               int32_t block, const bsa_neighborhood *nb, int32_t inverse, void *stream);
+/* Split recommendation for a neighbourhood layout (see bsa_split_policy_arrow). */
+int32_t bsa_split_policy_neighborhood(int64_t B, int64_t H, int32_t block, const bsa_neighborhood *nb,
+                                      bsa_split *out);
 int64_t bsa_neighborhood_capacity(int64_t B, int64_t H, int32_t block, const bsa_neighborhood *nb);
 bsa_status bsa_build_neighborhood_layout(int64_t B, int64_t H, int32_t block, const bsa_neighborhood *nb,
                                          int32_t *row_ptr, int32_t *col_idx, int32_t *entry_flags,

@@ -142,8 +142,9 @@ def test_split_policies():
     assert plan3 is not None and plan3["max_split_rows"] == 36 + 63 * 4
     # uniform rows: nothing to split
     assert bsa.select_split_policy(1, 32, 512, 0, ((0, 480, 144), (480, 512, 10))) is None
-    # the list schedule itself
-    assert bsa._makespan([3, 1, 1, 1], 2) == 3 and bsa._makespan([1, 1, 1, 1], 2) == 2
+    # invalid arguments raise
+    with pytest.raises(ValueError):
+        bsa.arrow_split_policy(1, 2, 512, 96, 0, [1, 1], [1, 1])
 
 
 def test_pool_scores_validation():
@@ -395,21 +396,17 @@ def test_binding_refuses_host_tensors():
         bsa._desc(torch.zeros(1, 1, 64, 64), "q")
 
 
-def test_row_split_policy_reads_row_lengths():
-    # the policy from a built block list: 8 heads of 64 blocks whose first row
-    # is dense (64 blocks) and the others hold 2; the dense rows set the
-    # makespan and are cut into 4 chunks of 16
-    nB, BH = 64, 8
-    lens = [64] + [2] * 63
-    rp = [0]
-    for _ in range(BH):
-        for x in lens:
-            rp.append(rp[-1] + x)
-    plan = bsa.row_split_policy(rp, 1, BH, nB, 128)
-    assert plan == {"chunk_blocks": 16, "max_chunks": 4, "max_split_rows": BH}
-    # uniform rows: nothing to split
-    rp_u = [3 * r for r in range(BH * nB + 1)]
-    assert bsa.row_split_policy(rp_u, 1, BH, nB, 128) is None
+def test_neighborhood_split_policy_from_the_geometry():
+    # the 2-D neighbourhood workload (512 text tokens, 128 x 128 grid, 8 x 16
+    # tiles, 32 x 32 window): at strides 1 and 16 the windowed rows are long
+    # enough that the 132-block text rows fit the average load; at stride 32
+    # the windows shrink to whole tiles and the text rows are cut into 4
+    for stride, want in (((1, 1), None), ((16, 16), None),
+                         ((32, 32), {"chunk_blocks": 33, "max_chunks": 4, "max_split_rows": 96})):
+        nb = bsa.neighborhood(512, (128, 128), (8, 16), (32, 32), stride)
+        assert bsa.neighborhood_split_policy(1, 24, nb, 128) == want
+    with pytest.raises(ValueError):          # tile of 128 tokens against block 64
+        bsa.neighborhood_split_policy(1, 24, bsa.neighborhood(512, (128, 128), (8, 16), (32, 32)), 64)
 
 
 @pytest.mark.parametrize("mode,N,D,block,r", [

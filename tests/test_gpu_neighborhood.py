@@ -107,14 +107,14 @@ def test_forward_split_rows_and_large_logits():
 @pytest.mark.parametrize("stride", [(1, 1), (16, 16), (32, 32)])
 def test_workload_g1(stride):
     """The full G1 workload in the launch configuration bench.py times: the
-    natural-order forward with the long-row split the bench derives from the
-    built layout (rows whole at stride 1, split at stride 32)."""
+    natural-order forward with the long-row split the bench takes from the
+    geometry (rows whole at stride 1, split at stride 32)."""
     wl = synth.WORKLOADS["G1"]
     x = synth.make_inputs(wl)
     B, H, N, D = wl.B, wl.H, wl.N, wl.D
     nb = bsa.neighborhood(wl.text_len, wl.nb_grid, wl.nb_tile, wl.nb_window, stride)
     rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
-    split = bsa.row_split_policy(rp.cpu().tolist(), B, H, wl.n_blocks, wl.block)
+    split = bsa.neighborhood_split_policy(B, H, nb, wl.block)
     _log(f"G1 stride {stride}: split {split}")
     O, L = bsa.forward_neighborhood(*(to_dev_bf16(a) for a in (x["q"], x["k"], x["v"])), rp, ci, fl, nb,
                                     split=split, natural=True)
