@@ -101,6 +101,11 @@ def main():
                     help="only run the forward-time sweep over the top-k budget on a content-driven "
                          "workload (C3: k of the 64 image key blocks; C5: the fraction rho of each "
                          "column group) with a least-squares fit")
+    ap.add_argument("--pool-probe", action="store_true",
+                    help="only time the mean-pool scoring (bsa_pool_scores, MEANPOOL_PROJ) on Q and K of "
+                         "the long-context shape (B=1, H=32, N=65536, D=128, block 128: 1.07 GB read), "
+                         "with the last-level cache flushed before every call; a bandwidth probe, "
+                         "not a workload")
     ap.add_argument("--unfused", action="store_true",
                     help="content-driven mean-pool workloads: score (bsa_pool_scores) and select "
                          "(bsa_select_topk) in two calls instead of the fused bsa_select_meanpool")
@@ -133,6 +138,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": max(args.steps, 1)}))
+        return
+    if args.pool_probe:
+        pool_probe(torch, bsa, dev, reps=max(args.steps // 5, 5))
         return
     if args.gemm_ceiling:
         # the practical bf16 MFMA rate on this machine: a large dense GEMM of
@@ -455,20 +463,70 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def _evict_buffer(torch, dev):
+    """512 MB, twice the last-level cache, written once here."""
+    return torch.ones(128 << 20, dtype=torch.int32, device=dev)
+
+
+def _evict(buf):
+    """Read the eviction buffer (a reduction): the cache then holds its clean
+    lines instead of the next call's inputs, and no dirty lines are left to
+    be written back while the timed call runs."""
+    buf.max()
+
+
+def pool_probe(torch, bsa, dev, reps: int = 10):
+    """Mean-pool scoring bandwidth at the long-context shape: Q and K (bf16
+    [1, 32, 65536, 128], 1.07 GB) read once by the pooling kernel; the call
+    also projects (r = 32) and scores the 512 x 512 block pairs of every head.
+    Inputs are random (the rate does not depend on the values); a 512 MB
+    read before every call evicts them from the 256 MB last-level cache."""
+    B, H, N, D, block, r = 1, 32, 65536, 128, 128, 32
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    q = torch.randn((B, H, N, D), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, H, N, D), generator=g, device=dev).to(torch.bfloat16)
+    w = torch.randn((D, r), generator=g, device=dev) / math.sqrt(D)
+    nB = N // block
+    S = torch.empty((B, H, nB, nB), dtype=torch.float32, device=dev)
+    ws = torch.empty(bsa.pool_scores_workspace_size(B, H, N, D, block, bsa.SCORE_MEANPOOL_PROJ, r),
+                     dtype=torch.uint8, device=dev)
+    scratch = _evict_buffer(torch, dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        bsa.pool_scores(q, k, block, bsa.SCORE_MEANPOOL_PROJ, w=w, out=S, workspace=ws)
+    ts = []
+    for _ in range(reps):
+        _evict(scratch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bsa.pool_scores(q, k, block, bsa.SCORE_MEANPOOL_PROJ, w=w, out=S, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    nbytes = 2 * B * H * N * D * 2
+    print(json.dumps({"pool_probe": {"shape": [B, H, N, D], "block": block, "r": r, "bytes_read": nbytes,
+                                     "ms": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                     "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                     "note": "pool + projection + the 512 x 512 scores of 32 heads, cold cache"}}),
+          flush=True)
+
+
 def cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr, exact: bool, iters: int = 10,
                       fused: bool = False):
-    """pool_scores and select timed with a 512 MB scratch write before every
+    """pool_scores and select timed with a 512 MB read before every
     call, so the 256 MB last-level cache does not serve their inputs.  Rates
     against the algorithmic work: mean-pool scores are HBM-bound (Q and K
     read once); exact scores are MFMA-bound (one Q K^T over all pairs, plus
     one exp per pair); select reads the score matrix once and writes the
     CSR once.  The fused mean-pool selection is one call: its rate counts Q
     and K read once."""
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scratch = _evict_buffer(torch, dev)
     if fused:
         t = []
         for _ in range(iters):
-            scratch.fill_(1)
+            _evict(scratch)
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
             layout()
@@ -481,7 +539,7 @@ def cold_layout_parts(torch, dev, stream, layout, B, H, N, D, nB, row_ptr, exact
                 "hbm_peak_GBps": PEAK_HBM_GBS}
     pool, sel = [], []
     for _ in range(iters):
-        scratch.fill_(1)
+        _evict(scratch)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record(stream)
         layout(mark=lambda: e[1].record(stream))

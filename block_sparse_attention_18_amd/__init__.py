@@ -341,9 +341,10 @@ MPS_MAX_BLOCKS, MPS_MAX_PROJ = 256, 4096
 
 
 def select_meanpool_applies(nB: int, r: int, text_blocks: int, groups) -> bool:
-    """Whether bsa_select_meanpool takes this shape: nB <= 256, nB * r <= 4096,
-    the groups with k > 0 pairwise disjoint and clear of the text columns."""
-    if nB > MPS_MAX_BLOCKS or nB * r > MPS_MAX_PROJ or not 1 <= r <= 64:
+    """Whether bsa_select_meanpool takes this shape: nB <= 256, nB * r4 <= 4096
+    (r4 = r rounded up to a multiple of 4), the groups with k > 0 pairwise
+    disjoint and clear of the text columns."""
+    if nB > MPS_MAX_BLOCKS or nB * ((r + 3) // 4 * 4) > MPS_MAX_PROJ or not 1 <= r <= 64:
         return False
     live = sorted((int(g[0]), int(g[1])) for g in groups if int(g[2]) > 0)
     if any(c0 < text_blocks for (c0, _) in live):

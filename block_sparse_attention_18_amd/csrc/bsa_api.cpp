@@ -379,7 +379,7 @@ size_t bsa_select_meanpool_workspace_size(int64_t B, int64_t H, int64_t N, int32
 {
     if (B <= 0 || H <= 0 || N <= 0 || !block_ok(block) || r < 1 || r > 64) return 0;
     const size_t bh = (size_t)(B * H), nB = (size_t)ceil_div(N, block);
-    return up256(bh * nB * (size_t)r * sizeof(float)) + bh * nB * (size_t)r * sizeof(float);
+    return 2 * bh * nB * (size_t)r * sizeof(float);
 }
 
 bsa_status bsa_select_meanpool(const bsa_tensor *q, const bsa_tensor *k, int32_t block, const float *w, int32_t r,
@@ -395,9 +395,10 @@ bsa_status bsa_select_meanpool(const bsa_tensor *q, const bsa_tensor *k, int32_t
     if (!w || !row_ptr || !col_idx) return fail(BSA_ERR_INVALID_ARG, "w, row_ptr or col_idx null");
     if (r < 1 || r > 64) return fail(BSA_ERR_INVALID_ARG, "projection width r=%d outside 1..64", r);
     const int64_t nB = ceil_div(q->N, block);
-    if (nB > bsa::kMpsMaxBlocks || nB * r > bsa::kMpsMaxProj)
+    if (nB > bsa::kMpsMaxBlocks || nB * ((r + 3) & ~3) > bsa::kMpsMaxProj)
         return fail(BSA_ERR_UNSUPPORTED,
-                    "fused selection holds at most %d blocks and %d projection values per head (nB=%lld, r=%d); "
+                    "fused selection holds at most %d blocks and %d projection values (r rounded up to a multiple "
+                    "of 4) per head (nB=%lld, r=%d); "
                     "use bsa_pool_scores and bsa_select_topk", bsa::kMpsMaxBlocks, bsa::kMpsMaxProj,
                     (long long)nB, r);
     if (q->B * q->H * nB >= (1ll << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many blocks");
@@ -429,14 +430,12 @@ bsa_status bsa_select_meanpool(const bsa_tensor *q, const bsa_tensor *k, int32_t
     if (!workspace || !aligned16(workspace) || workspace_bytes < ws)
         return fail(BSA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned)", ws);
 
-    const size_t bh = (size_t)(q->B * q->H);
     char *wsp = static_cast<char *>(workspace);
     bsa::MeanpoolSelectParams mp{};
     mp.q = t4(q);
     mp.k = t4(k);
     mp.w = w;
-    mp.proj_q = reinterpret_cast<float *>(wsp);
-    mp.proj_kt = reinterpret_cast<float *>(wsp + up256(bh * nB * r * sizeof(float)));
+    mp.proj = reinterpret_cast<float *>(wsp);
     mp.scores = scores;
     mp.row_ptr = row_ptr;
     mp.col_idx = col_idx;

@@ -47,6 +47,14 @@ __device__ __forceinline__ uint4 ld_g16(const uint16_t *p)
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
 // Wave-wide (64 lanes) inclusive prefix sum of an int.
+// x / r for 0 <= x < 2^20 and 1 <= r <= 64 by one fp32 multiply: (x + 0.5)
+// / r lies at least 0.5 / r from every integer, far more than the rounding
+// of the product and of inv_r = 1 / r.
+__device__ __forceinline__ int div_small(int x, float inv_r)
+{
+    return (int)(((float)x + 0.5f) * inv_r);
+}
+
 __device__ __forceinline__ int wave_incl_scan(int x)
 {
     const int lane = threadIdx.x & 63;

@@ -267,8 +267,7 @@ constexpr int kMpsMaxProj = 4096;      // nB * r floats of one side's projection
 struct MeanpoolSelectParams {
     Tensor4 q, k;
     const float *w;             // [D][r]
-    float *proj_q;              // workspace [B*H*nB][r]
-    float *proj_kt;             // workspace [B*H][r][nB]
+    float *proj;                // workspace [2][B*H*nB][r]: projected Q blocks, then K blocks
     float *scores;              // [B*H][nB][nB] or null
     int32_t *row_ptr, *col_idx;
     int64_t capacity;

@@ -24,17 +24,27 @@
 namespace bsa {
 
 // ---------------------------------------------------------------------------
-// mean-pool + projection: grid (B*H*nB, 2), 256 threads
+// mean-pool + projection: grid (B*H*nB, 2), 256 threads, one block of Q or K
+// per workgroup.  Every 16-byte load of the block is issued first (BETA * D
+// / 2048 per thread: 8 at block 128, D 128), and the thread's slice of W is
+// fetched while they are in flight.  The column sums are reduced across the
+// wavefront's row slots with lane shuffles, across the four wavefronts
+// through LDS; the projection is split over all 256 threads (output m =
+// tid / 8, every eighth dimension), so the tail after the last load is a
+// few dozen instructions.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void pool_proj_kernel(const PoolParams p, int beta)
+template <int BETA, int D>
+__global__ __launch_bounds__(256) void pool_proj_kernel(const PoolParams p)
 {
     constexpr int CH = D / 8;          // 16-byte chunks per row
     constexpr int RS = 256 / CH;       // row slots
-    __shared__ float red[RS][D];
+    constexpr int IT = BETA / RS;      // rows per thread
+    constexpr int DP = D / 8;          // dimensions per projection thread
+    static_assert(BETA % RS == 0 && CH <= 64, "rows split evenly");
+    __shared__ float red[4][D];
     __shared__ float mean[D];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int item = blockIdx.x;
     const int which = blockIdx.y;
     const int bh = item / p.nB, i = item - bh * p.nB;
@@ -42,15 +52,134 @@ __global__ __launch_bounds__(256) void pool_proj_kernel(const PoolParams p, int 
     const Tensor4 X = p.x[which];
     const uint16_t *base = X.p + b * X.sb + hh * X.sh;
     const int cc = tid % CH, rs = tid / CH;
-    const int t0 = i * beta;
-    const int n_i = min(beta, p.N - t0);
+    const int t0 = i * BETA;
+    const int n_i = min(BETA, p.N - t0);
+
+    // rows past the end of a ragged last block re-read its last row (no
+    // branch around a load, so none waits for another) and are zeroed after
+    uint4 u[IT];
+#pragma unroll
+    for (int a = 0; a < IT; ++a) {
+        const int t = min(rs + a * RS, n_i - 1);
+        u[a] = ld_g16(base + (int64_t)(t0 + t) * X.sn + cc * 8);
+    }
+    const int m = tid >> 3, part = tid & 7;
+    float wm[DP];
+    const int mc = min(m, p.r - 1);          // lanes of outputs past r load a valid column, zeroed below
+#pragma unroll
+    for (int t = 0; t < DP; ++t) wm[t] = p.w[(part + 8 * t) * p.r + mc];
+    // keep every load above this point: none may be issued after the first wait
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int t = rs; t < n_i; t += RS) {
-        const uint4 u = ld_g16(base + (int64_t)(t0 + t) * X.sn + cc * 8);
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int a = 0; a < IT; ++a) {
+        const uint32_t live = rs + a * RS < n_i ? 0xFFFFFFFFu : 0u;
+        const uint32_t wd[4] = {u[a].x & live, u[a].y & live, u[a].z & live, u[a].w & live};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += __uint_as_float(wd[e] << 16);
+            acc[2 * e + 1] += __uint_as_float(wd[e] & 0xFFFF0000u);
+        }
+    }
+    // lanes l and l ^ x (x >= CH) hold the same columns of other rows
+#pragma unroll
+    for (int x = CH; x < 64; x <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], x, 64);
+    if (lane < CH)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wv][lane * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        const float s = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+        mean[tid] = s / (float)n_i;
+        if (p.mean) p.mean[((int64_t)which * p.B * p.H * p.nB + item) * D + tid] = mean[tid];
+    }
+    __syncthreads();
+    const int64_t out = ((int64_t)which * p.B * p.H * p.nB + item) * p.r;
+    float a = 0.f;
+#pragma unroll
+    for (int t = 0; t < DP; ++t) a = __builtin_fmaf(m < p.r ? wm[t] : 0.f, mean[part + 8 * t], a);
+    a += __shfl_xor(a, 1, 64);
+    a += __shfl_xor(a, 2, 64);
+    a += __shfl_xor(a, 4, 64);
+    if (part == 0 && m < p.r) p.proj[out + m] = a;
+    // outputs 32 .. r-1 (r > 32): a second pass, the eight lanes of an output together
+    for (int m2 = m + 32; m2 < p.r; m2 += 32) {
+        float c = 0.f;
+#pragma unroll
+        for (int t = 0; t < DP; ++t) c = __builtin_fmaf(p.w[(part + 8 * t) * p.r + m2], mean[part + 8 * t], c);
+        c += __shfl_xor(c, 1, 64);
+        c += __shfl_xor(c, 2, 64);
+        c += __shfl_xor(c, 4, 64);
+        if (part == 0) p.proj[out + m2] = c;
+    }
+}
+
+// Small blocks (BETA * D <= 8192 elements, 16 KB): one wavefront per block,
+// four blocks to a workgroup, so a workgroup still streams 32-64 KB.  W
+// [D][r] is staged in LDS once per workgroup (its loads issued first, so the
+// wait for them leaves the block's loads in flight); each wavefront sums its
+// block in registers, reduces across its row slots with lane shuffles, parks
+// the mean in LDS and projects it: lane m + 32 h sums half h of the
+// dimensions for output m, one shuffle adds the halves.  No workgroup
+// barrier after the one for W.
+template <int BETA, int D>
+__global__ __launch_bounds__(256) void pool_wave_kernel(const PoolParams p)
+{
+    constexpr int CH = D / 8;          // 16-byte chunks per row
+    constexpr int RSW = 64 / CH;       // row slots per wavefront
+    constexpr int IT = BETA / RSW;     // rows per lane
+    static_assert(BETA * D <= 8192 && BETA % RSW == 0, "block fits one wavefront");
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    float *w_s = smem;                               // [D][r]
+    float *mean_s = smem + D * p.r;                  // [4][D]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t items = (uint32_t)(p.B * p.H * p.nB);
+    const uint32_t gidx = blockIdx.x * 4u + (uint32_t)wv;     // over [2][items]
+    const bool live = gidx < 2u * items;
+    const int which = live && gidx >= items ? 1 : 0;
+    const uint32_t item = live ? gidx - (uint32_t)which * items : 0u;
+    const uint32_t bh = item / (uint32_t)p.nB;
+    const int i = (int)(item - bh * (uint32_t)p.nB);
+    const int b = (int)(bh / (uint32_t)p.H), hh = (int)bh - b * p.H;
+    const Tensor4 X = p.x[which];
+    const uint16_t *base = X.p + b * X.sb + hh * X.sh;
+    const int t0 = i * BETA, n_i = min(BETA, p.N - t0);
+    const int cc = lane % CH, rs = lane / CH;
+    const int nw = D * p.r;
+
+    // W first (every thread a share), then the block: waiting for W leaves
+    // the block's loads in flight
+    constexpr int WU = 8192 / 256;                   // D * r <= 128 * 64
+    float wv_r[WU];
+#pragma unroll
+    for (int u = 0; u < WU; ++u)
+        if (u * 256 < nw) wv_r[u] = p.w[min(u * 256 + tid, nw - 1)];
+    uint4 x[IT];
+#pragma unroll
+    for (int a = 0; a < IT; ++a) {
+        const int t = min(rs + a * RSW, n_i - 1);
+        x[a] = ld_g16(base + (int64_t)(t0 + t) * X.sn + cc * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < WU; ++u)
+        if (u * 256 + tid < nw) w_s[u * 256 + tid] = wv_r[u];
+    __syncthreads();
+    if (!live) return;
+
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int a = 0; a < IT; ++a) {
+        const uint32_t keep = rs + a * RSW < n_i ? 0xFFFFFFFFu : 0u;
+        const uint32_t wd[4] = {x[a].x & keep, x[a].y & keep, x[a].z & keep, x[a].w & keep};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             acc[2 * e] += __uint_as_float(wd[e] << 16);
@@ -58,20 +187,27 @@ __global__ __launch_bounds__(256) void pool_proj_kernel(const PoolParams p, int 
         }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[rs][cc * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < D) {
-        float s = 0.f;
-        for (int r = 0; r < RS; ++r) s += red[r][tid];
-        mean[tid] = s / (float)n_i;
-        if (p.mean) p.mean[((int64_t)which * p.B * p.H * p.nB + item) * D + tid] = mean[tid];
+    for (int xm = CH; xm < 64; xm <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], xm, 64);
+    float *mean = mean_s + wv * D;
+    const float inv_n = 1.0f / (float)n_i;
+    const int64_t slot = (int64_t)which * items + item;
+    if (lane < CH) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mean[lane * 8 + e] = acc[e] * inv_n;
+        if (p.mean)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p.mean[slot * D + lane * 8 + e] = acc[e] * inv_n;
     }
-    __syncthreads();
-    if (tid < p.r) {
-        float a = 0.f;
-        for (int d = 0; d < D; ++d) a = __builtin_fmaf(p.w[d * p.r + tid], mean[d], a);
-        const int64_t rows = (int64_t)p.B * p.H * p.nB;
-        p.proj[((int64_t)which * rows + item) * p.r + tid] = a;
+    // the wavefront's own LDS writes are visible to its later reads
+    const int m0 = lane & 31, h = lane >> 5;
+    for (int m = m0; m < p.r; m += 32) {
+        float s = 0.f;
+#pragma unroll 8
+        for (int d = h * (D / 2); d < (h + 1) * (D / 2); ++d) s = __builtin_fmaf(w_s[d * p.r + m], mean[d], s);
+        s += __shfl_xor(s, 32, 64);
+        if (h == 0) p.proj[slot * p.r + m] = s;
     }
 }
 
@@ -79,39 +215,103 @@ hipError_t launch_pool_proj(const PoolParams &p, int block, int D, hipStream_t s
 {
     const int64_t items = (int64_t)p.B * p.H * p.nB;
     if (items == 0) return hipSuccess;
-    if (D == 128)
-        hipLaunchKernelGGL(pool_proj_kernel<128>, dim3((unsigned)items, 2), dim3(256), 0, s, p, block);
-    else if (D == 64)
-        hipLaunchKernelGGL(pool_proj_kernel<64>, dim3((unsigned)items, 2), dim3(256), 0, s, p, block);
-    else
-        return hipErrorInvalidValue;
+    if (p.r < 1 || p.r > 64 || 2 * items >= (1ll << 31)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)items, 2), thr(256);
+    const dim3 wgrid((unsigned)((2 * items + 3) / 4));
+    const size_t wsh = (size_t)(D * p.r + 4 * D) * sizeof(float);
+    if (block == 128 && D == 128) hipLaunchKernelGGL((pool_proj_kernel<128, 128>), grid, thr, 0, s, p);
+    else if (block == 128 && D == 64) hipLaunchKernelGGL((pool_wave_kernel<128, 64>), wgrid, thr, wsh, s, p);
+    else if (block == 64 && D == 128) hipLaunchKernelGGL((pool_wave_kernel<64, 128>), wgrid, thr, wsh, s, p);
+    else if (block == 64 && D == 64) hipLaunchKernelGGL((pool_wave_kernel<64, 64>), wgrid, thr, wsh, s, p);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// S_ij = p_i . p'_j : one workgroup per query-block row
+// S_ij = p_i . p'_j: one workgroup (256 threads) per head, QR query blocks
+// and CB key blocks.  The projected key blocks are staged in LDS transposed
+// ([m][j], rows padded by one word against bank conflicts), the projected
+// query blocks beside them (read as 4-wide broadcasts); every load of the
+// staging is issued before the first LDS write, so it costs one memory
+// round trip.  Thread t computes column t % CB of QR / 2 rows; each row of
+// S is written as coalesced runs.
 // ---------------------------------------------------------------------------
+namespace sc {
+constexpr int QR = 16;              // query blocks per workgroup
+constexpr int CB = 128;             // key blocks per workgroup
+constexpr int RP = 64;              // r padded (r <= 64)
+constexpr int KU = CB * RP / 256;   // staged key values per thread at most
+constexpr int QU = QR * RP / 256;   // staged query values per thread
+}
+
 __global__ __launch_bounds__(256) void scores_kernel(const ScoreParams p)
 {
-    __shared__ float pq[64];
-    const int item = blockIdx.x;
-    const int bh = item / p.nB;
-    const int64_t rows = (int64_t)p.BH * p.nB;
-    if (threadIdx.x < p.r) pq[threadIdx.x] = p.proj[(int64_t)item * p.r + threadIdx.x];
-    __syncthreads();
-    for (int j = threadIdx.x; j < p.nB; j += blockDim.x) {
-        const float *pk = p.proj + (rows + (int64_t)bh * p.nB + j) * p.r;
-        float s = 0.f;
-        for (int m = 0; m < p.r; ++m) s = __builtin_fmaf(pq[m], pk[m], s);
-        p.S[(int64_t)item * p.nB + j] = s;
+    __shared__ __attribute__((aligned(16))) float pkt[sc::RP][sc::CB + 1];
+    __shared__ __attribute__((aligned(16))) float pq[sc::QR][sc::RP];
+    const int tid = threadIdx.x;
+    const int nB = p.nB, r = p.r, r4 = (r + 3) & ~3;
+    const int rt = (nB + sc::QR - 1) / sc::QR, ct = (nB + sc::CB - 1) / sc::CB;
+    const int bh = blockIdx.x / (rt * ct), rest = blockIdx.x - bh * (rt * ct);
+    const int i0 = (rest / ct) * sc::QR, j0 = (rest % ct) * sc::CB;
+    const int nq = min(sc::QR, nB - i0), nj = min(sc::CB, nB - j0), nk = nj * r;
+    const int64_t rows = (int64_t)p.BH * nB;
+    const float *proj_q = p.proj + ((int64_t)bh * nB + i0) * r;
+    const float *proj_k = p.proj + (rows + (int64_t)bh * nB + j0) * r;
+    const float inv_r = 1.0f / (float)r;
+    // indices past the end re-read a valid element, dropped after
+    float vk[sc::KU], vq[sc::QU];
+#pragma unroll
+    for (int u = 0; u < sc::QU; ++u) {
+        const int x = u * 256 + tid, q = x / sc::RP, m = x % sc::RP;
+        vq[u] = proj_q[(q < nq && m < r) ? q * r + m : 0];
     }
+#pragma unroll
+    for (int u = 0; u < sc::KU; ++u) vk[u] = proj_k[min(u * 256 + tid, nk - 1)];
+    // the loads stay here, not sunk into the guarded writes below
+#pragma unroll
+    for (int u = 0; u < sc::KU; ++u) asm volatile("" ::"v"(vk[u]));
+#pragma unroll
+    for (int u = 0; u < sc::KU; ++u) {
+        const int x = u * 256 + tid;
+        const int j = div_small(x, inv_r), m = x - j * r;
+        if (x < nk) pkt[m][j] = vk[u];
+    }
+    for (int x = tid; x < (r4 - r) * sc::CB; x += 256) pkt[r + x / sc::CB][x % sc::CB] = 0.f;
+#pragma unroll
+    for (int u = 0; u < sc::QU; ++u) {
+        const int x = u * 256 + tid, q = x / sc::RP, m = x % sc::RP;
+        pq[q][m] = (q < nq && m < r) ? vq[u] : 0.f;
+    }
+    __syncthreads();
+    const int col = tid % sc::CB, q0 = (tid / sc::CB) * (sc::QR / 2);
+    if (col >= nj) return;
+    float acc[sc::QR / 2];
+#pragma unroll
+    for (int q = 0; q < sc::QR / 2; ++q) acc[q] = 0.f;
+    for (int m = 0; m < r4; m += 4) {
+        const float k0 = pkt[m][col], k1 = pkt[m + 1][col], k2 = pkt[m + 2][col], k3 = pkt[m + 3][col];
+#pragma unroll
+        for (int q = 0; q < sc::QR / 2; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(&pq[q0 + q][m]);
+            acc[q] = __builtin_fmaf(v.x, k0, acc[q]);
+            acc[q] = __builtin_fmaf(v.y, k1, acc[q]);
+            acc[q] = __builtin_fmaf(v.z, k2, acc[q]);
+            acc[q] = __builtin_fmaf(v.w, k3, acc[q]);
+        }
+    }
+    float *out = p.S + ((int64_t)bh * nB + i0 + q0) * nB + j0 + col;
+#pragma unroll
+    for (int q = 0; q < sc::QR / 2; ++q)
+        if (q0 + q < nq) out[(int64_t)q * nB] = acc[q];
 }
 
 hipError_t launch_scores(const ScoreParams &p, hipStream_t s)
 {
-    const int64_t items = (int64_t)p.BH * p.nB;
-    if (items == 0) return hipSuccess;
-    hipLaunchKernelGGL(scores_kernel, dim3((unsigned)items), dim3(256), 0, s, p);
+    if ((int64_t)p.BH * p.nB == 0) return hipSuccess;
+    if (p.r < 1 || p.r > sc::RP) return hipErrorInvalidValue;
+    const int64_t wgs = (int64_t)((p.nB + sc::QR - 1) / sc::QR) * ((p.nB + sc::CB - 1) / sc::CB) * p.BH;
+    if (wgs >= (1ll << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scores_kernel, dim3((unsigned)wgs), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -2,14 +2,16 @@
 // 2.3; SparseD notes, isolated selection).
 //
 // Three small kernels:
-//  1. select: one wavefront per query-block row.  Text rows keep every
+//  1. select: one wavefront per query-block row, four to a workgroup; the
+//     row's scores are staged in LDS in one round trip.  Text rows keep every
 //     column; other rows keep the text columns plus, per column group, the
 //     k best columns.  Only the k-th best score of a group is needed, not a
 //     sorted order: each score becomes an order-preserving 32-bit key
 //     (-0.0 folded onto +0.0, NaN mapped below -inf), the group's keys sit in
 //     registers (lane l holds columns c + 64 e + l), and a bitwise search
 //     from the top bit finds the largest key T with at least k keys >= T --
-//     32 rounds of one compare and one ballot per register.  The row keeps
+//     at most 32 rounds of one compare and one ballot per register (it stops
+//     early at a probe with exactly k keys at or above it).  The row keeps
 //     every key above T and, of the keys equal to T, the lowest columns up
 //     to k (lane prefix counts of the equality ballots, taken in column
 //     order).  The kept set is a per-row bitmask in LDS; its population
@@ -20,31 +22,55 @@
 // When the column groups are pairwise disjoint and leave the text columns
 // alone, every row's length is known beforehand (text rows nB, the others
 // text_blocks + sum of k), so select writes its row_ptr entry and its
-// column indices itself and the other two kernels are not launched.
+// column indices itself (a lane per column, positions from ballots) and the
+// other two kernels are not launched.
 #include "common.h"
 #include "internal.h"
 #include "topk.h"
 
 namespace bsa {
 
-__global__ __launch_bounds__(64) void select_kernel(const SelectParams p)
-{
-    __shared__ uint32_t wbits[kMaxSelectBlocks / 32];
-    const int lane = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const int i = (int)(row % p.nB);
-    const float *srow = p.S + row * p.nB;
+namespace sel {
+constexpr int RW = 4;                                   // rows (wavefronts) per workgroup
+constexpr int LU = kMaxSelectBlocks / 64;               // score loads per lane, at most
+}
 
-    for (int w = lane; w < p.words; w += 64) {
-        uint32_t v = 0u;
-        const int lim = (i < p.text_blocks) ? p.nB : p.text_blocks;   // dense row / text columns
-        const int lo = w * 32;
-        if (lim >= lo + 32) v = 0xFFFFFFFFu;
-        else if (lim > lo) v = (1u << (lim - lo)) - 1u;
-        wbits[w] = v;
+__global__ __launch_bounds__(256) void select_kernel(const SelectParams p)
+{
+    __shared__ float srow_s[sel::RW][kMaxSelectBlocks];
+    __shared__ uint32_t wbits_s[sel::RW][kMaxSelectBlocks / 32];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nB = p.nB;
+    // a workgroup holds RW consecutive rows of one head
+    const uint32_t per_head = (uint32_t)(nB + sel::RW - 1) / sel::RW;
+    const uint32_t bh = blockIdx.x / per_head;
+    const int i = (int)(blockIdx.x - bh * per_head) * sel::RW + wv;
+    const bool live = i < nB;
+    const int64_t row = (int64_t)bh * nB + i;
+    float *srow = srow_s[wv];
+    uint32_t *wbits = wbits_s[wv];
+    // the whole score row in one round trip: every load issued before the
+    // first LDS write (loads past the row re-read its last element)
+    if (live) {
+        const float *g = p.S + row * nB;
+        float v[sel::LU] = {};
+#pragma unroll
+        for (int u = 0; u < sel::LU; ++u)
+            if (u * 64 < nB) v[u] = g[min(u * 64 + lane, nB - 1)];
+#pragma unroll
+        for (int u = 0; u < sel::LU; ++u) asm volatile("" ::"v"(v[u]));
+#pragma unroll
+        for (int u = 0; u < sel::LU; ++u)
+            if (u * 64 + lane < nB) srow[u * 64 + lane] = v[u];
+        const int lim = (i < p.text_blocks) ? nB : p.text_blocks;   // dense row / text columns
+        for (int w = lane; w < p.words; w += 64) {
+            const int lo = w * 32;
+            wbits[w] = lim >= lo + 32 ? 0xFFFFFFFFu : (lim > lo ? (1u << (lim - lo)) - 1u : 0u);
+        }
     }
     __syncthreads();
-    if (i >= p.text_blocks) {
+    if (live && i >= p.text_blocks) {
         for (int g = 0; g < p.n_groups; ++g) {
             const int c0 = p.g_begin[g], c1 = p.g_end[g], kk = p.g_k[g];
             const int width = c1 - c0;
@@ -56,32 +82,20 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectParams p)
             else if (width <= 512) select_group<8>(srow, c0, c1, kk, wbits, p.words);
             else select_group<16>(srow, c0, c1, kk, wbits, p.words);
         }
-        __syncthreads();
     }
+    __syncthreads();
+    if (!live) return;
     if (p.direct) {
         // closed-form offsets: each head holds text_blocks rows of nB columns,
         // then nB - text_blocks rows of row_len columns
         const int64_t tb = p.text_blocks;
-        const int64_t head = tb * p.nB + (int64_t)(p.nB - tb) * p.row_len;
-        int64_t start = (row / p.nB) * head + (i < tb ? (int64_t)i * p.nB : tb * p.nB + (int64_t)(i - tb) * p.row_len);
+        const int64_t head = tb * nB + (int64_t)(nB - tb) * p.row_len;
+        const int64_t start = (int64_t)bh * head + (i < tb ? (int64_t)i * nB : tb * nB + (int64_t)(i - tb) * p.row_len);
         if (lane == 0) {
-            p.row_ptr[row + 1] = (int32_t)(start + (i < tb ? p.nB : p.row_len));
+            p.row_ptr[row + 1] = (int32_t)(start + (i < tb ? nB : p.row_len));
             if (row == 0) p.row_ptr[0] = 0;
         }
-        for (int w0 = 0; w0 < p.words; w0 += 64) {
-            const int w = w0 + lane;
-            uint32_t v = w < p.words ? wbits[w] : 0u;
-            const int c = __popc(v);
-            const int incl = wave_incl_scan(c);
-            int64_t pos = start + incl - c;
-            while (v) {
-                const int bit = __ffs(v) - 1;
-                v &= v - 1u;
-                if (pos < p.capacity) p.col_idx[pos] = w * 32 + bit;
-                ++pos;
-            }
-            start += __shfl(incl, 63, 64);
-        }
+        write_row_columns(wbits, nB, start, p.col_idx, p.capacity);
         return;
     }
     int cnt = 0;
@@ -101,7 +115,10 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectParams p)
 hipError_t launch_select(const SelectParams &p, hipStream_t s)
 {
     if (p.rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)p.rows), dim3(64), 0, s, p);
+    if (p.nB > kMaxSelectBlocks) return hipErrorInvalidValue;
+    const int64_t heads = p.rows / p.nB, per_head = (p.nB + sel::RW - 1) / sel::RW;
+    if (heads * per_head >= (1ll << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(select_kernel, dim3((unsigned)(heads * per_head)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -32,14 +32,19 @@ __device__ void select_group(const float *srow, int c0, int c1, int kk, uint32_t
         const int col = c0 + e * 64 + lane;
         key[e] = col < c1 ? score_key(srow[col]) : 0u;
     }
-    // T = the kk-th largest key: the largest value with >= kk keys at or above it
+    // T = the kk-th largest key: the largest value with >= kk keys at or
+    // above it.  The search may stop at the first probe with exactly kk keys
+    // at or above it: the kept set (below) is then those kk keys.
     uint32_t T = 0u;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = T | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) cnt += ballot_count(key[e] >= cand);
-        if (cnt >= kk) T = cand;
+        if (cnt >= kk) {
+            T = cand;
+            if (cnt == kk) break;
+        }
     }
     int need = kk;
 #pragma unroll
@@ -88,17 +93,30 @@ __device__ void select_rows(const float (&s)[R][E], int c0, int c1, int kk, uint
             key[q][e] = (col >= c0 && col < c1) ? score_key(s[q][e]) : 0u;
         }
     uint32_t T[R];
+    bool live[R];
 #pragma unroll
-    for (int q = 0; q < R; ++q) T[q] = 0u;
+    for (int q = 0; q < R; ++q) {
+        T[q] = 0u;
+        live[q] = true;
+    }
+    // the rows' searches run in lockstep; a row stops at its first probe
+    // with exactly kk keys at or above it (as in select_group)
     for (int bit = 31; bit >= 0; --bit) {
+        bool any = false;
 #pragma unroll
         for (int q = 0; q < R; ++q) {
+            if (!live[q]) continue;
             const uint32_t cand = T[q] | (1u << bit);
             int cnt = 0;
 #pragma unroll
             for (int e = 0; e < E; ++e) cnt += ballot_count(key[q][e] >= cand);
-            if (cnt >= kk) T[q] = cand;
+            if (cnt >= kk) {
+                T[q] = cand;
+                live[q] = cnt != kk;
+            }
+            any = any || live[q];
         }
+        if (!any) break;
     }
 #pragma unroll
     for (int q = 0; q < R; ++q) {
@@ -119,6 +137,24 @@ __device__ void select_rows(const float (&s)[R][E], int c0, int c1, int kk, uint
                 if (v) atomicOr(&wb[q][2 * e + lane], v);
             }
         }
+    }
+}
+
+// Write the set bits of a row bitmask of nB columns as ascending column
+// indices from col_idx[start] (entries at or past capacity are dropped): a
+// lane per column, 64 columns a round, each position from the lanes below.
+__device__ __forceinline__ void write_row_columns(const uint32_t *wb, int nB, int64_t start, int32_t *col_idx,
+                                                  int64_t capacity)
+{
+    const int lane = threadIdx.x & 63;
+    for (int c0 = 0; c0 < nB; c0 += 64) {
+        const int col = c0 + lane;
+        const bool on = col < nB && ((wb[col >> 5] >> (col & 31)) & 1u);
+        const uint64_t m = __ballot(on);
+        const int64_t pos =
+            start + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (on && pos < capacity) col_idx[pos] = col;
+        start += __popcll(m);
     }
 }
 

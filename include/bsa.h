@@ -200,18 +200,18 @@ bsa_status bsa_select_topk(const float *scores, int64_t B, int64_t H, int32_t n_
  * mean-pool, one small projection, dot-product score, top-k; [W] 2.3: text
  * rows and columns dense).  Computes the MEANPOOL_PROJ scores of
  * bsa_pool_scores and the selection of bsa_select_topk in two short
- * kernels: every block of Q and K is pooled and projected once, then one
- * workgroup per head scores and selects that head's rows without the score
- * matrix leaving the chip.  The scores agree with bsa_pool_scores to fp32
- * rounding (the summation order differs); the CSR is the one
- * bsa_select_topk gives for the scores written to `scores`.
+ * kernels: every block of Q and K is pooled and projected once (the
+ * pooling kernel of bsa_pool_scores), then one workgroup per 16 rows of a
+ * head scores and selects them without the score matrix leaving the chip.
+ * The scores equal bsa_pool_scores' bit for bit (same pooling, same
+ * summation order); the CSR is the one bsa_select_topk gives for them.
  *
  * q, k, block, w [D][r] and r as in bsa_pool_scores; text_blocks, groups,
  * row_ptr, col_idx and capacity as in bsa_select_topk.  scores: device fp32
  * [B][H][nB][nB] or NULL (not written).
- * Limits: nB <= 256 and nB * r <= 4096; the groups with k > 0 pairwise
- * disjoint and clear of the text columns (every row's length is then known
- * in advance).  Outside them the call fails with BSA_ERR_UNSUPPORTED; use
+ * Limits: nB <= 256 and nB * r4 <= 4096 (r4 = r rounded up to a multiple
+ * of 4); the groups with k > 0 pairwise disjoint and clear of the text
+ * columns (every row's length is then known in advance).  Outside them the call fails with BSA_ERR_UNSUPPORTED; use
  * bsa_pool_scores and bsa_select_topk.
  * workspace: bsa_select_meanpool_workspace_size() bytes, 16-byte aligned
  * (the projected blocks; contents on return are unspecified).

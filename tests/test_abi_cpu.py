@@ -431,6 +431,7 @@ def test_pool_scores_noalloc_rejects_requests_beyond_its_scratch(mode, N, D, blo
     (4352, 64, 32, 4, [(4, 60, 8), (50, 68, 2)], 2, "disjoint"),   # overlapping groups
     (300 * 64, 64, 8, 0, [(0, 300, 10)], 2, "at most 256"),        # more blocks than the fused kernel holds
     (4352, 64, 64, 4, [(4, 68, 16)], 2, "at most"),                # nB * r above 4096
+    (220 * 64, 64, 18, 4, [(4, 220, 16)], 2, "at most"),           # nB * r <= 4096, r padded to 20 is not
     (4352, 64, 32, 4, [(4, 68, 70)], 1, "invalid"),                # k above the group's width
 ])
 def test_select_meanpool_validation(N, block, r, tb, groups, code, msg):
@@ -451,3 +452,5 @@ def test_select_meanpool_applies_mirrors_the_abi_limits():
     assert not bsa.select_meanpool_applies(68, 32, 4, [(4, 60, 8), (50, 68, 2)])
     assert not bsa.select_meanpool_applies(257, 8, 0, [(0, 257, 10)])
     assert not bsa.select_meanpool_applies(68, 64, 4, [(4, 68, 16)])
+    assert bsa.select_meanpool_applies(256, 13, 2, [(2, 200, 50), (200, 256, 9)])   # r padded to 16: 4096
+    assert not bsa.select_meanpool_applies(220, 18, 4, [(4, 220, 16)])               # r padded to 20: 4400

@@ -1,6 +1,7 @@
 """The fused content-driven selection (bsa_select_meanpool: mean-pool,
 projection, scores and top-k in one call) against the oracle: scores to
-fp32 rounding of the fp64 definition, and the CSR bit-exact with the
+fp32 rounding of the fp64 definition (and bit for bit those of
+bsa_pool_scores), and the CSR bit-exact with the
 oracle's selection on the kernel's own fp32 scores (the same rule the
 C5 test applies), plus the near-tie rule against the oracle's fp64 scores."""
 import math
@@ -37,6 +38,10 @@ def _check_fused(q, k, w, block, tb, groups, ws=None):
     torch.cuda.synchronize()
     So = oracle.scores_meanpool_proj(q, k, block, w)
     Sg = S.cpu().numpy()
+    # the same pooling kernel and summation order as bsa_pool_scores: equal bit for bit
+    Sp = bsa.pool_scores(to_dev_bf16(q), to_dev_bf16(k), block, bsa.SCORE_MEANPOOL_PROJ,
+                         w=torch.from_numpy(w).to(dev())).cpu().numpy()
+    np.testing.assert_array_equal(Sg.view(np.uint32), Sp.view(np.uint32))
     assert np.all(np.abs(Sg.astype(np.float64) - So) <= 1e-5 * np.abs(So).max(axis=-1, keepdims=True) + 1e-7)
     rpg, cig = rp.cpu().numpy(), ci.cpu().numpy()
     check_csr_valid(rpg, cig[:rpg[-1]], nB)
@@ -60,6 +65,7 @@ FUSED_CASES = [
     (1, 2, 200 * 64 + 5, 64, 64, 16, 3, ((3, 120, 30), (130, 201, 71), (120, 130, 0)), 504),  # k = width, k = 0, nB > 128
     (1, 1, 3 * 128 + 40, 128, 128, 64, 2, (), 505),                    # text columns only
     (1, 3, 40 * 64, 64, 64, 8, 40, ((0, 40, 3),), 506),                # every row a text row
+    (1, 2, 256 * 64, 64, 64, 13, 2, ((2, 200, 50), (200, 256, 9)), 507),  # nB and padded r at the limits
 ]
 
 
