@@ -362,11 +362,13 @@ __device__ __forceinline__ void last_step(const uint16_t *__restrict__ Vp, bool 
     pv_mfma<BETA, D>(Vp, pf, st);
 }
 
-// Occupancy: two waves per SIMD (β=128: two 4-wave workgroups per CU; β=64,
-// D=64: four 2-wave workgroups, whose 32 KB of tiles fit the LDS four
-// times).  The launch bound's second argument is waves per SIMD.
+// Occupancy: two waves per SIMD at β=128 (two 4-wave workgroups per CU).
+// β=64, D=64 asks for three: the register budget of 168 holds its state
+// without spilling (at two the allocator spends all 256 and still spills),
+// and five 2-wave workgroups, whose 32 KB of tiles fit the LDS five times,
+// share a CU.  The launch bound's second argument is waves per SIMD.
 template <int BETA, int D>
-constexpr int fwd_waves_per_simd() { return 2; }
+constexpr int fwd_waves_per_simd() { return (BETA == 64 && D == 64) ? 3 : 2; }
 
 // NBM: neighbourhood masking of the tiles the layout flags as partial.
 template <int BETA, int D, bool NBM>
