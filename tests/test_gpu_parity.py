@@ -377,11 +377,15 @@ def test_select_nan_and_infinite_scores(B, H, nB, tb, groups):
 # ---------------------------------------------------------------------------
 # block scores
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("B,H,N,D,block", [(2, 3, 5 * 64 + 9, 64, 64), (1, 2, 4 * 128, 128, 128),
-                                           (1, 2, 3 * 128 + 1, 64, 128)])
-def test_meanpool_scores_and_selection(B, H, N, D, block):
+@pytest.mark.parametrize("B,H,N,D,block,r", [
+    (2, 3, 5 * 64 + 9, 64, 64, 32), (1, 2, 4 * 128, 128, 128, 32), (1, 2, 3 * 128 + 1, 64, 128, 32),
+    (1, 2, 7 * 64 + 5, 128, 64, 32),          # block 64 at D 128
+    (1, 1, 300 * 64 + 3, 64, 64, 19),         # 301 blocks: several 16 x 128 score tiles, r not a multiple of 4
+    (1, 1, 140 * 128, 128, 128, 64),          # the widest r, 140 x 140 scores
+])
+def test_meanpool_scores_and_selection(B, H, N, D, block, r):
     q, k, _ = synth.random_qkv(B, H, N, D, seed=150 + N)
-    w = np.random.default_rng(151).standard_normal((D, 32)).astype(np.float32) / math.sqrt(D)
+    w = np.random.default_rng(151).standard_normal((D, r)).astype(np.float32) / math.sqrt(D)
     S = bsa.pool_scores(to_dev_bf16(q), to_dev_bf16(k), block, bsa.SCORE_MEANPOOL_PROJ,
                         w=torch.from_numpy(w).to(dev()))
     torch.cuda.synchronize()
