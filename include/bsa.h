@@ -201,8 +201,8 @@ bsa_status bsa_select_topk(const float *scores, int64_t B, int64_t H, int32_t n_
  * rows and columns dense).  Computes the MEANPOOL_PROJ scores of
  * bsa_pool_scores and the selection of bsa_select_topk in two short
  * kernels: every block of Q and K is pooled and projected once (the
- * pooling kernel of bsa_pool_scores), then one workgroup per 16 rows of a
- * head scores and selects them without the score matrix leaving the chip.
+ * pooling kernel of bsa_pool_scores), then one wavefront per row scores
+ * and selects it without the score matrix leaving the chip.
  * The scores equal bsa_pool_scores' bit for bit (same pooling, same
  * summation order); the CSR is the one bsa_select_topk gives for them.
  *
