@@ -38,7 +38,6 @@ mask that is selected once and reused:
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import threading
 from typing import Optional, Sequence, Tuple
@@ -160,6 +159,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                 TP, TP, TP, V, SZ, V]),
             "bsa_backward_neighborhood_natural": (I32, [TP, TP, TP, TP, TP, I32, V, V, V,
                                                         ctypes.POINTER(BsaNeighborhood), V, F, TP, TP, TP, V, SZ, V]),
+            "bsa_reuse_full_steps": (I32, [I32, ctypes.c_double]),
+            "bsa_reuse_step_action": (I32, [I32, ctypes.c_double, I32]),
             "bsa_status_string": (ctypes.c_char_p, [I32]),
             "bsa_last_error": (ctypes.c_char_p, []),
             "bsa_version": (ctypes.c_char_p, []),
@@ -855,24 +856,28 @@ class ReuseSchedule:
     selected once and reused (SparseD, "skipping sparse" and "sparse
     reuse"): steps 0 .. n_full-1 run full attention, n_full = floor(T *
     skip); step n_full selects the mask (exact avgpool scores and isolated
-    top-k) and runs sparse attention with it; every later step reuses it."""
+    top-k) and runs sparse attention with it; every later step reuses it.
+    The schedule comes from bsa_reuse_full_steps / bsa_reuse_step_action."""
 
     FULL, SELECT, SPARSE = "full", "select", "sparse"
+    _ACTIONS = (FULL, SELECT, SPARSE)
 
     def __init__(self, steps: int, skip: float = 0.2):
-        if steps < 1 or not (0.0 <= skip <= 1.0):
-            raise ValueError("steps >= 1 and 0 <= skip <= 1 required")
+        if not (1 <= steps < 2 ** 31) or not (0.0 <= skip <= 1.0):
+            raise ValueError("1 <= steps < 2^31 and 0 <= skip <= 1 required")
         self.steps = int(steps)
         self.skip = float(skip)
-        # floor, with a guard against T * skip landing a rounding error below an integer
-        self.n_full = min(self.steps, int(math.floor(self.steps * self.skip + 1e-9)))
+        self.n_full = int(load().bsa_reuse_full_steps(self.steps, self.skip))
+        if self.n_full < 0:
+            raise ValueError("bsa_reuse_full_steps rejected the schedule")
 
     def action(self, step: int) -> str:
         if not 0 <= step < self.steps:
             raise IndexError(step)
-        if step < self.n_full:
-            return self.FULL
-        return self.SELECT if step == self.n_full else self.SPARSE
+        a = load().bsa_reuse_step_action(self.steps, self.skip, int(step))
+        if a < 0:
+            raise ValueError("bsa_reuse_step_action rejected the step")
+        return self._ACTIONS[a]
 
     def counts(self) -> dict:
         n_sel = 1 if self.n_full < self.steps else 0

@@ -154,6 +154,23 @@ const char *bsa_status_string(bsa_status s)
 
 const char *bsa_last_error(void) { return g_err; }
 
+int32_t bsa_reuse_full_steps(int32_t steps, double skip)
+{
+    if (steps < 1 || !(skip >= 0.0 && skip <= 1.0)) return -1;
+    // floor of steps * skip; the guard keeps a product rounded just below an
+    // integer (10 * 0.3 = 2.9999999999999996) at that integer
+    const double f = std::floor((double)steps * skip + 1e-9);
+    return (int32_t)std::min<double>(steps, f);
+}
+
+int32_t bsa_reuse_step_action(int32_t steps, double skip, int32_t step)
+{
+    const int32_t n_full = bsa_reuse_full_steps(steps, skip);
+    if (n_full < 0 || step < 0 || step >= steps) return -1;
+    if (step < n_full) return BSA_STEP_FULL;
+    return step == n_full ? BSA_STEP_SELECT : BSA_STEP_SPARSE;
+}
+
 const char *bsa_version(void) { return "bsa 0.1.0 gfx950"; }
 
 // ---------------------------------------------------------------------------

@@ -551,6 +551,23 @@ bsa_status bsa_mask_jaccard(int64_t B, int64_t H, int32_t n_blocks, const int32_
                             double *jaccard, void *stream);
 
 /* ------------------------------------------------------------------------
+ * bsa_reuse_full_steps, bsa_reuse_step_action -- the select-once schedule
+ * of [S] (skipping sparse, then sparse reuse) over `steps` denoising steps.
+ * Steps 0 .. n_full-1 run full attention, n_full = floor(steps * skip); a
+ * product that lands within 1e-9 below an integer counts as that integer
+ * (10 x 0.3 gives 3).  Step n_full computes the exact avgpool scores,
+ * selects the mask and runs sparse attention with it; every later step
+ * reuses that mask.  Host only, nothing is enqueued.
+ * bsa_reuse_full_steps returns n_full (0 .. steps), or -1 when steps < 1 or
+ * skip is not in [0, 1] (NaN included).  bsa_reuse_step_action returns the
+ * BSA_STEP_* action of step `step`, or -1 on the same errors or when step
+ * is not in [0, steps).
+ * ---------------------------------------------------------------------- */
+enum { BSA_STEP_FULL = 0, BSA_STEP_SELECT = 1, BSA_STEP_SPARSE = 2 };
+int32_t bsa_reuse_full_steps(int32_t steps, double skip);
+int32_t bsa_reuse_step_action(int32_t steps, double skip, int32_t step);
+
+/* ------------------------------------------------------------------------
  * Utilities.
  * ---------------------------------------------------------------------- */
 /* Name of a status code (static string). */

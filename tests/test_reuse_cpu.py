@@ -31,3 +31,20 @@ def test_amortised_speedup():
     s = bsa.ReuseSchedule(10, 0.2)          # 2 full, 1 select + sparse, 7 sparse
     # 10 * 4 / (2 * 4 + (3 + 1) + 7 * 1) = 40 / 19
     assert s.amortised_speedup(4.0, 3.0, 1.0) == pytest.approx(40 / 19)
+
+
+def test_c_abi_schedule_calls():
+    lib = bsa.load()
+    # exhaustive over small T against the definition: first floor(T*skip) steps full,
+    # the next one selects, the rest reuse (skip values that are exact in binary)
+    for T in range(1, 40):
+        for skip in (0.0, 0.25, 0.5, 0.75, 1.0):
+            n = int(T * skip)
+            assert lib.bsa_reuse_full_steps(T, skip) == n
+            want = [0] * n + ([1] if n < T else []) + [2] * (T - n - 1)
+            assert [lib.bsa_reuse_step_action(T, skip, s) for s in range(T)] == want
+    assert lib.bsa_reuse_full_steps(0, 0.2) == -1
+    assert lib.bsa_reuse_full_steps(10, -0.1) == -1
+    assert lib.bsa_reuse_full_steps(10, float("nan")) == -1
+    assert lib.bsa_reuse_step_action(10, 0.2, 10) == -1
+    assert lib.bsa_reuse_step_action(10, 0.2, -1) == -1
