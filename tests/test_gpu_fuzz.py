@@ -245,3 +245,49 @@ def test_fuzz_forward_fp8_exact_weights(seed):
     if modes is not None and (~comp).any():
         np.testing.assert_array_equal(bf16_bits(O)[:, ~comp], cache[:, ~comp])
         np.testing.assert_array_equal(L.cpu().numpy()[:, ~comp], lse_c[:, ~comp])
+
+
+# ---------------------------------------------------------------------------
+# 2-D neighbourhood geometries: permutation and layout bit for bit, and the
+# natural-order forward against the oracle's per-token masked softmax
+# ---------------------------------------------------------------------------
+def _random_geometry(r):
+    block = int(r.choice([64, 128]))
+    tw = int(r.choice([8, 16, 32, 64] + ([128] if block == 128 else [])))
+    th = block // tw
+    R = th * int(r.integers(1, max(2, 48 // th + 1)))
+    C = tw * int(r.integers(1, max(2, 256 // tw + 1)))
+    while R * C > 4096:
+        R, C = (R - th, C) if R > th else (R, C - tw)
+    T = block * int(r.integers(0, 3))
+    window = (int(r.integers(1, R + 1)), int(r.integers(1, C + 1)))
+    stride = (int(r.integers(1, min(4, window[0]) + 1)), int(r.integers(1, min(4, window[1]) + 1)))
+    return T, (R, C), (th, tw), window, stride, block
+
+
+@pytest.mark.parametrize("seed", range(1400, 1424))
+def test_fuzz_neighborhood(seed):
+    r = np.random.default_rng(seed)
+    T, grid, tile, window, stride, block = _random_geometry(r)
+    D = int(r.choice([64, 128]))
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 3))
+    N = T + grid[0] * grid[1]
+    _log(f"fuzz neighbourhood seed={seed} T={T} grid={grid} tile={tile} window={window} stride={stride} D={D}")
+    nb = bsa.neighborhood(T, grid, tile, window, stride)
+    q, k, v = synth.random_qkv(B, H, N, D, seed=seed)
+    perm = oracle.tile_permutation(T, grid, tile)
+    y = bsa.permute_tokens(to_dev_bf16(q), nb)
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(y), q[:, :, perm])
+    rpo, cio, flo = oracle.neighborhood_layout(T, grid, tile, window, stride)
+    nnz = int(rpo[-1])
+    want_rp = np.concatenate([[0]] + [rpo[1:] + h * nnz for h in range(B * H)])
+    np.testing.assert_array_equal(rp.cpu().numpy(), want_rp)
+    np.testing.assert_array_equal(ci.cpu().numpy()[:B * H * nnz], np.tile(cio, B * H))
+    np.testing.assert_array_equal(fl.cpu().numpy()[:B * H * nnz], np.tile(flo.astype(np.int32), B * H))
+    # the forward on natural-order tensors (gathered and scattered by the kernel)
+    O, L = bsa.forward_neighborhood(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), rp, ci, fl, nb, natural=True)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.forward_neighborhood(q, k, v, T, grid, window, stride)
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, f"neighbourhood fuzz {seed}")
