@@ -291,3 +291,85 @@ def test_fuzz_neighborhood(seed):
     torch.cuda.synchronize()
     Oo, Lo = oracle.forward_neighborhood(q, k, v, T, grid, window, stride)
     check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, f"neighbourhood fuzz {seed}")
+
+
+# ---------------------------------------------------------------------------
+# backward, exact avgpool scores and the score gradient
+# ---------------------------------------------------------------------------
+def _rel_close(got, want, max_rel, mean_rel, what):
+    d = np.abs(got - want)
+    mx = float(d.max()) / max(float(np.abs(want).max()), 1e-30)
+    mean = float(d.mean()) / max(float(np.abs(want).mean()), 1e-30)
+    assert mx <= max_rel and mean <= mean_rel, f"{what}: max {mx:.2e}, mean {mean:.2e}"
+
+
+@pytest.mark.parametrize("seed", range(1500, 1516))
+def test_fuzz_backward(seed):
+    """Tolerances as for the hand-picked backward cases: bf16 P, dS and
+    gradients leave a few 2^-9 of each gradient's size (2e-2 of its largest
+    element, 1e-2 of its mean magnitude)."""
+    r = np.random.default_rng(seed)
+    block = int(r.choice([64, 128]))
+    D = int(r.choice([64, 128]))
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 3))
+    N = int(r.integers(1, 5 * block))
+    scale = float(r.uniform(0.05, 0.15)) if r.random() < 0.5 else None
+    _log(f"fuzz backward seed={seed} B={B} H={H} N={N} D={D} block={block} scale={scale}")
+    q, k, v = synth.random_qkv(B, H, N, D, seed=seed)
+    g = synth.random_qkv(B, H, N, D, seed=seed + 50)[0]
+    nB = -(-N // block)
+    rp, ci = synth.random_block_lists(B, H, nB, seed=seed + 1, density=float(r.uniform(0.2, 1.0)),
+                                      empty_rows=min(1, B * H * nB), full_rows=min(1, max(0, B * H * nB - 1)))
+    qd, kd, vd, gd = (to_dev_bf16(a) for a in (q, k, v, g))
+    rpd, cid = _i32(rp), _i32(ci)
+    O, L = bsa.forward(qd, kd, vd, block, rpd, cid, scale=scale)
+    dq, dk, dv = bsa.backward(qd, kd, vd, O, gd, block, rpd, cid, L, scale=scale)
+    torch.cuda.synchronize()
+    wq, wk, wv = oracle.backward(q, k, v, g, block, rp, ci, scale=scale)
+    for got, want, name in ((dq, wq, "dQ"), (dk, wk, "dK"), (dv, wv, "dV")):
+        if np.abs(want).max() == 0:
+            assert torch.all(got == 0), name
+        else:
+            _rel_close(bf16_to_f64(got), want, 2e-2, 1e-2, f"fuzz {seed} {name}")
+
+
+@pytest.mark.parametrize("seed", range(1600, 1612))
+def test_fuzz_exact_scores(seed):
+    """fp32 sums of exp2 against the fp64 oracle: 2e-5 of each row's
+    largest score, as for the hand-picked cases."""
+    r = np.random.default_rng(seed)
+    block = int(r.choice([64, 128]))
+    D = int(r.choice([64, 128]))
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 3))
+    N = int(r.integers(1, 8 * block))
+    sigma = float(r.uniform(0.5, 2.0))
+    _log(f"fuzz exact scores seed={seed} B={B} H={H} N={N} D={D} block={block} sigma={sigma:.2f}")
+    q, k, _ = synth.random_qkv(B, H, N, D, seed=seed, scale=sigma)
+    S = bsa.pool_scores(to_dev_bf16(q), to_dev_bf16(k), block, bsa.SCORE_EXACT_AVGPOOL)
+    torch.cuda.synchronize()
+    So = oracle.scores_exact_avgpool(q, k, block)
+    err = np.abs(S.cpu().numpy().astype(np.float64) - So) / np.abs(So).max(axis=-1, keepdims=True)
+    assert err.max() <= 2e-5, f"max rel err {err.max():.2e}"
+
+
+@pytest.mark.parametrize("seed", range(1700, 1712))
+def test_fuzz_score_grad(seed):
+    """fp32 throughout: 1e-4 of the largest element, 1e-5 of the mean
+    magnitude, as for the hand-picked cases."""
+    r = np.random.default_rng(seed)
+    block = int(r.choice([64, 128]))
+    D = int(r.choice([64, 128]))
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 3))
+    N = int(r.integers(1, 8 * block))
+    rr = int(r.integers(1, 65))
+    _log(f"fuzz score grad seed={seed} B={B} H={H} N={N} D={D} block={block} r={rr}")
+    q, k, _ = synth.random_qkv(B, H, N, D, seed=seed)
+    w = (r.standard_normal((D, rr)) / np.sqrt(D)).astype(np.float32)
+    nB = -(-N // block)
+    dS = r.standard_normal((B, H, nB, nB)).astype(np.float32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+    dw, dqp, dkp = bsa.score_grad(to_dev_bf16(q), to_dev_bf16(k), block, t(w), t(dS), pooled=True)
+    torch.cuda.synchronize()
+    wdw, wdq, wdk = oracle.score_grad(q, k, block, w, dS.astype(np.float64))
+    for got, want, name in ((dw, wdw, "dW"), (dqp, wdq, "dQ pooled"), (dkp, wdk, "dK pooled")):
+        _rel_close(got.cpu().numpy().astype(np.float64), want, 1e-4, 1e-5, f"fuzz {seed} {name}")
