@@ -535,7 +535,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_waves_per_simd<BETA, D>())) vo
         for (int d = 0; d < Sh::DT; ++d)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<float4 *>(slot + tq * D + d * 32 + 8 * g + 4 * hl) =
+                *reinterpret_cast<float4 *>(slot + partial_o_index(BETA, d * 32 + 8 * g + 4 * hl, tq)) =
                     make_float4(st.oacc[d][4 * g + 0], st.oacc[d][4 * g + 1], st.oacc[d][4 * g + 2],
                                 st.oacc[d][4 * g + 3]);
         if (hl == 0) {
@@ -656,68 +656,70 @@ hipError_t launch_plan(const PlanParams &p, hipStream_t s)
 
 // Merge the chunks of one split row: with reference maxima m_c and sums l_c,
 // M = max m_c, L = sum l_c 2^(m_c - M), O = sum O_c 2^(m_c - M) / L and
-// LSE = (M + log2 L) ln 2.  One workgroup per split row, two threads per
-// query (half the head dimension each).
-template <int D>
+// LSE = (M + log2 L) ln 2.  One workgroup per split row, 256 / BETA threads
+// per query, each a share of the head dimension's groups of four channels.
+template <int BETA, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p)
 {
-    constexpr int HALF = D / 2;
+    constexpr int TPQ = 256 / BETA;     // threads per query
+    constexpr int NG = D / 4 / TPQ;     // groups of four channels per thread
     if ((int)blockIdx.x >= p.counts[1]) return;
     const int2 sr = p.split_rows[blockIdx.x];
     const int row = sr.x, chunks = sr.y;
     const int bh = row / p.nB, i = row - bh * p.nB;
     const int b = bh / p.H, hh = bh - b * p.H;
-    const int64_t slot_floats = partial_slot_floats(p.block, D);
+    const int64_t slot_floats = partial_slot_floats(BETA, D);
     const float *base = p.partials + (int64_t)blockIdx.x * p.max_chunks * slot_floats;
-    for (int x = threadIdx.x; x < 2 * p.block; x += blockDim.x) {
-        const int tq = x >> 1, d0 = (x & 1) * HALF;
-        const int t = i * p.block + tq;
-        if (t >= p.N) continue;
-        const int tpos = p.natural ? nb_natural(p.nb, p.block, t) : t;
-        float M = -INFINITY;
-        for (int c = 0; c < chunks; ++c) M = fmaxf(M, base[c * slot_floats + p.block * D + tq]);
-        float L = 0.f;
-        float acc[HALF];
+    // thread x owns query x mod BETA and the channel groups x / BETA + TPQ g:
+    // for each g the threads read consecutive 16-byte groups of a slot
+    const int tq = threadIdx.x % BETA, part = threadIdx.x / BETA;
+    const int t = i * BETA + tq;
+    if (t >= p.N) return;
+    const int tpos = p.natural ? nb_natural(p.nb, BETA, t) : t;
+    float M = -INFINITY;
+    for (int c = 0; c < chunks; ++c) M = fmaxf(M, base[c * slot_floats + BETA * D + tq]);
+    float L = 0.f;
+    float4 acc[NG];
 #pragma unroll
-        for (int d = 0; d < HALF; ++d) acc[d] = 0.f;
-        for (int c = 0; c < chunks; ++c) {
-            const float *slot = base + c * slot_floats;
-            const float mc = slot[p.block * D + tq];
-            const float w = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
-            L += slot[p.block * D + p.block + tq] * w;
-            const float *src = slot + tq * D + d0;
+    for (int g = 0; g < NG; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < chunks; ++c) {
+        const float *slot = base + c * slot_floats;
+        const float mc = slot[BETA * D + tq];
+        const float w = (mc == -INFINITY) ? 0.f : fast_exp2(mc - M);
+        L += slot[BETA * D + BETA + tq] * w;
 #pragma unroll
-            for (int d = 0; d < HALF; d += 4) {
-                const float4 a = *reinterpret_cast<const float4 *>(src + d);
-                acc[d] += a.x * w;
-                acc[d + 1] += a.y * w;
-                acc[d + 2] += a.z * w;
-                acc[d + 3] += a.w * w;
-            }
+        for (int g = 0; g < NG; ++g) {
+            const float4 a = *reinterpret_cast<const float4 *>(slot + partial_o_index(BETA, 4 * (part + TPQ * g), tq));
+            acc[g].x += a.x * w;
+            acc[g].y += a.y * w;
+            acc[g].z += a.z * w;
+            acc[g].w += a.w * w;
         }
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)tpos * p.o_sn + d0;
-#pragma unroll
-        for (int d = 0; d < HALF; d += 8) {
-            uint4 st;
-            st.x = pack_bf16x2(acc[d] * inv, acc[d + 1] * inv);
-            st.y = pack_bf16x2(acc[d + 2] * inv, acc[d + 3] * inv);
-            st.z = pack_bf16x2(acc[d + 4] * inv, acc[d + 5] * inv);
-            st.w = pack_bf16x2(acc[d + 6] * inv, acc[d + 7] * inv);
-            *reinterpret_cast<uint4 *>(orow + d) = st;
-        }
-        if (p.lse && (x & 1) == 0)
-            p.lse[(int64_t)bh * p.N + tpos] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t *orow = p.o + b * p.o_sb + hh * p.o_sh + (int64_t)tpos * p.o_sn;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        uint2 st;
+        st.x = pack_bf16x2(acc[g].x * inv, acc[g].y * inv);
+        st.y = pack_bf16x2(acc[g].z * inv, acc[g].w * inv);
+        *reinterpret_cast<uint2 *>(orow + 4 * (part + TPQ * g)) = st;
+    }
+    if (p.lse && part == 0)
+        p.lse[(int64_t)bh * p.N + tpos] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s)
 {
     if (grid <= 0) return hipSuccess;
-    if (p.D == 128)
-        hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, p);
-    else if (p.D == 64)
-        hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    if (p.block == 128 && p.D == 128)
+        hipLaunchKernelGGL((combine_kernel<128, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else if (p.block == 128 && p.D == 64)
+        hipLaunchKernelGGL((combine_kernel<128, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else if (p.block == 64 && p.D == 128)
+        hipLaunchKernelGGL((combine_kernel<64, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else if (p.block == 64 && p.D == 64)
+        hipLaunchKernelGGL((combine_kernel<64, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

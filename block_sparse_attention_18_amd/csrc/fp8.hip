@@ -696,7 +696,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
             for (int g = 0; g < 4; ++g) {
                 const int c0 = d * 32 + 8 * g + 4 * hl;
                 const float4 s4 = *reinterpret_cast<const float4 *>(vs + c0);
-                *reinterpret_cast<float4 *>(slot + tq * D + c0) =
+                *reinterpret_cast<float4 *>(slot + partial_o_index(BETA, c0, tq)) =
                     make_float4(st.oacc[d][4 * g + 0] * s4.x, st.oacc[d][4 * g + 1] * s4.y,
                                 st.oacc[d][4 * g + 2] * s4.z, st.oacc[d][4 * g + 3] * s4.w);
             }

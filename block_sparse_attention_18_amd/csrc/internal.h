@@ -356,8 +356,16 @@ hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, int64_t g
 hipError_t launch_skip_copy(const SkipCopyParams &p, hipStream_t s);
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s);
-// bytes of one partial-result slot (O [block][D] fp32, then max and sum [block])
+// floats of one partial-result slot: the unnormalised O as [D / 4][block]
+// groups of four channels (query-minor, so that a wavefront's lanes, one
+// query each, write and read consecutive 16-byte groups), then the
+// reference max [block] and the sum [block]
 __host__ __device__ inline int64_t partial_slot_floats(int block, int D) { return (int64_t)block * D + 2 * block; }
+// float offset in a slot of channels c0 .. c0 + 3 (c0 a multiple of 4) of query tq
+__host__ __device__ inline int64_t partial_o_index(int block, int c0, int tq)
+{
+    return ((int64_t)(c0 >> 2) * block + tq) * 4;
+}
 hipError_t launch_pool_proj(const PoolParams &p, int block, int D, hipStream_t s);
 hipError_t launch_scores(const ScoreParams &p, hipStream_t s);
 hipError_t launch_score_grad(const ScoreGradParams &p, hipStream_t s);
