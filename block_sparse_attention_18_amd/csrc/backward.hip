@@ -259,7 +259,8 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane >> 5, n = lane & 31;
     const int BH = p.B * p.H;
-    const int i = blockIdx.x / BH, bh = blockIdx.x - i * BH;
+    int i, bh;
+    work_item((int)blockIdx.x, BH, p.nB, i, bh);
     const int b = bh / p.H, hh = bh - b * p.H;
     const int64_t row = (int64_t)bh * p.nB + i;
     const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
@@ -520,7 +521,8 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
     const int kg = wv % G::NKG, qh = wv / G::NKG;
     const int hl = lane >> 5, n = lane & 31;
     const int BH = p.B * p.H;
-    const int j = blockIdx.x / BH, bh = blockIdx.x - j * BH;
+    int j, bh;
+    work_item((int)blockIdx.x, BH, p.nB, j, bh);   // key block j
     const int b = bh / p.H, hh = bh - b * p.H;
     // natural-order tensors: rows gathered from (and dK, dV scattered to)
     // the natural positions of the tile-major tokens

@@ -10,10 +10,10 @@
 //
 // Mapping onto CDNA4:
 //  * one workgroup per (query block i, head); BETA/32 waves, each owning 32
-//    query rows.  Work items are ordered query-block-major so that the long
-//    text rows of every head are dispatched first, and consecutive
-//    workgroups (which the dispatcher deals round-robin to the 8 XCDs) walk
-//    different heads, so each XCD's L2 keeps a few heads' K/V windows.
+//    query rows.  The leading query blocks of every head (the long text
+//    rows) are dispatched first; the other rows go head by head on each of
+//    the 8 XCDs, so an XCD's L2 holds the key blocks one head's rows share
+//    (work_item).
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 d from LDS,
 //    B = 16 d x 32 queries held in registers for the whole kernel).  K rows
 //    are fed in a permuted order (bits 2 and 3 of the row index swapped)
@@ -405,9 +405,8 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_waves_per_simd<BETA, D>())) vo
         chunk = it.y;
         chunks = it.z;
         rank = it.w;
-    } else {         // query-block-major: every head's text rows first
-        i = blockIdx.x / BH;
-        bh = blockIdx.x - i * BH;
+    } else {         // the text rows of every head first, then head by head per XCD
+        work_item((int)blockIdx.x, BH, p.nB, i, bh);
     }
     const int b = bh / p.H;
     const int hh = bh - b * p.H;

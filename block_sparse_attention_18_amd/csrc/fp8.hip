@@ -545,9 +545,8 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void fwd8_kernel(const Fp8FwdPar
         chunk = it.y;
         chunks = it.z;
         rank = it.w;
-    } else {         // query-block-major: every head's text rows first
-        i = blockIdx.x / BH;
-        bh = blockIdx.x - i * BH;
+    } else {         // the text rows of every head first, then head by head per XCD
+        work_item((int)blockIdx.x, BH, p.nB, i, bh);
     }
     const int b = bh / p.H, hh = bh - b * p.H;
     if ((p.skip_bits[hh >> 5] >> (hh & 31)) & 1u) return;

@@ -356,6 +356,30 @@ hipError_t launch_forward_fp8(const Fp8FwdParams &p, int block, int D, int64_t g
 hipError_t launch_skip_copy(const SkipCopyParams &p, hipStream_t s);
 hipError_t launch_plan(const PlanParams &p, hipStream_t s);
 hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s);
+// Work order of the kernels with one workgroup per (query block, head).
+// Workgroup w runs on XCD w mod 8 (workgroups are dealt round-robin to the
+// 8 XCDs, each with its own L2).  The first kLeadBlocks query blocks of
+// every head -- the text rows of the multimodal layouts, the longest rows
+// -- go first, query-block-major; the others are walked head by head on
+// each XCD (XCD x takes heads x, x + 8, ...), so the key blocks that the
+// rows of one head share stay in that XCD's L2.  With a head count that is
+// not a multiple of 8 every row goes query-block-major.
+constexpr int kLeadBlocks = 16;
+__device__ __forceinline__ void work_item(int w, int BH, int nB, int &i, int &bh)
+{
+    const int lead = nB < kLeadBlocks ? nB : kLeadBlocks;
+    if ((BH & 7) == 0 && w >= lead * BH) {
+        const int v = w - lead * BH;
+        const int x = v & 7, sq = v >> 3, rows = nB - lead;
+        const int hg = sq / rows;
+        i = lead + sq - hg * rows;
+        bh = hg * 8 + x;
+    } else {
+        i = w / BH;
+        bh = w - i * BH;
+    }
+}
+
 // floats of one partial-result slot: the unnormalised O as [D / 4][block]
 // groups of four channels (query-minor, so that a wavefront's lanes, one
 // query each, write and read consecutive 16-byte groups), then the
