@@ -373,3 +373,40 @@ def test_fuzz_score_grad(seed):
     wdw, wdq, wdk = oracle.score_grad(q, k, block, w, dS.astype(np.float64))
     for got, want, name in ((dw, wdw, "dW"), (dqp, wdq, "dQ pooled"), (dkp, wdk, "dK pooled")):
         _rel_close(got.cpu().numpy().astype(np.float64), want, 1e-4, 1e-5, f"fuzz {seed} {name}")
+
+
+# ---------------------------------------------------------------------------
+# the XCD work order (a multiple of 8 heads and more than 16 query blocks:
+# the leading blocks query-block-major, the rest head by head per XCD)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,nB,block,D,seed", [
+    (1, 8, 17, 64, 64, 1800),      # one row per head after the leading blocks
+    (2, 4, 40, 64, 128, 1801),
+    (1, 16, 21, 128, 64, 1802),
+])
+def test_work_order_many_heads(B, H, nB, block, D, seed):
+    N = nB * block - 5
+    _log(f"work order B={B} H={H} nB={nB} block={block} D={D}")
+    q, k, v = synth.random_qkv(B, H, N, D, seed=seed)
+    g = synth.random_qkv(B, H, N, D, seed=seed + 50)[0]
+    rp, ci = synth.random_block_lists(B, H, nB, seed=seed + 1, density=0.4, empty_rows=2, full_rows=2)
+    qd, kd, vd, gd = (to_dev_bf16(a) for a in (q, k, v, g))
+    rpd, cid = _i32(rp), _i32(ci)
+    O, L = bsa.forward(qd, kd, vd, block, rpd, cid)
+    dq, dk, dv = bsa.backward(qd, kd, vd, O, gd, block, rpd, cid, L)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.forward(q, k, v, block, rp, ci)
+    check_forward(bf16_to_f64(O), L.cpu().numpy().astype(np.float64), Oo, Lo, "work order forward")
+    wq, wk, wv = oracle.backward(q, k, v, g, block, rp, ci)
+    for got, want, name in ((dq, wq, "dQ"), (dk, wk, "dK"), (dv, wv, "dV")):
+        _rel_close(bf16_to_f64(got), want, 2e-2, 1e-2, f"work order {name}")
+    # FP8 on the exact-weight construction
+    q8, k8, v8, scale = _pow2_inputs(B, H, N, D, seed, 0, (0,), 4)
+    qkv = bsa.quantize_fp8(to_dev_bf16(q8), to_dev_bf16(k8), to_dev_bf16(v8))
+    O8, L8 = bsa.forward_fp8(qkv, block, rpd, cid, scale=scale)
+    torch.cuda.synchronize()
+    Oo8, Lo8 = oracle.forward_fp8(*oracle.quantize_fp8(q8, k8, v8), block, rp, ci, scale=scale)
+    vmax = np.abs(synth.bf16_to_f32(v8)).max(axis=2, keepdims=True)
+    assert not (np.abs(bf16_to_f64(O8) - Oo8) > 2.0 ** -8 * np.abs(Oo8) + 1e-4 * vmax).any()
+    fin = np.isfinite(Lo8)
+    np.testing.assert_allclose(L8.cpu().numpy()[fin], Lo8[fin], rtol=0, atol=3e-5)
