@@ -975,12 +975,17 @@ static bsa_status forward_impl(const bsa_tensor *q, const bsa_tensor *k, const b
     fp.partials = run.partials;
     fp.max_chunks = run.max_chunks;
 
+    if (any_skip) {   // the forward's SKIP-row workgroups copy the caches
+        fp.oc = t4(o_cache);
+        fp.lse_src = (lse_cache && lse && lse_cache != lse) ? lse_cache : nullptr;
+        fp.copy_o = !(o_cache->data == o->data && o_cache->stride_b == o->stride_b &&
+                      o_cache->stride_h == o->stride_h && o_cache->stride_n == o->stride_n);
+    }
     if (split && (st = split_plan(run, row_ptr, q->B * H, H, nB, split, fp.skip_bits, s)) != BSA_OK) return st;
     hipError_t e;
     if ((e = bsa::launch_forward(fp, block, (int)q->D, run.grid, s)) != hipSuccess)
         return hip_fail(e, "forward launch");
     if (split && (st = split_combine(run, o, lse, H, q->N, nB, q->D, block, natural, nb, s)) != BSA_OK) return st;
-    if (any_skip && (st = skip_heads_copy(o_cache, lse_cache, o, lse, fp.skip_bits, s)) != BSA_OK) return st;
     return BSA_OK;
 }
 

@@ -371,6 +371,29 @@ __device__ __forceinline__ void last_step(const uint16_t *__restrict__ Vp, bool 
     pv_mfma<BETA, D>(Vp, pf, st);
 }
 
+// A SKIP row (DiTFastAttnV2, "Head-wise Caching"): the rows of query block i
+// of head (b, hh) take the cached output bit for bit, 16 bytes a copy, and
+// the cached LSE when one is given.
+template <int BETA, int D>
+__device__ __forceinline__ void skip_row_copy(const FwdParams &p, int b, int hh, int bh, int i, int tid)
+{
+    constexpr int NT = FwdShape<BETA, D>::NT;
+    constexpr int CH = D / 8;                  // 16-byte chunks per row
+    const int t0 = i * BETA, rows = min(BETA, p.N - t0);
+    if (p.copy_o) {
+        const uint16_t *src = p.oc.p + b * p.oc.sb + hh * p.oc.sh;
+        uint16_t *dst = p.o + b * p.o_sb + hh * p.o_sh;
+        for (int x = tid; x < rows * CH; x += NT) {
+            const int r = x / CH, c = x - r * CH;
+            const int64_t t = t0 + r;
+            *reinterpret_cast<uint4 *>(dst + t * p.o_sn + 8 * c) =
+                *reinterpret_cast<const uint4 *>(src + t * p.oc.sn + 8 * c);
+        }
+    }
+    if (p.lse_src && p.lse)
+        for (int r = tid; r < rows; r += NT) p.lse[(int64_t)bh * p.N + t0 + r] = p.lse_src[(int64_t)bh * p.N + t0 + r];
+}
+
 // Occupancy: two waves per SIMD at β=128 (two 4-wave workgroups per CU).
 // β=64, D=64 asks for three: the register budget of 168 holds its state
 // without spilling (at two the allocator spends all 256 and still spills),
@@ -410,7 +433,10 @@ __global__ __launch_bounds__(BETA / 32 * 64, (fwd_waves_per_simd<BETA, D>())) vo
     }
     const int b = bh / p.H;
     const int hh = bh - b * p.H;
-    if ((p.skip_bits[hh >> 5] >> (hh & 31)) & 1u) return;
+    if ((p.skip_bits[hh >> 5] >> (hh & 31)) & 1u) {
+        skip_row_copy<BETA, D>(p, b, hh, bh, i, tid);
+        return;
+    }
 
     const int64_t row = (int64_t)bh * p.nB + i;
     int e0 = p.row_ptr[row];

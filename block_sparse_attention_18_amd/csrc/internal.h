@@ -133,6 +133,11 @@ struct FwdParams {
     const int32_t *flags;
     NbGeom nb;
     int32_t natural;            // neighbourhood: Q, K, V, O, LSE in natural token order
+    // SKIP heads: the workgroup of a SKIP row copies that row's cached
+    // output (when copy_o) and LSE (when lse_src is set) instead of computing
+    Tensor4 oc;                 // o_cache
+    const float *lse_src;       // lse_cache [B][H][N] or null
+    int32_t copy_o;
 };
 
 // Backward of the forward (see bsa_backward).  The dK/dV kernel keeps the
