@@ -781,8 +781,10 @@ static bsa_status skip_heads_copy(const bsa_tensor *o_cache, const float *lse_ca
 
 // ---------------------------------------------------------------------------
 // Long-row split policy (host computation from the layout's closed-form row
-// lengths; no device data).  Rows are dispatched query-block-major, then
-// batch and head; a row of L blocks costs L + kItemOverhead block steps of
+// lengths; no device data).  The model takes the rows query-block-major (the
+// order of a split launch's work list; a whole-row launch also starts with
+// the leading query blocks of every head); a row of L blocks costs L +
+// kItemOverhead block steps of
 // one workgroup, and `slots` workgroups run at once (two per CU at block
 // 128, about four at block 64).  Rows longer than L0 = max(typical,
 // ceil(nB / 4)) would be cut into at most ceil(nB / L0) chunks; the split is
