@@ -370,6 +370,7 @@ hipError_t launch_combine(const CombineParams &p, int64_t grid, hipStream_t s);
 // rows of one head share stay in that XCD's L2.  With a head count that is
 // not a multiple of 8 every row goes query-block-major.
 constexpr int kLeadBlocks = 16;
+#ifdef __HIPCC__
 __device__ __forceinline__ void work_item(int w, int BH, int nB, int &i, int &bh)
 {
     const int lead = nB < kLeadBlocks ? nB : kLeadBlocks;
@@ -384,6 +385,7 @@ __device__ __forceinline__ void work_item(int w, int BH, int nB, int &i, int &bh
         bh = w - i * BH;
     }
 }
+#endif
 
 // floats of one partial-result slot: the unnormalised O as [D / 4][block]
 // groups of four channels (query-minor, so that a wavefront's lanes, one
