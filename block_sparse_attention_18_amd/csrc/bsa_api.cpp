@@ -399,6 +399,29 @@ size_t bsa_select_meanpool_workspace_size(int64_t B, int64_t H, int64_t N, int32
     return 2 * bh * nB * (size_t)r * sizeof(float);
 }
 
+// The groups in ascending column order (a stable insertion sort of at most
+// 8): the selection kernels that write a row's columns as they choose them
+// (disjoint groups clear of the text columns) take the groups in this order;
+// the bitmask path does not depend on it.
+static void groups_by_column(const bsa_group *groups, int32_t n_groups, int32_t *g_begin, int32_t *g_end,
+                             int32_t *g_k)
+{
+    int32_t order[8];
+    for (int32_t g = 0; g < n_groups; ++g) {
+        int32_t at = g;
+        while (at > 0 && groups[order[at - 1]].col_begin > groups[g].col_begin) {
+            order[at] = order[at - 1];
+            --at;
+        }
+        order[at] = g;
+    }
+    for (int32_t g = 0; g < n_groups; ++g) {
+        g_begin[g] = groups[order[g]].col_begin;
+        g_end[g] = groups[order[g]].col_end;
+        g_k[g] = groups[order[g]].k;
+    }
+}
+
 bsa_status bsa_select_meanpool(const bsa_tensor *q, const bsa_tensor *k, int32_t block, const float *w, int32_t r,
                                int32_t text_blocks, const bsa_group *groups, int32_t n_groups, float *scores,
                                int32_t *row_ptr, int32_t *col_idx, int64_t capacity, void *workspace,
@@ -461,11 +484,7 @@ bsa_status bsa_select_meanpool(const bsa_tensor *q, const bsa_tensor *k, int32_t
     mp.text_blocks = text_blocks;
     mp.n_groups = n_groups;
     mp.row_len = (int32_t)select_row_bound(nB, text_blocks, groups, n_groups);
-    for (int32_t g = 0; g < n_groups; ++g) {
-        mp.g_begin[g] = groups[g].col_begin;
-        mp.g_end[g] = groups[g].col_end;
-        mp.g_k[g] = groups[g].k;
-    }
+    groups_by_column(groups, n_groups, mp.g_begin, mp.g_end, mp.g_k);
     hipError_t e = bsa::launch_meanpool_select(mp, block, (int)q->D, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "mean-pool selection launch");
     return BSA_OK;
@@ -530,11 +549,7 @@ bsa_status bsa_select_topk(const float *scores, int64_t B, int64_t H, int32_t n_
     sp.words = (int32_t)ceil_div(n_blocks, 32);
     sp.text_blocks = text_blocks;
     sp.n_groups = n_groups;
-    for (int32_t g = 0; g < n_groups; ++g) {
-        sp.g_begin[g] = groups[g].col_begin;
-        sp.g_end[g] = groups[g].col_end;
-        sp.g_k[g] = groups[g].k;
-    }
+    groups_by_column(groups, n_groups, sp.g_begin, sp.g_end, sp.g_k);
     // disjoint groups that leave the text columns alone fix every row's length
     bool direct = true;
     for (int32_t g = 0; g < n_groups && direct; ++g) {

@@ -25,8 +25,7 @@ namespace bsa {
 namespace mps {
 constexpr int NT = 256;             // threads per score-select workgroup
 constexpr int NW = NT / 64;
-constexpr int R = 1;                // rows a wave selects at a time
-constexpr int ROWS = NW * R;        // rows per workgroup
+constexpr int ROWS = NW;            // rows per workgroup, one per wavefront
 }
 
 // Scores and selection of ROWS query-block rows of one head: the head's
@@ -38,7 +37,6 @@ __global__ __launch_bounds__(256) void score_select_kernel(const MeanpoolSelectP
 {
     __shared__ __attribute__((aligned(16))) float pkt[kMpsMaxProj + 64];
     __shared__ __attribute__((aligned(16))) float pq[mps::ROWS][64];
-    __shared__ uint32_t bits[mps::NW][mps::R][kMpsMaxBlocks / 32];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nB = p.nB, r = p.r, r4 = (r + 3) & ~3;
@@ -83,76 +81,61 @@ __global__ __launch_bounds__(256) void score_select_kernel(const MeanpoolSelectP
     __syncthreads();
     const int tb = p.text_blocks;
     const int64_t head = (int64_t)tb * nB + (int64_t)(nB - tb) * p.row_len;
-    uint32_t *wb[mps::R];
+    const int row = row_base + wv;
+    if (row >= nB) return;
+    // lane j scores column j + 64 e of the row
+    float s[E];
 #pragma unroll
-    for (int q = 0; q < mps::R; ++q) wb[q] = bits[wv][q];
-    const int row0 = row_base + wv * mps::R;
-    if (row0 >= nB) return;
-    // scores of rows row0 .. row0 + R - 1 (rows past nB score 0 and are dropped)
-    float s[mps::R][E];
-#pragma unroll
-    for (int q = 0; q < mps::R; ++q)
-#pragma unroll
-        for (int e = 0; e < E; ++e) s[q][e] = 0.f;
+    for (int e = 0; e < E; ++e) s[e] = 0.f;
     for (int mm = 0; mm < r4; mm += 4) {
         float kv[4][E];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int e = 0; e < E; ++e) kv[t][e] = (e * 64 + lane < nB) ? pkt[(mm + t) * ld + e * 64 + lane] : 0.f;
+        const float4 v = *reinterpret_cast<const float4 *>(&pq[wv][mm]);
 #pragma unroll
-        for (int q = 0; q < mps::R; ++q) {
-            const float4 v = *reinterpret_cast<const float4 *>(&pq[wv * mps::R + q][mm]);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                s[q][e] = __builtin_fmaf(v.x, kv[0][e], s[q][e]);
-                s[q][e] = __builtin_fmaf(v.y, kv[1][e], s[q][e]);
-                s[q][e] = __builtin_fmaf(v.z, kv[2][e], s[q][e]);
-                s[q][e] = __builtin_fmaf(v.w, kv[3][e], s[q][e]);
-            }
+        for (int e = 0; e < E; ++e) {
+            s[e] = __builtin_fmaf(v.x, kv[0][e], s[e]);
+            s[e] = __builtin_fmaf(v.y, kv[1][e], s[e]);
+            s[e] = __builtin_fmaf(v.z, kv[2][e], s[e]);
+            s[e] = __builtin_fmaf(v.w, kv[3][e], s[e]);
         }
     }
-    const int words = (nB + 31) >> 5;
+    if (p.scores)
 #pragma unroll
-    for (int q = 0; q < mps::R; ++q) {
-        const int row = row0 + q;
-        if (row >= nB) break;
-        if (p.scores)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                if (e * 64 + lane < nB) p.scores[((int64_t)bh * nB + row) * nB + e * 64 + lane] = s[q][e];
-        if (lane < words) {
-            const int lim = row < tb ? nB : tb, lo = lane * 32;
-            wb[q][lane] = lim >= lo + 32 ? 0xFFFFFFFFu : (lim > lo ? (1u << (lim - lo)) - 1u : 0u);
-        }
+        for (int e = 0; e < E; ++e)
+            if (e * 64 + lane < nB) p.scores[((int64_t)bh * nB + row) * nB + e * 64 + lane] = s[e];
+    // closed-form offset of the row (text rows nB columns, others row_len);
+    // the text columns, then each group's columns in ascending order (the
+    // groups come sorted by column and lie past the text columns)
+    int64_t pos = bh * head + (row < tb ? (int64_t)row * nB : (int64_t)tb * nB + (int64_t)(row - tb) * p.row_len);
+    if (lane == 0) {
+        p.row_ptr[(int64_t)bh * nB + row + 1] = (int32_t)(pos + (row < tb ? nB : p.row_len));
+        if (bh == 0 && row == 0) p.row_ptr[0] = 0;
     }
-    // the rows are selected when one of them is not a text row (a text row's
-    // mask is already dense, so the selection's bits leave it unchanged)
-    if (row0 + mps::R > tb) {
-        for (int g = 0; g < p.n_groups; ++g) {
-            const int c0 = p.g_begin[g], c1 = p.g_end[g], kk = p.g_k[g];
-            if (kk <= 0) continue;
-            if (kk >= c1 - c0) {
-#pragma unroll
-                for (int q = 0; q < mps::R; ++q)
-                    if (row0 + q >= tb && row0 + q < nB) select_all(c0, c1, wb[q]);
-            } else {
-                select_rows<E, mps::R>(s, c0, c1, kk, wb);
-            }
+    const int lead = row < tb ? nB : tb;
+    for (int c = lane; c < lead; c += 64)
+        if (pos + c < p.capacity) p.col_idx[pos + c] = c;
+    if (row < tb) return;
+    pos += tb;
+    for (int g = 0; g < p.n_groups; ++g) {
+        const int c0 = p.g_begin[g], c1 = p.g_end[g], kk = p.g_k[g];
+        if (kk <= 0) continue;
+        if (kk >= c1 - c0) {
+            for (int c = lane; c < c1 - c0; c += 64)
+                if (pos + c < p.capacity) p.col_idx[pos + c] = c0 + c;
+            pos += c1 - c0;
+            continue;
         }
-    }
+        uint32_t key[E];
 #pragma unroll
-    for (int q = 0; q < mps::R; ++q) {
-        const int row = row0 + q;
-        if (row >= nB) break;
-        // closed-form offset of the row (text rows nB columns, others row_len)
-        const int64_t start =
-            bh * head + (row < tb ? (int64_t)row * nB : (int64_t)tb * nB + (int64_t)(row - tb) * p.row_len);
-        if (lane == 0) {
-            p.row_ptr[(int64_t)bh * nB + row + 1] = (int32_t)(start + (row < tb ? nB : p.row_len));
-            if (bh == 0 && row == 0) p.row_ptr[0] = 0;
+        for (int e = 0; e < E; ++e) {
+            const int col = e * 64 + lane;
+            key[e] = (col >= c0 && col < c1) ? score_key(s[e]) : 0u;
         }
-        write_row_columns(wb[q], nB, start, p.col_idx, p.capacity);
+        topk_keys_write<E>(key, 0, c0, c1, kk, p.col_idx, pos, p.capacity);
+        pos += kk;
     }
 }
 

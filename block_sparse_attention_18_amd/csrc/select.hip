@@ -14,16 +14,18 @@
 //     early at a probe with exactly k keys at or above it).  The row keeps
 //     every key above T and, of the keys equal to T, the lowest columns up
 //     to k (lane prefix counts of the equality ballots, taken in column
-//     order).  The kept set is a per-row bitmask in LDS; its population
-//     count is the row length.
+//     order).  On the two-pass path below the kept set is a per-row
+//     bitmask in LDS; its population count is the row length.
 //  2. scan: one workgroup turns the row lengths into row_ptr in place.
 //  3. expand: one wavefront per row writes the set bits as ascending
 //     column indices at row_ptr[row].
 // When the column groups are pairwise disjoint and leave the text columns
 // alone, every row's length is known beforehand (text rows nB, the others
 // text_blocks + sum of k), so select writes its row_ptr entry and its
-// column indices itself (a lane per column, positions from ballots) and the
-// other two kernels are not launched.
+// column indices itself and the other two kernels are not launched: the
+// groups arrive in ascending column order, and each group's kept columns
+// are written as soon as its search ends (positions from ballot prefix
+// counts), with no bitmask.
 #include "common.h"
 #include "internal.h"
 #include "topk.h"
@@ -63,13 +65,52 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectParams p)
 #pragma unroll
         for (int u = 0; u < sel::LU; ++u)
             if (u * 64 + lane < nB) srow[u * 64 + lane] = v[u];
-        const int lim = (i < p.text_blocks) ? nB : p.text_blocks;   // dense row / text columns
-        for (int w = lane; w < p.words; w += 64) {
-            const int lo = w * 32;
-            wbits[w] = lim >= lo + 32 ? 0xFFFFFFFFu : (lim > lo ? (1u << (lim - lo)) - 1u : 0u);
+        if (!p.direct) {
+            const int lim = (i < p.text_blocks) ? nB : p.text_blocks;   // dense row / text columns
+            for (int w = lane; w < p.words; w += 64) {
+                const int lo = w * 32;
+                wbits[w] = lim >= lo + 32 ? 0xFFFFFFFFu : (lim > lo ? (1u << (lim - lo)) - 1u : 0u);
+            }
         }
     }
     __syncthreads();
+    if (p.direct) {
+        // closed-form offsets: each head holds text_blocks rows of nB columns,
+        // then nB - text_blocks rows of row_len columns.  The groups come in
+        // ascending column order, after the text columns, so the row's
+        // columns are written in order as they are chosen.
+        if (!live) return;
+        const int64_t tb = p.text_blocks;
+        const int64_t head = tb * nB + (int64_t)(nB - tb) * p.row_len;
+        int64_t pos = (int64_t)bh * head + (i < tb ? (int64_t)i * nB : tb * nB + (int64_t)(i - tb) * p.row_len);
+        if (lane == 0) {
+            p.row_ptr[row + 1] = (int32_t)(pos + (i < tb ? nB : p.row_len));
+            if (row == 0) p.row_ptr[0] = 0;
+        }
+        const int lead = i < tb ? nB : (int)tb;   // dense row / text columns
+        for (int c = lane; c < lead; c += 64)
+            if (pos + c < p.capacity) p.col_idx[pos + c] = c;
+        if (i < tb) return;
+        pos += tb;
+        for (int g = 0; g < p.n_groups; ++g) {
+            const int c0 = p.g_begin[g], c1 = p.g_end[g], kk = p.g_k[g];
+            const int width = c1 - c0;
+            if (kk <= 0) continue;
+            if (kk >= width) {
+                for (int c = lane; c < width; c += 64)
+                    if (pos + c < p.capacity) p.col_idx[pos + c] = c0 + c;
+                pos += width;
+                continue;
+            }
+            if (width <= 64) topk_write<1>(srow, c0, c1, kk, p.col_idx, pos, p.capacity);
+            else if (width <= 128) topk_write<2>(srow, c0, c1, kk, p.col_idx, pos, p.capacity);
+            else if (width <= 256) topk_write<4>(srow, c0, c1, kk, p.col_idx, pos, p.capacity);
+            else if (width <= 512) topk_write<8>(srow, c0, c1, kk, p.col_idx, pos, p.capacity);
+            else topk_write<16>(srow, c0, c1, kk, p.col_idx, pos, p.capacity);
+            pos += kk;
+        }
+        return;
+    }
     if (live && i >= p.text_blocks) {
         for (int g = 0; g < p.n_groups; ++g) {
             const int c0 = p.g_begin[g], c1 = p.g_end[g], kk = p.g_k[g];
@@ -85,19 +126,6 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectParams p)
     }
     __syncthreads();
     if (!live) return;
-    if (p.direct) {
-        // closed-form offsets: each head holds text_blocks rows of nB columns,
-        // then nB - text_blocks rows of row_len columns
-        const int64_t tb = p.text_blocks;
-        const int64_t head = tb * nB + (int64_t)(nB - tb) * p.row_len;
-        const int64_t start = (int64_t)bh * head + (i < tb ? (int64_t)i * nB : tb * nB + (int64_t)(i - tb) * p.row_len);
-        if (lane == 0) {
-            p.row_ptr[row + 1] = (int32_t)(start + (i < tb ? nB : p.row_len));
-            if (row == 0) p.row_ptr[0] = 0;
-        }
-        write_row_columns(wbits, nB, start, p.col_idx, p.capacity);
-        return;
-    }
     int cnt = 0;
     for (int w = lane; w < p.words; w += 64) {
         const uint32_t v = wbits[w];

@@ -19,6 +19,105 @@ __device__ __forceinline__ uint32_t score_key(float s)
 
 __device__ __forceinline__ int ballot_count(bool x) { return __popcll(__ballot(x)); }
 
+__device__ __forceinline__ int lanes_below(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Number of keys >= cand over the wavefront.  Each register's compare gives
+// a 64-lane mask in scalar registers; the scalar unit (one per CU, shared by
+// its four SIMDs) counts most of them, the vector unit counts the last EV
+// (v_bcnt of the two mask halves into a lane-uniform sum), so that the two
+// issue ports split the work of a search round; a group of one or two
+// registers is counted by the scalar unit alone (shorter dependency chain).
+template <int E>
+__device__ __forceinline__ int count_at_least(const uint32_t (&key)[E], uint32_t cand)
+{
+    constexpr int EV = E >= 4 ? E / 2 : 0;
+    int s = 0;
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint64_t m = __ballot(key[e] >= cand);
+        if (e < E - EV) {
+            s += __popcll(m);
+        } else {
+            // the mask was just written by a vector compare: a vector read of
+            // it needs two wait states, which the compiler does not insert
+            // ahead of an asm statement
+            asm("s_nop 1\n\tv_bcnt_u32_b32 %0, %1, %0\n\tv_bcnt_u32_b32 %0, %2, %0"
+                : "+v"(acc)
+                : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)));
+        }
+    }
+    if (EV > 0) s += __builtin_amdgcn_readfirstlane(acc);
+    return s;
+}
+
+// Top kk of the column group [c0, c1) (0 < kk < c1 - c0), written as
+// ascending column indices from col_idx[pos] (entries at or past capacity
+// are dropped).  key[e] is the key of column cbase + 64 e + lane, 0 for a
+// column outside the group (no probe, which is >= 1, counts it).
+//
+// The bits of T, the kk-th largest key, are decided from the top: a probe
+// cand = T | bit is taken when at least kk keys are >= cand.  Alongside, the
+// search keeps the number of keys whose leading (decided) bits exceed T's:
+// it becomes the count of a rejected probe and is unchanged by a taken one,
+// so after the last bit it is the number of keys > T, and the keys equal to
+// T that are kept (lowest columns first) need no further count.  The search
+// stops early at a probe with exactly kk keys at or above it: the kept set
+// is then the keys >= T.
+template <int E>
+__device__ void topk_keys_write(const uint32_t (&key)[E], int cbase, int c0, int c1, int kk, int32_t *col_idx,
+                                int64_t pos, int64_t capacity)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t T = 0u, probe = 0x80000000u;
+    int above = 0, cnt;
+    for (;;) {
+        const uint32_t cand = __builtin_amdgcn_readfirstlane(T | probe);
+        cnt = count_at_least<E>(key, cand);
+        const bool take = cnt >= kk;
+        T = take ? cand : T;
+        above = take ? above : cnt;
+        probe = cnt == kk ? 0u : probe >> 1;
+        asm("" : "+s"(probe));      // one scalar test ends the loop
+        if (probe == 0u) break;
+    }
+    // keys equal to T to keep, lowest columns first (all of them when exact)
+    int need = cnt == kk ? 0x7fffffff : kk - above;
+    int at0 = (int)pos;                         // CSR positions fit in int32
+    const int cap = (int)min(capacity, (int64_t)0x7fffffff);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int col = cbase + e * 64 + lane;
+        const bool eq = (col >= c0) & (col < c1) & (key[e] == T);
+        const uint64_t me = __ballot(eq);
+        const bool keep = (key[e] > T) | (eq & (lanes_below(me) < need));
+        need -= __popcll(me);
+        const uint64_t K = __ballot(keep);
+        const int at = at0 + lanes_below(K);
+        if (keep & (at < cap)) col_idx[at] = col;
+        at0 += __popcll(K);
+    }
+}
+
+// topk_keys_write for a group whose scores sit in LDS (srow[c] is column c):
+// lane l takes columns c0 + 64 e + l.
+template <int E>
+__device__ void topk_write(const float *srow, int c0, int c1, int kk, int32_t *col_idx, int64_t pos,
+                           int64_t capacity)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int col = c0 + e * 64 + lane;
+        key[e] = col < c1 ? score_key(srow[col]) : 0u;
+    }
+    topk_keys_write<E>(key, c0, c0, c1, kk, col_idx, pos, capacity);
+}
+
 // Keep the kk best columns of [c0, c1) (kk < c1 - c0): set their bits in the
 // row bitmask wbits.  Columns past c1 are padding with key 0 and the highest
 // columns, so they never reach the kept set.
@@ -73,89 +172,6 @@ __device__ void select_group(const float *srow, int c0, int c1, int kk, uint32_t
 __device__ void select_all(int c0, int c1, uint32_t *wbits)
 {
     for (int col = c0 + (int)(threadIdx.x & 63); col < c1; col += 64) atomicOr(&wbits[col >> 5], 1u << (col & 31));
-}
-
-// Top-k of the column group [c0, c1) (kk < c1 - c0) for R rows at once,
-// with the scores in registers in absolute column order: s[q][e] is the
-// score of row q at column 64 e + lane.  Columns outside the group get key
-// 0 and are never counted (every probe value is at least 1) nor kept.
-// Sets the kept bits of row q in wb[q] (words of 32 columns).
-template <int E, int R>
-__device__ void select_rows(const float (&s)[R][E], int c0, int c1, int kk, uint32_t *const (&wb)[R])
-{
-    const int lane = threadIdx.x & 63;
-    uint32_t key[R][E];
-#pragma unroll
-    for (int q = 0; q < R; ++q)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int col = e * 64 + lane;
-            key[q][e] = (col >= c0 && col < c1) ? score_key(s[q][e]) : 0u;
-        }
-    uint32_t T[R];
-    bool live[R];
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        T[q] = 0u;
-        live[q] = true;
-    }
-    // the rows' searches run in lockstep; a row stops at its first probe
-    // with exactly kk keys at or above it (as in select_group)
-    for (int bit = 31; bit >= 0; --bit) {
-        bool any = false;
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            if (!live[q]) continue;
-            const uint32_t cand = T[q] | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) cnt += ballot_count(key[q][e] >= cand);
-            if (cnt >= kk) {
-                T[q] = cand;
-                live[q] = cnt != kk;
-            }
-            any = any || live[q];
-        }
-        if (!any) break;
-    }
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        int need = kk;
-#pragma unroll
-        for (int e = 0; e < E; ++e) need -= ballot_count(key[q][e] > T[q]);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int col = e * 64 + lane;
-            const bool inside = col >= c0 && col < c1;
-            const uint64_t eq = __ballot(inside && key[q][e] == T[q]);
-            const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0));
-            const bool keep = inside && (key[q][e] > T[q] || (key[q][e] == T[q] && rank < need));
-            need -= __popcll(eq);
-            const uint64_t K = __ballot(keep);
-            if (K != 0ull && lane < 2) {
-                const uint32_t v = lane == 0 ? (uint32_t)K : (uint32_t)(K >> 32);
-                if (v) atomicOr(&wb[q][2 * e + lane], v);
-            }
-        }
-    }
-}
-
-// Write the set bits of a row bitmask of nB columns as ascending column
-// indices from col_idx[start] (entries at or past capacity are dropped): a
-// lane per column, 64 columns a round, each position from the lanes below.
-__device__ __forceinline__ void write_row_columns(const uint32_t *wb, int nB, int64_t start, int32_t *col_idx,
-                                                  int64_t capacity)
-{
-    const int lane = threadIdx.x & 63;
-    for (int c0 = 0; c0 < nB; c0 += 64) {
-        const int col = c0 + lane;
-        const bool on = col < nB && ((wb[col >> 5] >> (col & 31)) & 1u);
-        const uint64_t m = __ballot(on);
-        const int64_t pos =
-            start + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (on && pos < capacity) col_idx[pos] = col;
-        start += __popcll(m);
-    }
 }
 
 }  // namespace bsa
