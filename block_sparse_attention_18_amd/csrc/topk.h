@@ -24,6 +24,28 @@ __device__ __forceinline__ int lanes_below(uint64_t m)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
+// AND and OR of a value over the 64 lanes of a wavefront (uniform results):
+// each 16-lane row folds into its lane 15 by DPP row shifts (a shifted-in
+// lane reads the identity), lanes 15 and 31 are broadcast into the rows
+// above them, and lane 63 holds the result.
+__device__ __forceinline__ void wave_and_or(uint32_t &a, uint32_t &o)
+{
+    a &= __builtin_amdgcn_update_dpp(~0u, a, 0x111, 0xf, 0xf, false);     // row_shr:1
+    o |= __builtin_amdgcn_update_dpp(0u, o, 0x111, 0xf, 0xf, false);
+    a &= __builtin_amdgcn_update_dpp(~0u, a, 0x112, 0xf, 0xf, false);     // row_shr:2
+    o |= __builtin_amdgcn_update_dpp(0u, o, 0x112, 0xf, 0xf, false);
+    a &= __builtin_amdgcn_update_dpp(~0u, a, 0x114, 0xf, 0xf, false);     // row_shr:4
+    o |= __builtin_amdgcn_update_dpp(0u, o, 0x114, 0xf, 0xf, false);
+    a &= __builtin_amdgcn_update_dpp(~0u, a, 0x118, 0xf, 0xf, false);     // row_shr:8
+    o |= __builtin_amdgcn_update_dpp(0u, o, 0x118, 0xf, 0xf, false);
+    a &= __builtin_amdgcn_update_dpp(~0u, a, 0x142, 0xa, 0xf, false);     // row_bcast:15
+    o |= __builtin_amdgcn_update_dpp(0u, o, 0x142, 0xa, 0xf, false);
+    a &= __builtin_amdgcn_update_dpp(~0u, a, 0x143, 0xc, 0xf, false);     // row_bcast:31
+    o |= __builtin_amdgcn_update_dpp(0u, o, 0x143, 0xc, 0xf, false);
+    a = __builtin_amdgcn_readlane(a, 63);
+    o = __builtin_amdgcn_readlane(o, 63);
+}
+
 // Number of keys >= cand over the wavefront.  Each register's compare gives
 // a 64-lane mask in scalar registers; the scalar unit (one per CU, shared by
 // its four SIMDs) counts most of them, the vector unit counts the last EV
@@ -72,9 +94,30 @@ __device__ void topk_keys_write(const uint32_t (&key)[E], int cbase, int c0, int
                                 int64_t pos, int64_t capacity)
 {
     const int lane = threadIdx.x & 63;
-    uint32_t T = 0u, probe = 0x80000000u;
+    // Above the highest bit where two of the group's keys differ, every probe
+    // is decided without a count: all keys share those bits, so T has them
+    // too and no key exceeds T there.  The search starts at that bit.
+    uint32_t a = ~0u, o = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int col = cbase + e * 64 + lane;
+        a &= ((col >= c0) & (col < c1)) ? key[e] : ~0u;
+        o |= key[e];                            // 0 outside the group
+    }
+    wave_and_or(a, o);
+    const uint32_t dx = a ^ o;
+    uint32_t T, probe;
     int above = 0, cnt;
-    for (;;) {
+    if (dx == 0u) {                             // all keys equal: the first kk columns
+        T = a;
+        probe = 0u;
+        cnt = c1 - c0;
+    } else {
+        const int h = 31 - __builtin_clz(dx);
+        T = a & ~((2u << h) - 1u);
+        probe = 1u << h;
+    }
+    while (probe != 0u) {
         const uint32_t cand = __builtin_amdgcn_readfirstlane(T | probe);
         cnt = count_at_least<E>(key, cand);
         const bool take = cnt >= kk;
@@ -82,7 +125,6 @@ __device__ void topk_keys_write(const uint32_t (&key)[E], int cbase, int c0, int
         above = take ? above : cnt;
         probe = cnt == kk ? 0u : probe >> 1;
         asm("" : "+s"(probe));      // one scalar test ends the loop
-        if (probe == 0u) break;
     }
     // keys equal to T to keep, lowest columns first (all of them when exact)
     int need = cnt == kk ? 0x7fffffff : kk - above;
