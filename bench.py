@@ -335,26 +335,32 @@ def main():
     actual_flop = flop_pair * kept_pairs
     dense_flop = 4.0 * N * N * D * B * H
 
-    # timed region: K steps; events on the launch stream mark the start of the
-    # step, the boundary between the layout parts, and the forward
+    # timed region: K steps; events on the launch stream mark the boundary
+    # between the layout parts, the start and the end of the forward, and the
+    # end of the step (a step starts where the previous one ended: no event
+    # is recorded twice at one point of the stream)
     def new_ev():
         return torch.cuda.Event(enable_timing=True)
     ev = [[new_ev() for _ in range(len(layout_parts) + 3)] for _ in range(args.steps)]
-    t0, t1 = new_ev(), new_ev()
+    t0 = new_ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
+    prev = t0
     for s in range(args.steps):
         e = ev[s]
-        e[0].record(stream)
+        e[0] = prev
         layout(mark=lambda: e[1].record(stream))
         e[-3].record(stream)
         forward()
         e[-2].record(stream)
         if post is not None:
             post()
-        e[-1].record(stream)
-    t1.record(stream)
+            e[-1].record(stream)
+        else:
+            e[-1] = e[-2]
+        prev = e[-1]
+    t1 = prev
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
