@@ -47,11 +47,12 @@ __device__ __forceinline__ void wave_and_or(uint32_t &a, uint32_t &o)
 }
 
 // Number of keys >= cand over the wavefront.  Each register's compare gives
-// a 64-lane mask in scalar registers; the scalar unit (one per CU, shared by
-// its four SIMDs) counts most of them, the vector unit counts the last EV
-// (v_bcnt of the two mask halves into a lane-uniform sum), so that the two
-// issue ports split the work of a search round; a group of one or two
-// registers is counted by the scalar unit alone (shorter dependency chain).
+// a 64-lane mask in scalar registers; for a group of four or more registers
+// the scalar unit (one per CU, shared by its four SIMDs) counts half of the
+// masks and the vector unit the other half (v_bcnt of the two mask halves
+// into a lane-uniform sum), so that the two issue ports split the work of a
+// search round; one or two registers are counted by the scalar unit alone
+// (a shorter dependency chain).
 template <int E>
 __device__ __forceinline__ int count_at_least(const uint32_t (&key)[E], uint32_t cand)
 {
