@@ -325,6 +325,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 2) void bwd_dq_kernel(const BwdPara
             uint16_t *Kc = smem + (t & 1) * 2 * Sh::TILE, *Vc = Kc + Sh::TILE;
             bool vnxt = false;
             int knxt = 0;
+            wait_tile_copies();
             __syncthreads();   // tile t in LDS; buffer (t+1)&1 free
             if (t + 1 < T) {
                 knxt = key0(t + 1, vnxt);
@@ -614,6 +615,7 @@ __global__ __launch_bounds__(2 * BETA / 32 * 64, 2) void bwd_dkdv_kernel(const B
         bw_load_rows<BETA, D, G::NT, BETA>(Vt, vrs, p.v.sn, j * BETA, p.N, tid, nat, p.nb);
         load(0);
         for (int t = 0; t < T; ++t) {
+            wait_tile_copies();
             __syncthreads();                  // sub-tile t in LDS; buffer (t+1)&1 free
             if (t + 1 < T) load(t + 1);
             const uint16_t *Qc = buf(t), *Gc = Qc + G::QT;

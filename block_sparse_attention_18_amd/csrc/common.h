@@ -31,6 +31,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait for this wave's outstanding vector-memory operations, its
+// global-to-LDS tile copies among them.  Every wave calls it right before
+// the barrier that hands a copied tile to the other waves: the barrier does
+// not wait for copies in flight, and the compiler does not place this wait
+// by itself in every loop shape (without it, a wave could read a tile whose
+// copy by another wave had not landed).
+__device__ __forceinline__ void wait_tile_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -558,6 +558,7 @@ __global__ __launch_bounds__(BETA / 32 * 64, 4) void exact_scores_kernel(const E
 
         __syncthreads();   // the previous item is done with K0 / K1 and lse2
         exact_load_k<BETA, D>(K0, krs, p.k.sn, st.kdma, p.N, 0, wv, lane);
+        wait_tile_copies();
         __syncthreads();   // K(0) in LDS
         // sub-tile t in K[t&1]; step t copies K(t+1) into the other buffer.
         // Step 0 (no previous half to fold) is peeled.
@@ -567,14 +568,17 @@ __global__ __launch_bounds__(BETA / 32 * 64, 4) void exact_scores_kernel(const E
         exact_mask_half(0, 0, p.N, lane, sa);
         exact_qk_half<BETA, D>(K0, 1, st, sb);
         exact_fold_commit<BETA, D>(exact_fold_sum<BETA, D>(sa, p.scale_log2, st), sa, p.scale_log2, st);
+        wait_tile_copies();
         __syncthreads();
         for (int t = 1; t < T; t += 2) {
             exact_step<BETA, D>(K1, K0, t + 1 < T, (t + 1) * 64, t * 64, ((t - 1) % Sh::SUB) == Sh::SUB - 1,
                                 (t - 1) / Sh::SUB, krs, p, slot, wv, lane, st, sa, sb);
+            wait_tile_copies();
             __syncthreads();
             if (t + 1 >= T) break;
             exact_step<BETA, D>(K0, K1, t + 2 < T, (t + 2) * 64, (t + 1) * 64, (t % Sh::SUB) == Sh::SUB - 1,
                                 t / Sh::SUB, krs, p, slot, wv, lane, st, sa, sb);
+            wait_tile_copies();
             __syncthreads();
         }
         // half 1 of the last sub-tile, then the last key block

@@ -134,6 +134,30 @@ def test_backward_full_g1_workload_sampled_rows_and_sums(stride):
     assert dk_sum.max() <= 2e-3 and dv_err.max() <= 2e-3
 
 
+def test_backward_full_g1_workload_is_deterministic():
+    """The full G1 natural-order backward three times on the same inputs:
+    the gradients agree bit for bit.  (Each tile copy must have landed in LDS
+    before the barrier that hands the tile to the other waves; a missing
+    wait there once left dQ rows differing from run to run at this size.)"""
+    wl = synth.WORKLOADS["G1"]
+    x = synth.make_inputs(wl)
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    nb = bsa.neighborhood(wl.text_len, wl.nb_grid, wl.nb_tile, wl.nb_window, wl.nb_stride)
+    g = synth.random_qkv(B, H, N, D, seed=1225)[0]
+    _log("nb backward full G1: determinism over three runs")
+    qd, kd, vd, gd = (to_dev_bf16(a) for a in (x["q"], x["k"], x["v"], g))
+    rp, ci, fl = bsa.build_neighborhood_layout(B, H, nb, device=dev())
+    O, L = bsa.forward_neighborhood(qd, kd, vd, rp, ci, fl, nb, natural=True)
+    runs = []
+    for _ in range(3):
+        got = bsa.backward_neighborhood(qd, kd, vd, O, gd, rp, ci, fl, nb, L, natural=True)
+        torch.cuda.synchronize()
+        runs.append([bf16_bits(t) for t in got])
+    for r in (1, 2):
+        for name, a, b in zip(("dQ", "dK", "dV"), runs[0], runs[r]):
+            np.testing.assert_array_equal(a, b, err_msg=f"{name}, run {r} against run 0")
+
+
 @pytest.mark.parametrize("T,grid,tile,window,stride,D", GEOMS)
 def test_natural_order_backward_equals_the_permuted_path(T, grid, tile, window, stride, D):
     """bsa_backward_neighborhood_natural takes natural-order Q, K, V, O, dO and
